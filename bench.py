@@ -1,0 +1,331 @@
+#!/usr/bin/env python3
+"""Benchmark of one decode step over a paged KV cache on one MI355X.
+
+A step is one pass of the whole path over one batch: copy_blocks (when the
+workload has copy-on-write pairs), reshape_and_cache of the new tokens (when
+it has any), then pa_decode.  Inputs are generated on the device before the
+timed region.  The headline workload is the LLaMA-13B-shaped layer: 128
+sequences at context 2048, 40 heads, head_dim 128, block size 16, bf16, with
+128 new tokens stored through a shuffled slot mapping.
+
+Printed: one JSON line with tokens/s per layer (value), the decode kernel's
+roofline (algorithmic HBM bytes / measured launch time against 8 TB/s), the
+oracle timed on the host cores on a bounded sample (cpu_baseline), and the
+other workloads' figures under "workloads".
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+METRIC = "paged-attn decode tokens/s per layer + achieved HBM GB/s (% of peak), 1 GPU"
+PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "decode_traffic.json")
+KERNEL_SRC = os.path.join(HERE, "paged_kv_cache_321_amd", "csrc", "pa_kernels.hip")
+
+DESCRIPTION = {
+    "llama13b": "LLaMA-13B-shaped layer decode: 128 seqs x ctx 2048, H=Hkv=40, D=128, BS=16, bf16, "
+                "reshape_and_cache of 128 new tokens + pa_decode",
+    "llama7b": "LLaMA-7B-shaped layer decode: 64 seqs, ctx U[128,2048], H=Hkv=32, D=128, BS=16, bf16",
+    "gqa70b": "GQA 70B-shaped long-context decode: 16 seqs x ctx 32768, H=64, Hkv=8, D=128, BS=32, bf16",
+    "beam": "beam decode with copy-on-write: 32 groups x 4 beams, shared 1024-token prefix + tails "
+            "U[1,256], H=32, Hkv=8, D=128, BS=16, bf16; copy_blocks + reshape_and_cache + pa_decode",
+    "tiny": "tiny paged decode: 4 seqs ctx {1,17,33,100}, H=Hkv=4, D=64, BS=16, fp32",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama13b", choices=sorted(DESCRIPTION))
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--others", default="llama7b,gqa70b,beam",
+                    help="comma list of extra workloads to report ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target wall time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for counter scaling)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(plan, spec) -> int:
+    """K and V read once + q read + out written + block-table entries + context lengths."""
+    e = 4 if spec.dtype == "f32" else 2
+    ctx = [int(c) for c in plan.context_lens]
+    kv = sum(2 * spec.num_kv_heads * c * spec.head_dim * e for c in ctx)
+    qo = 2 * len(ctx) * spec.num_heads * spec.head_dim * e
+    table = 4 * sum(-(-c // plan.block_size) for c in ctx)
+    return kv + qo + table + 4 * len(ctx)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from rocprofv3 counters, if taken on this kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def run_workload(name, steps, warmup, partition_tokens, flush=False):
+    import torch
+    from paged_kv_cache_321_amd import binding
+    from paged_kv_cache_321_amd import workloads as wl
+
+    x = wl.make_inputs(name, device="cuda", poison=False)
+    spec, plan = x.spec, x.plan
+    out = torch.empty_like(x.q)
+    code = binding.PA_F32 if spec.dtype == "f32" else binding.PA_BF16
+    ws_bytes = binding.pa_decode_workspace_size(plan.num_seqs, spec.num_heads, spec.num_kv_heads,
+                                                spec.head_dim, plan.block_size,
+                                                plan.max_context_len, code, partition_tokens)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if flush else None
+    stream = torch.cuda.current_stream()
+    has_pairs = plan.block_pairs.shape[0] > 0
+    has_tokens = plan.slot_mapping.shape[0] > 0
+
+    def step(ev=None):
+        if has_pairs:
+            binding.pa_copy_blocks(x.k_cache, x.v_cache, x.block_pairs, stream=stream)
+        if has_tokens:
+            binding.pa_reshape_and_cache(x.key, x.value, x.k_cache, x.v_cache, x.slot_mapping,
+                                         stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        binding.pa_decode(out, x.q, x.k_cache, x.v_cache, x.block_tables, x.context_lens,
+                          x.scale, plan.max_context_len, partition_tokens=partition_tokens,
+                          workspace=ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+    wall = 0.0
+    if flush:
+        # Cold cache: the scratch write between steps evicts the 256 MiB MALL;
+        # only the step itself (between the events) is timed.
+        for i in range(steps):
+            scratch.fill_(i & 0xFF)
+            events[i][2].record(stream)
+            step((events[i][0], events[i][1]))
+            events[i][3].record(stream)
+        torch.cuda.synchronize()
+        step_ms = [a[2].elapsed_time(a[3]) for a in events]
+        ms_per_step = sum(step_ms) / steps
+    else:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        events[0][2].record(stream)
+        for i in range(steps):
+            step((events[i][0], events[i][1]))
+        events[-1][3].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms_per_step = events[0][2].elapsed_time(events[-1][3]) / steps
+    decode_ms = [a[0].elapsed_time(a[1]) for a in events]
+    decode_ms.sort()
+    avg_decode_ms = sum(decode_ms) / len(decode_ms)
+    med_decode_ms = decode_ms[len(decode_ms) // 2]
+    nbytes = algorithmic_bytes(plan, spec)
+    res = {
+        "workload": name,
+        "description": DESCRIPTION[name],
+        "num_seqs": plan.num_seqs,
+        "total_context_tokens": int(sum(int(c) for c in plan.context_lens)),
+        "ms_per_step": ms_per_step,
+        "wall_ms_per_step": wall * 1e3 / steps if wall else None,
+        "tokens_per_s": plan.num_seqs / (ms_per_step / 1e3),
+        "decode_avg_us": avg_decode_ms * 1e3,
+        "decode_median_us": med_decode_ms * 1e3,
+        "decode_tokens_per_s": plan.num_seqs / (avg_decode_ms / 1e3),
+        "decode_algorithmic_bytes": nbytes,
+        "decode_GBps": nbytes / (avg_decode_ms / 1e3) / 1e9,
+        "decode_frac_of_peak": nbytes / (avg_decode_ms / 1e3) / 1e9 / PEAK_GBPS,
+        "copy_pairs": int(plan.block_pairs.shape[0]),
+        "new_tokens": int(plan.slot_mapping.shape[0]),
+        "partition_tokens": partition_tokens,
+        "cache": "cold (MALL flushed between steps)" if flush else "warm",
+    }
+    del x, out, ws, scratch
+    torch.cuda.empty_cache()
+    return res, spec, plan
+
+
+def cpu_baseline(name, target_s):
+    """The oracle, single-threaded, on a bounded sample of the workload."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+    import oracle.paged_attention as op
+    from paged_kv_cache_321_amd import workloads as wl
+    from paged_kv_cache_321_amd.workloads import to_host_numpy
+
+    x = wl.make_inputs(name, device="cuda", poison=False)
+    plan, spec = x.plan, x.spec
+    bs = plan.block_size
+    order = list(range(plan.num_seqs))
+    done = 0
+    t_total = 0.0
+    with threadpool_limits(limits=1):
+        for s in order:
+            nb = -(-int(plan.context_lens[s]) // bs)
+            ids = [int(b) for b in plan.block_tables[s][:nb]]
+            idx = torch.tensor(ids, dtype=torch.long, device="cuda")
+            kc = to_host_numpy(x.k_cache.index_select(0, idx)).copy()
+            vc = to_host_numpy(x.v_cache.index_select(0, idx)).copy()
+            q = to_host_numpy(x.q[s:s + 1])
+            table = np.arange(nb, dtype=np.int32)[None]
+            ctx = plan.context_lens[s:s + 1]
+            t0 = time.perf_counter()
+            # The oracle's step for this sequence: store its new token (if any), decode.
+            tok = np.nonzero(plan.new_token_seqs == s)[0]
+            if len(tok):
+                pos = int(ctx[0]) - 1
+                slot = np.array([(pos // bs) * bs + pos % bs], dtype=np.int64)
+                op.reshape_and_cache(to_host_numpy(x.key[tok[0]:tok[0] + 1]),
+                                     to_host_numpy(x.value[tok[0]:tok[0] + 1]), kc, vc, slot)
+            op.decode(q, kc, vc, table, ctx, x.scale, spec.dtype)
+            t_total += time.perf_counter() - t0
+            done += 1
+            if t_total >= target_s:
+                break
+    del x
+    torch.cuda.empty_cache()
+    tokens = int(sum(int(plan.context_lens[s]) for s in order[:done]))
+    return {
+        "value": done / t_total,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} of {plan.num_seqs} sequences of the {name} workload "
+                  f"({tokens} context tokens), fp64 NumPy oracle, one BLAS thread, "
+                  f"{t_total:.1f} s",
+        "seconds": t_total,
+        "host_cpus_available": len(os.sched_getaffinity(0)),
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 1 GiB, for scaling the HBM counters."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "launches": 3}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the decode path needs no collective and is measured at N=1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    head, spec, plan = run_workload(args.workload, args.steps, args.warmup, args.partition_tokens)
+    others = []
+    for name in [n for n in args.others.split(",") if n and n != args.workload]:
+        r, _, _ = run_workload(name, args.steps, args.warmup, args.partition_tokens)
+        others.append(r)
+        if name == "beam":
+            r2, _, _ = run_workload(name, args.steps, args.warmup, args.partition_tokens, flush=True)
+            others.append(r2)
+
+    traffic = measured_traffic(args.workload)
+    roof = {
+        "bound": "hbm",
+        "kernel": "pa_decode (decode_partition_kernel; one launch per step at this shape)",
+        "achieved": head["decode_GBps"],
+        "peak": PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": head["decode_GBps"] / PEAK_GBPS,
+        "traffic": traffic,
+        "algorithmic_bytes_per_launch": head["decode_algorithmic_bytes"],
+        "avg_launch_us": head["decode_avg_us"],
+    }
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload, args.cpu_seconds)
+    line = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if spec.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) K/V/Q, shuffled physical blocks; no weights)",
+        "config": {
+            "workload": DESCRIPTION[args.workload],
+            "num_seqs": plan.num_seqs,
+            "context_len": plan.max_context_len,
+            "num_heads": spec.num_heads,
+            "num_kv_heads": spec.num_kv_heads,
+            "head_dim": spec.head_dim,
+            "block_size": plan.block_size,
+            "num_blocks": plan.num_blocks,
+            "new_tokens": head["new_tokens"],
+            "parallelism": "single GPU",
+        },
+        "decode": {k: head[k] for k in ("decode_avg_us", "decode_median_us", "decode_tokens_per_s",
+                                        "decode_GBps", "decode_frac_of_peak")},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "workloads": others,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

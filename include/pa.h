@@ -1,0 +1,166 @@
+/*
+ * pa.h -- C ABI of libpa.so: decode attention over a paged KV cache on AMD
+ * MI355X (gfx950).
+ *
+ * What is computed comes from these pages:
+ *  [tbr8]     "详解vLLM推理引擎架构：PagedAttention原理与LLM高效部署实践"
+ *             (tbr8.org/?p=10846): "PagedAttention 的核心思想" (K/V split into
+ *             fixed-size blocks of 16 or 32 tokens, reached through a per-sequence
+ *             block table) and "Copy-on-Write 与内存共享" (a shared block is
+ *             copied to a fresh one before it is written).
+ *  [luoboask] "vLLM 深度解读" (luoboask.github.io/fde-learning/opensource/vllm/):
+ *             section 3 "PagedAttention CUDA Kernel" (one query per sequence and
+ *             head; scores scale * q.k over every context token found through the
+ *             block table; softmax; weighted sum of V), section 7 (each new token's
+ *             K/V is stored into the cache, then paged attention runs).
+ *
+ * Layouts (row-major, element type T = float or bf16, the same T for every
+ * floating-point buffer of one call):
+ *   q, out          [num_seqs, num_heads, head_dim]
+ *   key, value      [num_tokens, num_kv_heads, head_dim]
+ *   k_cache, v_cache[num_blocks, num_kv_heads, block_size, head_dim]
+ *                   (one (block, kv_head) page is a contiguous block_size x
+ *                   head_dim tile)
+ *   block_tables    int32 [num_seqs, max_blocks_per_seq]; entry j of row s is
+ *                   the physical block holding tokens j*block_size ..
+ *                   (j+1)*block_size-1 of sequence s
+ *   context_lens    int32 [num_seqs]
+ *   slot_mapping    int64 [num_tokens]; slot = block * block_size + offset
+ *   block_pairs     int64 [num_pairs, 2]; (src, dst) physical block ids
+ *
+ * Conventions shared by every entry point:
+ *  - Every buffer pointer is a DEVICE pointer.  The caller owns every buffer;
+ *    the library allocates nothing and keeps no global state.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *    null stream).  A return of PA_OK means the kernels were enqueued.
+ *  - A negative return means nothing was launched, except PA_ERR_LAUNCH, which
+ *    reports a failure seen by hipGetLastError after the launch.
+ *  - Arguments are validated on the host before any HIP call, so every error
+ *    path below is reachable without a GPU.
+ *  - Values that live in device memory (table entries, context lengths, slots,
+ *    block pairs) cannot be checked on the host without a synchronisation.
+ *    Their preconditions are listed per call; the kernels bound-check them and
+ *    never access memory outside the buffers: a violated precondition gives the
+ *    documented result (a skipped write, or NaN in the affected output row),
+ *    not a fault.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL                        */
+  PA_ERR_SHAPE = -2,       /* a size is negative/zero where it must not be, or  */
+                           /* sizes are inconsistent (num_heads % num_kv_heads, */
+                           /* max_blocks_per_seq * block_size < max_context_len)*/
+  PA_ERR_DTYPE = -3,       /* dtype is not PA_F32 or PA_BF16                    */
+  PA_ERR_UNSUPPORTED = -4, /* head_dim not 64/128, block_size not 16/32, group  */
+                           /* size num_heads/num_kv_heads not 1/2/4/8, or a grid */
+                           /* dimension over the hardware limit                 */
+  PA_ERR_ALIGN = -5,       /* a floating-point buffer is not 16-byte aligned, or*/
+                           /* an index buffer is not aligned to its element size*/
+  PA_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required        */
+  PA_ERR_LAUNCH = -7       /* the HIP runtime reported an error after launch    */
+} pa_status;
+
+/*
+ * pa_reshape_and_cache -- store new tokens' K and V rows into their cache slots.
+ * ([luoboask] section 7: the K/V of each new token is written into the paged
+ * cache in place before attention.)
+ *
+ * For every token i with 0 <= slot_mapping[i] < num_blocks*block_size:
+ *   b = slot / block_size, o = slot % block_size, and for every kv head h
+ *   k_cache[b, h, o, :] = key[i, h, :]  and  v_cache[b, h, o, :] = value[i, h, :]
+ * (a bit-exact copy).  Negative slots mean "no write" (padding).  Slots at or
+ * past num_blocks*block_size violate the precondition and are skipped.
+ * Precondition: the non-negative slots are distinct (otherwise which token lands
+ * in a slot is unspecified).  num_tokens == 0 is a no-op.
+ */
+int pa_reshape_and_cache(const void* key, const void* value,
+                         void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping,
+                         int num_tokens, int num_blocks, int num_kv_heads,
+                         int block_size, int head_dim, int dtype, void* stream);
+
+/*
+ * pa_copy_blocks -- copy whole cache blocks, K and V, src -> dst.
+ * ([tbr8] "Copy-on-Write 与内存共享": before a block with more than one owner is
+ * written, its content is copied to a freshly allocated block.)
+ *
+ * For every pair p: k_cache[dst] = k_cache[src] and v_cache[dst] = v_cache[src]
+ * over all kv heads and all block_size slots (bit-exact).
+ * Preconditions: 0 <= src, dst < num_blocks (pairs outside are skipped); the dst
+ * ids are distinct and no dst is also a src (otherwise the result depends on
+ * the order of the copies).  num_pairs == 0 is a no-op.
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs,
+                   int num_pairs, int num_blocks, int num_kv_heads,
+                   int block_size, int head_dim, int dtype, void* stream);
+
+/*
+ * pa_decode_workspace_size -- bytes of device workspace pa_decode needs for
+ * these sizes.  Long contexts are cut into partitions of `partition_tokens`
+ * tokens (0 = the library's default for this shape); each partition leaves a
+ * partial result (running max, running sum, unnormalised output) in float32
+ * that a second kernel merges.  Returns 0 when no sequence can need more than
+ * one partition (then pa_decode accepts workspace == NULL), and (size_t)-1 for
+ * arguments pa_decode would reject.
+ */
+size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
+                                int head_dim, int block_size, int max_context_len,
+                                int dtype, int partition_tokens);
+
+/*
+ * pa_decode -- single-query decode attention over the paged cache.
+ * ([luoboask] section 3; [tbr8] "PagedAttention 的核心思想".)
+ *
+ * For every sequence s with L = context_lens[s] and every query head h, with
+ * G = num_heads / num_kv_heads and kv head g = h / G (contiguous groups):
+ *   K_t = k_cache[block_tables[s, t / block_size], g, t % block_size, :]
+ *   V_t likewise, for t = 0 .. L-1
+ *   w   = softmax_t(scale * dot(q[s, h, :], K_t))
+ *   out[s, h, :] = sum_t w_t * V_t
+ * accumulated in float32 and rounded to T (round-to-nearest-even for bf16).
+ * L == 0 gives an all-zero row.  Slots past L in the last block and table
+ * entries past ceil(L / block_size) are never read, so they may hold anything
+ * (NaN included).
+ *
+ * Arguments: max_blocks_per_seq is the row stride of block_tables;
+ * max_context_len is an upper bound on every context_lens[s] (it sizes the
+ * grid); num_blocks is the pool size; scale is usually 1/sqrt(head_dim);
+ * partition_tokens: 0 = default, else a multiple of block_size, at most
+ * 256 * block_size.  The way a sequence is partitioned depends only on its own
+ * length, so a sequence's output does not depend on the other sequences of the
+ * batch or on which physical blocks hold its pages.
+ * workspace: device buffer of at least pa_decode_workspace_size(...) bytes with
+ * 16-byte alignment (NULL allowed when that size is 0).
+ * Preconditions (device values): 0 <= context_lens[s] <= max_context_len and
+ * 0 <= block_tables[s, j] < num_blocks for j < ceil(L / block_size).  A row that
+ * breaks them is written as NaN instead of being computed.
+ */
+int pa_decode(void* out, const void* q,
+              const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, int max_blocks_per_seq,
+              const int32_t* context_lens,
+              int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+              int block_size, int num_blocks, int max_context_len,
+              float scale, int dtype, int partition_tokens,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* pa_status_string -- static, human-readable name of a status code. */
+const char* pa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

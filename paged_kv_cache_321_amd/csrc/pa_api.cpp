@@ -1,0 +1,184 @@
+// C entry points of libpa.so: argument validation, workspace carving and
+// kernel dispatch.  Every check here runs on the host before any HIP call, so
+// each error path is reachable without a GPU.  Semantics are documented in
+// include/pa.h.
+#include "pa.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace {
+
+constexpr int kMaxGridYZ = 65535;
+
+int elem_bytes(int dtype) { return dtype == PA_F32 ? 4 : 2; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_head_dim(int d) { return d == 64 || d == 128; }
+bool supported_block_size(int bs) { return bs == 16 || bs == 32; }
+bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+int cache_shape_status(int num_blocks, int num_kv_heads, int block_size, int head_dim, int dtype) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_DTYPE;
+  if (num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0 || head_dim <= 0) return PA_ERR_SHAPE;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+// Resolved partition length, or a negative status.
+int resolve_partition(int partition_tokens, int dtype, int head_dim, int block_size, int group) {
+  if (partition_tokens == 0) return pa::default_partition_tokens(dtype, head_dim, block_size, group);
+  if (partition_tokens < 0 || partition_tokens % block_size != 0) return PA_ERR_SHAPE;
+  if (partition_tokens / block_size > pa::kMaxPagesPerPartition) return PA_ERR_UNSUPPORTED;
+  return partition_tokens;
+}
+
+struct DecodeSizes {
+  int status;
+  int partition_tokens;
+  int max_parts;
+  size_t ml_bytes;   // offset of the accumulator area, 256-byte aligned
+  size_t total;      // 0 when a single partition always suffices
+};
+
+DecodeSizes decode_sizes(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                         int max_context_len, int dtype, int partition_tokens) {
+  DecodeSizes z{PA_OK, 0, 1, 0, 0};
+  if (dtype != PA_F32 && dtype != PA_BF16) { z.status = PA_ERR_DTYPE; return z; }
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_context_len < 0) {
+    z.status = PA_ERR_SHAPE;
+    return z;
+  }
+  if (num_heads % num_kv_heads != 0) { z.status = PA_ERR_SHAPE; return z; }
+  const int group = num_heads / num_kv_heads;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size) || !supported_group(group)) {
+    z.status = PA_ERR_UNSUPPORTED;
+    return z;
+  }
+  const int pt = resolve_partition(partition_tokens, dtype, head_dim, block_size, group);
+  if (pt < 0) { z.status = pt; return z; }
+  z.partition_tokens = pt;
+  z.max_parts = max_context_len <= pt ? 1 : (max_context_len + pt - 1) / pt;
+  if (z.max_parts > 1) {
+    const uint64_t rows = (uint64_t)num_seqs * (uint64_t)num_heads * (uint64_t)z.max_parts;
+    const uint64_t ml = (rows * 2 * sizeof(float) + 255) / 256 * 256;
+    z.ml_bytes = (size_t)ml;
+    z.total = (size_t)(ml + rows * (uint64_t)head_dim * sizeof(float));
+  }
+  return z;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: inconsistent or invalid sizes";
+    case PA_ERR_DTYPE: return "PA_ERR_DTYPE: dtype must be PA_F32 or PA_BF16";
+    case PA_ERR_UNSUPPORTED:
+      return "PA_ERR_UNSUPPORTED: head_dim must be 64/128, block_size 16/32, heads per kv head "
+             "1/2/4/8, grid within limits";
+    case PA_ERR_ALIGN: return "PA_ERR_ALIGN: buffer not aligned (16 bytes for data, element size for indices)";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: HIP reported an error after the launch";
+    default: return "unknown pa status";
+  }
+}
+
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int num_tokens, int num_blocks, int num_kv_heads,
+                         int block_size, int head_dim, int dtype, void* stream) {
+  int st = cache_shape_status(num_blocks, num_kv_heads, block_size, head_dim, dtype);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  if (!k_cache || !v_cache) return PA_ERR_NULL;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(slot_mapping, 8))
+    return PA_ERR_ALIGN;
+  const int64_t items = (int64_t)num_tokens * num_kv_heads * head_dim * elem_bytes(dtype) / 16;
+  if ((items + 255) / 256 > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+  pa::ReshapeLaunch a{key, value, k_cache, v_cache, slot_mapping, num_tokens, num_blocks,
+                      num_kv_heads, block_size, head_dim, elem_bytes(dtype),
+                      static_cast<hipStream_t>(stream)};
+  return pa::launch_reshape_and_cache(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs, int num_pairs,
+                   int num_blocks, int num_kv_heads, int block_size, int head_dim, int dtype,
+                   void* stream) {
+  int st = cache_shape_status(num_blocks, num_kv_heads, block_size, head_dim, dtype);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return PA_ERR_SHAPE;
+  if (!k_cache || !v_cache) return PA_ERR_NULL;
+  if (num_pairs == 0) return PA_OK;
+  if (!block_pairs) return PA_ERR_NULL;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_pairs, 8)) return PA_ERR_ALIGN;
+  pa::CopyLaunch a{k_cache, v_cache, block_pairs, num_pairs, num_blocks, num_kv_heads,
+                   block_size, head_dim, elem_bytes(dtype), static_cast<hipStream_t>(stream)};
+  return pa::launch_copy_blocks(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                int block_size, int max_context_len, int dtype, int partition_tokens) {
+  const DecodeSizes z = decode_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                     max_context_len, dtype, partition_tokens);
+  return z.status == PA_OK ? z.total : (size_t)-1;
+}
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+              int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+              int num_blocks, int max_context_len, float scale, int dtype, int partition_tokens,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  const DecodeSizes z = decode_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                     max_context_len, dtype, partition_tokens);
+  if (z.status != PA_OK) return z.status;
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size < max_context_len) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return PA_ERR_ALIGN;
+  if (num_seqs > kMaxGridYZ || num_kv_heads > kMaxGridYZ || num_heads > kMaxGridYZ)
+    return PA_ERR_UNSUPPORTED;
+  if (z.total > 0) {
+    if (!workspace || workspace_bytes < z.total) return PA_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
+  }
+  char* ws = static_cast<char*>(workspace);
+  pa::DecodeLaunch a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.scale = scale;
+  a.dtype = dtype;
+  a.partition_tokens = z.partition_tokens;
+  a.max_parts = z.max_parts;
+  a.ws_ml = z.total ? reinterpret_cast<float*>(ws) : nullptr;
+  a.ws_acc = z.total ? reinterpret_cast<float*>(ws + z.ml_bytes) : nullptr;
+  a.stream = static_cast<hipStream_t>(stream);
+  return pa::launch_decode(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // extern "C"

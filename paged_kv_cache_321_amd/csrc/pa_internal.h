@@ -1,0 +1,63 @@
+// Internal interface between the validating C entry points (pa_api.cpp) and
+// the kernel launchers (pa_kernels.hip).  Not part of the public ABI.
+#ifndef PA_INTERNAL_H_
+#define PA_INTERNAL_H_
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Waves per decode workgroup.  The pages of one partition are dealt out to
+// the waves round-robin; each wave keeps one page id per lane, so a partition
+// holds at most kWaves * 64 pages.
+constexpr int kWaves = 4;
+constexpr int kMaxPagesPerPartition = kWaves * 64;
+
+struct DecodeLaunch {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  const int32_t* context_lens;
+  int num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks;
+  int max_context_len;
+  float scale;
+  int dtype;
+  int partition_tokens;  // resolved, > 0
+  int max_parts;         // ceil(max_context_len / partition_tokens), >= 1
+  float* ws_ml;          // [S, H, max_parts, 2] (running max, running sum); null if max_parts == 1
+  float* ws_acc;         // [S, H, max_parts, D] unnormalised outputs; null if max_parts == 1
+  hipStream_t stream;
+};
+
+struct ReshapeLaunch {
+  const void* key;
+  const void* value;
+  void* k_cache;
+  void* v_cache;
+  const int64_t* slot_mapping;
+  int num_tokens, num_blocks, num_kv_heads, block_size, head_dim, elem_bytes;
+  hipStream_t stream;
+};
+
+struct CopyLaunch {
+  void* k_cache;
+  void* v_cache;
+  const int64_t* block_pairs;
+  int num_pairs, num_blocks, num_kv_heads, block_size, head_dim, elem_bytes;
+  hipStream_t stream;
+};
+
+// Default partition length (tokens) for a shape; a multiple of block_size.
+int default_partition_tokens(int dtype, int head_dim, int block_size, int group);
+
+hipError_t launch_decode(const DecodeLaunch& a);
+hipError_t launch_reshape_and_cache(const ReshapeLaunch& a);
+hipError_t launch_copy_blocks(const CopyLaunch& a);
+
+}  // namespace pa
+
+#endif  // PA_INTERNAL_H_

@@ -8,3 +8,15 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an AMD MI355X (gfx950) GPU and the built libpa.so")
+
+
+import pytest  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name each GPU case on stderr (unbuffered) before it touches the GPU."""
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.__stderr__.write(f"\n[gpu-case] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield
