@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libpa.so")
 ARCH = "gfx950"
 
-SOURCES = ["pa_api.cpp", "pa_kernels.hip"]
+SOURCES = ["pa_api.cpp", "pa_cache.hip", "pa_decode.hip", "pa_decode_valu.hip",
+           "pa_decode_mfma.hip"]
 
 # Packed-fp32 VALU ops are switched off for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -41,21 +42,30 @@ def _run(cmd):
     return proc.stdout
 
 
+def _compile_cmd(cc: str, src: str, obj: str):
+    cmd = [cc, *COMMON_FLAGS]
+    if src.endswith(".hip"):
+        cmd += ["-x", "hip", *DEVICE_FLAGS]
+    return cmd + ["-c", os.path.join(CSRC, src), "-o", obj]
+
+
 def build_library(verbose: bool = False) -> str:
-    """Compile every source and link libpa.so (atomically replaced)."""
+    """Compile every source (in parallel) and link libpa.so (atomically replaced)."""
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="pa_build_") as tmp:
-        objs = []
-        for src in SOURCES:
-            obj = os.path.join(tmp, src + ".o")
-            cmd = [cc, *COMMON_FLAGS]
-            if src.endswith(".hip"):
-                cmd += ["-x", "hip", *DEVICE_FLAGS]
-            cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
-            out = _run(cmd)
-            if verbose and out.strip():
+        objs = [os.path.join(tmp, src + ".o") for src in SOURCES]
+        procs = [(src, subprocess.Popen(_compile_cmd(cc, src, obj), stdout=subprocess.PIPE,
+                                        stderr=subprocess.STDOUT, text=True))
+                 for src, obj in zip(SOURCES, objs)]
+        failed = []
+        for src, proc in procs:
+            out, _ = proc.communicate()
+            if proc.returncode != 0:
+                failed.append(f"{src}:\n{out}")
+            elif verbose and out.strip():
                 print(out)
-            objs.append(obj)
+        if failed:
+            raise RuntimeError("build failed:\n" + "\n".join(failed))
         tmp_lib = os.path.join(tmp, "libpa.so")
         _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib])
         staged = LIB_PATH + ".tmp"

@@ -1,0 +1,295 @@
+// Decode partition kernel on the matrix cores, for bf16 caches where several
+// query heads share a kv head (grouped-query attention, G = H / Hkv > 1).
+//
+// What is computed is the same as the vector kernel ("vLLM 深度解读",
+// luoboask.github.io, section 3 "PagedAttention CUDA Kernel"): per query head,
+// softmax over scale * q.k of every context token reached through the block
+// table, then the weighted sum of V.  With grouping, one kv page serves G
+// query heads, so the two products become dense tiles:
+//
+//   S^T [tokens x heads] = K_page [tokens x D] . Q_group^T [D x heads]
+//   O^T [D x heads]     += V_page^T [D x tokens] . P^T [tokens x heads]
+//
+// both on v_mfma_f32_16x16x32_bf16 (16x16x16 for 16-token pages), with the
+// head dimension of the tile padded to 16 (zero query rows).
+//
+// Operand layouts (checked on gfx950): A lane i holds row i%16, k = 8*(i/16)+j;
+// B lane i holds column i%16, the same k; the f32 result lane i holds rows
+// 4*(i/16)+j of column i%16.  Therefore
+//  * K goes from HBM straight into the A operand (lane i reads 16 bytes of
+//    token i%16), no staging;
+//  * the S^T result already sits where the B operand of the PV product wants
+//    P^T (tokens along k in the same slots), after a round-to-nearest-even
+//    cast to bf16 -- no data movement;
+//  * V is the one operand that needs a transpose: each wave writes its page
+//    to LDS (rows swizzled so the transposed reads hit distinct banks, rows
+//    past the context written as zeros so NaN in unused slots can never reach
+//    the product) and reads V^T back as the A operand.
+// The online softmax runs on the S^T tile: each lane holds 4 tokens of one
+// head per 16-token tile; the max over tokens takes two cross-lane steps.
+
+#include "pa_device.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Orders this wave's LDS writes before its later LDS reads (and the reverse)
+// as seen by the compiler; the LDS unit serves one wave's requests in order.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16_bits(lo)) | (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+}
+
+// 16-byte chunk c of LDS row `row` is stored at chunk c ^ swz(row).  Rows
+// 4 apart (the rows one transposed read touches) land 2 chunks apart, so the
+// four 32-byte segments of a read fall in distinct banks.
+__device__ __forceinline__ int swz(int row) { return 2 * ((row >> 2) & 3); }
+
+template <int D, int BS, int G>
+__global__ __launch_bounds__(kWaves * 64) void decode_partition_mfma_kernel(DecodeParams p) {
+  constexpr int NT = BS / 16;       // 16-token tiles per page
+  constexpr int NC = D / 32;        // 32-wide steps of the QK contraction
+  constexpr int NM = D / 16;        // 16-wide output tiles along head_dim
+  constexpr int ROWB = D * 2;       // bytes of one token row
+  constexpr int NCH = ROWB / 16;    // 16-byte chunks per row
+  constexpr int RPL = 64 / NCH;     // rows per row-contiguous wave load
+  constexpr int NV = BS / RPL;      // V loads per lane per page
+  constexpr int PAGEB = BS * ROWB;  // bytes of one page
+  constexpr int EPI = (kWaves * G * D + 2 * kWaves * G) * 4;
+  constexpr int SMEM = kWaves * PAGEB > EPI ? kWaves * PAGEB : EPI;
+  static_assert(G >= 2 && G <= 16 && NCH >= 8 && BS % RPL == 0, "tile shape");
+
+  const int part = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int s = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int g4 = lane >> 4;
+
+  const PartitionRange r = partition_range(p, s, part, wave, BS);
+  if (part >= r.nparts) return;  // uniform over the workgroup
+  const int tok1 = r.tok1;
+  const int nk = r.nk;
+  bool ids_bad;
+  const int my_id = load_page_ids(p, s, r, wave, lane, &ids_bad);
+  const bool bad = r.ctx_bad || ids_bad;
+
+  // B operand of S^T = K Q^T: lane holds Q[head l16][32c + 8 g4 .. +7]; zero
+  // for the padding heads l16 >= G.
+  bf16x8_t qb[NC];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) +
+                         ((int64_t)s * p.num_heads + (int64_t)kvh * G + (l16 < G ? l16 : 0)) * D + 8 * g4;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (l16 < G) v = *reinterpret_cast<const uint4*>(qp + 32 * c);
+      qb[c] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  f32x4_t acc[NM];  // O^T[d = 16 m + 4 g4 + j][head l16]
+#pragma unroll
+  for (int m = 0; m < NM; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -FLT_MAX;  // running max of head l16 (same in the 4 lanes of a head)
+  float l_run = 0.f;       // this lane's share of the running sum
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  unsigned char* vbuf = smem + wave * PAGEB;
+
+  const uint16_t* kc = static_cast<const uint16_t*>(p.k_cache) + (int64_t)kvh * BS * D;
+  const uint16_t* vc = static_cast<const uint16_t*>(p.v_cache) + (int64_t)kvh * BS * D;
+  const int k_off = l16 * D + 8 * g4;          // A operand: token l16, 8 elements at 8 g4
+  const int v_row = lane / NCH;                // row-contiguous V load
+  const int v_ch = lane % NCH;
+  const int v_off = v_row * D + v_ch * 8;
+
+  auto load_k = [&](int k, uint4 (&kr)[NT][NC]) {
+    const int64_t phys = __builtin_amdgcn_readlane(my_id, k);
+    const uint16_t* kp = kc + phys * p.block_stride + k_off;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kr[tt][c] = *reinterpret_cast<const uint4*>(kp + tt * 16 * D + 32 * c);
+  };
+  auto load_v = [&](int k, uint4 (&vr)[NV]) {
+    const int64_t phys = __builtin_amdgcn_readlane(my_id, k);
+    const uint16_t* vp = vc + phys * p.block_stride + v_off;
+#pragma unroll
+    for (int n = 0; n < NV; ++n) vr[n] = *reinterpret_cast<const uint4*>(vp + n * RPL * D);
+  };
+  auto stage_v = [&](int k, const uint4 (&vr)[NV]) {
+    const int t0 = (r.pg0 + wave + k * kWaves) * BS;
+    const bool full = t0 + BS <= tok1;
+    wave_lds_fence();
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      const int row = n * RPL + v_row;
+      uint4 v = vr[n];
+      if (!full && t0 + row >= tok1) v = make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(vbuf + row * ROWB + ((v_ch ^ swz(row)) << 4)) = v;
+    }
+    wave_lds_fence();
+  };
+  auto v_at = [&](int t, int d) -> uint16_t {
+    return *reinterpret_cast<const uint16_t*>(vbuf + t * ROWB + (((d >> 3) ^ swz(t)) << 4) + ((d & 7) << 1));
+  };
+
+  auto scores = [&](const uint4 (&kr)[NT][NC], f32x4_t (&st)[NT]) {
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      st[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        st[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[tt][c]), qb[c],
+                                                         st[tt], 0, 0, 0);
+    }
+  };
+
+  auto softmax_pv = [&](int k, const f32x4_t (&st)[NT]) {
+    const int t0 = (r.pg0 + wave + k * kWaves) * BS;
+    const bool full = t0 + BS <= tok1;
+    // Scores of token 16 tt + 4 g4 + j for head l16; masked past the context.
+    float sv[NT][4];
+    float mx = m_run;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool valid = full || (t0 + 16 * tt + 4 * g4 + j < tok1);
+        sv[tt][j] = valid ? st[tt][j] * p.scale_log2e : -__builtin_inff();
+        mx = fmaxf(mx, sv[tt][j]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float alpha = fast_exp2(m_run - mx);
+    m_run = mx;
+    float ps = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sv[tt][j] = fast_exp2(sv[tt][j] - mx);
+        ps += sv[tt][j];
+      }
+    l_run = l_run * alpha + ps;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) acc[m] *= alpha;
+
+    if constexpr (BS == 32) {
+      // P^T as the B operand: k slot j of lane group g4 is token 4 g4 + j
+      // (j < 4, first tile) or 16 + 4 g4 + j - 4 (second tile).
+      uint4 pbits;
+      pbits.x = pack_bf16x2(sv[0][0], sv[0][1]);
+      pbits.y = pack_bf16x2(sv[0][2], sv[0][3]);
+      pbits.z = pack_bf16x2(sv[1][0], sv[1][1]);
+      pbits.w = pack_bf16x2(sv[1][2], sv[1][3]);
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pbits);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const int d = 16 * m + l16;
+        uint4 vbits;
+        vbits.x = (uint32_t)v_at(4 * g4 + 0, d) | ((uint32_t)v_at(4 * g4 + 1, d) << 16);
+        vbits.y = (uint32_t)v_at(4 * g4 + 2, d) | ((uint32_t)v_at(4 * g4 + 3, d) << 16);
+        vbits.z = (uint32_t)v_at(16 + 4 * g4 + 0, d) | ((uint32_t)v_at(16 + 4 * g4 + 1, d) << 16);
+        vbits.w = (uint32_t)v_at(16 + 4 * g4 + 2, d) | ((uint32_t)v_at(16 + 4 * g4 + 3, d) << 16);
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vbits), pb, acc[m],
+                                                         0, 0, 0);
+      }
+    } else {
+      // 16-token pages: k slot j of lane group g4 is token 4 g4 + j.
+      uint2 pbits;
+      pbits.x = pack_bf16x2(sv[0][0], sv[0][1]);
+      pbits.y = pack_bf16x2(sv[0][2], sv[0][3]);
+      const s16x4_t pb = __builtin_bit_cast(s16x4_t, pbits);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const int d = 16 * m + l16;
+        uint2 vbits;
+        vbits.x = (uint32_t)v_at(4 * g4 + 0, d) | ((uint32_t)v_at(4 * g4 + 1, d) << 16);
+        vbits.y = (uint32_t)v_at(4 * g4 + 2, d) | ((uint32_t)v_at(4 * g4 + 3, d) << 16);
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, vbits), pb, acc[m],
+                                                           0, 0, 0);
+      }
+    }
+  };
+
+  // One K and one V register buffer: the next page's V is requested as soon
+  // as this page's V sits in LDS, the next K as soon as the QK products have
+  // consumed this page's K, so one page per wave is always in flight.
+  if (!bad && nk > 0) {
+    uint4 kr[NT][NC], vr[NV];
+    load_k(0, kr);
+    load_v(0, vr);
+    for (int k = 0; k < nk; ++k) {
+      stage_v(k, vr);
+      if (k + 1 < nk) load_v(k + 1, vr);
+      f32x4_t st[NT];
+      scores(kr, st);
+      if (k + 1 < nk) load_k(k + 1, kr);
+      softmax_pv(k, st);
+    }
+  }
+
+  // The four lanes of a head each hold a share of its running sum.
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+
+  __syncthreads();  // every wave is done with its page buffer: reuse the LDS
+  float* sm_acc = reinterpret_cast<float*>(smem);
+  float* sm_m = sm_acc + kWaves * G * D;
+  float* sm_l = sm_m + kWaves * G;
+  if (l16 < G) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm_acc[(wave * G + l16) * D + 16 * m + 4 * g4 + j] = acc[m][j];
+    if (g4 == 0) {
+      sm_m[wave * G + l16] = bad ? 0.f : m_run;
+      sm_l[wave * G + l16] = bad ? __builtin_nanf("") : l_run;
+    }
+  }
+  __syncthreads();
+  merge_waves_and_store<uint16_t, D, G>(p, sm_acc, sm_m, sm_l, s, kvh, part, r.nparts);
+}
+
+template <int D, int BS, int G>
+hipError_t launch_t(const DecodeLaunch& a, const DecodeParams& p) {
+  dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
+  hipLaunchKernelGGL((decode_partition_mfma_kernel<D, BS, G>), grid, dim3(kWaves * 64), 0, a.stream, p);
+  return hipGetLastError();
+}
+
+template <int D, int BS>
+hipError_t by_group(const DecodeLaunch& a, const DecodeParams& p) {
+  switch (a.num_heads / a.num_kv_heads) {
+    case 2: return launch_t<D, BS, 2>(a, p);
+    case 4: return launch_t<D, BS, 4>(a, p);
+    case 8: return launch_t<D, BS, 8>(a, p);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t by_block(const DecodeLaunch& a, const DecodeParams& p) {
+  return a.block_size == 16 ? by_group<D, 16>(a, p) : by_group<D, 32>(a, p);
+}
+
+}  // namespace
+
+hipError_t launch_partition_mfma(const DecodeLaunch& a, const DecodeParams& p) {
+  return a.head_dim == 64 ? by_block<64>(a, p) : by_block<128>(a, p);
+}
+
+}  // namespace pa

@@ -1,0 +1,164 @@
+// Device-side pieces shared by the decode kernels: element access, the
+// launch parameter block, the partition arithmetic and the workgroup epilogue
+// that merges the waves' online-softmax states.
+#ifndef PA_DEVICE_H_
+#define PA_DEVICE_H_
+
+#include <float.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// bf16 is handled as raw uint16_t bits: widening puts the 16 bits on top of a
+// binary32 word (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round-to-nearest-even binary32 -> bf16 bits (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<float> {
+  static constexpr int kVec = 4;  // elements per 16-byte load
+  __device__ static __forceinline__ void unpack(const uint4& r, float* f) {
+    f[0] = __uint_as_float(r.x);
+    f[1] = __uint_as_float(r.y);
+    f[2] = __uint_as_float(r.z);
+    f[3] = __uint_as_float(r.w);
+  }
+  __device__ static __forceinline__ void store(float* p, float v) { *p = v; }
+};
+
+template <>
+struct Elem<uint16_t> {
+  static constexpr int kVec = 8;
+  __device__ static __forceinline__ void unpack(const uint4& r, float* f) {
+    f[0] = bf16_lo(r.x);
+    f[1] = bf16_hi(r.x);
+    f[2] = bf16_lo(r.y);
+    f[3] = bf16_hi(r.y);
+    f[4] = bf16_lo(r.z);
+    f[5] = bf16_hi(r.z);
+    f[6] = bf16_lo(r.w);
+    f[7] = bf16_hi(r.w);
+  }
+  __device__ static __forceinline__ void store(uint16_t* p, float v) { *p = f32_to_bf16_bits(v); }
+};
+
+struct DecodeParams {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_ml;
+  float* ws_acc;
+  int64_t block_stride;  // elements between consecutive physical blocks
+  int max_blocks_per_seq;
+  int num_heads;
+  int num_blocks;
+  int max_context_len;
+  int partition_tokens;
+  int max_parts;
+  float scale_log2e;
+};
+
+__device__ __forceinline__ int parts_for(int ctx, int partition_tokens) {
+  return ctx <= partition_tokens ? 1 : (ctx + partition_tokens - 1) / partition_tokens;
+}
+
+// Where one workgroup's work lies: partition `part` of sequence `s`, its
+// token range [tok0, tok1) and the pages dealt to this wave.  A context
+// length outside [0, max_context_len] marks the row bad (written as NaN).
+struct PartitionRange {
+  int ctx, nparts, tok0, tok1, pg0, npg, nk;
+  bool ctx_bad;
+};
+
+__device__ __forceinline__ PartitionRange partition_range(const DecodeParams& p, int s, int part,
+                                                          int wave, int block_size) {
+  PartitionRange r;
+  r.ctx = p.context_lens[s];
+  r.ctx_bad = r.ctx < 0 || r.ctx > p.max_context_len;
+  r.nparts = r.ctx_bad ? 1 : parts_for(r.ctx, p.partition_tokens);
+  r.tok0 = part * p.partition_tokens;
+  r.tok1 = r.ctx_bad ? r.tok0 : min(r.ctx, r.tok0 + p.partition_tokens);
+  r.pg0 = r.tok0 / block_size;
+  r.npg = r.tok1 > r.tok0 ? (r.tok1 - r.tok0 + block_size - 1) / block_size : 0;
+  r.nk = r.npg > wave ? (r.npg - wave + kWaves - 1) / kWaves : 0;  // <= 64
+  return r;
+}
+
+// Physical ids of this wave's pages (page pg0 + wave + k*kWaves for lane k),
+// one per lane.  Ids outside [0, num_blocks) are replaced by 0 and reported.
+__device__ __forceinline__ int load_page_ids(const DecodeParams& p, int s, const PartitionRange& r,
+                                             int wave, int lane, bool* any_bad) {
+  int id = 0;
+  bool bad = false;
+  if (lane < r.nk) {
+    id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + r.pg0 + wave + lane * kWaves];
+    bad = id < 0 || id >= p.num_blocks;
+    if (bad) id = 0;
+  }
+  *any_bad = __any(bad);
+  return id;
+}
+
+// Epilogue: the kWaves partial states of each query head of the group sit in
+// LDS (sm_acc [kWaves][G][D], sm_m / sm_l [kWaves][G]); merge them with the
+// log-sum-exp rule and write either the final row (single partition) or the
+// partition's (max, sum, accumulator) triple to the workspace.
+template <typename T, int D, int G>
+__device__ __forceinline__ void merge_waves_and_store(const DecodeParams& p, const float* sm_acc,
+                                                      const float* sm_m, const float* sm_l, int s,
+                                                      int kvh, int part, int nparts) {
+  for (int idx = threadIdx.x; idx < G * D; idx += kWaves * 64) {
+    const int g = idx / D;
+    const int d = idx % D;
+    float mm = -FLT_MAX;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm_m[w * G + g]);
+    float ll = 0.f, aa = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float wt = fast_exp2(sm_m[w * G + g] - mm);
+      ll += sm_l[w * G + g] * wt;
+      aa += sm_acc[(w * G + g) * D + d] * wt;
+    }
+    const int64_t sh = (int64_t)s * p.num_heads + (int64_t)kvh * G + g;
+    if (nparts == 1) {
+      const float o = (ll == 0.f) ? 0.f : aa / ll;
+      Elem<T>::store(static_cast<T*>(p.out) + sh * D + d, o);
+    } else {
+      const int64_t slot = sh * p.max_parts + part;
+      p.ws_acc[slot * D + d] = aa;
+      if (d == 0) {
+        p.ws_ml[slot * 2] = mm;
+        p.ws_ml[slot * 2 + 1] = ll;
+      }
+    }
+  }
+}
+
+// Kernel launchers of the two decode-partition variants (one per file).
+hipError_t launch_partition_valu(const DecodeLaunch& a, const DecodeParams& p);
+hipError_t launch_partition_mfma(const DecodeLaunch& a, const DecodeParams& p);
+
+}  // namespace pa
+
+#endif  // PA_DEVICE_H_

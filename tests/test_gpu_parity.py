@@ -59,6 +59,9 @@ SHAPES = [
     (4, 4, 64, 16, "f32"), (4, 4, 64, 32, "f32"), (4, 2, 128, 16, "f32"), (8, 1, 128, 32, "f32"),
     (8, 8, 64, 16, "bf16"), (8, 4, 64, 32, "bf16"), (16, 4, 128, 16, "bf16"),
     (16, 2, 128, 32, "bf16"), (8, 8, 128, 32, "bf16"),
+    # grouped heads on the matrix-core path (bf16, group 2/4/8, both block sizes, both dims)
+    (16, 8, 64, 16, "bf16"), (32, 4, 64, 16, "bf16"), (8, 2, 128, 32, "bf16"),
+    (16, 8, 128, 16, "bf16"), (64, 8, 128, 32, "bf16"), (32, 8, 128, 16, "bf16"),
 ]
 
 
