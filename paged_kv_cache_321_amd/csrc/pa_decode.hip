@@ -14,25 +14,55 @@
 namespace pa {
 namespace {
 
+// One wave per (head, sequence).  Lanes own partitions when reading the
+// (max, sum) pairs, so those loads are issued together; the weights of each
+// chunk of 64 partitions go through LDS to the lanes that own output columns.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams p) {
+  constexpr int E = D / 64;  // output columns per lane
+  __shared__ float sw[64];
   const int h = blockIdx.x;
   const int s = blockIdx.y;
+  const int lane = threadIdx.x;
   const int ctx = p.context_lens[s];
   if (ctx < 0 || ctx > p.max_context_len) return;  // written as NaN by the partition kernel
   const int nparts = parts_for(ctx, p.partition_tokens);
   if (nparts <= 1) return;                          // written by the partition kernel
   const int64_t base = ((int64_t)s * p.num_heads + h) * p.max_parts;
-  const float* ml = p.ws_ml + base * 2;
+  const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + base;
   float mm = -FLT_MAX;
-  for (int q = 0; q < nparts; ++q) mm = fmaxf(mm, ml[2 * q]);
+  for (int q = lane; q < nparts; q += 64) mm = fmaxf(mm, ml[q].x);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off));
   float ll = 0.f;
-  for (int q = 0; q < nparts; ++q) ll += ml[2 * q + 1] * fast_exp2(ml[2 * q] - mm);
-  for (int d = threadIdx.x; d < D; d += 64) {
-    float aa = 0.f;
-    for (int q = 0; q < nparts; ++q) aa += p.ws_acc[(base + q) * D + d] * fast_exp2(ml[2 * q] - mm);
-    const float o = (ll == 0.f) ? 0.f : aa / ll;
-    Elem<T>::store(static_cast<T*>(p.out) + ((int64_t)s * p.num_heads + h) * D + d, o);
+  float aa[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) aa[e] = 0.f;
+  const float* acc = p.ws_acc + base * D + lane;
+  for (int q0 = 0; q0 < nparts; q0 += 64) {
+    const int q = q0 + lane;
+    float w = 0.f;
+    if (q < nparts) {
+      const float2 v = ml[q];
+      w = fast_exp2(v.x - mm);
+      ll += v.y * w;
+    }
+    __syncthreads();
+    sw[lane] = w;
+    __syncthreads();
+    const int n = min(64, nparts - q0);
+    for (int j = 0; j < n; ++j) {
+      const float wj = sw[j];
+#pragma unroll
+      for (int e = 0; e < E; ++e) aa[e] += acc[(int64_t)(q0 + j) * D + 64 * e] * wj;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ll += __shfl_xor(ll, off);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const float o = (ll == 0.f) ? 0.f : aa[e] / ll;
+    Elem<T>::store(static_cast<T*>(p.out) + ((int64_t)s * p.num_heads + h) * D + lane + 64 * e, o);
   }
 }
 
@@ -50,10 +80,14 @@ hipError_t launch_reduce(const DecodeLaunch& a, const DecodeParams& p) {
 
 static bool use_mfma_path(int dtype, int group) { return dtype == 1 && group >= 2; }
 
-int default_partition_tokens(int /*dtype*/, int /*head_dim*/, int block_size, int /*group*/) {
-  // 2048 tokens: 128 pages of 16 or 64 pages of 32 per workgroup.
-  const int t = 2048;
-  return t - t % block_size;
+int default_partition_tokens(int dtype, int /*head_dim*/, int block_size, int group) {
+  // Fixed lengths (never the batch size, so a sequence's result does not
+  // depend on the batch).  Vector path: 2048 tokens; matrix-core path: 4096
+  // tokens (fewer, longer workgroups measured faster on long GQA contexts).
+  const int t = use_mfma_path(dtype, group) ? 4096 : 2048;
+  const int cap = kMaxPagesPerPartition * block_size;
+  const int u = t < cap ? t : cap;
+  return u - u % block_size;
 }
 
 hipError_t launch_decode(const DecodeLaunch& a) {

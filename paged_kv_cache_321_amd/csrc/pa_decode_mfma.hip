@@ -26,7 +26,10 @@
 //    past the context written as zeros so NaN in unused slots can never reach
 //    the product) and reads V^T back as the A operand.
 // The online softmax runs on the S^T tile: each lane holds 4 tokens of one
-// head per 16-token tile; the max over tokens takes two cross-lane steps.
+// head per 16-token tile; the max over tokens takes two cross-lane steps.  The
+// reference max is moved lazily (only when exceeded by more than 2^8), which
+// keeps the accumulator rescale off the common path; numerator and
+// denominator share the same reference, so the ratio is unchanged.
 
 #include "pa_device.h"
 
@@ -121,13 +124,13 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partition_mfma_kernel(Deco
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) kr[tt][c] = *reinterpret_cast<const uint4*>(kp + tt * 16 * D + 32 * c);
+      for (int c = 0; c < NC; ++c) kr[tt][c] = load_stream16(kp + tt * 16 * D + 32 * c);
   };
   auto load_v = [&](int k, uint4 (&vr)[NV]) {
     const int64_t phys = __builtin_amdgcn_readlane(my_id, k);
     const uint16_t* vp = vc + phys * p.block_stride + v_off;
 #pragma unroll
-    for (int n = 0; n < NV; ++n) vr[n] = *reinterpret_cast<const uint4*>(vp + n * RPL * D);
+    for (int n = 0; n < NV; ++n) vr[n] = load_stream16(vp + n * RPL * D);
   };
   auto stage_v = [&](int k, const uint4 (&vr)[NV]) {
     const int t0 = (r.pg0 + wave + k * kWaves) * BS;
@@ -173,19 +176,25 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partition_mfma_kernel(Deco
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float alpha = fast_exp2(m_run - mx);
-    m_run = mx;
+    // Lazy rescaling: the reference max moves only when a score exceeds it
+    // by more than 2^kRescaleLog2, so weights stay <= 2^kRescaleLog2 and the
+    // accumulators are rescaled on few pages (a wave-uniform branch).
+    if (__any(mx > m_run + kRescaleLog2)) {
+      const float alpha = fast_exp2(m_run - mx);
+      m_run = mx;
+      l_run *= alpha;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) acc[m] *= alpha;
+    }
     float ps = 0.f;
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        sv[tt][j] = fast_exp2(sv[tt][j] - mx);
+        sv[tt][j] = fast_exp2(sv[tt][j] - m_run);
         ps += sv[tt][j];
       }
-    l_run = l_run * alpha + ps;
-#pragma unroll
-    for (int m = 0; m < NM; ++m) acc[m] *= alpha;
+    l_run += ps;
 
     if constexpr (BS == 32) {
       // P^T as the B operand: k slot j of lane group g4 is token 4 g4 + j

@@ -11,10 +11,12 @@
 //    Each wave reads it with 16-byte loads, one token row per D/VEC lanes, so
 //    a load instruction moves 1 KiB of contiguous memory straight into the
 //    registers that consume it (nothing is reused, so no LDS round trip).
-//  * Scores are reduced across the lanes of a token row with xor shuffles; the
+//  * bf16 scores use v_dot2_f32_bf16 on packed pairs; the partial scores are
+//    summed across the lanes of a token row with DPP adds; the
 //    online-softmax state (max, sum, accumulator) is kept per row, so no
 //    cross-row traffic happens inside the page loop; rows and waves are merged
 //    once per partition.
+//  * Page loads carry the non-temporal hint (each page is read once).
 //  * The next page's loads are in flight while the current page is consumed
 //    (two register buffers).  The page ids of a wave sit one per lane and are
 //    read with readlane, so the table walk is one coalesced load.
@@ -24,6 +26,14 @@
 
 namespace pa {
 namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// a.x * b.x + a.y * b.y + c over packed bf16 pairs (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
 
 // One workgroup = kWaves waves = one (partition, kv head, sequence); it serves
 // the G query heads that share the kv head.
@@ -53,13 +63,20 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partition_valu_kernel(Deco
   const int my_id = load_page_ids(p, s, r, wave, lane, &ids_bad);
   const bool bad = r.ctx_bad || ids_bad;
 
-  // Query rows of the group, pre-scaled by scale * log2(e).
+  // Query rows of the group: bf16 pairs kept packed for v_dot2 (the scale is
+  // applied to the reduced score); fp32 pre-scaled by scale * log2(e).
+  constexpr bool kBf16 = sizeof(T) == 2;
   float qf[G][VEC];
+  uint32_t qw[G][4];
   {
     const T* qb = static_cast<const T*>(p.q) + ((int64_t)s * p.num_heads + (int64_t)kvh * G) * D + col * VEC;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const uint4 q4 = *reinterpret_cast<const uint4*>(qb + g * D);
+      qw[g][0] = q4.x;
+      qw[g][1] = q4.y;
+      qw[g][2] = q4.z;
+      qw[g][3] = q4.w;
       E::unpack(q4, qf[g]);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) qf[g][e] *= p.scale_log2e;
@@ -83,9 +100,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partition_valu_kernel(Deco
     const T* kp = kbase + phys * p.block_stride;
     const T* vp = vbase + phys * p.block_stride;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) kr[i] = *reinterpret_cast<const uint4*>(kp + i * TPL * D);
+    for (int i = 0; i < NLD; ++i) kr[i] = load_stream16(kp + i * TPL * D);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) vr[i] = *reinterpret_cast<const uint4*>(vp + i * TPL * D);
+    for (int i = 0; i < NLD; ++i) vr[i] = load_stream16(vp + i * TPL * D);
   };
 
   auto consume_page = [&](int k, const uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
@@ -94,23 +111,34 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partition_valu_kernel(Deco
     float sc[G][NLD];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      float kf[VEC];
-      E::unpack(kr[i], kf);
+      if constexpr (kBf16) {
+        const uint32_t kw[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float a = 0.f;
+        for (int g = 0; g < G; ++g) {
+          float a = 0.f;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) a = fmaf(qf[g][e], kf[e], a);
-        sc[g][i] = a;
+          for (int w = 0; w < 4; ++w) a = dot2_bf16(qw[g][w], kw[w], a);
+          sc[g][i] = a;
+        }
+      } else {
+        float kf[VEC];
+        E::unpack(kr[i], kf);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float a = 0.f;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) a = fmaf(qf[g][e], kf[e], a);
+          sc[g][i] = a;
+        }
       }
     }
 #pragma unroll
-    for (int off = 1; off < LPT; off <<= 1) {
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) sc[g][i] += __shfl_xor(sc[g][i], off);
-    }
+      for (int i = 0; i < NLD; ++i) {
+        sc[g][i] = row_sum<LPT>(sc[g][i]);
+        if constexpr (kBf16) sc[g][i] *= p.scale_log2e;
+      }
     bool valid[NLD];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) valid[i] = full || (t0 + i * TPL + row < tok1);

