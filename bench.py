@@ -30,7 +30,10 @@ sys.path.insert(0, HERE)
 METRIC = "paged-attn decode tokens/s per layer + achieved HBM GB/s (% of peak), 1 GPU"
 PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "decode_traffic.json")
-KERNEL_SRC = os.path.join(HERE, "paged_kv_cache_321_amd", "csrc", "pa_kernels.hip")
+# Sources that determine the decode kernels; the counter record is valid only
+# for the exact text it was measured on.
+KERNEL_SRCS = [os.path.join(HERE, "paged_kv_cache_321_amd", "csrc", n) for n in
+               ("pa_device.h", "pa_decode.hip", "pa_decode_valu.hip", "pa_decode_mfma.hip")]
 
 DESCRIPTION = {
     "llama13b": "LLaMA-13B-shaped layer decode: 128 seqs x ctx 2048, H=Hkv=40, D=128, BS=16, bf16, "
@@ -71,8 +74,11 @@ def algorithmic_bytes(plan, spec) -> int:
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
@@ -105,6 +111,9 @@ def run_workload(name, steps, warmup, partition_tokens, flush=False):
     stream = torch.cuda.current_stream()
     has_pairs = plan.block_pairs.shape[0] > 0
     has_tokens = plan.slot_mapping.shape[0] > 0
+    # Workloads whose sequences share physical blocks (beam prefixes) ask for
+    # the default cache policy so later readers of a shared page hit in cache.
+    shared = bool(plan.shared_prefix_blocks)
 
     def step(ev=None):
         if has_pairs:
@@ -116,7 +125,7 @@ def run_workload(name, steps, warmup, partition_tokens, flush=False):
             ev[0].record(stream)
         binding.pa_decode(out, x.q, x.k_cache, x.v_cache, x.block_tables, x.context_lens,
                           x.scale, plan.max_context_len, partition_tokens=partition_tokens,
-                          workspace=ws, stream=stream)
+                          workspace=ws, stream=stream, shared_pages=shared)
         if ev is not None:
             ev[1].record(stream)
 
@@ -170,6 +179,7 @@ def run_workload(name, steps, warmup, partition_tokens, flush=False):
         "copy_pairs": int(plan.block_pairs.shape[0]),
         "new_tokens": int(plan.slot_mapping.shape[0]),
         "partition_tokens": partition_tokens,
+        "shared_pages_flag": shared,
         "cache": "cold (MALL flushed between steps)" if flush else "warm",
     }
     del x, out, ws, scratch

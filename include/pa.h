@@ -56,6 +56,15 @@ extern "C" {
 
 typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
 
+/* pa_decode flags */
+enum {
+  /* Physical blocks may be shared by several sequences of the batch (prefix
+   * sharing, beams).  Pages are then read with the default cache policy so
+   * that later readers of a shared page can hit in cache; without the flag
+   * pages are read with the non-temporal hint (each page read once). */
+  PA_DECODE_SHARED_PAGES = 1
+};
+
 typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_NULL = -1,        /* a required pointer is NULL                        */
@@ -138,7 +147,9 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
  * max_context_len is an upper bound on every context_lens[s] (it sizes the
  * grid); num_blocks is the pool size; scale is usually 1/sqrt(head_dim);
  * partition_tokens: 0 = default, else a multiple of block_size, at most
- * 256 * block_size.  The way a sequence is partitioned depends only on its own
+ * 256 * block_size.  flags: 0 or PA_DECODE_SHARED_PAGES (any other bit gives
+ * PA_ERR_UNSUPPORTED); the flag changes only the cache policy of the loads,
+ * never the result.  The way a sequence is partitioned depends only on its own
  * length, so a sequence's output does not depend on the other sequences of the
  * batch or on which physical blocks hold its pages.
  * workspace: device buffer of at least pa_decode_workspace_size(...) bytes with
@@ -153,7 +164,7 @@ int pa_decode(void* out, const void* q,
               const int32_t* context_lens,
               int num_seqs, int num_heads, int num_kv_heads, int head_dim,
               int block_size, int num_blocks, int max_context_len,
-              float scale, int dtype, int partition_tokens,
+              float scale, int dtype, int partition_tokens, int flags,
               void* workspace, size_t workspace_bytes, void* stream);
 
 /* pa_status_string -- static, human-readable name of a status code. */

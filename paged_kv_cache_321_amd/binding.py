@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(HERE, "libpa.so")
 
 PA_F32 = 0
 PA_BF16 = 1
+PA_DECODE_SHARED_PAGES = 1
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
           -4: "PA_ERR_UNSUPPORTED", -5: "PA_ERR_ALIGN", -6: "PA_ERR_WORKSPACE",
           -7: "PA_ERR_LAUNCH"}
@@ -47,7 +48,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_workspace_size.argtypes = [_c_int] * 8
     lib.pa_decode_workspace_size.restype = _c_size
     lib.pa_decode.argtypes = ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp] + [_c_int] * 7 +
-                              [_c_float, _c_int, _c_int, _vp, _c_size, _vp])
+                              [_c_float, _c_int, _c_int, _c_int, _vp, _c_size, _vp])
     lib.pa_decode.restype = _c_int
     lib.pa_status_string.argtypes = [_c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -140,11 +141,13 @@ def pa_decode_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, h
 def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
               block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
               max_context_len: int, partition_tokens: int = 0,
-              workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+              workspace: Optional[torch.Tensor] = None, stream=None,
+              shared_pages: bool = False) -> None:
     """Decode attention of q [S, H, D] over the paged caches into out [S, H, D].
 
     ``workspace`` (uint8 device tensor) is allocated here when not given and
-    the shape needs one.
+    the shape needs one.  ``shared_pages`` sets PA_DECODE_SHARED_PAGES (pages
+    may be shared between sequences: read them with the default cache policy).
     """
     for n, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
                  ("block_tables", block_tables), ("context_lens", context_lens)):
@@ -166,5 +169,6 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
     st = LIB.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                        block_tables.shape[1], _ptr(context_lens), s, h, hkv, d, bs, nb,
                        int(max_context_len), float(scale), code, int(partition_tokens),
+                       PA_DECODE_SHARED_PAGES if shared_pages else 0,
                        _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "pa_decode")

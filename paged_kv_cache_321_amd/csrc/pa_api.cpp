@@ -138,12 +138,13 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
               int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
               int num_blocks, int max_context_len, float scale, int dtype, int partition_tokens,
-              void* workspace, size_t workspace_bytes, void* stream) {
+              int flags, void* workspace, size_t workspace_bytes, void* stream) {
   const DecodeSizes z = decode_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                                      max_context_len, dtype, partition_tokens);
   if (z.status != PA_OK) return z.status;
   if (num_blocks <= 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * block_size < max_context_len) return PA_ERR_SHAPE;
+  if (flags & ~PA_DECODE_SHARED_PAGES) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
@@ -174,6 +175,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   a.scale = scale;
   a.dtype = dtype;
   a.partition_tokens = z.partition_tokens;
+  a.shared_pages = (flags & PA_DECODE_SHARED_PAGES) != 0;
   a.max_parts = z.max_parts;
   a.ws_ml = z.total ? reinterpret_cast<float*>(ws) : nullptr;
   a.ws_acc = z.total ? reinterpret_cast<float*>(ws + z.ml_bytes) : nullptr;

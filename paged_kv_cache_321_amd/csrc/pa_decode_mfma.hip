@@ -57,7 +57,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // four 32-byte segments of a read fall in distinct banks.
 __device__ __forceinline__ int swz(int row) { return 2 * ((row >> 2) & 3); }
 
-template <int D, int BS, int G>
+template <int D, int BS, int G, bool NONTEMPORAL>
 __global__ __launch_bounds__(kWaves * 64) void decode_partition_mfma_kernel(DecodeParams p) {
   constexpr int NT = BS / 16;       // 16-token tiles per page
   constexpr int NC = D / 32;        // 32-wide steps of the QK contraction
@@ -124,13 +124,13 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partition_mfma_kernel(Deco
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) kr[tt][c] = load_stream16(kp + tt * 16 * D + 32 * c);
+      for (int c = 0; c < NC; ++c) kr[tt][c] = load_page16<NONTEMPORAL>(kp + tt * 16 * D + 32 * c);
   };
   auto load_v = [&](int k, uint4 (&vr)[NV]) {
     const int64_t phys = __builtin_amdgcn_readlane(my_id, k);
     const uint16_t* vp = vc + phys * p.block_stride + v_off;
 #pragma unroll
-    for (int n = 0; n < NV; ++n) vr[n] = load_stream16(vp + n * RPL * D);
+    for (int n = 0; n < NV; ++n) vr[n] = load_page16<NONTEMPORAL>(vp + n * RPL * D);
   };
   auto stage_v = [&](int k, const uint4 (&vr)[NV]) {
     const int t0 = (r.pg0 + wave + k * kWaves) * BS;
@@ -276,7 +276,10 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partition_mfma_kernel(Deco
 template <int D, int BS, int G>
 hipError_t launch_t(const DecodeLaunch& a, const DecodeParams& p) {
   dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((decode_partition_mfma_kernel<D, BS, G>), grid, dim3(kWaves * 64), 0, a.stream, p);
+  if (a.shared_pages)
+    hipLaunchKernelGGL((decode_partition_mfma_kernel<D, BS, G, false>), grid, dim3(kWaves * 64), 0, a.stream, p);
+  else
+    hipLaunchKernelGGL((decode_partition_mfma_kernel<D, BS, G, true>), grid, dim3(kWaves * 64), 0, a.stream, p);
   return hipGetLastError();
 }
 

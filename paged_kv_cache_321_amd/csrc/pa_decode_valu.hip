@@ -16,7 +16,8 @@
 //    online-softmax state (max, sum, accumulator) is kept per row, so no
 //    cross-row traffic happens inside the page loop; rows and waves are merged
 //    once per partition.
-//  * Page loads carry the non-temporal hint (each page is read once).
+//  * Page loads carry the non-temporal hint (each page is read once), unless
+//    the caller says pages may be shared between sequences.
 //  * The next page's loads are in flight while the current page is consumed
 //    (two register buffers).  The page ids of a wave sit one per lane and are
 //    read with readlane, so the table walk is one coalesced load.
@@ -37,7 +38,7 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 // One workgroup = kWaves waves = one (partition, kv head, sequence); it serves
 // the G query heads that share the kv head.
-template <typename T, int D, int BS, int G>
+template <typename T, int D, int BS, int G, bool NONTEMPORAL>
 __global__ __launch_bounds__(kWaves * 64) void decode_partition_valu_kernel(DecodeParams p) {
   using E = Elem<T>;
   constexpr int VEC = E::kVec;
@@ -100,9 +101,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partition_valu_kernel(Deco
     const T* kp = kbase + phys * p.block_stride;
     const T* vp = vbase + phys * p.block_stride;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) kr[i] = load_stream16(kp + i * TPL * D);
+    for (int i = 0; i < NLD; ++i) kr[i] = load_page16<NONTEMPORAL>(kp + i * TPL * D);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) vr[i] = load_stream16(vp + i * TPL * D);
+    for (int i = 0; i < NLD; ++i) vr[i] = load_page16<NONTEMPORAL>(vp + i * TPL * D);
   };
 
   auto consume_page = [&](int k, const uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
@@ -233,8 +234,12 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partition_valu_kernel(Deco
 template <typename T, int D, int BS, int G>
 hipError_t launch_t(const DecodeLaunch& a, const DecodeParams& p) {
   dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((decode_partition_valu_kernel<T, D, BS, G>), grid, dim3(kWaves * 64), 0,
-                     a.stream, p);
+  if (a.shared_pages)
+    hipLaunchKernelGGL((decode_partition_valu_kernel<T, D, BS, G, false>), grid, dim3(kWaves * 64), 0,
+                       a.stream, p);
+  else
+    hipLaunchKernelGGL((decode_partition_valu_kernel<T, D, BS, G, true>), grid, dim3(kWaves * 64), 0,
+                       a.stream, p);
   return hipGetLastError();
 }
 

@@ -43,6 +43,13 @@ __device__ __forceinline__ uint4 load_stream16(const void* p) {
   return __builtin_bit_cast(uint4, v);
 }
 
+// Page load: non-temporal unless pages may be shared between sequences.
+template <bool kNonTemporal>
+__device__ __forceinline__ uint4 load_page16(const void* p) {
+  if constexpr (kNonTemporal) return load_stream16(p);
+  return *reinterpret_cast<const uint4*>(p);
+}
+
 // Sum over groups of LPT consecutive lanes (LPT a power of two); every lane
 // of a group receives the group's total.  Steps inside a 16-lane row use DPP
 // (quad permutes, half-row and row mirrors), so they fold into the adds.

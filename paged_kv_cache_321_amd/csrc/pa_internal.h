@@ -27,6 +27,7 @@ struct DecodeLaunch {
   float scale;
   int dtype;
   int partition_tokens;  // resolved, > 0
+  bool shared_pages;     // pages may be shared: default cache policy, else non-temporal
   int max_parts;         // ceil(max_context_len / partition_tokens), >= 1
   float* ws_ml;          // [S, H, max_parts, 2] (running max, running sum); null if max_parts == 1
   float* ws_acc;         // [S, H, max_parts, D] unnormalised outputs; null if max_parts == 1

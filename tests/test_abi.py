@@ -45,11 +45,11 @@ def test_status_strings():
 
 def decode(**kw):
     a = dict(out=P, q=P, k=P, v=P, bt=P, mb=8, ctx=P, S=2, H=8, Hkv=2, D=128, BS=16, NB=32,
-             maxctx=100, scale=0.1, dtype=BF16, pt=0, ws=None, wsb=0)
+             maxctx=100, scale=0.1, dtype=BF16, pt=0, flags=0, ws=None, wsb=0)
     a.update(kw)
     return LIB.pa_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["mb"], a["ctx"], a["S"],
                          a["H"], a["Hkv"], a["D"], a["BS"], a["NB"], a["maxctx"], a["scale"],
-                         a["dtype"], a["pt"], a["ws"], a["wsb"], None)
+                         a["dtype"], a["pt"], a["flags"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -83,7 +83,10 @@ def decode(**kw):
     (dict(maxctx=3000, mb=200, pt=1024), WS),           # workspace required but missing
     (dict(maxctx=3000, mb=200, pt=1024, ws=P, wsb=16), WS),
     (dict(maxctx=3000, mb=200, pt=1024, ws=MIS, wsb=1 << 30), ALIGN),
+    (dict(flags=2), UNSUP),             # unknown flag bit
+    (dict(flags=-1), UNSUP),
     (dict(S=0), OK),                    # empty batch: nothing to launch
+    (dict(S=0, flags=1), OK),
 ])
 def test_decode_validation(kw, code):
     assert decode(**kw) == code

@@ -131,6 +131,16 @@ def test_batch_invariance_bitwise():
     assert torch.equal(out[keep], out2)
 
 
+@pytest.mark.parametrize("name", ["beam", "llama13b", "tiny"])
+def test_shared_pages_flag_changes_nothing(name):
+    """PA_DECODE_SHARED_PAGES only changes the cache policy: same bits out."""
+    x = wl.make_inputs(name, **SMALL[name])
+    a, _ = gpu_step(x)
+    b, _ = gpu_step(x, shared_pages=True)
+    assert torch.equal(a, b)
+    check_case(x)
+
+
 def test_repeat_is_deterministic():
     x = wl.make_inputs("beam", **SMALL["beam"])
     a, _ = gpu_step(x)
