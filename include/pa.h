@@ -152,6 +152,11 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
  * never the result.  The way a sequence is partitioned depends only on its own
  * length, so a sequence's output does not depend on the other sequences of the
  * batch or on which physical blocks hold its pages.
+ * seq_order: NULL, or a device int32 [num_seqs] permutation of 0..num_seqs-1
+ * giving the order in which sequences are dispatched; longest contexts first
+ * shortens the tail of a ragged batch.  It never changes a result.
+ * Precondition: a permutation (entries outside [0, num_seqs) are skipped, and a
+ * row whose index is missing is left unwritten).
  * workspace: device buffer of at least pa_decode_workspace_size(...) bytes with
  * 16-byte alignment (NULL allowed when that size is 0).
  * Preconditions (device values): 0 <= context_lens[s] <= max_context_len and
@@ -161,7 +166,7 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
 int pa_decode(void* out, const void* q,
               const void* k_cache, const void* v_cache,
               const int32_t* block_tables, int max_blocks_per_seq,
-              const int32_t* context_lens,
+              const int32_t* context_lens, const int32_t* seq_order,
               int num_seqs, int num_heads, int num_kv_heads, int head_dim,
               int block_size, int num_blocks, int max_context_len,
               float scale, int dtype, int partition_tokens, int flags,

@@ -47,7 +47,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_copy_blocks.restype = _c_int
     lib.pa_decode_workspace_size.argtypes = [_c_int] * 8
     lib.pa_decode_workspace_size.restype = _c_size
-    lib.pa_decode.argtypes = ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp] + [_c_int] * 7 +
+    lib.pa_decode.argtypes = ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp] + [_c_int] * 7 +
                               [_c_float, _c_int, _c_int, _c_int, _vp, _c_size, _vp])
     lib.pa_decode.restype = _c_int
     lib.pa_status_string.argtypes = [_c_int]
@@ -138,16 +138,28 @@ def pa_decode_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, h
     return n
 
 
+def longest_first(context_lens, device="cuda") -> torch.Tensor:
+    """Dispatch order with the longest contexts first, from host-side lengths.
+
+    Ties keep their index order, so the order is a function of the lengths only.
+    """
+    lens = torch.as_tensor(context_lens, dtype=torch.int64).cpu()
+    order = sorted(range(len(lens)), key=lambda i: (-int(lens[i]), i))
+    return torch.tensor(order, dtype=torch.int32, device=device)
+
+
 def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
               block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
               max_context_len: int, partition_tokens: int = 0,
               workspace: Optional[torch.Tensor] = None, stream=None,
-              shared_pages: bool = False) -> None:
+              shared_pages: bool = False, seq_order: Optional[torch.Tensor] = None) -> None:
     """Decode attention of q [S, H, D] over the paged caches into out [S, H, D].
 
     ``workspace`` (uint8 device tensor) is allocated here when not given and
     the shape needs one.  ``shared_pages`` sets PA_DECODE_SHARED_PAGES (pages
     may be shared between sequences: read them with the default cache policy).
+    ``seq_order`` (int32 device tensor [S], a permutation) sets the dispatch
+    order of the sequences; see ``longest_first``.
     """
     for n, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
                  ("block_tables", block_tables), ("context_lens", context_lens)):
@@ -160,6 +172,10 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
     _need(d2 == d and out.shape == q.shape and v_cache.shape == k_cache.shape, "shape mismatch")
     _need(block_tables.dim() == 2 and block_tables.shape[0] == s, "block_tables must be [S, MB]")
     _need(context_lens.shape == (s,), "context_lens must be [S]")
+    if seq_order is not None:
+        _device_contig("seq_order", seq_order)
+        _need(seq_order.dtype == torch.int32 and seq_order.shape == (s,),
+              "seq_order must be int32 [S]")
     code = _dtype_code(q)
     need = pa_decode_workspace_size(s, h, hkv, d, bs, max_context_len, code, partition_tokens) \
         if h > 0 and hkv > 0 and h % hkv == 0 else 0
@@ -167,7 +183,7 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = LIB.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                       block_tables.shape[1], _ptr(context_lens), s, h, hkv, d, bs, nb,
+                       block_tables.shape[1], _ptr(context_lens), _ptr(seq_order), s, h, hkv, d, bs, nb,
                        int(max_context_len), float(scale), code, int(partition_tokens),
                        PA_DECODE_SHARED_PAGES if shared_pages else 0,
                        _ptr(workspace), ws_bytes, _stream(stream))

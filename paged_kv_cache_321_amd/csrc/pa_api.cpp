@@ -136,7 +136,8 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, i
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
-              int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+              const int32_t* seq_order, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+              int block_size,
               int num_blocks, int max_context_len, float scale, int dtype, int partition_tokens,
               int flags, void* workspace, size_t workspace_bytes, void* stream) {
   const DecodeSizes z = decode_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
@@ -148,7 +149,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(seq_order, 4))
     return PA_ERR_ALIGN;
   if (num_seqs > kMaxGridYZ || num_kv_heads > kMaxGridYZ || num_heads > kMaxGridYZ)
     return PA_ERR_UNSUPPORTED;
@@ -165,6 +166,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   a.block_tables = block_tables;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.context_lens = context_lens;
+  a.seq_order = seq_order;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.num_kv_heads = num_kv_heads;

@@ -98,10 +98,12 @@ hipError_t launch_decode(const DecodeLaunch& a) {
   p.v_cache = a.v_cache;
   p.block_tables = a.block_tables;
   p.context_lens = a.context_lens;
+  p.seq_order = a.seq_order;
   p.ws_ml = a.ws_ml;
   p.ws_acc = a.ws_acc;
   p.block_stride = (int64_t)a.num_kv_heads * a.block_size * a.head_dim;
   p.max_blocks_per_seq = a.max_blocks_per_seq;
+  p.num_seqs = a.num_seqs;
   p.num_heads = a.num_heads;
   p.num_blocks = a.num_blocks;
   p.max_context_len = a.max_context_len;

@@ -49,7 +49,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partition_valu_kernel(Deco
 
   const int part = blockIdx.x;
   const int kvh = blockIdx.y;
-  const int s = blockIdx.z;
+  const int s = sequence_of(p, blockIdx.z);
+  if (s < 0) return;  // uniform over the workgroup
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;

@@ -110,10 +110,12 @@ struct DecodeParams {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const int32_t* seq_order;  // null = natural order
   float* ws_ml;
   float* ws_acc;
   int64_t block_stride;  // elements between consecutive physical blocks
   int max_blocks_per_seq;
+  int num_seqs;
   int num_heads;
   int num_blocks;
   int max_context_len;
@@ -121,6 +123,14 @@ struct DecodeParams {
   int max_parts;
   float scale_log2e;
 };
+
+// Sequence served by grid slot z (the caller may reorder dispatch); -1 if the
+// order array names no valid sequence there.
+__device__ __forceinline__ int sequence_of(const DecodeParams& p, int z) {
+  if (p.seq_order == nullptr) return z;
+  const int s = p.seq_order[z];
+  return (s >= 0 && s < p.num_seqs) ? s : -1;
+}
 
 __device__ __forceinline__ int parts_for(int ctx, int partition_tokens) {
   return ctx <= partition_tokens ? 1 : (ctx + partition_tokens - 1) / partition_tokens;

@@ -27,7 +27,7 @@ def on_device(x: Inputs) -> dict:
 
 
 def gpu_step(x: Inputs, t: dict | None = None, partition_tokens: int = 0, copy: bool = True,
-             reshape: bool = True, shared_pages: bool = False):
+             reshape: bool = True, shared_pages: bool = False, seq_order=None):
     """copy_blocks -> reshape_and_cache -> decode on the GPU; returns (out, t)."""
     t = on_device(x) if t is None else t
     if copy and t["block_pairs"].shape[0]:
@@ -38,7 +38,8 @@ def gpu_step(x: Inputs, t: dict | None = None, partition_tokens: int = 0, copy: 
     out = torch.empty_like(t["q"])
     binding.pa_decode(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
                       t["context_lens"], x.scale, x.max_context_len,
-                      partition_tokens=partition_tokens, shared_pages=shared_pages)
+                      partition_tokens=partition_tokens, shared_pages=shared_pages,
+                      seq_order=seq_order)
     torch.cuda.synchronize()
     return out, t
 

@@ -44,10 +44,11 @@ def test_status_strings():
 
 
 def decode(**kw):
-    a = dict(out=P, q=P, k=P, v=P, bt=P, mb=8, ctx=P, S=2, H=8, Hkv=2, D=128, BS=16, NB=32,
-             maxctx=100, scale=0.1, dtype=BF16, pt=0, flags=0, ws=None, wsb=0)
+    a = dict(out=P, q=P, k=P, v=P, bt=P, mb=8, ctx=P, order=None, S=2, H=8, Hkv=2, D=128, BS=16,
+             NB=32, maxctx=100, scale=0.1, dtype=BF16, pt=0, flags=0, ws=None, wsb=0)
     a.update(kw)
-    return LIB.pa_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["mb"], a["ctx"], a["S"],
+    return LIB.pa_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["mb"], a["ctx"], a["order"],
+                         a["S"],
                          a["H"], a["Hkv"], a["D"], a["BS"], a["NB"], a["maxctx"], a["scale"],
                          a["dtype"], a["pt"], a["flags"], a["ws"], a["wsb"], None)
 
@@ -79,6 +80,7 @@ def decode(**kw):
     (dict(out=MIS), ALIGN),
     (dict(k=MIS), ALIGN),
     (dict(bt=P + 2), ALIGN),
+    (dict(order=P + 2), ALIGN),
     (dict(S=70000, maxctx=10), UNSUP),  # grid limit
     (dict(maxctx=3000, mb=200, pt=1024), WS),           # workspace required but missing
     (dict(maxctx=3000, mb=200, pt=1024, ws=P, wsb=16), WS),
@@ -158,3 +160,8 @@ def test_binding_raises_runtime_error_with_status():
     assert isinstance(err, RuntimeError) and "PA_ERR_SHAPE" in str(err)
     with pytest.raises(ValueError):
         binding.pa_decode_workspace_size(1, 6, 4, 128, 16, 100, BF16)
+
+
+def test_longest_first_order():
+    o = binding.longest_first([5, 9, 1, 9, 0], device="cpu").tolist()
+    assert o == [1, 3, 0, 2, 4]

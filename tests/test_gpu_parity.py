@@ -141,6 +141,20 @@ def test_shared_pages_flag_changes_nothing(name):
     check_case(x)
 
 
+@pytest.mark.parametrize("name,pt", [("llama7b", 0), ("llama7b", 256), ("gqa70b", 1024), ("beam", 0)])
+def test_dispatch_order_changes_nothing(name, pt):
+    """seq_order only reorders dispatch: every row is bitwise the same."""
+    from paged_kv_cache_321_amd import binding
+    x = wl.make_inputs(name, **SMALL[name])
+    a, _ = gpu_step(x, partition_tokens=pt)
+    order = binding.longest_first(x.plan.context_lens)
+    b, _ = gpu_step(x, partition_tokens=pt, seq_order=order)
+    assert torch.equal(a, b)
+    rev = torch.arange(x.plan.num_seqs - 1, -1, -1, dtype=torch.int32, device="cuda")
+    c, _ = gpu_step(x, partition_tokens=pt, seq_order=rev)
+    assert torch.equal(a, c)
+
+
 def test_repeat_is_deterministic():
     x = wl.make_inputs("beam", **SMALL["beam"])
     a, _ = gpu_step(x)
