@@ -58,7 +58,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ int swz(int row) { return 2 * ((row >> 2) & 3); }
 
 template <int D, int BS, int G, bool NONTEMPORAL>
-__global__ __launch_bounds__(kWaves * 64) void decode_partition_mfma_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void decode_partition_mfma_kernel(DecodeParams p) {
   constexpr int NT = BS / 16;       // 16-token tiles per page
   constexpr int NC = D / 32;        // 32-wide steps of the QK contraction
   constexpr int NM = D / 16;        // 16-wide output tiles along head_dim

@@ -155,6 +155,35 @@ def test_dispatch_order_changes_nothing(name, pt):
     assert torch.equal(a, c)
 
 
+@pytest.mark.parametrize("name,pt", [("llama7b", 64), ("gqa70b", 1024)])
+def test_workspace_reuse(name, pt):
+    """One caller-owned workspace serves repeated multi-partition calls."""
+    from paged_kv_cache_321_amd import binding
+    x = wl.make_inputs(name, **SMALL[name])
+    t = on_device(x)
+    spec, plan = x.spec, x.plan
+    code = binding.PA_BF16 if spec.dtype == "bf16" else binding.PA_F32
+    n = binding.pa_decode_workspace_size(plan.num_seqs, spec.num_heads, spec.num_kv_heads,
+                                         spec.head_dim, plan.block_size, plan.max_context_len,
+                                         code, pt)
+    assert n > 0
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")  # contents never matter
+    if t["slot_mapping"].shape[0]:  # store the new tokens first (their slots hold NaN)
+        binding.pa_reshape_and_cache(t["key"], t["value"], t["k_cache"], t["v_cache"],
+                                     t["slot_mapping"])
+    outs = []
+    for _ in range(3):
+        out = torch.empty_like(t["q"])
+        binding.pa_decode(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                          t["context_lens"], x.scale, x.max_context_len, partition_tokens=pt,
+                          workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    ref, _, _ = oracle_step(x)
+    assert_close(as_f64(outs[0]), ref, spec.dtype, name)
+
+
 def test_repeat_is_deterministic():
     x = wl.make_inputs("beam", **SMALL["beam"])
     a, _ = gpu_step(x)
