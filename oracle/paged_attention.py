@@ -39,8 +39,9 @@ the design notes of the repository as well):
 * The KV-size formula's "h" and "d" are the head count and the per-head
   dimension (so h * d is the hidden size), see ``kv_cache_bytes``.
 
-Floating point: bf16 inputs arrive as uint16 bit patterns and fp32 inputs as
-float32 arrays; both are widened exactly to float64 here.  The attention
+Floating point: bf16 inputs arrive as uint16 bit patterns, fp32 inputs as
+float32 arrays and E4M3 cache entries as uint8 codes; all are widened exactly
+to float64 here.  The attention
 result is the exact softmax attention in float64 (the plain definition that
 the paged kernel reaches up to rounding order).
 
@@ -58,7 +59,11 @@ import numpy as np
 __all__ = [
     "BF16",
     "F32",
+    "FP8",
     "widen",
+    "e4m3_values",
+    "e4m3_encode",
+    "e4m3_inverse_scale",
     "kv_cache_bytes",
     "num_required_blocks",
     "kv_head_for",
@@ -73,6 +78,76 @@ __all__ = [
 
 BF16 = "bf16"
 F32 = "f32"
+FP8 = "fp8"   # OCP 8-bit floating point E4M3 codes, stored as uint8
+
+
+# --------------------------------------------------------------------------
+# FP8 (E4M3) KV cache.  [tbr8] section "量化集成与部署" offers an fp8 KV
+# cache option without fixing a format; the reading taken here is the OCP
+# E4M3 format (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, no
+# infinities, S.1111.111 = NaN, largest finite 448) with one float32 scale
+# per cache: the stored code of x is the finite E4M3 value nearest to
+# x * fl32(1 / scale) (ties to the even code, magnitudes beyond 448 become
+# 448), and a code c stands for value(c) * scale.
+# --------------------------------------------------------------------------
+
+def e4m3_values() -> np.ndarray:
+    """float64 value of each of the 256 E4M3 codes (NaN for the two NaN codes)."""
+    vals = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        sign = -1.0 if code & 0x80 else 1.0
+        exp = (code >> 3) & 0xF
+        man = code & 0x7
+        if exp == 0xF and man == 0x7:
+            vals[code] = np.nan
+        elif exp == 0:
+            vals[code] = sign * (man / 8.0) * 2.0 ** (1 - 7)
+        else:
+            vals[code] = sign * (1.0 + man / 8.0) * 2.0 ** (exp - 7)
+    return vals
+
+
+def e4m3_inverse_scale(scale: float) -> np.float32:
+    """fl32(1 / scale): the factor new tokens are multiplied by before encoding."""
+    return np.float32(1.0) / np.float32(scale)
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """Nearest finite E4M3 code of each float32 value (ties to even codes).
+
+    Written from the definition: compare |x| against every non-negative finite
+    E4M3 magnitude (codes 0x00..0x7E, increasing), take the closest, break a
+    tie towards the code with a zero lowest bit, saturate beyond 448, keep the
+    sign bit (so -0.0 -> 0x80), and map NaN to 0x7F with the sign bit of x.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    mags = e4m3_values()[:0x7F]                      # 0x00 .. 0x7E, increasing
+    flat = x.reshape(-1).astype(np.float64)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    signs = np.signbit(x.reshape(-1))
+    for i, v in enumerate(flat):
+        sign = 0x80 if signs[i] else 0x00
+        if np.isnan(v):
+            out[i] = sign | 0x7F
+            continue
+        a = abs(v)
+        if a >= mags[-1]:
+            out[i] = sign | 0x7E
+            continue
+        hi = int(np.searchsorted(mags, a, side="left"))  # mags[hi-1] < a <= mags[hi]
+        if mags[hi] == a:
+            code = hi
+        else:
+            lo = hi - 1
+            dlo, dhi = a - mags[lo], mags[hi] - a
+            if dlo < dhi:
+                code = lo
+            elif dhi < dlo:
+                code = hi
+            else:
+                code = lo if lo % 2 == 0 else hi
+        out[i] = sign | code
+    return out.reshape(x.shape)
 
 
 # --------------------------------------------------------------------------
@@ -94,6 +169,10 @@ def widen(x: np.ndarray, dtype: str) -> np.ndarray:
         if x.dtype != np.float32:
             raise TypeError("f32 data must be given as float32")
         return x.astype(np.float64)
+    if dtype == FP8:
+        if x.dtype != np.uint8:
+            raise TypeError("fp8 data must be given as uint8 E4M3 codes")
+        return e4m3_values()[x]
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -141,15 +220,25 @@ def kv_head_for(head: int, num_heads: int, num_kv_heads: int) -> int:
 
 def reshape_and_cache(key: np.ndarray, value: np.ndarray,
                       k_cache: np.ndarray, v_cache: np.ndarray,
-                      slot_mapping: np.ndarray) -> None:
+                      slot_mapping: np.ndarray, src_dtype: str = None,
+                      k_scale: float = 1.0, v_scale: float = 1.0) -> None:
     """Store each new token's K and V rows into its cache slot, in place.
 
     key, value: [T, Hkv, D]; k_cache, v_cache: [NB, Hkv, BS, D];
     slot_mapping: [T] integers.  Token i goes to block slot // BS, offset
-    slot % BS, for every kv head; a negative slot is skipped.  Elements are
-    copied as they are (raw bits for bf16), so the result is exact.
+    slot % BS, for every kv head; a negative slot is skipped.  When the caches
+    hold the same element type as key/value the elements are copied as they
+    are (raw bits for bf16), so the result is exact.  When the caches hold
+    E4M3 codes (uint8) and key/value are ``src_dtype`` values, each row is
+    encoded as e4m3_encode(fl32(x) * fl32(1 / scale)) in float32 arithmetic.
     """
     block_size = k_cache.shape[2]
+    if k_cache.dtype == np.uint8 and key.dtype != np.uint8:
+        if src_dtype is None:
+            raise ValueError("src_dtype is needed to encode into an fp8 cache")
+        kf = widen(key, src_dtype).astype(np.float32) * e4m3_inverse_scale(k_scale)
+        vf = widen(value, src_dtype).astype(np.float32) * e4m3_inverse_scale(v_scale)
+        key, value = e4m3_encode(kf), e4m3_encode(vf)
     for i in range(key.shape[0]):
         slot = int(slot_mapping[i])
         if slot < 0:
@@ -215,12 +304,15 @@ def attend_one(q: np.ndarray, k: np.ndarray, v: np.ndarray,
 
 def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
            block_tables: np.ndarray, context_lens: np.ndarray,
-           scale: float, dtype: str, return_weights: bool = False):
+           scale: float, dtype: str, return_weights: bool = False,
+           cache_dtype: str = None, k_scale: float = 1.0, v_scale: float = 1.0):
     """Single-query decode attention over a paged cache, float64 result.
 
     q: [S, H, D]; caches [NB, Hkv, BS, D]; block_tables [S, MB];
     context_lens [S].  ``scale`` is taken as the float32 value the GPU path
     receives, promoted exactly.  Sequences with context length 0 give zeros.
+    ``cache_dtype`` (default: ``dtype``) is the cache element type; for E4M3
+    caches a code c stands for value(c) * k_scale (keys) or * v_scale (values).
     Returns out [S, H, D] (and, if asked, a list of per-(s, h) weights).
     """
     num_seqs, num_heads, head_dim = q.shape
@@ -231,7 +323,8 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
     for s in range(num_seqs):
         out[s], w = decode_rows(q[s], k_cache, v_cache, block_tables[s],
                                 int(context_lens[s]), scale64, dtype,
-                                num_heads, num_kv_heads)
+                                num_heads, num_kv_heads, cache_dtype=cache_dtype,
+                                k_scale=k_scale, v_scale=v_scale)
         if return_weights:
             for h, wh in enumerate(w):
                 weights[(s, h)] = wh
@@ -243,19 +336,24 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
 def decode_rows(q_s: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                 block_table_row: np.ndarray, context_len: int, scale: float,
                 dtype: str, num_heads: int, num_kv_heads: int,
-                heads=None):
+                heads=None, cache_dtype: str = None, k_scale: float = 1.0,
+                v_scale: float = 1.0):
     """Decode output for one sequence (all heads, or the listed ``heads``).
 
     q_s: [H, D].  Returns (out [len(heads), D] float64, list of weights).
     """
     heads = list(range(num_heads)) if heads is None else list(heads)
+    cache_dtype = dtype if cache_dtype is None else cache_dtype
     head_dim = q_s.shape[-1]
     out = np.zeros((len(heads), head_dim), dtype=np.float64)
     weights = []
     if context_len == 0:
         return out, [np.zeros(0) for _ in heads]
-    k_ctx = widen(gather_context(k_cache, block_table_row, context_len), dtype)
-    v_ctx = widen(gather_context(v_cache, block_table_row, context_len), dtype)
+    k_ctx = widen(gather_context(k_cache, block_table_row, context_len), cache_dtype)
+    v_ctx = widen(gather_context(v_cache, block_table_row, context_len), cache_dtype)
+    if cache_dtype == FP8:
+        k_ctx = k_ctx * float(np.float32(k_scale))
+        v_ctx = v_ctx * float(np.float32(v_scale))
     q64 = widen(np.ascontiguousarray(q_s), dtype)
     for i, h in enumerate(heads):
         kvh = kv_head_for(h, num_heads, num_kv_heads)

@@ -319,12 +319,77 @@ def pin_copy_blocks():
     assert np.array_equal(kc, ref_k) and np.array_equal(vc, ref_v)
 
 
+def pin_e4m3_table():
+    """Code values: the format's landmarks and torch's float8_e4m3fn decoding."""
+    v = op.e4m3_values()
+    assert v[0x7E] == 448.0 and v[0xFE] == -448.0          # largest finite
+    assert v[0x08] == 2.0 ** -6 and v[0x01] == 2.0 ** -9    # min normal, min subnormal
+    assert v[0x07] == 7 * 2.0 ** -9 and v[0x38] == 1.0 and v[0xC0] == -2.0
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+    assert v[0x00] == 0.0 and np.signbit(v[0x80])
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(v), np.isnan(t))
+    assert np.array_equal(v[~np.isnan(v)], t[~np.isnan(t)])
+
+
+def pin_e4m3_encode():
+    """Encoding: torch's RNE cast in range, round trips, ties, saturation, NaN."""
+    rng = np.random.default_rng(31)
+    x = np.concatenate([rng.standard_normal(4000) * s for s in (1e-3, 0.05, 1, 30, 200)])
+    x = x.astype(np.float32)
+    x = x[np.abs(x) < 448.0]  # torch's cast gives NaN past the largest finite value
+    got = op.e4m3_encode(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref)
+    v = op.e4m3_values()
+    finite = [c for c in range(256) if not np.isnan(v[c])]
+    assert np.array_equal(op.e4m3_encode(v[finite].astype(np.float32)), np.array(finite, dtype=np.uint8))
+    ties = np.array([1.0625, 1.1875, 2.0 ** -10, 1.5 * 2.0 ** -9, 400.0, 432.0, -1.0625],
+                    dtype=np.float32)
+    assert op.e4m3_encode(ties).tolist() == [0x38, 0x3A, 0x00, 0x02, 0x7C, 0x7E, 0xB8]
+    big = np.array([448.0, 449.0, 464.0, 1e6, np.inf, -np.inf, -500.0], dtype=np.float32)
+    assert op.e4m3_encode(big).tolist() == [0x7E] * 5 + [0xFE, 0xFE]
+    assert op.e4m3_encode(np.array([np.nan], dtype=np.float32))[0] & 0x7F == 0x7F
+
+
+def pin_fp8_reshape_and_decode():
+    """An E4M3 cache: stored codes are the encoded scaled rows; decode is the
+    softmax attention over the dequantised values (checked against SDPA)."""
+    rng = np.random.default_rng(32)
+    hkv, h, d, bs, nb, ks, vs = 2, 4, 16, 16, 6, 0.02, 0.03
+    kc = np.zeros((nb, hkv, bs, d), dtype=np.uint8)
+    vc = np.zeros_like(kc)
+    key = torch.from_numpy(rng.standard_normal((20, hkv, d)).astype(np.float32)).to(torch.bfloat16)
+    val = torch.from_numpy(rng.standard_normal((20, hkv, d)).astype(np.float32)).to(torch.bfloat16)
+    kb = key.view(torch.int16).numpy().view(np.uint16)
+    vb = val.view(torch.int16).numpy().view(np.uint16)
+    table = np.array([4, 1], dtype=np.int32)
+    slots = np.array([table[t // bs] * bs + t % bs for t in range(20)], dtype=np.int64)
+    op.reshape_and_cache(kb, vb, kc, vc, slots, src_dtype=op.BF16, k_scale=ks, v_scale=vs)
+    inv_k = np.float32(1) / np.float32(ks)
+    expect = torch.from_numpy(key.float().numpy() * inv_k).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(kc[4, :, 3], expect[3])
+    assert np.array_equal(kc[1, :, 2], expect[18])
+    q = rng.standard_normal((h, d)).astype(np.float32)
+    out = op.decode(q[None], kc, vc, table[None], np.array([20]), 0.25, op.F32,
+                    cache_dtype=op.FP8, k_scale=ks, v_scale=vs)[0]
+    vals = op.e4m3_values()
+    kd = np.stack([vals[kc[table[t // bs], :, t % bs]] for t in range(20)], axis=1) * np.float32(ks)
+    vd = np.stack([vals[vc[table[t // bs], :, t % bs]] for t in range(20)], axis=1) * np.float32(vs)
+    kt = torch.from_numpy(kd).repeat_interleave(2, dim=0)[None]
+    vt = torch.from_numpy(vd).repeat_interleave(2, dim=0)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q).double()[None, :, None, :], kt, vt, scale=0.25)
+    assert np.allclose(out, ref[0, :, 0].numpy(), rtol=0, atol=1e-12)
+
+
 PINS = [pin_bruteforce, pin_sdpa, pin_worked_tables, pin_block_counts, pin_kv_bytes,
         pin_ctx1_returns_v, pin_weights_sum_to_one, pin_q_zero_gives_mean,
         pin_constant_v, pin_shift_invariance, pin_block_permutation,
         pin_block_size_independent, pin_gqa_equals_repeated_mha,
         pin_nan_poison_ignored, pin_zero_context, pin_batch_invariance, pin_widen,
-        pin_reshape_library, pin_reshape_roundtrip, pin_copy_blocks]
+        pin_reshape_library, pin_reshape_roundtrip, pin_copy_blocks, pin_e4m3_table,
+        pin_e4m3_encode, pin_fp8_reshape_and_decode]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -383,7 +448,7 @@ def _widen_bad(x, dtype):
     return x.astype(np.float64)
 
 
-def _reshape_swapped(key, value, kc, vc, slots):
+def _reshape_swapped(key, value, kc, vc, slots, **kw):
     bs = kc.shape[2]
     for i, slot in enumerate(slots):
         if slot < 0:
@@ -398,7 +463,46 @@ def _copy_k_only(kc, vc, pairs):
         kc[int(d)] = kc[int(s)]
 
 
+def _e4m3_ties_away(x):
+    x = np.asarray(x, dtype=np.float32)
+    mags = _E4M3_TRUE_VALUES()[:0x7F]
+    out = []
+    for v in x.reshape(-1).astype(np.float64):
+        sign = 0x80 if np.signbit(v) else 0
+        if np.isnan(v):
+            out.append(sign | 0x7F)
+            continue
+        a = min(abs(v), 448.0)
+        d = np.abs(mags - a)
+        best = np.flatnonzero(d == d.min())
+        out.append(sign | int(best[-1]))   # ties go to the larger magnitude
+    return np.array(out, dtype=np.uint8).reshape(x.shape)
+
+
+def _E4M3_TRUE_VALUES():
+    return _ORIG_E4M3_VALUES()
+
+
+def _e4m3_values_bias8():
+    v = _ORIG_E4M3_VALUES().copy()
+    return v / 2.0
+
+
+def _e4m3_no_saturation(x):
+    x = np.asarray(x, dtype=np.float32)
+    out = _ORIG_E4M3_ENCODE(x)
+    over = np.abs(x) > 448.0
+    out[over] = 0x7F
+    return out
+
+
+_ORIG_E4M3_VALUES = op.e4m3_values
+_ORIG_E4M3_ENCODE = op.e4m3_encode
+
 MUTATIONS = {
+    "e4m3_ties_away_from_even": ("e4m3_encode", _e4m3_ties_away),
+    "e4m3_bias_8": ("e4m3_values", _e4m3_values_bias8),
+    "e4m3_overflow_to_nan": ("e4m3_encode", _e4m3_no_saturation),
     "interleaved_kv_head": ("kv_head_for", _interleaved_kv_head),
     "gather_ignores_table": ("gather_context", _gather_ignoring_table),
     "gather_off_by_one": ("gather_context", _gather_one_extra),
