@@ -44,6 +44,8 @@ DESCRIPTION = {
             "U[1,256], H=32, Hkv=8, D=128, BS=16, bf16; copy_blocks + reshape_and_cache + pa_decode",
     "tiny": "tiny paged decode: 4 seqs ctx {1,17,33,100}, H=Hkv=4, D=64, BS=16, fp32",
 }
+for _n in ("llama7b", "llama13b", "gqa70b", "beam"):
+    DESCRIPTION[_n + "_fp8"] = DESCRIPTION[_n].replace(", bf16", ", bf16 query / fp8 E4M3 KV cache")
 
 
 def parse():
@@ -53,7 +55,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama13b", choices=sorted(DESCRIPTION))
     ap.add_argument("--partition-tokens", type=int, default=0)
-    ap.add_argument("--others", default="llama7b,gqa70b,beam",
+    ap.add_argument("--others", default="llama7b,gqa70b,beam,llama13b_fp8,gqa70b_fp8",
                     help="comma list of extra workloads to report ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -66,8 +68,9 @@ def parse():
 def algorithmic_bytes(plan, spec) -> int:
     """K and V read once + q read + out written + block-table entries + context lengths."""
     e = 4 if spec.dtype == "f32" else 2
+    ekv = {"f32": 4, "bf16": 2, "fp8": 1}[spec.cache_dtype]
     ctx = [int(c) for c in plan.context_lens]
-    kv = sum(2 * spec.num_kv_heads * c * spec.head_dim * e for c in ctx)
+    kv = sum(2 * spec.num_kv_heads * c * spec.head_dim * ekv for c in ctx)
     qo = 2 * len(ctx) * spec.num_heads * spec.head_dim * e
     table = 4 * sum(-(-c // plan.block_size) for c in ctx)
     return kv + qo + table + 4 * len(ctx)
@@ -103,9 +106,12 @@ def run_workload(name, steps, warmup, partition_tokens, flush=False):
     spec, plan = x.spec, x.plan
     out = torch.empty_like(x.q)
     code = binding.PA_F32 if spec.dtype == "f32" else binding.PA_BF16
+    ccode = {"f32": binding.PA_F32, "bf16": binding.PA_BF16,
+             "fp8": binding.PA_FP8_E4M3}[spec.cache_dtype]
     ws_bytes = binding.pa_decode_workspace_size(plan.num_seqs, spec.num_heads, spec.num_kv_heads,
                                                 spec.head_dim, plan.block_size,
-                                                plan.max_context_len, code, partition_tokens)
+                                                plan.max_context_len, code, partition_tokens,
+                                                ccode)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if flush else None
     stream = torch.cuda.current_stream()
@@ -124,12 +130,13 @@ def run_workload(name, steps, warmup, partition_tokens, flush=False):
             binding.pa_copy_blocks(x.k_cache, x.v_cache, x.block_pairs, stream=stream)
         if has_tokens:
             binding.pa_reshape_and_cache(x.key, x.value, x.k_cache, x.v_cache, x.slot_mapping,
-                                         stream=stream)
+                                         stream=stream, k_scale=x.k_scale, v_scale=x.v_scale)
         if ev is not None:
             ev[0].record(stream)
         binding.pa_decode(out, x.q, x.k_cache, x.v_cache, x.block_tables, x.context_lens,
                           x.scale, plan.max_context_len, partition_tokens=partition_tokens,
-                          workspace=ws, stream=stream, shared_pages=shared, seq_order=order)
+                          workspace=ws, stream=stream, shared_pages=shared, seq_order=order,
+                          k_scale=x.k_scale, v_scale=x.v_scale)
         if ev is not None:
             ev[1].record(stream)
 
@@ -185,6 +192,7 @@ def run_workload(name, steps, warmup, partition_tokens, flush=False):
         "partition_tokens": partition_tokens,
         "shared_pages_flag": shared,
         "cache": "cold (MALL flushed between steps)" if flush else "warm",
+        "kv_cache_dtype": spec.cache_dtype,
     }
     del x, out, ws, scratch
     torch.cuda.empty_cache()

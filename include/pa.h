@@ -14,8 +14,8 @@
  *             block table; softmax; weighted sum of V), section 7 (each new token's
  *             K/V is stored into the cache, then paged attention runs).
  *
- * Layouts (row-major, element type T = float or bf16, the same T for every
- * floating-point buffer of one call):
+ * Layouts (row-major; element type `dtype` = float or bf16 for q, out, key and
+ * value; `cache_dtype` for the caches: the same as dtype, or PA_FP8_E4M3):
  *   q, out          [num_seqs, num_heads, head_dim]
  *   key, value      [num_tokens, num_kv_heads, head_dim]
  *   k_cache, v_cache[num_blocks, num_kv_heads, block_size, head_dim]
@@ -54,7 +54,12 @@
 extern "C" {
 #endif
 
-typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+/* Element types.  PA_FP8_E4M3 is a cache type only: OCP 8-bit floating point
+ * E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, S.1111.111 = NaN, largest finite 448), one float scale per cache:
+ * a code c stands for value(c) * scale.  ([tbr8] section "量化集成与部署"
+ * offers an fp8 KV cache without fixing the format; this is the reading used.) */
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
 
 /* pa_decode flags */
 enum {
@@ -78,7 +83,8 @@ typedef enum pa_status {
   PA_ERR_ALIGN = -5,       /* a floating-point buffer is not 16-byte aligned, or*/
                            /* an index buffer is not aligned to its element size*/
   PA_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required        */
-  PA_ERR_LAUNCH = -7       /* the HIP runtime reported an error after launch    */
+  PA_ERR_LAUNCH = -7,      /* the HIP runtime reported an error after launch    */
+  PA_ERR_VALUE = -8        /* a scale of an fp8 cache is not finite and > 0     */
 } pa_status;
 
 /*
@@ -89,16 +95,23 @@ typedef enum pa_status {
  * For every token i with 0 <= slot_mapping[i] < num_blocks*block_size:
  *   b = slot / block_size, o = slot % block_size, and for every kv head h
  *   k_cache[b, h, o, :] = key[i, h, :]  and  v_cache[b, h, o, :] = value[i, h, :]
- * (a bit-exact copy).  Negative slots mean "no write" (padding).  Slots at or
- * past num_blocks*block_size violate the precondition and are skipped.
+ * -- a bit-exact copy when cache_dtype == dtype.  With cache_dtype ==
+ * PA_FP8_E4M3 each element x is stored as the E4M3 code nearest to
+ * x * fl32(1 / k_scale) (v_scale for values), computed in binary32, ties to the
+ * even code, magnitudes >= 448 saturating to 448, NaN to a NaN code.
+ * Negative slots mean "no write" (padding).  Slots at or past
+ * num_blocks*block_size violate the precondition and are skipped.
  * Precondition: the non-negative slots are distinct (otherwise which token lands
- * in a slot is unspecified).  num_tokens == 0 is a no-op.
+ * in a slot is unspecified).  num_tokens == 0 is a no-op.  dtype is PA_F32 or
+ * PA_BF16; k_scale and v_scale are read only for an fp8 cache (finite, > 0,
+ * else PA_ERR_VALUE).
  */
 int pa_reshape_and_cache(const void* key, const void* value,
                          void* k_cache, void* v_cache,
                          const int64_t* slot_mapping,
                          int num_tokens, int num_blocks, int num_kv_heads,
-                         int block_size, int head_dim, int dtype, void* stream);
+                         int block_size, int head_dim, int dtype, int cache_dtype,
+                         float k_scale, float v_scale, void* stream);
 
 /*
  * pa_copy_blocks -- copy whole cache blocks, K and V, src -> dst.
@@ -113,7 +126,7 @@ int pa_reshape_and_cache(const void* key, const void* value,
  */
 int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs,
                    int num_pairs, int num_blocks, int num_kv_heads,
-                   int block_size, int head_dim, int dtype, void* stream);
+                   int block_size, int head_dim, int cache_dtype, void* stream);
 
 /*
  * pa_decode_workspace_size -- bytes of device workspace pa_decode needs for
@@ -126,7 +139,7 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs,
  */
 size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
                                 int head_dim, int block_size, int max_context_len,
-                                int dtype, int partition_tokens);
+                                int dtype, int cache_dtype, int partition_tokens);
 
 /*
  * pa_decode -- single-query decode attention over the paged cache.
@@ -135,10 +148,13 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
  * For every sequence s with L = context_lens[s] and every query head h, with
  * G = num_heads / num_kv_heads and kv head g = h / G (contiguous groups):
  *   K_t = k_cache[block_tables[s, t / block_size], g, t % block_size, :]
- *   V_t likewise, for t = 0 .. L-1
+ *   V_t likewise, for t = 0 .. L-1 (for an fp8 cache: the codes' values times
+ *   k_scale, resp. v_scale)
  *   w   = softmax_t(scale * dot(q[s, h, :], K_t))
  *   out[s, h, :] = sum_t w_t * V_t
- * accumulated in float32 and rounded to T (round-to-nearest-even for bf16).
+ * accumulated in float32 and rounded to dtype (round-to-nearest-even for
+ * bf16).  Supported (dtype, cache_dtype): (F32, F32), (BF16, BF16),
+ * (BF16, FP8_E4M3); k_scale and v_scale are read only for an fp8 cache.
  * L == 0 gives an all-zero row.  Slots past L in the last block and table
  * entries past ceil(L / block_size) are never read, so they may hold anything
  * (NaN included).
@@ -169,7 +185,8 @@ int pa_decode(void* out, const void* q,
               const int32_t* context_lens, const int32_t* seq_order,
               int num_seqs, int num_heads, int num_kv_heads, int head_dim,
               int block_size, int num_blocks, int max_context_len,
-              float scale, int dtype, int partition_tokens, int flags,
+              float scale, int dtype, int cache_dtype, float k_scale, float v_scale,
+              int partition_tokens, int flags,
               void* workspace, size_t workspace_bytes, void* stream);
 
 /* pa_status_string -- static, human-readable name of a status code. */

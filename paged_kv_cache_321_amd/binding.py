@@ -20,10 +20,11 @@ LIB_PATH = os.path.join(HERE, "libpa.so")
 
 PA_F32 = 0
 PA_BF16 = 1
+PA_FP8_E4M3 = 2
 PA_DECODE_SHARED_PAGES = 1
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
           -4: "PA_ERR_UNSUPPORTED", -5: "PA_ERR_ALIGN", -6: "PA_ERR_WORKSPACE",
-          -7: "PA_ERR_LAUNCH"}
+          -7: "PA_ERR_LAUNCH", -8: "PA_ERR_VALUE"}
 EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_workspace_size",
            "pa_decode", "pa_status_string")
 
@@ -41,14 +42,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise ImportError(f"{path} is not built; run `python -m paged_kv_cache_321_amd.build` "
                           "(or __graft_entry__.build())")
     lib = ctypes.CDLL(path)
-    lib.pa_reshape_and_cache.argtypes = [_vp, _vp, _vp, _vp, _vp] + [_c_int] * 6 + [_vp]
+    lib.pa_reshape_and_cache.argtypes = ([_vp, _vp, _vp, _vp, _vp] + [_c_int] * 7 +
+                                         [_c_float, _c_float, _vp])
     lib.pa_reshape_and_cache.restype = _c_int
     lib.pa_copy_blocks.argtypes = [_vp, _vp, _vp] + [_c_int] * 6 + [_vp]
     lib.pa_copy_blocks.restype = _c_int
-    lib.pa_decode_workspace_size.argtypes = [_c_int] * 8
+    lib.pa_decode_workspace_size.argtypes = [_c_int] * 9
     lib.pa_decode_workspace_size.restype = _c_size
     lib.pa_decode.argtypes = ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp] + [_c_int] * 7 +
-                              [_c_float, _c_int, _c_int, _c_int, _vp, _c_size, _vp])
+                              [_c_float, _c_int, _c_int, _c_float, _c_float, _c_int, _c_int, _vp,
+                               _c_size, _vp])
     lib.pa_decode.restype = _c_int
     lib.pa_status_string.argtypes = [_c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -68,11 +71,14 @@ def _check(status: int, what: str) -> None:
 
 
 def _dtype_code(t: torch.Tensor) -> int:
+    """Element type code; caches of E4M3 codes may be float8_e4m3fn or uint8."""
     if t.dtype == torch.float32:
         return PA_F32
     if t.dtype == torch.bfloat16:
         return PA_BF16
-    raise TypeError(f"unsupported element type {t.dtype} (float32 or bfloat16)")
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return PA_FP8_E4M3
+    raise TypeError(f"unsupported element type {t.dtype} (float32, bfloat16, or fp8 codes)")
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -96,20 +102,26 @@ def _device_contig(name: str, t: torch.Tensor) -> None:
 
 
 def pa_reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
-                         v_cache: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
-    """Store key/value [T, Hkv, D] into caches [NB, Hkv, BS, D] at slot_mapping [T]."""
+                         v_cache: torch.Tensor, slot_mapping: torch.Tensor, stream=None,
+                         k_scale: float = 1.0, v_scale: float = 1.0) -> None:
+    """Store key/value [T, Hkv, D] into caches [NB, Hkv, BS, D] at slot_mapping [T].
+
+    fp8 caches (float8_e4m3fn or uint8 code tensors) receive the E4M3 codes of
+    key / k_scale and value / v_scale.
+    """
     for n, t in (("key", key), ("value", value), ("k_cache", k_cache), ("v_cache", v_cache),
                  ("slot_mapping", slot_mapping)):
         _device_contig(n, t)
     _need(slot_mapping.dtype == torch.int64, "slot_mapping must be int64")
-    _need(key.dtype == value.dtype == k_cache.dtype == v_cache.dtype, "element types differ")
+    _need(key.dtype == value.dtype and k_cache.dtype == v_cache.dtype, "element types differ")
     nb, hkv, bs, d = k_cache.shape
     _need(v_cache.shape == k_cache.shape, "k_cache and v_cache shapes differ")
     t = key.shape[0]
     _need(key.shape == (t, hkv, d) and value.shape == key.shape, "key/value must be [T, Hkv, D]")
     _need(slot_mapping.shape == (t,), "slot_mapping must be [T]")
     st = LIB.pa_reshape_and_cache(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
-                                  _ptr(slot_mapping), t, nb, hkv, bs, d, _dtype_code(k_cache),
+                                  _ptr(slot_mapping), t, nb, hkv, bs, d, _dtype_code(key),
+                                  _dtype_code(k_cache), float(k_scale), float(v_scale),
                                   _stream(stream))
     _check(st, "pa_reshape_and_cache")
 
@@ -130,9 +142,10 @@ def pa_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_pairs: to
 
 def pa_decode_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
                              block_size: int, max_context_len: int, dtype: int,
-                             partition_tokens: int = 0) -> int:
+                             partition_tokens: int = 0, cache_dtype: Optional[int] = None) -> int:
+    cache_dtype = dtype if cache_dtype is None else cache_dtype
     n = LIB.pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                                     max_context_len, dtype, partition_tokens)
+                                     max_context_len, dtype, cache_dtype, partition_tokens)
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("pa_decode_workspace_size: arguments rejected by the library")
     return n
@@ -152,21 +165,23 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
               block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
               max_context_len: int, partition_tokens: int = 0,
               workspace: Optional[torch.Tensor] = None, stream=None,
-              shared_pages: bool = False, seq_order: Optional[torch.Tensor] = None) -> None:
+              shared_pages: bool = False, seq_order: Optional[torch.Tensor] = None,
+              k_scale: float = 1.0, v_scale: float = 1.0) -> None:
     """Decode attention of q [S, H, D] over the paged caches into out [S, H, D].
 
     ``workspace`` (uint8 device tensor) is allocated here when not given and
     the shape needs one.  ``shared_pages`` sets PA_DECODE_SHARED_PAGES (pages
     may be shared between sequences: read them with the default cache policy).
     ``seq_order`` (int32 device tensor [S], a permutation) sets the dispatch
-    order of the sequences; see ``longest_first``.
+    order of the sequences; see ``longest_first``.  fp8 caches (float8_e4m3fn
+    or uint8 codes) stand for code * k_scale / code * v_scale.
     """
     for n, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
                  ("block_tables", block_tables), ("context_lens", context_lens)):
         _device_contig(n, t)
     _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
           "block_tables and context_lens must be int32")
-    _need(q.dtype == out.dtype == k_cache.dtype == v_cache.dtype, "element types differ")
+    _need(q.dtype == out.dtype and k_cache.dtype == v_cache.dtype, "element types differ")
     s, h, d = q.shape
     nb, hkv, bs, d2 = k_cache.shape
     _need(d2 == d and out.shape == q.shape and v_cache.shape == k_cache.shape, "shape mismatch")
@@ -177,14 +192,16 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
         _need(seq_order.dtype == torch.int32 and seq_order.shape == (s,),
               "seq_order must be int32 [S]")
     code = _dtype_code(q)
-    need = pa_decode_workspace_size(s, h, hkv, d, bs, max_context_len, code, partition_tokens) \
-        if h > 0 and hkv > 0 and h % hkv == 0 else 0
+    ccode = _dtype_code(k_cache)
+    need = pa_decode_workspace_size(s, h, hkv, d, bs, max_context_len, code, partition_tokens,
+                                    ccode) if h > 0 and hkv > 0 and h % hkv == 0 else 0
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = LIB.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                        block_tables.shape[1], _ptr(context_lens), _ptr(seq_order), s, h, hkv, d, bs, nb,
-                       int(max_context_len), float(scale), code, int(partition_tokens),
+                       int(max_context_len), float(scale), code, ccode, float(k_scale),
+                       float(v_scale), int(partition_tokens),
                        PA_DECODE_SHARED_PAGES if shared_pages else 0,
                        _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "pa_decode")

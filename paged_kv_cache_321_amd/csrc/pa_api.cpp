@@ -5,6 +5,7 @@
 #include "pa.h"
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "pa_internal.h"
@@ -13,7 +14,11 @@ namespace {
 
 constexpr int kMaxGridYZ = 65535;
 
-int elem_bytes(int dtype) { return dtype == PA_F32 ? 4 : 2; }
+int elem_bytes(int dtype) { return dtype == PA_F32 ? 4 : dtype == PA_BF16 ? 2 : 1; }
+
+bool value_dtype(int dtype) { return dtype == PA_F32 || dtype == PA_BF16; }
+bool cache_dtype_ok(int dtype) { return value_dtype(dtype) || dtype == PA_FP8_E4M3; }
+bool good_scale(float s) { return isfinite(s) && s > 0.f; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -21,16 +26,18 @@ bool supported_head_dim(int d) { return d == 64 || d == 128; }
 bool supported_block_size(int bs) { return bs == 16 || bs == 32; }
 bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
-int cache_shape_status(int num_blocks, int num_kv_heads, int block_size, int head_dim, int dtype) {
-  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_DTYPE;
+int cache_shape_status(int num_blocks, int num_kv_heads, int block_size, int head_dim, int cache_dtype) {
+  if (!cache_dtype_ok(cache_dtype)) return PA_ERR_DTYPE;
   if (num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0 || head_dim <= 0) return PA_ERR_SHAPE;
   if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
 
 // Resolved partition length, or a negative status.
-int resolve_partition(int partition_tokens, int dtype, int head_dim, int block_size, int group) {
-  if (partition_tokens == 0) return pa::default_partition_tokens(dtype, head_dim, block_size, group);
+int resolve_partition(int partition_tokens, int dtype, int cache_dtype, int head_dim, int block_size,
+                      int group) {
+  if (partition_tokens == 0)
+    return pa::default_partition_tokens(dtype, cache_dtype, head_dim, block_size, group);
   if (partition_tokens < 0 || partition_tokens % block_size != 0) return PA_ERR_SHAPE;
   if (partition_tokens / block_size > pa::kMaxPagesPerPartition) return PA_ERR_UNSUPPORTED;
   return partition_tokens;
@@ -45,9 +52,13 @@ struct DecodeSizes {
 };
 
 DecodeSizes decode_sizes(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
-                         int max_context_len, int dtype, int partition_tokens) {
+                         int max_context_len, int dtype, int cache_dtype, int partition_tokens) {
   DecodeSizes z{PA_OK, 0, 1, 0, 0};
-  if (dtype != PA_F32 && dtype != PA_BF16) { z.status = PA_ERR_DTYPE; return z; }
+  if (!value_dtype(dtype) || !cache_dtype_ok(cache_dtype)) { z.status = PA_ERR_DTYPE; return z; }
+  if (cache_dtype != dtype && !(dtype == PA_BF16 && cache_dtype == PA_FP8_E4M3)) {
+    z.status = PA_ERR_UNSUPPORTED;
+    return z;
+  }
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
       max_context_len < 0) {
     z.status = PA_ERR_SHAPE;
@@ -59,7 +70,7 @@ DecodeSizes decode_sizes(int num_seqs, int num_heads, int num_kv_heads, int head
     z.status = PA_ERR_UNSUPPORTED;
     return z;
   }
-  const int pt = resolve_partition(partition_tokens, dtype, head_dim, block_size, group);
+  const int pt = resolve_partition(partition_tokens, dtype, cache_dtype, head_dim, block_size, group);
   if (pt < 0) { z.status = pt; return z; }
   z.partition_tokens = pt;
   z.max_parts = max_context_len <= pt ? 1 : (max_context_len + pt - 1) / pt;
@@ -81,22 +92,30 @@ const char* pa_status_string(int status) {
     case PA_OK: return "PA_OK";
     case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
     case PA_ERR_SHAPE: return "PA_ERR_SHAPE: inconsistent or invalid sizes";
-    case PA_ERR_DTYPE: return "PA_ERR_DTYPE: dtype must be PA_F32 or PA_BF16";
+    case PA_ERR_DTYPE:
+      return "PA_ERR_DTYPE: dtype must be PA_F32 or PA_BF16, a cache type PA_F32, PA_BF16 or PA_FP8_E4M3";
     case PA_ERR_UNSUPPORTED:
       return "PA_ERR_UNSUPPORTED: head_dim must be 64/128, block_size 16/32, heads per kv head "
-             "1/2/4/8, grid within limits";
+             "1/2/4/8, (dtype, cache_dtype) one of (F32, F32), (BF16, BF16), (BF16, FP8_E4M3), "
+             "grid within limits";
     case PA_ERR_ALIGN: return "PA_ERR_ALIGN: buffer not aligned (16 bytes for data, element size for indices)";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: HIP reported an error after the launch";
+    case PA_ERR_VALUE: return "PA_ERR_VALUE: an fp8 cache scale must be finite and > 0";
     default: return "unknown pa status";
   }
 }
 
 int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                          const int64_t* slot_mapping, int num_tokens, int num_blocks, int num_kv_heads,
-                         int block_size, int head_dim, int dtype, void* stream) {
-  int st = cache_shape_status(num_blocks, num_kv_heads, block_size, head_dim, dtype);
+                         int block_size, int head_dim, int dtype, int cache_dtype, float k_scale,
+                         float v_scale, void* stream) {
+  if (!value_dtype(dtype)) return PA_ERR_DTYPE;
+  int st = cache_shape_status(num_blocks, num_kv_heads, block_size, head_dim, cache_dtype);
   if (st != PA_OK) return st;
+  if (cache_dtype != dtype && cache_dtype != PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
+  const bool fp8 = cache_dtype == PA_FP8_E4M3;
+  if (fp8 && (!good_scale(k_scale) || !good_scale(v_scale))) return PA_ERR_VALUE;
   if (num_tokens < 0) return PA_ERR_SHAPE;
   if (!k_cache || !v_cache) return PA_ERR_NULL;
   if (num_tokens == 0) return PA_OK;
@@ -104,18 +123,19 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
   if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(slot_mapping, 8))
     return PA_ERR_ALIGN;
-  const int64_t items = (int64_t)num_tokens * num_kv_heads * head_dim * elem_bytes(dtype) / 16;
+  const int64_t items = (int64_t)num_tokens * num_kv_heads * head_dim * elem_bytes(cache_dtype) / 16;
   if ((items + 255) / 256 > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
   pa::ReshapeLaunch a{key, value, k_cache, v_cache, slot_mapping, num_tokens, num_blocks,
-                      num_kv_heads, block_size, head_dim, elem_bytes(dtype),
+                      num_kv_heads, block_size, head_dim, dtype, cache_dtype,
+                      fp8 ? 1.0f / k_scale : 1.f, fp8 ? 1.0f / v_scale : 1.f,
                       static_cast<hipStream_t>(stream)};
   return pa::launch_reshape_and_cache(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs, int num_pairs,
-                   int num_blocks, int num_kv_heads, int block_size, int head_dim, int dtype,
+                   int num_blocks, int num_kv_heads, int block_size, int head_dim, int cache_dtype,
                    void* stream) {
-  int st = cache_shape_status(num_blocks, num_kv_heads, block_size, head_dim, dtype);
+  int st = cache_shape_status(num_blocks, num_kv_heads, block_size, head_dim, cache_dtype);
   if (st != PA_OK) return st;
   if (num_pairs < 0) return PA_ERR_SHAPE;
   if (!k_cache || !v_cache) return PA_ERR_NULL;
@@ -123,14 +143,15 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs, int
   if (!block_pairs) return PA_ERR_NULL;
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_pairs, 8)) return PA_ERR_ALIGN;
   pa::CopyLaunch a{k_cache, v_cache, block_pairs, num_pairs, num_blocks, num_kv_heads,
-                   block_size, head_dim, elem_bytes(dtype), static_cast<hipStream_t>(stream)};
+                   block_size, head_dim, elem_bytes(cache_dtype), static_cast<hipStream_t>(stream)};
   return pa::launch_copy_blocks(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
-                                int block_size, int max_context_len, int dtype, int partition_tokens) {
+                                int block_size, int max_context_len, int dtype, int cache_dtype,
+                                int partition_tokens) {
   const DecodeSizes z = decode_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                                     max_context_len, dtype, partition_tokens);
+                                     max_context_len, dtype, cache_dtype, partition_tokens);
   return z.status == PA_OK ? z.total : (size_t)-1;
 }
 
@@ -138,11 +159,14 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
               const int32_t* seq_order, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
               int block_size,
-              int num_blocks, int max_context_len, float scale, int dtype, int partition_tokens,
-              int flags, void* workspace, size_t workspace_bytes, void* stream) {
+              int num_blocks, int max_context_len, float scale, int dtype, int cache_dtype,
+              float k_scale, float v_scale, int partition_tokens, int flags, void* workspace,
+              size_t workspace_bytes, void* stream) {
   const DecodeSizes z = decode_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                                     max_context_len, dtype, partition_tokens);
+                                     max_context_len, dtype, cache_dtype, partition_tokens);
   if (z.status != PA_OK) return z.status;
+  const bool fp8 = cache_dtype == PA_FP8_E4M3;
+  if (fp8 && (!good_scale(k_scale) || !good_scale(v_scale))) return PA_ERR_VALUE;
   if (num_blocks <= 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * block_size < max_context_len) return PA_ERR_SHAPE;
   if (flags & ~PA_DECODE_SHARED_PAGES) return PA_ERR_UNSUPPORTED;
@@ -176,6 +200,9 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   a.max_context_len = max_context_len;
   a.scale = scale;
   a.dtype = dtype;
+  a.cache_dtype = cache_dtype;
+  a.k_scale = fp8 ? k_scale : 1.f;
+  a.v_scale = fp8 ? v_scale : 1.f;
   a.partition_tokens = z.partition_tokens;
   a.shared_pages = (flags & PA_DECODE_SHARED_PAGES) != 0;
   a.max_parts = z.max_parts;

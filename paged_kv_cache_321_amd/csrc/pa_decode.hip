@@ -61,7 +61,7 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams p) {
   for (int off = 32; off >= 1; off >>= 1) ll += __shfl_xor(ll, off);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const float o = (ll == 0.f) ? 0.f : aa[e] / ll;
+    const float o = (ll == 0.f) ? 0.f : aa[e] * p.v_scale / ll;
     Elem<T>::store(static_cast<T*>(p.out) + ((int64_t)s * p.num_heads + h) * D + lane + 64 * e, o);
   }
 }
@@ -78,9 +78,10 @@ hipError_t launch_reduce(const DecodeLaunch& a, const DecodeParams& p) {
 
 }  // namespace
 
-static bool use_mfma_path(int dtype, int group) { return dtype == 1 && group >= 2; }
+// Grouped heads with a bf16 query (bf16 or fp8 cache) run on the matrix cores.
+static bool use_mfma_path(int dtype, int group) { return dtype == kDtypeBf16 && group >= 2; }
 
-int default_partition_tokens(int dtype, int /*head_dim*/, int block_size, int group) {
+int default_partition_tokens(int dtype, int /*cache_dtype*/, int /*head_dim*/, int block_size, int group) {
   // Fixed lengths (never the batch size, so a sequence's result does not
   // depend on the batch).  Vector path: 2048 tokens; matrix-core path: 4096
   // tokens (fewer, longer workgroups measured faster on long GQA contexts).
@@ -109,11 +110,13 @@ hipError_t launch_decode(const DecodeLaunch& a) {
   p.max_context_len = a.max_context_len;
   p.partition_tokens = a.partition_tokens;
   p.max_parts = a.max_parts;
-  p.scale_log2e = a.scale * kLog2e;
+  const bool fp8 = a.cache_dtype == kDtypeFp8;
+  p.scale_log2e = a.scale * kLog2e * (fp8 ? a.k_scale : 1.f);
+  p.v_scale = fp8 ? a.v_scale : 1.f;
   const int group = a.num_heads / a.num_kv_heads;
   hipError_t e = use_mfma_path(a.dtype, group) ? launch_partition_mfma(a, p) : launch_partition_valu(a, p);
   if (e != hipSuccess || a.max_parts <= 1) return e;
-  return a.dtype == 0 ? launch_reduce<float>(a, p) : launch_reduce<uint16_t>(a, p);
+  return a.dtype == kDtypeF32 ? launch_reduce<float>(a, p) : launch_reduce<uint16_t>(a, p);
 }
 
 }  // namespace pa

@@ -1,5 +1,6 @@
-// Decode partition kernel on the matrix cores, for bf16 caches where several
-// query heads share a kv head (grouped-query attention, G = H / Hkv > 1).
+// Decode partition kernel on the matrix cores, for a bf16 query where several
+// query heads share a kv head (grouped-query attention, G = H / Hkv > 1); the
+// cache holds bf16 or E4M3 fp8 codes (widened to bf16 in registers, exactly).
 //
 // What is computed is the same as the vector kernel ("vLLM 深度解读",
 // luoboask.github.io, section 3 "PagedAttention CUDA Kernel"): per query head,
@@ -52,21 +53,42 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16_bits(lo)) | (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
 }
 
+// Eight E4M3 codes -> eight bf16 (exact: an E4M3 value needs 3 mantissa bits,
+// so its binary32 form has 16 zero low bits and the high half is its bf16).
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  float f[8];
+  fp8x4_to_f32(lo, f);
+  fp8x4_to_f32(hi, f + 4);
+  uint4 r;
+  r.x = (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
+  r.y = (__float_as_uint(f[2]) >> 16) | (__float_as_uint(f[3]) & 0xffff0000u);
+  r.z = (__float_as_uint(f[4]) >> 16) | (__float_as_uint(f[5]) & 0xffff0000u);
+  r.w = (__float_as_uint(f[6]) >> 16) | (__float_as_uint(f[7]) & 0xffff0000u);
+  return r;
+}
+
 // 16-byte chunk c of LDS row `row` is stored at chunk c ^ swz(row).  Rows
 // 4 apart (the rows one transposed read touches) land 2 chunks apart, so the
 // four 32-byte segments of a read fall in distinct banks.
 __device__ __forceinline__ int swz(int row) { return 2 * ((row >> 2) & 3); }
 
-template <int D, int BS, int G, bool NONTEMPORAL>
+// TC: cache element type, bf16 bits (uint16_t) or E4M3 codes (uint8_t); the
+// query is bf16 either way and the products run on bf16 MFMA (E4M3 widens to
+// bf16 exactly).
+template <typename TC, int D, int BS, int G, bool NONTEMPORAL>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void decode_partition_mfma_kernel(DecodeParams p) {
+  constexpr bool kFp8 = sizeof(TC) == 1;
   constexpr int NT = BS / 16;       // 16-token tiles per page
   constexpr int NC = D / 32;        // 32-wide steps of the QK contraction
   constexpr int NM = D / 16;        // 16-wide output tiles along head_dim
-  constexpr int ROWB = D * 2;       // bytes of one token row
-  constexpr int NCH = ROWB / 16;    // 16-byte chunks per row
-  constexpr int RPL = 64 / NCH;     // rows per row-contiguous wave load
+  constexpr int ROWB = D * 2;       // bytes of one bf16 token row (LDS page)
+  constexpr int NCH = ROWB / 16;    // 16-byte bf16 chunks per row
+  constexpr int CROWB = D * (int)sizeof(TC);  // bytes of one cache token row
+  constexpr int CNCH = CROWB / 16;  // 16-byte cache chunks per row
+  constexpr int RPL = 64 / CNCH;    // rows per row-contiguous wave load of V
   constexpr int NV = BS / RPL;      // V loads per lane per page
-  constexpr int PAGEB = BS * ROWB;  // bytes of one page
+  constexpr int NKL = kFp8 ? D / 64 : NC;  // K loads per 16-token tile
+  constexpr int PAGEB = BS * ROWB;  // bytes of one bf16 page in LDS
   constexpr int EPI = (kWaves * G * D + 2 * kWaves * G) * 4;
   constexpr int SMEM = kWaves * PAGEB > EPI ? kWaves * PAGEB : EPI;
   static_assert(G >= 2 && G <= 16 && NCH >= 8 && BS % RPL == 0, "tile shape");
@@ -89,16 +111,20 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   const int my_id = load_page_ids(p, s, r, wave, lane, &ids_bad);
   const bool bad = r.ctx_bad || ids_bad;
 
-  // B operand of S^T = K Q^T: lane holds Q[head l16][32c + 8 g4 .. +7]; zero
-  // for the padding heads l16 >= G.
+  // B operand of S^T = K Q^T: for bf16 caches lane holds Q[head l16][32c +
+  // 8 g4 .. +7]; for fp8 caches, whose 16-byte K loads carry 16 columns, step
+  // c = 2kk + h holds columns 64kk + 16 g4 + 8h .. +7 (the K operand uses the
+  // same column order, so the contraction is unchanged).  Zero for the padding
+  // heads l16 >= G.
   bf16x8_t qb[NC];
   {
     const uint16_t* qp = static_cast<const uint16_t*>(p.q) +
-                         ((int64_t)s * p.num_heads + (int64_t)kvh * G + (l16 < G ? l16 : 0)) * D + 8 * g4;
+                         ((int64_t)s * p.num_heads + (int64_t)kvh * G + (l16 < G ? l16 : 0)) * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
+      const int col0 = kFp8 ? 64 * (c >> 1) + 16 * g4 + 8 * (c & 1) : 32 * c + 8 * g4;
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (l16 < G) v = *reinterpret_cast<const uint4*>(qp + 32 * c);
+      if (l16 < G) v = *reinterpret_cast<const uint4*>(qp + col0);
       qb[c] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -112,24 +138,27 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   unsigned char* vbuf = smem + wave * PAGEB;
 
-  const uint16_t* kc = static_cast<const uint16_t*>(p.k_cache) + (int64_t)kvh * BS * D;
-  const uint16_t* vc = static_cast<const uint16_t*>(p.v_cache) + (int64_t)kvh * BS * D;
-  const int k_off = l16 * D + 8 * g4;          // A operand: token l16, 8 elements at 8 g4
-  const int v_row = lane / NCH;                // row-contiguous V load
-  const int v_ch = lane % NCH;
-  const int v_off = v_row * D + v_ch * 8;
+  const TC* kc = static_cast<const TC*>(p.k_cache) + (int64_t)kvh * BS * D;
+  const TC* vc = static_cast<const TC*>(p.v_cache) + (int64_t)kvh * BS * D;
+  // A operand of S^T: token l16; bf16: 8 columns at 32c + 8 g4; fp8: 16 columns
+  // at 64kk + 16 g4.
+  const int k_off = l16 * D + (kFp8 ? 16 : 8) * g4;
+  const int v_row = lane / CNCH;               // row-contiguous V load
+  const int v_ch = lane % CNCH;
+  const int v_off = v_row * D + v_ch * (16 / (int)sizeof(TC));
 
-  auto load_k = [&](int k, uint4 (&kr)[NT][NC]) {
+  auto load_k = [&](int k, uint4 (&kr)[NT][NKL]) {
     const int64_t phys = __builtin_amdgcn_readlane(my_id, k);
-    const uint16_t* kp = kc + phys * p.block_stride + k_off;
+    const TC* kp = kc + phys * p.block_stride + k_off;
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) kr[tt][c] = load_page16<NONTEMPORAL>(kp + tt * 16 * D + 32 * c);
+      for (int c = 0; c < NKL; ++c)
+        kr[tt][c] = load_page16<NONTEMPORAL>(kp + tt * 16 * D + (kFp8 ? 64 : 32) * c);
   };
   auto load_v = [&](int k, uint4 (&vr)[NV]) {
     const int64_t phys = __builtin_amdgcn_readlane(my_id, k);
-    const uint16_t* vp = vc + phys * p.block_stride + v_off;
+    const TC* vp = vc + phys * p.block_stride + v_off;
 #pragma unroll
     for (int n = 0; n < NV; ++n) vr[n] = load_page16<NONTEMPORAL>(vp + n * RPL * D);
   };
@@ -140,9 +169,19 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
       const int row = n * RPL + v_row;
-      uint4 v = vr[n];
-      if (!full && t0 + row >= tok1) v = make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4*>(vbuf + row * ROWB + ((v_ch ^ swz(row)) << 4)) = v;
+      const bool keep = full || t0 + row < tok1;
+      if constexpr (kFp8) {
+        // 16 codes -> 16 bf16: LDS chunks 2 v_ch and 2 v_ch + 1 of the row.
+        uint4 a = fp8x8_to_bf16x8(vr[n].x, vr[n].y);
+        uint4 b = fp8x8_to_bf16x8(vr[n].z, vr[n].w);
+        if (!keep) a = b = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(vbuf + row * ROWB + (((2 * v_ch) ^ swz(row)) << 4)) = a;
+        *reinterpret_cast<uint4*>(vbuf + row * ROWB + (((2 * v_ch + 1) ^ swz(row)) << 4)) = b;
+      } else {
+        uint4 v = vr[n];
+        if (!keep) v = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(vbuf + row * ROWB + ((v_ch ^ swz(row)) << 4)) = v;
+      }
     }
     wave_lds_fence();
   };
@@ -150,14 +189,22 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     return *reinterpret_cast<const uint16_t*>(vbuf + t * ROWB + (((d >> 3) ^ swz(t)) << 4) + ((d & 7) << 1));
   };
 
-  auto scores = [&](const uint4 (&kr)[NT][NC], f32x4_t (&st)[NT]) {
+  auto scores = [&](const uint4 (&kr)[NT][NKL], f32x4_t (&st)[NT]) {
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
       st[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        st[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[tt][c]), qb[c],
-                                                         st[tt], 0, 0, 0);
+      for (int c = 0; c < NC; ++c) {
+        uint4 ka;
+        if constexpr (kFp8) {
+          const uint4& w = kr[tt][c >> 1];
+          ka = (c & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
+        } else {
+          ka = kr[tt][c];
+        }
+        st[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qb[c], st[tt], 0,
+                                                         0, 0);
+      }
     }
   };
 
@@ -239,7 +286,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   // as this page's V sits in LDS, the next K as soon as the QK products have
   // consumed this page's K, so one page per wave is always in flight.
   if (!bad && nk > 0) {
-    uint4 kr[NT][NC], vr[NV];
+    uint4 kr[NT][NKL], vr[NV];
     load_k(0, kr);
     load_v(0, vr);
     for (int k = 0; k < nk; ++k) {
@@ -274,35 +321,40 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   merge_waves_and_store<uint16_t, D, G>(p, sm_acc, sm_m, sm_l, s, kvh, part, r.nparts);
 }
 
-template <int D, int BS, int G>
+template <typename TC, int D, int BS, int G>
 hipError_t launch_t(const DecodeLaunch& a, const DecodeParams& p) {
   dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
   if (a.shared_pages)
-    hipLaunchKernelGGL((decode_partition_mfma_kernel<D, BS, G, false>), grid, dim3(kWaves * 64), 0, a.stream, p);
+    hipLaunchKernelGGL((decode_partition_mfma_kernel<TC, D, BS, G, false>), grid, dim3(kWaves * 64), 0, a.stream, p);
   else
-    hipLaunchKernelGGL((decode_partition_mfma_kernel<D, BS, G, true>), grid, dim3(kWaves * 64), 0, a.stream, p);
+    hipLaunchKernelGGL((decode_partition_mfma_kernel<TC, D, BS, G, true>), grid, dim3(kWaves * 64), 0, a.stream, p);
   return hipGetLastError();
 }
 
-template <int D, int BS>
+template <typename TC, int D, int BS>
 hipError_t by_group(const DecodeLaunch& a, const DecodeParams& p) {
   switch (a.num_heads / a.num_kv_heads) {
-    case 2: return launch_t<D, BS, 2>(a, p);
-    case 4: return launch_t<D, BS, 4>(a, p);
-    case 8: return launch_t<D, BS, 8>(a, p);
+    case 2: return launch_t<TC, D, BS, 2>(a, p);
+    case 4: return launch_t<TC, D, BS, 4>(a, p);
+    case 8: return launch_t<TC, D, BS, 8>(a, p);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int D>
+template <typename TC, int D>
 hipError_t by_block(const DecodeLaunch& a, const DecodeParams& p) {
-  return a.block_size == 16 ? by_group<D, 16>(a, p) : by_group<D, 32>(a, p);
+  return a.block_size == 16 ? by_group<TC, D, 16>(a, p) : by_group<TC, D, 32>(a, p);
+}
+
+template <typename TC>
+hipError_t by_dim(const DecodeLaunch& a, const DecodeParams& p) {
+  return a.head_dim == 64 ? by_block<TC, 64>(a, p) : by_block<TC, 128>(a, p);
 }
 
 }  // namespace
 
 hipError_t launch_partition_mfma(const DecodeLaunch& a, const DecodeParams& p) {
-  return a.head_dim == 64 ? by_block<64>(a, p) : by_block<128>(a, p);
+  return a.cache_dtype == kDtypeFp8 ? by_dim<uint8_t>(a, p) : by_dim<uint16_t>(a, p);
 }
 
 }  // namespace pa

@@ -1,5 +1,8 @@
 // Decode partition kernel on the vector ALUs: used when every page serves one
 // query head (no grouping), for fp32 caches, and as the general fallback.
+// Caches may hold bf16, fp32 or E4M3 fp8 codes (16 per 16-byte load, widened
+// with v_cvt_pk_f32_fp8; k_scale is folded into the score scale and v_scale
+// into the final normalisation).
 //
 // What is computed: "vLLM 深度解读" (luoboask.github.io), section 3
 // "PagedAttention CUDA Kernel" -- per (sequence, query head), scale * q.k for
@@ -37,11 +40,13 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 // One workgroup = kWaves waves = one (partition, kv head, sequence); it serves
-// the G query heads that share the kv head.
-template <typename T, int D, int BS, int G, bool NONTEMPORAL>
+// the G query heads that share the kv head.  TQ is the query/output element
+// type (float or bf16 bits), TC the cache element type (the same, or E4M3
+// codes with a bf16 query).
+template <typename TQ, typename TC, int D, int BS, int G, bool NONTEMPORAL>
 __global__ __launch_bounds__(kWaves * 64) void decode_partition_valu_kernel(DecodeParams p) {
-  using E = Elem<T>;
-  constexpr int VEC = E::kVec;
+  using E = Elem<TC>;
+  constexpr int VEC = E::kVec;  // cache elements per 16-byte load
   constexpr int LPT = D / VEC;   // lanes per token row
   constexpr int TPL = 64 / LPT;  // token rows per wave-wide load
   constexpr int NLD = BS / TPL;  // loads per page
@@ -65,21 +70,29 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partition_valu_kernel(Deco
   const int my_id = load_page_ids(p, s, r, wave, lane, &ids_bad);
   const bool bad = r.ctx_bad || ids_bad;
 
-  // Query rows of the group: bf16 pairs kept packed for v_dot2 (the scale is
-  // applied to the reduced score); fp32 pre-scaled by scale * log2(e).
-  constexpr bool kBf16 = sizeof(T) == 2;
+  // Query rows of the group (this lane's VEC columns): with bf16 query and
+  // cache the pairs stay packed for v_dot2 (the scale is applied to the
+  // reduced score); otherwise they are widened and pre-scaled.
+  constexpr bool kDot2 = sizeof(TQ) == 2 && sizeof(TC) == 2;
+  constexpr int QVEC = Elem<TQ>::kVec;  // query elements per 16-byte load
+  static_assert(VEC % QVEC == 0, "query load");
   float qf[G][VEC];
   uint32_t qw[G][4];
   {
-    const T* qb = static_cast<const T*>(p.q) + ((int64_t)s * p.num_heads + (int64_t)kvh * G) * D + col * VEC;
+    const TQ* qb = static_cast<const TQ*>(p.q) + ((int64_t)s * p.num_heads + (int64_t)kvh * G) * D + col * VEC;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const uint4 q4 = *reinterpret_cast<const uint4*>(qb + g * D);
-      qw[g][0] = q4.x;
-      qw[g][1] = q4.y;
-      qw[g][2] = q4.z;
-      qw[g][3] = q4.w;
-      E::unpack(q4, qf[g]);
+#pragma unroll
+      for (int c = 0; c < VEC / QVEC; ++c) {
+        const uint4 q4 = *reinterpret_cast<const uint4*>(qb + g * D + c * QVEC);
+        if (c == 0) {
+          qw[g][0] = q4.x;
+          qw[g][1] = q4.y;
+          qw[g][2] = q4.z;
+          qw[g][3] = q4.w;
+        }
+        Elem<TQ>::unpack(q4, qf[g] + c * QVEC);
+      }
 #pragma unroll
       for (int e = 0; e < VEC; ++e) qf[g][e] *= p.scale_log2e;
     }
@@ -94,13 +107,13 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partition_valu_kernel(Deco
     for (int e = 0; e < VEC; ++e) acc[g][e] = 0.f;
   }
 
-  const T* kbase = static_cast<const T*>(p.k_cache) + (int64_t)kvh * BS * D + row * D + col * VEC;
-  const T* vbase = static_cast<const T*>(p.v_cache) + (int64_t)kvh * BS * D + row * D + col * VEC;
+  const TC* kbase = static_cast<const TC*>(p.k_cache) + (int64_t)kvh * BS * D + row * D + col * VEC;
+  const TC* vbase = static_cast<const TC*>(p.v_cache) + (int64_t)kvh * BS * D + row * D + col * VEC;
 
   auto load_page = [&](int k, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
     const int64_t phys = __builtin_amdgcn_readlane(my_id, k);
-    const T* kp = kbase + phys * p.block_stride;
-    const T* vp = vbase + phys * p.block_stride;
+    const TC* kp = kbase + phys * p.block_stride;
+    const TC* vp = vbase + phys * p.block_stride;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) kr[i] = load_page16<NONTEMPORAL>(kp + i * TPL * D);
 #pragma unroll
@@ -113,7 +126,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partition_valu_kernel(Deco
     float sc[G][NLD];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      if constexpr (kBf16) {
+      if constexpr (kDot2) {
         const uint32_t kw[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -139,7 +152,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partition_valu_kernel(Deco
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         sc[g][i] = row_sum<LPT>(sc[g][i]);
-        if constexpr (kBf16) sc[g][i] *= p.scale_log2e;
+        if constexpr (kDot2) sc[g][i] *= p.scale_log2e;
       }
     bool valid[NLD];
 #pragma unroll
@@ -229,46 +242,47 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partition_valu_kernel(Deco
     }
   }
   __syncthreads();
-  merge_waves_and_store<T, D, G>(p, sm_acc, sm_m, sm_l, s, kvh, part, r.nparts);
+  merge_waves_and_store<TQ, D, G>(p, sm_acc, sm_m, sm_l, s, kvh, part, r.nparts);
 }
 
-template <typename T, int D, int BS, int G>
+template <typename TQ, typename TC, int D, int BS, int G>
 hipError_t launch_t(const DecodeLaunch& a, const DecodeParams& p) {
   dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
   if (a.shared_pages)
-    hipLaunchKernelGGL((decode_partition_valu_kernel<T, D, BS, G, false>), grid, dim3(kWaves * 64), 0,
+    hipLaunchKernelGGL((decode_partition_valu_kernel<TQ, TC, D, BS, G, false>), grid, dim3(kWaves * 64), 0,
                        a.stream, p);
   else
-    hipLaunchKernelGGL((decode_partition_valu_kernel<T, D, BS, G, true>), grid, dim3(kWaves * 64), 0,
+    hipLaunchKernelGGL((decode_partition_valu_kernel<TQ, TC, D, BS, G, true>), grid, dim3(kWaves * 64), 0,
                        a.stream, p);
   return hipGetLastError();
 }
 
-template <typename T, int D, int BS>
+template <typename TQ, typename TC, int D, int BS>
 hipError_t by_group(const DecodeLaunch& a, const DecodeParams& p) {
   switch (a.num_heads / a.num_kv_heads) {
-    case 1: return launch_t<T, D, BS, 1>(a, p);
-    case 2: return launch_t<T, D, BS, 2>(a, p);
-    case 4: return launch_t<T, D, BS, 4>(a, p);
-    case 8: return launch_t<T, D, BS, 8>(a, p);
+    case 1: return launch_t<TQ, TC, D, BS, 1>(a, p);
+    case 2: return launch_t<TQ, TC, D, BS, 2>(a, p);
+    case 4: return launch_t<TQ, TC, D, BS, 4>(a, p);
+    case 8: return launch_t<TQ, TC, D, BS, 8>(a, p);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T, int D>
+template <typename TQ, typename TC, int D>
 hipError_t by_block(const DecodeLaunch& a, const DecodeParams& p) {
-  return a.block_size == 16 ? by_group<T, D, 16>(a, p) : by_group<T, D, 32>(a, p);
+  return a.block_size == 16 ? by_group<TQ, TC, D, 16>(a, p) : by_group<TQ, TC, D, 32>(a, p);
 }
 
-template <typename T>
+template <typename TQ, typename TC>
 hipError_t by_dim(const DecodeLaunch& a, const DecodeParams& p) {
-  return a.head_dim == 64 ? by_block<T, 64>(a, p) : by_block<T, 128>(a, p);
+  return a.head_dim == 64 ? by_block<TQ, TC, 64>(a, p) : by_block<TQ, TC, 128>(a, p);
 }
 
 }  // namespace
 
 hipError_t launch_partition_valu(const DecodeLaunch& a, const DecodeParams& p) {
-  return a.dtype == 0 ? by_dim<float>(a, p) : by_dim<uint16_t>(a, p);
+  if (a.cache_dtype == kDtypeFp8) return by_dim<uint16_t, uint8_t>(a, p);
+  return a.dtype == kDtypeF32 ? by_dim<float, float>(a, p) : by_dim<uint16_t, uint16_t>(a, p);
 }
 
 }  // namespace pa

@@ -87,6 +87,49 @@ struct Elem<float> {
   __device__ static __forceinline__ void store(float* p, float v) { *p = v; }
 };
 
+// OCP E4M3 codes (gfx950's fp8 format: bias 7, largest finite 448, no
+// infinities).  Widening uses v_cvt_pk_f32_fp8, exact for every code.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
+  const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+  const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+  f[0] = lo.x;
+  f[1] = lo.y;
+  f[2] = hi.x;
+  f[3] = hi.y;
+}
+
+// Nearest finite E4M3 code of x, ties to even, |x| >= 448 saturating to 448,
+// NaN to 0x7F (with the sign of x).  Written on the binary32 bit pattern:
+// below 2^-6 the code is the integer nearest x * 2^9; above, the 23-bit
+// mantissa is rounded to 3 bits in place (a carry moves into the exponent) and
+// the exponent is re-biased from 127 to 7.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;       // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;      // >= 448 (and inf): saturate
+  if (a < 0x3c800000u) {                          // < 2^-6: multiples of 2^-9
+    return sign | static_cast<uint32_t>(__builtin_rintf(__uint_as_float(a) * 512.f));
+  }
+  const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
+  const uint32_t code = (r >> 20) - (120u << 3);
+  return sign | (code > 0x7eu ? 0x7eu : code);
+}
+
+template <>
+struct Elem<uint8_t> {
+  static constexpr int kVec = 16;
+  __device__ static __forceinline__ void unpack(const uint4& r, float* f) {
+    fp8x4_to_f32(r.x, f);
+    fp8x4_to_f32(r.y, f + 4);
+    fp8x4_to_f32(r.z, f + 8);
+    fp8x4_to_f32(r.w, f + 12);
+  }
+};
+
 template <>
 struct Elem<uint16_t> {
   static constexpr int kVec = 8;
@@ -121,7 +164,8 @@ struct DecodeParams {
   int max_context_len;
   int partition_tokens;
   int max_parts;
-  float scale_log2e;
+  float scale_log2e;  // softmax scale * log2(e), times k_scale for fp8 caches
+  float v_scale;      // multiplies the output (1 unless the cache holds fp8 codes)
 };
 
 // Sequence served by grid slot z (the caller may reorder dispatch); -1 if the
@@ -196,7 +240,7 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeParams& p, con
     }
     const int64_t sh = (int64_t)s * p.num_heads + (int64_t)kvh * G + g;
     if (nparts == 1) {
-      const float o = (ll == 0.f) ? 0.f : aa / ll;
+      const float o = (ll == 0.f) ? 0.f : aa * p.v_scale / ll;
       Elem<T>::store(static_cast<T*>(p.out) + sh * D + d, o);
     } else {
       const int64_t slot = sh * p.max_parts + part;

@@ -12,6 +12,11 @@ namespace pa {
 // the waves round-robin; each wave keeps one page id per lane, so a partition
 // holds at most kWaves * 64 pages.
 constexpr int kWaves = 4;
+
+// Element type codes (the values of pa_dtype in pa.h).
+constexpr int kDtypeF32 = 0;
+constexpr int kDtypeBf16 = 1;
+constexpr int kDtypeFp8 = 2;
 constexpr int kMaxPagesPerPartition = kWaves * 64;
 
 struct DecodeLaunch {
@@ -26,7 +31,10 @@ struct DecodeLaunch {
   int num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks;
   int max_context_len;
   float scale;
-  int dtype;
+  int dtype;        // query / output
+  int cache_dtype;  // k_cache / v_cache
+  float k_scale;    // fp8 caches: a code stands for value * scale
+  float v_scale;
   int partition_tokens;  // resolved, > 0
   bool shared_pages;     // pages may be shared: default cache policy, else non-temporal
   int max_parts;         // ceil(max_context_len / partition_tokens), >= 1
@@ -41,7 +49,11 @@ struct ReshapeLaunch {
   void* k_cache;
   void* v_cache;
   const int64_t* slot_mapping;
-  int num_tokens, num_blocks, num_kv_heads, block_size, head_dim, elem_bytes;
+  int num_tokens, num_blocks, num_kv_heads, block_size, head_dim;
+  int dtype;          // key / value
+  int cache_dtype;    // same as dtype (copy) or fp8 (encode)
+  float k_inv_scale;  // fp8: fl32(1 / k_scale)
+  float v_inv_scale;
   hipStream_t stream;
 };
 
@@ -54,7 +66,7 @@ struct CopyLaunch {
 };
 
 // Default partition length (tokens) for a shape; a multiple of block_size.
-int default_partition_tokens(int dtype, int head_dim, int block_size, int group);
+int default_partition_tokens(int dtype, int cache_dtype, int head_dim, int block_size, int group);
 
 hipError_t launch_decode(const DecodeLaunch& a);
 hipError_t launch_reshape_and_cache(const ReshapeLaunch& a);

@@ -25,6 +25,11 @@ type with round-to-nearest-even):
               beams whose last block already holds tokens find that block
               shared (reference count 2) and must copy it before the write.
 
+``<name>_fp8``  the same workload with an fp8 (OCP E4M3) KV cache: history
+              entries are N(0, 1) draws divided by the cache scale 1/64 and
+              cast to float8_e4m3fn (torch's cast, clamped to +-448), new
+              tokens stay bf16 and are encoded by reshape_and_cache.
+
 Physical pools hold ceil(1.1 x blocks needed) blocks unless a size is given;
 blocks are handed out in the order of a seeded permutation, sequence by
 sequence, so logically adjacent blocks are physically scattered.  Slots that
@@ -48,7 +53,7 @@ __all__ = ["Spec", "Plan", "Inputs", "SPECS", "uniform_plan", "beam_plan",
            "make_plan", "build_inputs", "make_inputs", "to_host_numpy",
            "TORCH_DTYPE"]
 
-TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
 
 
 @dataclass(frozen=True)
@@ -58,9 +63,16 @@ class Spec:
     num_kv_heads: int
     head_dim: int
     block_size: int
-    dtype: str
+    dtype: str                  # query / output / new-token element type
     seed: int
     q_std: float = 1.0
+    kv_dtype: Optional[str] = None   # cache element type (None: same as dtype)
+    kv_scale: float = 1.0            # fp8 caches: a code stands for value * kv_scale
+    recipe: Optional[str] = None     # plan recipe (None: the name)
+
+    @property
+    def cache_dtype(self) -> str:
+        return self.kv_dtype or self.dtype
 
 
 SPECS: Dict[str, Spec] = {
@@ -70,6 +82,11 @@ SPECS: Dict[str, Spec] = {
     "gqa70b": Spec("gqa70b", 64, 8, 128, 32, "bf16", seed=104, q_std=0.5),
     "beam": Spec("beam", 32, 8, 128, 16, "bf16", seed=105),
 }
+for _base in ("llama7b", "llama13b", "gqa70b", "beam"):
+    _b = SPECS[_base]
+    SPECS[_base + "_fp8"] = Spec(_base + "_fp8", _b.num_heads, _b.num_kv_heads, _b.head_dim,
+                                 _b.block_size, _b.dtype, seed=_b.seed + 1000, q_std=_b.q_std,
+                                 kv_dtype="fp8", kv_scale=1.0 / 64, recipe=_base)
 
 
 @dataclass
@@ -187,6 +204,7 @@ def make_plan(name: str, gen: torch.Generator, **kw) -> Plan:
     """The integer plan of a named workload (keyword overrides shrink it)."""
     spec = SPECS[name]
     bs = kw.pop("block_size", spec.block_size)
+    name = spec.recipe or name
     if name == "tiny":
         plan = uniform_plan(kw.pop("context_lens", [1, 17, 33, 100]), bs, gen,
                             new_tokens=True, num_blocks=kw.pop("num_blocks", 64))
@@ -228,6 +246,8 @@ class Inputs:
     context_lens: torch.Tensor   # int32 [S]
     block_pairs: torch.Tensor    # int64 [P, 2]
     scale: float
+    k_scale: float = 1.0         # fp8 caches only
+    v_scale: float = 1.0
 
     @property
     def max_context_len(self) -> int:
@@ -245,6 +265,17 @@ def _randn(shape, gen, device, std, dtype, chunk_rows: int = 1024):
         if std != 1.0:
             x.mul_(std)
         flat[r0:r1] = x.to(out.dtype)
+    return out
+
+
+def _fp8_codes(shape, gen, device, scale, chunk_rows: int = 256):
+    """E4M3 codes of N(0, 1) / scale draws (torch's float8_e4m3fn cast)."""
+    out = torch.empty(shape, dtype=torch.float8_e4m3fn, device=device)
+    flat = out.view(shape[0], -1)
+    for r0 in range(0, shape[0], chunk_rows):
+        r1 = min(shape[0], r0 + chunk_rows)
+        x = torch.randn((r1 - r0, flat.shape[1]), generator=gen, device=device, dtype=torch.float32)
+        flat[r0:r1] = x.mul_(1.0 / scale).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
     return out
 
 
@@ -275,15 +306,23 @@ def build_inputs(spec: Spec, plan: Plan, device="cpu", poison: bool = True,
     nb, bs = plan.num_blocks, plan.block_size
     hkv, d = spec.num_kv_heads, spec.head_dim
     q = _randn((s, spec.num_heads, d), gen, device, spec.q_std, spec.dtype)
-    k_cache = _randn((nb, hkv, bs, d), gen, device, 1.0, spec.dtype, chunk_rows=256)
-    v_cache = _randn((nb, hkv, bs, d), gen, device, 1.0, spec.dtype, chunk_rows=256)
+    if spec.cache_dtype == "fp8":
+        k_cache = _fp8_codes((nb, hkv, bs, d), gen, device, spec.kv_scale)
+        v_cache = _fp8_codes((nb, hkv, bs, d), gen, device, spec.kv_scale)
+    else:
+        k_cache = _randn((nb, hkv, bs, d), gen, device, 1.0, spec.dtype, chunk_rows=256)
+        v_cache = _randn((nb, hkv, bs, d), gen, device, 1.0, spec.dtype, chunk_rows=256)
     t = int(plan.slot_mapping.shape[0])
     key = _randn((max(t, 1), hkv, d), gen, device, 1.0, spec.dtype)[:t]
     value = _randn((max(t, 1), hkv, d), gen, device, 1.0, spec.dtype)[:t]
     empty = torch.from_numpy(~_history_mask(plan)).to(device)
-    fill = float("nan") if poison else 0.0
-    k_cache.masked_fill_(empty[:, None, :, None], fill)
-    v_cache.masked_fill_(empty[:, None, :, None], fill)
+    if spec.cache_dtype == "fp8":  # 0x7F is the E4M3 NaN code
+        for c in (k_cache, v_cache):
+            c.view(torch.uint8).masked_fill_(empty[:, None, :, None], 0x7F if poison else 0)
+    else:
+        fill = float("nan") if poison else 0.0
+        k_cache.masked_fill_(empty[:, None, :, None], fill)
+        v_cache.masked_fill_(empty[:, None, :, None], fill)
     return Inputs(
         spec=spec, plan=plan, q=q, k_cache=k_cache, v_cache=v_cache,
         key=key.contiguous(), value=value.contiguous(),
@@ -292,6 +331,8 @@ def build_inputs(spec: Spec, plan: Plan, device="cpu", poison: bool = True,
         context_lens=torch.from_numpy(plan.context_lens.copy()).to(device),
         block_pairs=torch.from_numpy(plan.block_pairs.copy()).to(device),
         scale=float(np.float32(1.0 / math.sqrt(d))),
+        k_scale=spec.kv_scale if spec.cache_dtype == "fp8" else 1.0,
+        v_scale=spec.kv_scale if spec.cache_dtype == "fp8" else 1.0,
     )
 
 
@@ -307,8 +348,10 @@ def make_inputs(name: str, device="cpu", poison: bool = True, **overrides) -> In
 
 
 def to_host_numpy(t: torch.Tensor) -> np.ndarray:
-    """Host NumPy view of a tensor: bf16 as uint16 bit patterns."""
+    """Host NumPy view of a tensor: bf16 as uint16 bit patterns, fp8 as uint8 codes."""
     t = t.detach().to("cpu").contiguous()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
     return t.numpy()

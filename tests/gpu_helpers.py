@@ -34,12 +34,12 @@ def gpu_step(x: Inputs, t: dict | None = None, partition_tokens: int = 0, copy: 
         binding.pa_copy_blocks(t["k_cache"], t["v_cache"], t["block_pairs"])
     if reshape and t["slot_mapping"].shape[0]:
         binding.pa_reshape_and_cache(t["key"], t["value"], t["k_cache"], t["v_cache"],
-                                     t["slot_mapping"])
+                                     t["slot_mapping"], k_scale=x.k_scale, v_scale=x.v_scale)
     out = torch.empty_like(t["q"])
     binding.pa_decode(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
                       t["context_lens"], x.scale, x.max_context_len,
                       partition_tokens=partition_tokens, shared_pages=shared_pages,
-                      seq_order=seq_order)
+                      seq_order=seq_order, k_scale=x.k_scale, v_scale=x.v_scale)
     torch.cuda.synchronize()
     return out, t
 
@@ -52,9 +52,11 @@ def oracle_step(x: Inputs, copy: bool = True, reshape: bool = True):
         op.copy_blocks(kc, vc, to_host_numpy(x.block_pairs))
     if reshape and x.slot_mapping.shape[0]:
         op.reshape_and_cache(to_host_numpy(x.key), to_host_numpy(x.value), kc, vc,
-                             to_host_numpy(x.slot_mapping))
+                             to_host_numpy(x.slot_mapping), src_dtype=x.spec.dtype,
+                             k_scale=x.k_scale, v_scale=x.v_scale)
     out = op.decode(to_host_numpy(x.q), kc, vc, to_host_numpy(x.block_tables),
-                    to_host_numpy(x.context_lens), x.scale, x.spec.dtype)
+                    to_host_numpy(x.context_lens), x.scale, x.spec.dtype,
+                    cache_dtype=x.spec.cache_dtype, k_scale=x.k_scale, v_scale=x.v_scale)
     return out, kc, vc
 
 
@@ -65,7 +67,7 @@ def as_f64(t: torch.Tensor) -> np.ndarray:
 def bits(t) -> np.ndarray:
     """Raw bit patterns (uint16 for bf16, uint32 for fp32) for exact comparison."""
     a = to_host_numpy(t) if isinstance(t, torch.Tensor) else np.asarray(t)
-    return a.view(np.uint16) if a.dtype.itemsize == 2 else a.view(np.uint32)
+    return a.view({1: np.uint8, 2: np.uint16, 4: np.uint32}[a.dtype.itemsize])
 
 
 def assert_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str = "") -> float:
@@ -112,11 +114,13 @@ def sampled_reference(x: Inputs, seqs):
         ti = torch.tensor(tok, dtype=torch.long, device=x.key.device)
         op.reshape_and_cache(to_host_numpy(x.key.index_select(0, ti)),
                              to_host_numpy(x.value.index_select(0, ti)), kc, vc,
-                             np.array(slots, dtype=np.int64))
+                             np.array(slots, dtype=np.int64), src_dtype=x.spec.dtype,
+                             k_scale=x.k_scale, v_scale=x.v_scale)
     tables = np.full((len(seqs), plan.block_tables.shape[1]), -1, dtype=np.int32)
     for r, s in enumerate(seqs):
         nb = -(-int(plan.context_lens[s]) // bs)
         tables[r, :nb] = [remap[int(b)] for b in plan.block_tables[s][:nb]]
     q = to_host_numpy(x.q)[list(seqs)]
-    out = op.decode(q, kc, vc, tables, plan.context_lens[list(seqs)], x.scale, x.spec.dtype)
+    out = op.decode(q, kc, vc, tables, plan.context_lens[list(seqs)], x.scale, x.spec.dtype,
+                    cache_dtype=x.spec.cache_dtype, k_scale=x.k_scale, v_scale=x.v_scale)
     return out, ids, kc, vc

@@ -16,8 +16,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pa.h")
 LIB = binding.LIB
 
-OK, NULL, SHAPE, DTYPE, UNSUP, ALIGN, WS = 0, -1, -2, -3, -4, -5, -6
-F32, BF16 = 0, 1
+OK, NULL, SHAPE, DTYPE, UNSUP, ALIGN, WS, VALUE = 0, -1, -2, -3, -4, -5, -6, -8
+F32, BF16, FP8 = 0, 1, 2
 
 # Host buffer standing in for device pointers: validation never dereferences.
 _BUF = ctypes.create_string_buffer(1 << 12)
@@ -45,12 +45,15 @@ def test_status_strings():
 
 def decode(**kw):
     a = dict(out=P, q=P, k=P, v=P, bt=P, mb=8, ctx=P, order=None, S=2, H=8, Hkv=2, D=128, BS=16,
-             NB=32, maxctx=100, scale=0.1, dtype=BF16, pt=0, flags=0, ws=None, wsb=0)
+             NB=32, maxctx=100, scale=0.1, dtype=BF16, cdtype=None, ks=0.5, vs=0.5, pt=0, flags=0,
+             ws=None, wsb=0)
     a.update(kw)
+    cdtype = a["dtype"] if a["cdtype"] is None else a["cdtype"]
     return LIB.pa_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["mb"], a["ctx"], a["order"],
                          a["S"],
                          a["H"], a["Hkv"], a["D"], a["BS"], a["NB"], a["maxctx"], a["scale"],
-                         a["dtype"], a["pt"], a["flags"], a["ws"], a["wsb"], None)
+                         a["dtype"], cdtype, a["ks"], a["vs"], a["pt"], a["flags"], a["ws"], a["wsb"],
+                         None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -85,6 +88,16 @@ def decode(**kw):
     (dict(maxctx=3000, mb=200, pt=1024), WS),           # workspace required but missing
     (dict(maxctx=3000, mb=200, pt=1024, ws=P, wsb=16), WS),
     (dict(maxctx=3000, mb=200, pt=1024, ws=MIS, wsb=1 << 30), ALIGN),
+    (dict(dtype=FP8), DTYPE),           # fp8 is a cache type only
+    (dict(cdtype=3), DTYPE),
+    (dict(dtype=F32, cdtype=FP8), UNSUP),
+    (dict(dtype=BF16, cdtype=F32), UNSUP),
+    (dict(cdtype=FP8, ks=0.0), VALUE),
+    (dict(cdtype=FP8, vs=-1.0), VALUE),
+    (dict(cdtype=FP8, ks=float("nan")), VALUE),
+    (dict(cdtype=FP8, vs=float("inf")), VALUE),
+    (dict(cdtype=FP8, S=0), OK),
+    (dict(ks=0.0, S=0), OK),            # scales are read only for an fp8 cache
     (dict(flags=2), UNSUP),             # unknown flag bit
     (dict(flags=-1), UNSUP),
     (dict(S=0), OK),                    # empty batch: nothing to launch
@@ -97,23 +110,28 @@ def test_decode_validation(kw, code):
 def test_workspace_size():
     ws = LIB.pa_decode_workspace_size
     # Single partition -> no workspace.
-    assert ws(4, 32, 32, 128, 16, 2048, BF16, 2048) == 0
-    assert ws(4, 32, 32, 128, 16, 100, BF16, 0) == 0
+    assert ws(4, 32, 32, 128, 16, 2048, BF16, BF16, 2048) == 0
+    assert ws(4, 32, 32, 128, 16, 100, BF16, BF16, 0) == 0
     # S=3, H=8, 4 partitions of 512: (m, l) area rounded to 256 B + accumulators.
     rows = 3 * 8 * 4
     ml = (rows * 2 * 4 + 255) // 256 * 256
-    assert ws(3, 8, 2, 64, 16, 2000, F32, 512) == ml + rows * 64 * 4
+    assert ws(3, 8, 2, 64, 16, 2000, F32, F32, 512) == ml + rows * 64 * 4
+    assert ws(3, 8, 2, 64, 16, 2000, BF16, FP8, 512) == ml + rows * 64 * 4
     bad = ctypes.c_size_t(-1).value
-    assert ws(3, 8, 3, 64, 16, 2000, F32, 512) == bad
-    assert ws(3, 8, 2, 64, 16, 2000, 7, 512) == bad
-    assert ws(3, 8, 2, 64, 16, 2000, F32, 500) == bad
+    assert ws(3, 8, 3, 64, 16, 2000, F32, F32, 512) == bad
+    assert ws(3, 8, 2, 64, 16, 2000, 7, 7, 512) == bad
+    assert ws(3, 8, 2, 64, 16, 2000, F32, F32, 500) == bad
+    assert ws(3, 8, 2, 64, 16, 2000, F32, FP8, 512) == bad
 
 
 def reshape(**kw):
-    a = dict(key=P, value=P, k=P, v=P, slots=P, T=4, NB=8, Hkv=2, BS=16, D=64, dtype=F32)
+    a = dict(key=P, value=P, k=P, v=P, slots=P, T=4, NB=8, Hkv=2, BS=16, D=64, dtype=F32,
+             cdtype=None, ks=1.0, vs=1.0)
     a.update(kw)
+    cdtype = a["dtype"] if a["cdtype"] is None else a["cdtype"]
     return LIB.pa_reshape_and_cache(a["key"], a["value"], a["k"], a["v"], a["slots"], a["T"],
-                                    a["NB"], a["Hkv"], a["BS"], a["D"], a["dtype"], None)
+                                    a["NB"], a["Hkv"], a["BS"], a["D"], a["dtype"], cdtype,
+                                    a["ks"], a["vs"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -128,6 +146,12 @@ def reshape(**kw):
     (dict(key=MIS), ALIGN),
     (dict(slots=P + 4), ALIGN),
     (dict(T=0, key=None, value=None, slots=None), OK),
+    (dict(dtype=FP8), DTYPE),                # sources are float or bf16
+    (dict(dtype=F32, cdtype=BF16), UNSUP),   # only copies or fp8 encoding
+    (dict(cdtype=FP8, ks=0.0), VALUE),
+    (dict(cdtype=FP8, vs=float("nan")), VALUE),
+    (dict(cdtype=FP8, T=0), OK),
+    (dict(dtype=BF16, cdtype=FP8, T=0), OK),
 ])
 def test_reshape_validation(kw, code):
     assert reshape(**kw) == code
@@ -150,6 +174,8 @@ def copy(**kw):
     (dict(k=MIS), ALIGN),
     (dict(pairs=P + 4), ALIGN),
     (dict(n=0, pairs=None), OK),
+    (dict(n=0, pairs=None, dtype=FP8), OK),  # fp8 caches copy like any other
+    (dict(dtype=3), DTYPE),
 ])
 def test_copy_validation(kw, code):
     assert copy(**kw) == code
@@ -160,6 +186,7 @@ def test_binding_raises_runtime_error_with_status():
     assert isinstance(err, RuntimeError) and "PA_ERR_SHAPE" in str(err)
     with pytest.raises(ValueError):
         binding.pa_decode_workspace_size(1, 6, 4, 128, 16, 100, BF16)
+    assert binding.pa_status_string(VALUE).startswith("PA_ERR_VALUE")
 
 
 def test_longest_first_order():

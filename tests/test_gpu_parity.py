@@ -26,6 +26,8 @@ SMALL = {
     "gqa70b": dict(num_seqs=2, context_len=4100),
     "beam": dict(groups=3, beams=4, prefix_len=64, tail_lo=1, tail_hi=40, cow_fraction=0.5),
 }
+for _n in ("llama7b", "llama13b", "gqa70b", "beam"):  # the same shapes with an fp8 cache
+    SMALL[_n + "_fp8"] = SMALL[_n]
 
 
 def check_case(x, partition_tokens=0):
@@ -74,6 +76,78 @@ def test_shapes(h, hkv, d, bs, dtype):
     x = wl.build_inputs(spec, plan)
     check_case(x)
     check_case(x, partition_tokens=4 * bs)
+
+
+FP8_SHAPES = [
+    # (H, Hkv, D, BS) with a bf16 query and an E4M3 cache
+    (8, 8, 128, 16), (8, 8, 64, 32), (16, 8, 128, 32), (16, 4, 64, 16), (32, 4, 128, 16),
+    (64, 8, 128, 32), (16, 2, 128, 16),
+]
+
+
+@pytest.mark.parametrize("h,hkv,d,bs", FP8_SHAPES)
+def test_shapes_fp8(h, hkv, d, bs):
+    spec = wl.Spec(f"fp8shape{h}x{hkv}x{d}x{bs}", h, hkv, d, bs, "bf16", seed=7 * h + d + bs,
+                   kv_dtype="fp8", kv_scale=1.0 / 64)
+    gen = torch.Generator().manual_seed(spec.seed)
+    ctx = [0, 1, bs - 1, bs + 1, 3 * bs + 5, 700, 1100]
+    plan = wl.uniform_plan(ctx, bs, gen, new_tokens=True)
+    x = wl.build_inputs(spec, plan)
+    check_case(x)
+    check_case(x, partition_tokens=4 * bs)
+
+
+def test_fp8_reshape_codes_exact():
+    """E4M3 encoding of new rows: ties, subnormals, saturation, NaN, -0, random."""
+    import oracle.paged_attention as op
+    x = wl.make_inputs("llama13b_fp8", num_seqs=6, context_len=40)
+    special = np.array([1.0625, 1.1875, 2.0 ** -10, 1.5 * 2.0 ** -9, 400.0, 432.0, 447.0, 448.0,
+                        449.0, 464.0, 1e9, -1e9, 0.0, -0.0, 2.0 ** -12, -(2.0 ** -7),
+                        0.015625 * 3.0, 1e-30], dtype=np.float32)
+    key = x.key.float().numpy().copy()
+    flat = key.reshape(-1)
+    flat[: len(special)] = special / np.float32(64.0)  # divided back by the scale in the kernel
+    flat[len(special): len(special) + 3] = [np.nan, np.inf, -np.inf]
+    x.key = torch.from_numpy(key).to(torch.bfloat16)
+    out, t = gpu_step(x)
+    ref, kc, vc = oracle_step(x)
+    assert np.array_equal(bits(t["k_cache"]), bits(kc))
+    assert np.array_equal(bits(t["v_cache"]), bits(vc))
+    # The rows really went through the saturating, NaN-preserving encoder.
+    slot = int(x.plan.slot_mapping[0])
+    row = bits(t["k_cache"])[slot // 16, :, slot % 16].reshape(-1)
+    assert row[8] == 0x7E and row[10] == 0x7E and row[11] == 0xFE and row[13] == 0x80
+    assert (row[len(special)] & 0x7F) == 0x7F
+    nan_row = int(x.plan.new_token_seqs[0])  # its newest token holds the NaN
+    others = [r for r in range(x.plan.num_seqs) if r != nan_row]
+    assert np.isfinite(as_f64(out)[others]).all()
+    assert_close(as_f64(out)[others], ref[others], "bf16", "fp8 rows")
+
+
+@pytest.mark.parametrize("name", ["gqa70b_fp8", "llama7b_fp8"])
+def test_fp8_context_one_every_code_bitwise(name):
+    """With one token the output is exactly code value * v_scale (a power of
+    two), for every finite E4M3 code, on the matrix-core and vector paths."""
+    import oracle.paged_attention as op
+    kw = dict(num_seqs=2, context_len=1) if name == "gqa70b_fp8" else \
+        dict(num_seqs=2, ctx_range=(1, 1))
+    x = wl.make_inputs(name, **kw)
+    t = on_device(x)
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    for s_ in range(x.plan.num_seqs):
+        b = int(x.plan.block_tables[s_][0])
+        n = x.spec.num_kv_heads * x.spec.head_dim
+        pattern = np.resize(np.roll(codes, 37 * s_), n).reshape(x.spec.num_kv_heads, x.spec.head_dim)
+        t["v_cache"].view(torch.uint8)[b, :, 0, :] = torch.from_numpy(pattern).cuda()
+    out, _ = gpu_step(x, t, copy=False, reshape=False)
+    vals = op.e4m3_values()
+    g = x.spec.num_heads // x.spec.num_kv_heads
+    v = t["v_cache"].view(torch.uint8).cpu().numpy()
+    for s_ in range(x.plan.num_seqs):
+        b = int(x.plan.block_tables[s_][0])
+        want = vals[v[b, :, 0, :]] * x.v_scale                    # exact in float64
+        want_bf16 = torch.from_numpy(np.repeat(want, g, axis=0)).float().to(torch.bfloat16)
+        assert torch.equal(out[s_].cpu(), want_bf16), s_
 
 
 def test_zero_context_rows_are_zero():
