@@ -25,7 +25,8 @@
 //  * V is the one operand that needs a transpose: each wave writes its page
 //    to LDS (rows swizzled so the transposed reads hit distinct banks, rows
 //    past the context written as zeros so NaN in unused slots can never reach
-//    the product) and reads V^T back as the A operand.
+//    the product) and reads V^T back as the A operand with gfx950's
+//    transposing LDS read, four k slots per instruction.
 // The online softmax runs on the S^T tile: each lane holds 4 tokens of one
 // head per 16-token tile; the max over tokens takes two cross-lane steps.  The
 // reference max is moved lazily (only when exceeded by more than 2^8), which
@@ -39,6 +40,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // Orders this wave's LDS writes before its later LDS reads (and the reverse)
@@ -67,10 +69,11 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return r;
 }
 
-// 16-byte chunk c of LDS row `row` is stored at chunk c ^ swz(row).  Rows
-// 4 apart (the rows one transposed read touches) land 2 chunks apart, so the
-// four 32-byte segments of a read fall in distinct banks.
-__device__ __forceinline__ int swz(int row) { return 2 * ((row >> 2) & 3); }
+// 16-byte chunk c of LDS row `row` is stored at chunk c ^ swz(row).  One
+// transposed read (below) has each 16-lane group read 4 consecutive rows at
+// the same columns; the swizzle puts those 4 rows' 32-byte segments 2 chunks
+// apart, in distinct banks.
+__device__ __forceinline__ int swz(int row) { return 2 * (row & 3); }
 
 // TC: cache element type, bf16 bits (uint16_t) or E4M3 codes (uint8_t); the
 // query is bf16 either way and the products run on bf16 MFMA (E4M3 widens to
@@ -185,8 +188,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     }
     wave_lds_fence();
   };
-  auto v_at = [&](int t, int d) -> uint16_t {
-    return *reinterpret_cast<const uint16_t*>(vbuf + t * ROWB + (((d >> 3) ^ swz(t)) << 4) + ((d & 7) << 1));
+  // V^T operand through ds_read_b64_tr_b16 (checked on gfx950): in each group
+  // of 16 lanes, lane 4r + c receives element c of the 8-byte rows addressed
+  // by lanes r, r + 4, r + 8, r + 12.  Lane l16 addresses token tb + l16 / 4 at
+  // columns d0 + 4 (l16 % 4) .. +3, so it receives column d0 + l16 of tokens
+  // tb .. tb + 3: four k slots of the A operand in one instruction.
+  auto vt4 = [&](int tb, int d0) -> s16x4_t {
+    const int t = tb + (l16 >> 2);
+    const int d = d0 + 4 * (l16 & 3);
+    const unsigned char* a = vbuf + t * ROWB + (((d >> 3) ^ swz(t)) << 4) + ((d & 7) << 1);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)a);
   };
 
   auto scores = [&](const uint4 (&kr)[NT][NKL], f32x4_t (&st)[NT]) {
@@ -255,14 +266,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pbits);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        const int d = 16 * m + l16;
-        uint4 vbits;
-        vbits.x = (uint32_t)v_at(4 * g4 + 0, d) | ((uint32_t)v_at(4 * g4 + 1, d) << 16);
-        vbits.y = (uint32_t)v_at(4 * g4 + 2, d) | ((uint32_t)v_at(4 * g4 + 3, d) << 16);
-        vbits.z = (uint32_t)v_at(16 + 4 * g4 + 0, d) | ((uint32_t)v_at(16 + 4 * g4 + 1, d) << 16);
-        vbits.w = (uint32_t)v_at(16 + 4 * g4 + 2, d) | ((uint32_t)v_at(16 + 4 * g4 + 3, d) << 16);
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vbits), pb, acc[m],
-                                                         0, 0, 0);
+        const s16x4_t lo = vt4(4 * g4, 16 * m);       // tokens 4 g4 .. +3
+        const s16x4_t hi = vt4(16 + 4 * g4, 16 * m);  // tokens 16 + 4 g4 .. +3
+        const s16x8_t va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pb, acc[m], 0, 0,
+                                                         0);
       }
     } else {
       // 16-token pages: k slot j of lane group g4 is token 4 g4 + j.
@@ -271,14 +279,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       pbits.y = pack_bf16x2(sv[0][2], sv[0][3]);
       const s16x4_t pb = __builtin_bit_cast(s16x4_t, pbits);
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        const int d = 16 * m + l16;
-        uint2 vbits;
-        vbits.x = (uint32_t)v_at(4 * g4 + 0, d) | ((uint32_t)v_at(4 * g4 + 1, d) << 16);
-        vbits.y = (uint32_t)v_at(4 * g4 + 2, d) | ((uint32_t)v_at(4 * g4 + 3, d) << 16);
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, vbits), pb, acc[m],
-                                                           0, 0, 0);
-      }
+      for (int m = 0; m < NM; ++m)
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt4(4 * g4, 16 * m), pb, acc[m], 0, 0, 0);
     }
   };
 
