@@ -51,22 +51,26 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Two finite floats -> two bf16, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16_bits(lo)) | (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+  typedef __bf16 pair_t __attribute__((ext_vector_type(2)));
+  const pair_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
-// Eight E4M3 codes -> eight bf16 (exact: an E4M3 value needs 3 mantissa bits,
-// so its binary32 form has 16 zero low bits and the high half is its bf16).
+// Eight E4M3 codes -> eight bf16, exact (an E4M3 value has 3 mantissa bits),
+// with v_cvt_scalef32_pk_bf16_fp8 at scale 1 (checked on gfx950: exact for all
+// 256 codes in both halves).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <bool kHigh>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHigh));
+}
+
 __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-  float f[8];
-  fp8x4_to_f32(lo, f);
-  fp8x4_to_f32(hi, f + 4);
-  uint4 r;
-  r.x = (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
-  r.y = (__float_as_uint(f[2]) >> 16) | (__float_as_uint(f[3]) & 0xffff0000u);
-  r.z = (__float_as_uint(f[4]) >> 16) | (__float_as_uint(f[5]) & 0xffff0000u);
-  r.w = (__float_as_uint(f[6]) >> 16) | (__float_as_uint(f[7]) & 0xffff0000u);
-  return r;
+  return make_uint4(fp8x2_to_bf16x2<false>(lo), fp8x2_to_bf16x2<true>(lo), fp8x2_to_bf16x2<false>(hi),
+                    fp8x2_to_bf16x2<true>(hi));
 }
 
 // 16-byte chunk c of LDS row `row` is stored at chunk c ^ swz(row).  One
