@@ -302,6 +302,7 @@ def main():
     others = []
     for name in [n for n in args.others.split(",") if n and n != args.workload]:
         r, _, _ = run_workload(name, args.steps, args.warmup, args.partition_tokens)
+        r["decode_traffic_bytes"] = measured_traffic(name)
         others.append(r)
         if name == "beam":
             r2, _, _ = run_workload(name, args.steps, args.warmup, args.partition_tokens, flush=True)
@@ -310,7 +311,7 @@ def main():
     traffic = measured_traffic(args.workload)
     roof = {
         "bound": "hbm",
-        "kernel": "pa_decode: decode_partition_valu_kernel<bf16, D=128, BS=16, G=1> "
+        "kernel": "pa_decode: decode_partition_valu_kernel<bf16 q, bf16 cache, D=128, BS=16, G=1> "
                   "(one launch per step at this shape)",
         "achieved": head["decode_GBps"],
         "peak": PEAK_GBPS,
