@@ -46,6 +46,10 @@ DESCRIPTION = {
 }
 for _n in ("llama7b", "llama13b", "gqa70b", "beam"):
     DESCRIPTION[_n + "_fp8"] = DESCRIPTION[_n].replace(", bf16", ", bf16 query / fp8 E4M3 KV cache")
+# "+prefix": the same step with pa_decode_shared_prefix (each shared page read
+# once per chunk of sequences) in place of pa_decode.
+for _n in ("beam", "beam_fp8"):
+    DESCRIPTION[_n + "+prefix"] = DESCRIPTION[_n].replace("+ pa_decode", "+ pa_decode_shared_prefix")
 
 
 def parse():
@@ -55,7 +59,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama13b", choices=sorted(DESCRIPTION))
     ap.add_argument("--partition-tokens", type=int, default=0)
-    ap.add_argument("--others", default="llama7b,gqa70b,beam,llama13b_fp8,gqa70b_fp8",
+    ap.add_argument("--others", default="llama7b,gqa70b,beam,beam+prefix,llama13b_fp8,gqa70b_fp8",
                     help="comma list of extra workloads to report ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -73,6 +77,36 @@ def algorithmic_bytes(plan, spec) -> int:
     kv = sum(2 * spec.num_kv_heads * c * spec.head_dim * ekv for c in ctx)
     qo = 2 * len(ctx) * spec.num_heads * spec.head_dim * e
     table = 4 * sum(-(-c // plan.block_size) for c in ctx)
+    return kv + qo + table + 4 * len(ctx)
+
+
+def decode_kernel_name(label, spec) -> str:
+    """The partition kernel a workload's decode launches (the dominant kernel)."""
+    group = spec.num_heads // spec.num_kv_heads
+    cache = {"f32": "f32", "bf16": "bf16", "fp8": "fp8 E4M3"}[spec.cache_dtype]
+    shape = f"D={spec.head_dim}, BS={spec.block_size}, G={group}"
+    if label.endswith("+prefix"):
+        return f"pa_decode_shared_prefix: decode_partition_mfma_kernel<{cache} cache, {shape}, shared>"
+    if spec.dtype == "bf16" and group >= 2:
+        return f"pa_decode: decode_partition_mfma_kernel<{cache} cache, {shape}>"
+    return f"pa_decode: decode_partition_valu_kernel<{spec.dtype} q, {cache} cache, {shape}>"
+
+
+def unique_bytes(plan, spec) -> int:
+    """Like algorithmic_bytes, but a physical block shared by several sequences
+    counts once (with the most tokens any of them uses from it)."""
+    e = 4 if spec.dtype == "f32" else 2
+    ekv = {"f32": 4, "bf16": 2, "fp8": 1}[spec.cache_dtype]
+    bs = plan.block_size
+    used = {}
+    ctx = [int(c) for c in plan.context_lens]
+    for s, c in enumerate(ctx):
+        for j in range(-(-c // bs)):
+            b = int(plan.block_tables[s][j])
+            used[b] = max(used.get(b, 0), min(bs, c - j * bs))
+    kv = 2 * spec.num_kv_heads * spec.head_dim * ekv * sum(used.values())
+    qo = 2 * len(ctx) * spec.num_heads * spec.head_dim * e
+    table = 4 * sum(-(-c // bs) for c in ctx)
     return kv + qo + table + 4 * len(ctx)
 
 
@@ -97,21 +131,32 @@ def measured_traffic(workload: str):
     return entry.get("bytes_per_launch")
 
 
-def run_workload(name, steps, warmup, partition_tokens, flush=False):
+def run_workload(label, steps, warmup, partition_tokens, flush=False):
     import torch
     from paged_kv_cache_321_amd import binding
     from paged_kv_cache_321_amd import workloads as wl
+    from paged_kv_cache_321_amd.block_pool import prefix_bounds, prefix_groups
 
+    name, _, variant = label.partition("+")
+    shared_prefix = variant == "prefix"
     x = wl.make_inputs(name, device="cuda", poison=False)
     spec, plan = x.spec, x.plan
     out = torch.empty_like(x.q)
     code = binding.PA_F32 if spec.dtype == "f32" else binding.PA_BF16
     ccode = {"f32": binding.PA_F32, "bf16": binding.PA_BF16,
              "fp8": binding.PA_FP8_E4M3}[spec.cache_dtype]
-    ws_bytes = binding.pa_decode_workspace_size(plan.num_seqs, spec.num_heads, spec.num_kv_heads,
-                                                spec.head_dim, plan.block_size,
-                                                plan.max_context_len, code, partition_tokens,
-                                                ccode)
+    if shared_prefix:  # grouping and bounds from the host-side tables, before the timed region
+        lead, nblk = prefix_groups(plan.block_tables, plan.context_lens, plan.block_size)
+        bounds = prefix_bounds(lead, nblk, plan.context_lens, plan.block_size)
+        lead = torch.tensor(lead, dtype=torch.int32, device="cuda")
+        nblk = torch.tensor(nblk, dtype=torch.int32, device="cuda")
+        ws_bytes = binding.pa_decode_shared_prefix_workspace_size(
+            plan.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_dim, plan.block_size,
+            plan.max_context_len, bounds[0], bounds[1], code, partition_tokens, ccode)
+    else:
+        ws_bytes = binding.pa_decode_workspace_size(
+            plan.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_dim, plan.block_size,
+            plan.max_context_len, code, partition_tokens, ccode)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if flush else None
     stream = torch.cuda.current_stream()
@@ -133,10 +178,18 @@ def run_workload(name, steps, warmup, partition_tokens, flush=False):
                                          stream=stream, k_scale=x.k_scale, v_scale=x.v_scale)
         if ev is not None:
             ev[0].record(stream)
-        binding.pa_decode(out, x.q, x.k_cache, x.v_cache, x.block_tables, x.context_lens,
-                          x.scale, plan.max_context_len, partition_tokens=partition_tokens,
-                          workspace=ws, stream=stream, shared_pages=shared, seq_order=order,
-                          k_scale=x.k_scale, v_scale=x.v_scale)
+        if shared_prefix:
+            binding.pa_decode_shared_prefix(out, x.q, x.k_cache, x.v_cache, x.block_tables,
+                                            x.context_lens, lead, nblk, x.scale,
+                                            plan.max_context_len, bounds[0], bounds[1],
+                                            partition_tokens=partition_tokens,
+                                            workspace=ws, stream=stream, k_scale=x.k_scale,
+                                            v_scale=x.v_scale)
+        else:
+            binding.pa_decode(out, x.q, x.k_cache, x.v_cache, x.block_tables, x.context_lens,
+                              x.scale, plan.max_context_len, partition_tokens=partition_tokens,
+                              workspace=ws, stream=stream, shared_pages=shared, seq_order=order,
+                              k_scale=x.k_scale, v_scale=x.v_scale)
         if ev is not None:
             ev[1].record(stream)
 
@@ -173,9 +226,10 @@ def run_workload(name, steps, warmup, partition_tokens, flush=False):
     avg_decode_ms = sum(decode_ms) / len(decode_ms)
     med_decode_ms = decode_ms[len(decode_ms) // 2]
     nbytes = algorithmic_bytes(plan, spec)
+    ubytes = unique_bytes(plan, spec)
     res = {
-        "workload": name,
-        "description": DESCRIPTION[name],
+        "workload": label,
+        "description": DESCRIPTION[label],
         "num_seqs": plan.num_seqs,
         "total_context_tokens": int(sum(int(c) for c in plan.context_lens)),
         "ms_per_step": ms_per_step,
@@ -187,10 +241,13 @@ def run_workload(name, steps, warmup, partition_tokens, flush=False):
         "decode_algorithmic_bytes": nbytes,
         "decode_GBps": nbytes / (avg_decode_ms / 1e3) / 1e9,
         "decode_frac_of_peak": nbytes / (avg_decode_ms / 1e3) / 1e9 / PEAK_GBPS,
+        "decode_unique_bytes": ubytes,
+        "decode_unique_GBps": ubytes / (avg_decode_ms / 1e3) / 1e9,
         "copy_pairs": int(plan.block_pairs.shape[0]),
         "new_tokens": int(plan.slot_mapping.shape[0]),
         "partition_tokens": partition_tokens,
-        "shared_pages_flag": shared,
+        "shared_pages_flag": shared and not shared_prefix,
+        "decode_entry_point": "pa_decode_shared_prefix" if shared_prefix else "pa_decode",
         "cache": "cold (MALL flushed between steps)" if flush else "warm",
         "kv_cache_dtype": spec.cache_dtype,
     }
@@ -304,15 +361,14 @@ def main():
         r, _, _ = run_workload(name, args.steps, args.warmup, args.partition_tokens)
         r["decode_traffic_bytes"] = measured_traffic(name)
         others.append(r)
-        if name == "beam":
+        if name.startswith("beam"):
             r2, _, _ = run_workload(name, args.steps, args.warmup, args.partition_tokens, flush=True)
             others.append(r2)
 
     traffic = measured_traffic(args.workload)
     roof = {
         "bound": "hbm",
-        "kernel": "pa_decode: decode_partition_valu_kernel<bf16 q, bf16 cache, D=128, BS=16, G=1> "
-                  "(one launch per step at this shape)",
+        "kernel": decode_kernel_name(args.workload, spec),
         "achieved": head["decode_GBps"],
         "peak": PEAK_GBPS,
         "unit": "GB/s",
@@ -321,7 +377,8 @@ def main():
         "algorithmic_bytes_per_launch": head["decode_algorithmic_bytes"],
         "avg_launch_us": head["decode_avg_us"],
     }
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload, args.cpu_seconds)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload.split("+")[0],
+                                                             args.cpu_seconds)
     line = {
         "metric": METRIC,
         "value": head["tokens_per_s"],

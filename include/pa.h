@@ -189,6 +189,80 @@ int pa_decode(void* out, const void* q,
               int partition_tokens, int flags,
               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pa_decode_shared_prefix_workspace_size -- bytes of device workspace
+ * pa_decode_shared_prefix needs for these sizes and bounds (0 when nothing can
+ * need a merge: no prefix and every context within one partition); (size_t)-1
+ * for arguments it would reject.  partition_tokens: 0 = the call's default.
+ */
+size_t pa_decode_shared_prefix_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
+                                              int head_dim, int block_size, int max_context_len,
+                                              int max_prefix_blocks, int max_tail_len,
+                                              int dtype, int cache_dtype, int partition_tokens);
+
+/*
+ * pa_decode_shared_prefix -- pa_decode for a batch whose sequences share
+ * leading cache blocks (beams forked from one sequence, or requests with a
+ * common prompt), reading each shared page once for several sequences.
+ * ([tbr8] "Copy-on-Write 与内存共享": beams and parallel samples of one request
+ * share their common prefix, their block-table entries naming the same physical
+ * pages until one of them writes; "Prefix Caching（前缀缓存）": requests with the
+ * same system prompt share its blocks.)
+ *
+ * The result is the one pa_decode defines for the same q, caches, block_tables
+ * and context_lens (the grouping below changes only which workgroup reads a
+ * page, not what is computed; rounding may differ from pa_decode's within the
+ * usual float32 accumulation error).
+ *
+ * Grouping (device int32 arrays [num_seqs]):
+ *   prefix_leader[s]  the first sequence L of s's group (L == s for the first
+ *                     member, or a sequence served alone); members of a group
+ *                     are consecutive: L, L+1, ...
+ *   prefix_blocks[L]  read at group leaders only: the number n of leading
+ *                     block-table entries that every member of the group holds
+ *                     in common (the shared blocks, each full: n * block_size
+ *                     <= every member's context length).  0 = no sharing.
+ * Members are served in chunks of 16 / G consecutive sequences counted from L
+ * (G = num_heads / num_kv_heads): one workgroup computes the shared part of a
+ * chunk, so each shared page is read once per chunk; each sequence's tokens
+ * past the prefix are read by its own workgroups; a merge kernel combines the
+ * partial results.  An entry that does not describe such a chunk (L < 0, L > s,
+ * prefix_leader[L] != L, or the first sequence of s's chunk in another group)
+ * makes s a sequence served alone (its prefix is 0), with the same result.
+ *
+ * Host bounds, which size the grid (like max_context_len):
+ *   max_prefix_blocks >= prefix_blocks[L] of every group, and
+ *   max_tail_len      >= context_lens[s] - (its shared prefix in tokens) for
+ *                        every s (the whole context for a sequence served alone),
+ * with max_prefix_blocks * block_size and max_tail_len at most max_context_len
+ * (else PA_ERR_SHAPE).
+ * Preconditions (device values, as for pa_decode, plus): the bounds above; for
+ * every member s of a group with n > 0, block_tables[s, j] == block_tables[c, j]
+ * for j < n, where c is the first sequence of s's chunk; n * block_size <=
+ * context_lens[s].  A member that breaks them gets a NaN row (if the first
+ * sequence of a chunk has an out-of-range table entry, the whole chunk's rows
+ * are NaN).
+ *
+ * Arguments not listed here mean what they mean for pa_decode.  dtype must be
+ * PA_BF16 (cache PA_BF16 or PA_FP8_E4M3); G may be 1, 2, 4 or 8; flags must be
+ * 0.  partition_tokens cuts the shared prefix and the rest of each context
+ * separately (0 = default: a quarter of max_prefix_blocks * block_size rounded
+ * up to a power of two, within [256, 2048]).  workspace: at least
+ * pa_decode_shared_prefix_workspace_size(...) bytes, 16-byte aligned (NULL
+ * allowed when that is 0).
+ */
+int pa_decode_shared_prefix(void* out, const void* q,
+                            const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int max_blocks_per_seq,
+                            const int32_t* context_lens,
+                            const int32_t* prefix_leader, const int32_t* prefix_blocks,
+                            int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                            int block_size, int num_blocks, int max_context_len,
+                            int max_prefix_blocks, int max_tail_len,
+                            float scale, int dtype, int cache_dtype, float k_scale, float v_scale,
+                            int partition_tokens, int flags,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* pa_status_string -- static, human-readable name of a status code. */
 const char* pa_status_string(int status);
 

@@ -26,7 +26,8 @@ STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
           -4: "PA_ERR_UNSUPPORTED", -5: "PA_ERR_ALIGN", -6: "PA_ERR_WORKSPACE",
           -7: "PA_ERR_LAUNCH", -8: "PA_ERR_VALUE"}
 EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_workspace_size",
-           "pa_decode", "pa_status_string")
+           "pa_decode", "pa_decode_shared_prefix_workspace_size", "pa_decode_shared_prefix",
+           "pa_status_string")
 
 _c_int, _c_size, _c_float, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
 
@@ -53,6 +54,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                               [_c_float, _c_int, _c_int, _c_float, _c_float, _c_int, _c_int, _vp,
                                _c_size, _vp])
     lib.pa_decode.restype = _c_int
+    lib.pa_decode_shared_prefix_workspace_size.argtypes = [_c_int] * 11
+    lib.pa_decode_shared_prefix_workspace_size.restype = _c_size
+    lib.pa_decode_shared_prefix.argtypes = ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp] +
+                                            [_c_int] * 9 +
+                                            [_c_float, _c_int, _c_int, _c_float, _c_float, _c_int,
+                                             _c_int, _vp, _c_size, _vp])
+    lib.pa_decode_shared_prefix.restype = _c_int
     lib.pa_status_string.argtypes = [_c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     return lib
@@ -205,3 +213,66 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
                        PA_DECODE_SHARED_PAGES if shared_pages else 0,
                        _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "pa_decode")
+
+
+def pa_decode_shared_prefix_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int,
+                                           head_dim: int, block_size: int, max_context_len: int,
+                                           max_prefix_blocks: int, max_tail_len: int, dtype: int,
+                                           partition_tokens: int = 0,
+                                           cache_dtype: Optional[int] = None) -> int:
+    cache_dtype = dtype if cache_dtype is None else cache_dtype
+    n = LIB.pa_decode_shared_prefix_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                   block_size, max_context_len, max_prefix_blocks,
+                                                   max_tail_len, dtype, cache_dtype,
+                                                   partition_tokens)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("pa_decode_shared_prefix_workspace_size: arguments rejected by the library")
+    return n
+
+
+def pa_decode_shared_prefix(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                            v_cache: torch.Tensor, block_tables: torch.Tensor,
+                            context_lens: torch.Tensor, prefix_leader: torch.Tensor,
+                            prefix_blocks: torch.Tensor, scale: float, max_context_len: int,
+                            max_prefix_blocks: int, max_tail_len: int, partition_tokens: int = 0,
+                            workspace: Optional[torch.Tensor] = None, stream=None,
+                            k_scale: float = 1.0, v_scale: float = 1.0) -> None:
+    """Decode attention where groups of sequences share leading cache blocks.
+
+    ``prefix_leader`` and ``prefix_blocks`` (int32 device tensors [S]) name
+    each sequence's group leader and, at leaders, the number of shared leading
+    blocks; ``max_prefix_blocks`` and ``max_tail_len`` bound them on the host
+    (see ``block_pool.prefix_groups`` and ``block_pool.prefix_bounds``).  Same
+    result as ``pa_decode``.
+    """
+    for n, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                 ("block_tables", block_tables), ("context_lens", context_lens),
+                 ("prefix_leader", prefix_leader), ("prefix_blocks", prefix_blocks)):
+        _device_contig(n, t)
+    _need(all(t.dtype == torch.int32 for t in (block_tables, context_lens, prefix_leader,
+                                                prefix_blocks)),
+          "block_tables, context_lens, prefix_leader and prefix_blocks must be int32")
+    _need(q.dtype == out.dtype and k_cache.dtype == v_cache.dtype, "element types differ")
+    s, h, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    _need(d2 == d and out.shape == q.shape and v_cache.shape == k_cache.shape, "shape mismatch")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == s, "block_tables must be [S, MB]")
+    _need(context_lens.shape == (s,) and prefix_leader.shape == (s,) and prefix_blocks.shape == (s,),
+          "context_lens, prefix_leader and prefix_blocks must be [S]")
+    code = _dtype_code(q)
+    ccode = _dtype_code(k_cache)
+    need = pa_decode_shared_prefix_workspace_size(s, h, hkv, d, bs, max_context_len,
+                                                  max_prefix_blocks, max_tail_len, code,
+                                                  partition_tokens, ccode) \
+        if h > 0 and hkv > 0 and h % hkv == 0 else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = LIB.pa_decode_shared_prefix(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+                                     _ptr(prefix_leader), _ptr(prefix_blocks), s, h, hkv, d, bs, nb,
+                                     int(max_context_len), int(max_prefix_blocks),
+                                     int(max_tail_len), float(scale), code, ccode, float(k_scale),
+                                     float(v_scale), int(partition_tokens), 0, _ptr(workspace),
+                                     ws_bytes, _stream(stream))
+    _check(st, "pa_decode_shared_prefix")

@@ -143,3 +143,60 @@ def padded_rows(tables: Iterable[Sequence[int]], width: Optional[int] = None,
     if any(len(r) > width for r in rows):
         raise ValueError("a table is wider than the requested width")
     return [r + [pad] * (width - len(r)) for r in rows]
+
+
+def prefix_groups(rows: Sequence[Sequence[int]], context_lens: Sequence[int],
+                  block_size: int) -> Tuple[List[int], List[int]]:
+    """Groups of consecutive sequences whose tables start with the same blocks.
+
+    Beams forked from one sequence, or requests that reuse one cached prompt,
+    name the same physical blocks in their leading table entries ("Copy-on-Write
+    与内存共享" and "Prefix Caching（前缀缓存）" on the tbr8.org page).  Returns
+    ``(leader, blocks)`` for ``pa_decode_shared_prefix``: ``leader[s]`` is the
+    first sequence of s's group, and at a leader ``blocks[L]`` is the number of
+    leading entries every member holds in common, counting only blocks that are
+    full for every member (``blocks * block_size <= context_len``).  A sequence
+    joins the group before it when it shares at least one such block with the
+    group's leader; other entries of ``blocks`` are 0.
+    """
+    n = len(rows)
+    leader = list(range(n))
+    blocks = [0] * n
+    lead = -1
+    for s in range(n):
+        full = int(context_lens[s]) // block_size
+        if lead >= 0:
+            limit = min(blocks[lead], full)
+            common = 0
+            while common < limit and rows[s][common] == rows[lead][common]:
+                common += 1
+            if common > 0:
+                leader[s] = lead
+                blocks[lead] = common
+                continue
+        lead = s
+        blocks[s] = full
+    # A leader without members shares nothing.
+    members = {leader[s] for s in range(n) if leader[s] != s}
+    for s in range(n):
+        if leader[s] == s and s not in members:
+            blocks[s] = 0
+    return leader, blocks
+
+
+def prefix_bounds(leader: Sequence[int], blocks: Sequence[int], context_lens: Sequence[int],
+                  block_size: int) -> Tuple[int, int]:
+    """Host bounds (max_prefix_blocks, max_tail_len) for a well-formed grouping.
+
+    ``leader``/``blocks`` as returned by ``prefix_groups``: every sequence's
+    shared prefix is its leader's block count, and its tail is the rest of its
+    context (the whole context when it shares nothing).
+    """
+    max_blocks = 0
+    max_tail = 0
+    for s, c in enumerate(context_lens):
+        lead = leader[s]
+        n = blocks[lead] if (leader[lead] == lead and blocks[lead] > 0) else 0
+        max_blocks = max(max_blocks, n)
+        max_tail = max(max_tail, int(c) - n * block_size)
+    return max_blocks, max_tail

@@ -35,9 +35,10 @@ int cache_shape_status(int num_blocks, int num_kv_heads, int block_size, int hea
 
 // Resolved partition length, or a negative status.
 int resolve_partition(int partition_tokens, int dtype, int cache_dtype, int head_dim, int block_size,
-                      int group) {
+                      int group, bool shared_prefix, int max_prefix_tokens) {
   if (partition_tokens == 0)
-    return pa::default_partition_tokens(dtype, cache_dtype, head_dim, block_size, group);
+    return pa::default_partition_tokens(dtype, cache_dtype, head_dim, block_size, group, shared_prefix,
+                                        max_prefix_tokens);
   if (partition_tokens < 0 || partition_tokens % block_size != 0) return PA_ERR_SHAPE;
   if (partition_tokens / block_size > pa::kMaxPagesPerPartition) return PA_ERR_UNSUPPORTED;
   return partition_tokens;
@@ -46,16 +47,27 @@ int resolve_partition(int partition_tokens, int dtype, int cache_dtype, int head
 struct DecodeSizes {
   int status;
   int partition_tokens;
-  int max_parts;
+  int grid_parts;    // partitions of the longest context
+  int max_parts;     // partition slots per (sequence, head) in the workspace
   size_t ml_bytes;   // offset of the accumulator area, 256-byte aligned
   size_t total;      // 0 when a single partition always suffices
+  int prefix_parts;  // shared-prefix decode: grid slots per sequence
+  int tail_parts;
 };
 
+// With a shared prefix a context is cut at the prefix end: at most
+// ceil(max_prefix_blocks * block_size / t) prefix partitions and
+// ceil(max_tail_len / t) (at least 1) partitions of the rest.
 DecodeSizes decode_sizes(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
-                         int max_context_len, int dtype, int cache_dtype, int partition_tokens) {
-  DecodeSizes z{PA_OK, 0, 1, 0, 0};
+                         int max_context_len, int dtype, int cache_dtype, int partition_tokens,
+                         bool shared_prefix, int max_prefix_blocks = 0, int max_tail_len = 0) {
+  DecodeSizes z{PA_OK, 0, 1, 1, 0, 0, 0, 1};
   if (!value_dtype(dtype) || !cache_dtype_ok(cache_dtype)) { z.status = PA_ERR_DTYPE; return z; }
   if (cache_dtype != dtype && !(dtype == PA_BF16 && cache_dtype == PA_FP8_E4M3)) {
+    z.status = PA_ERR_UNSUPPORTED;
+    return z;
+  }
+  if (shared_prefix && dtype != PA_BF16) {  // the shared-prefix tile runs on bf16 matrix cores
     z.status = PA_ERR_UNSUPPORTED;
     return z;
   }
@@ -70,10 +82,27 @@ DecodeSizes decode_sizes(int num_seqs, int num_heads, int num_kv_heads, int head
     z.status = PA_ERR_UNSUPPORTED;
     return z;
   }
-  const int pt = resolve_partition(partition_tokens, dtype, cache_dtype, head_dim, block_size, group);
+  if (shared_prefix &&
+      (max_prefix_blocks < 0 || max_tail_len < 0 ||
+       (int64_t)max_prefix_blocks * block_size > max_context_len || max_tail_len > max_context_len)) {
+    z.status = PA_ERR_SHAPE;
+    return z;
+  }
+  const int pt = resolve_partition(partition_tokens, dtype, cache_dtype, head_dim, block_size, group,
+                                   shared_prefix, max_prefix_blocks * block_size);
   if (pt < 0) { z.status = pt; return z; }
   z.partition_tokens = pt;
-  z.max_parts = max_context_len <= pt ? 1 : (max_context_len + pt - 1) / pt;
+  z.grid_parts = max_context_len <= pt ? 1 : (max_context_len + pt - 1) / pt;
+  z.max_parts = z.grid_parts;
+  if (shared_prefix) {
+    z.prefix_parts = (int)(((int64_t)max_prefix_blocks * block_size + pt - 1) / pt);
+    z.tail_parts = max_tail_len <= pt ? 1 : (max_tail_len + pt - 1) / pt;
+    z.max_parts = z.prefix_parts + z.tail_parts;
+    if ((int64_t)num_seqs * z.max_parts * num_kv_heads > 0x7fffffffLL) {  // one-dimensional grid
+      z.status = PA_ERR_UNSUPPORTED;
+      return z;
+    }
+  }
   if (z.max_parts > 1) {
     const uint64_t rows = (uint64_t)num_seqs * (uint64_t)num_heads * (uint64_t)z.max_parts;
     const uint64_t ml = (rows * 2 * sizeof(float) + 255) / 256 * 256;
@@ -97,7 +126,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_UNSUPPORTED:
       return "PA_ERR_UNSUPPORTED: head_dim must be 64/128, block_size 16/32, heads per kv head "
              "1/2/4/8, (dtype, cache_dtype) one of (F32, F32), (BF16, BF16), (BF16, FP8_E4M3), "
-             "grid within limits";
+             "grid within limits, known flags; the shared-prefix decode takes a bf16 query and flags 0";
     case PA_ERR_ALIGN: return "PA_ERR_ALIGN: buffer not aligned (16 bytes for data, element size for indices)";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: HIP reported an error after the launch";
@@ -151,29 +180,49 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, i
                                 int block_size, int max_context_len, int dtype, int cache_dtype,
                                 int partition_tokens) {
   const DecodeSizes z = decode_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                                     max_context_len, dtype, cache_dtype, partition_tokens);
+                                     max_context_len, dtype, cache_dtype, partition_tokens, false);
   return z.status == PA_OK ? z.total : (size_t)-1;
 }
 
-int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-              const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
-              const int32_t* seq_order, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
-              int block_size,
-              int num_blocks, int max_context_len, float scale, int dtype, int cache_dtype,
-              float k_scale, float v_scale, int partition_tokens, int flags, void* workspace,
-              size_t workspace_bytes, void* stream) {
+size_t pa_decode_shared_prefix_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
+                                              int head_dim, int block_size, int max_context_len,
+                                              int max_prefix_blocks, int max_tail_len, int dtype,
+                                              int cache_dtype, int partition_tokens) {
   const DecodeSizes z = decode_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                                     max_context_len, dtype, cache_dtype, partition_tokens);
+                                     max_context_len, dtype, cache_dtype, partition_tokens, true,
+                                     max_prefix_blocks, max_tail_len);
+  return z.status == PA_OK ? z.total : (size_t)-1;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Both decode entry points: validation, workspace carving, launch.  The
+// shared-prefix form passes its two per-sequence arrays (non-null).
+int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                const int32_t* seq_order, const int32_t* prefix_leader, const int32_t* prefix_blocks,
+                bool shared_prefix, int max_prefix_blocks, int max_tail_len, int num_seqs,
+                int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                int max_context_len, float scale, int dtype, int cache_dtype, float k_scale,
+                float v_scale, int partition_tokens, int flags, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  const DecodeSizes z = decode_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                     max_context_len, dtype, cache_dtype, partition_tokens, shared_prefix,
+                                     max_prefix_blocks, max_tail_len);
   if (z.status != PA_OK) return z.status;
   const bool fp8 = cache_dtype == PA_FP8_E4M3;
   if (fp8 && (!good_scale(k_scale) || !good_scale(v_scale))) return PA_ERR_VALUE;
   if (num_blocks <= 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * block_size < max_context_len) return PA_ERR_SHAPE;
-  if (flags & ~PA_DECODE_SHARED_PAGES) return PA_ERR_UNSUPPORTED;
+  if (flags & ~(shared_prefix ? 0 : PA_DECODE_SHARED_PAGES)) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (shared_prefix && (!prefix_leader || !prefix_blocks)) return PA_ERR_NULL;
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(seq_order, 4))
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(seq_order, 4) ||
+      !aligned(prefix_leader, 4) || !aligned(prefix_blocks, 4))
     return PA_ERR_ALIGN;
   if (num_seqs > kMaxGridYZ || num_kv_heads > kMaxGridYZ || num_heads > kMaxGridYZ)
     return PA_ERR_UNSUPPORTED;
@@ -205,11 +254,50 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   a.v_scale = fp8 ? v_scale : 1.f;
   a.partition_tokens = z.partition_tokens;
   a.shared_pages = (flags & PA_DECODE_SHARED_PAGES) != 0;
+  a.grid_parts = z.grid_parts;
   a.max_parts = z.max_parts;
   a.ws_ml = z.total ? reinterpret_cast<float*>(ws) : nullptr;
   a.ws_acc = z.total ? reinterpret_cast<float*>(ws + z.ml_bytes) : nullptr;
+  a.prefix_leader = shared_prefix ? prefix_leader : nullptr;
+  a.prefix_blocks = shared_prefix ? prefix_blocks : nullptr;
+  a.max_prefix_blocks = max_prefix_blocks;
+  a.max_tail_len = max_tail_len;
+  a.prefix_parts = z.prefix_parts;
+  a.tail_parts = z.tail_parts;
   a.stream = static_cast<hipStream_t>(stream);
   return pa::launch_decode(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+              const int32_t* seq_order, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+              int block_size, int num_blocks, int max_context_len, float scale, int dtype,
+              int cache_dtype, float k_scale, float v_scale, int partition_tokens, int flags,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     seq_order, nullptr, nullptr, false, 0, 0, num_seqs, num_heads, num_kv_heads, head_dim,
+                     block_size, num_blocks, max_context_len, scale, dtype, cache_dtype, k_scale,
+                     v_scale, partition_tokens, flags, workspace, workspace_bytes, stream);
+}
+
+int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int max_blocks_per_seq,
+                            const int32_t* context_lens, const int32_t* prefix_leader,
+                            const int32_t* prefix_blocks, int num_seqs, int num_heads,
+                            int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                            int max_context_len, int max_prefix_blocks, int max_tail_len,
+                            float scale, int dtype, int cache_dtype, float k_scale, float v_scale,
+                            int partition_tokens, int flags, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, nullptr,
+                     prefix_leader, prefix_blocks, true, max_prefix_blocks, max_tail_len, num_seqs,
+                     num_heads, num_kv_heads, head_dim,
+                     block_size, num_blocks, max_context_len, scale, dtype, cache_dtype, k_scale,
+                     v_scale, partition_tokens, flags, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

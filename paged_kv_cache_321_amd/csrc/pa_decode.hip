@@ -24,10 +24,10 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams p) {
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   const int lane = threadIdx.x;
-  const int ctx = p.context_lens[s];
-  if (ctx < 0 || ctx > p.max_context_len) return;  // written as NaN by the partition kernel
-  const int nparts = parts_for(ctx, p.partition_tokens);
-  if (nparts <= 1) return;                          // written by the partition kernel
+  const SeqSplit sp = split_context(p, p.context_lens[s], prefix_chunk(p, s).blocks);
+  if (sp.bad) return;  // written as NaN by the partition kernel
+  const int nparts = sp.nprefix + sp.ntail;
+  if (nparts <= 1) return;  // written by the partition kernel
   const int64_t base = ((int64_t)s * p.num_heads + h) * p.max_parts;
   const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + base;
   float mm = -FLT_MAX;
@@ -81,11 +81,20 @@ hipError_t launch_reduce(const DecodeLaunch& a, const DecodeParams& p) {
 // Grouped heads with a bf16 query (bf16 or fp8 cache) run on the matrix cores.
 static bool use_mfma_path(int dtype, int group) { return dtype == kDtypeBf16 && group >= 2; }
 
-int default_partition_tokens(int dtype, int /*cache_dtype*/, int /*head_dim*/, int block_size, int group) {
+int default_partition_tokens(int dtype, int /*cache_dtype*/, int /*head_dim*/, int block_size, int group,
+                             bool shared_prefix, int max_prefix_tokens) {
   // Fixed lengths (never the batch size, so a sequence's result does not
   // depend on the batch).  Vector path: 2048 tokens; matrix-core path: 4096
   // tokens (fewer, longer workgroups measured faster on long GQA contexts).
-  const int t = use_mfma_path(dtype, group) ? 4096 : 2048;
+  // Shared-prefix decode: a quarter of the longest shared prefix, rounded up
+  // to a power of two within [256, 2048] -- each prefix is spread over about
+  // four workgroups per kv head (measured best for 1024- and 4096-token
+  // prefixes of 4-beam groups).
+  int t = use_mfma_path(dtype, group) ? 4096 : 2048;
+  if (shared_prefix) {
+    t = 256;
+    while (t < 2048 && 4 * t < max_prefix_tokens) t *= 2;
+  }
   const int cap = kMaxPagesPerPartition * block_size;
   const int u = t < cap ? t : cap;
   return u - u % block_size;
@@ -106,6 +115,7 @@ hipError_t launch_decode(const DecodeLaunch& a) {
   p.max_blocks_per_seq = a.max_blocks_per_seq;
   p.num_seqs = a.num_seqs;
   p.num_heads = a.num_heads;
+  p.num_kv_heads = a.num_kv_heads;
   p.num_blocks = a.num_blocks;
   p.max_context_len = a.max_context_len;
   p.partition_tokens = a.partition_tokens;
@@ -114,7 +124,19 @@ hipError_t launch_decode(const DecodeLaunch& a) {
   p.scale_log2e = a.scale * kLog2e * (fp8 ? a.k_scale : 1.f);
   p.v_scale = fp8 ? a.v_scale : 1.f;
   const int group = a.num_heads / a.num_kv_heads;
-  hipError_t e = use_mfma_path(a.dtype, group) ? launch_partition_mfma(a, p) : launch_partition_valu(a, p);
+  p.prefix_leader = a.prefix_leader;
+  p.prefix_blocks = a.prefix_blocks;
+  p.chunk_seqs = 16 / group;
+  p.block_size = a.block_size;
+  p.max_prefix_blocks = a.max_prefix_blocks;
+  p.max_tail_len = a.max_tail_len;
+  p.prefix_parts = a.prefix_parts;
+  p.tail_parts = a.tail_parts;
+  // Shared-prefix decode always runs on the matrix cores (one 16-column tile
+  // holds the query heads of up to 16 / G sequences) and always merges.
+  const bool shared = a.prefix_leader != nullptr;
+  hipError_t e = shared || use_mfma_path(a.dtype, group) ? launch_partition_mfma(a, p)
+                                                         : launch_partition_valu(a, p);
   if (e != hipSuccess || a.max_parts <= 1) return e;
   return a.dtype == kDtypeF32 ? launch_reduce<float>(a, p) : launch_reduce<uint16_t>(a, p);
 }

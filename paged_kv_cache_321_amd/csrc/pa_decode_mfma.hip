@@ -82,7 +82,18 @@ __device__ __forceinline__ int swz(int row) { return 2 * (row & 3); }
 // TC: cache element type, bf16 bits (uint16_t) or E4M3 codes (uint8_t); the
 // query is bf16 either way and the products run on bf16 MFMA (E4M3 widens to
 // bf16 exactly).
-template <typename TC, int D, int BS, int G, bool NONTEMPORAL>
+//
+// SHARED (shared-prefix decode): the 16 columns of the tile are the query
+// heads of up to 16 / G sequences that hold the same leading pages (a beam
+// group, or requests with a common prompt), so each shared page is read once
+// for all of them.  The grid is one-dimensional, kv head fastest: the first
+// num_seqs * prefix_parts rows are prefix partitions of the chunk starting at
+// sequence row / prefix_parts, the rest serve each sequence's tokens past its
+// shared prefix (tail_parts rows per sequence).  Prefix workgroups read the
+// most pages, so they are dispatched first.  Both leave partition results
+// that the reduce kernel merges; the softmax algebra is the same as for one
+// sequence's partitions, since each column keeps its own running max and sum.
+template <typename TC, int D, int BS, int G, bool NONTEMPORAL, bool SHARED>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void decode_partition_mfma_kernel(DecodeParams p) {
   constexpr bool kFp8 = sizeof(TC) == 1;
   constexpr int NT = BS / 16;       // 16-token tiles per page
@@ -96,42 +107,126 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   constexpr int NV = BS / RPL;      // V loads per lane per page
   constexpr int NKL = kFp8 ? D / 64 : NC;  // K loads per 16-token tile
   constexpr int PAGEB = BS * ROWB;  // bytes of one bf16 page in LDS
-  constexpr int EPI = (kWaves * G * D + 2 * kWaves * G) * 4;
+  constexpr int NCOL = SHARED ? 16 : G;  // tile columns that carry results
+  constexpr int R = 16 / G;               // sequences per prefix chunk
+  constexpr int EPI = (kWaves * NCOL * D + 2 * kWaves * NCOL) * 4 + 2 * 16 * 4;
   constexpr int SMEM = kWaves * PAGEB > EPI ? kWaves * PAGEB : EPI;
-  static_assert(G >= 2 && G <= 16 && NCH >= 8 && BS % RPL == 0, "tile shape");
+  static_assert((G >= 2 || SHARED) && G <= 16 && NCH >= 8 && BS % RPL == 0, "tile shape");
 
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int s = sequence_of(p, blockIdx.z);
-  if (s < 0) return;  // uniform over the workgroup
+  int part = blockIdx.x;
+  const int kvh = SHARED ? (int)(blockIdx.x % p.num_kv_heads) : (int)blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
 
-  const PartitionRange r = partition_range(p, s, part, wave, BS);
-  if (part >= r.nparts) return;  // uniform over the workgroup
+  int s;                 // sequence whose table row supplies the page ids
+  PartitionRange r;
+  int my_id;
+  bool bad;              // this wave's pages cannot be read: its columns become NaN
+  int col_seq = -1;      // sequence of this lane's column l16 (-1: padding)
+  int col_total = 1;     // partitions of that sequence
+  bool col_bad = false;  // that sequence's table disagrees with the chunk's (NaN row)
+  int slot;              // partition slot of this workgroup's results (< max_parts)
+  if constexpr (!SHARED) {
+    slot = part;
+    s = sequence_of(p, blockIdx.z);
+    if (s < 0) return;  // uniform over the workgroup
+    r = partition_range(p, s, part, wave, BS);
+    if (part >= r.nparts) return;  // uniform over the workgroup
+    bool ids_bad;
+    my_id = load_page_ids(p, s, r, wave, lane, &ids_bad);
+    bad = r.ctx_bad || ids_bad;
+    col_seq = l16 < G ? s : -1;
+  } else {
+    const int pt = p.partition_tokens;
+    const int row = blockIdx.x / p.num_kv_heads;
+    const int prefix_rows = p.num_seqs * p.prefix_parts;
+    if (row < prefix_rows) {
+      // Prefix workgroup of the chunk that starts at sequence z.  Most rows
+      // are not chunk starts: that takes one load to see.
+      const int z = row / p.prefix_parts;
+      part = row % p.prefix_parts;
+      const int lead = p.prefix_leader[z];
+      if (lead < 0 || lead > z || (z - lead) % R != 0) return;
+      const PrefixChunk pc = prefix_chunk(p, z);
+      if (pc.blocks == 0 || pc.chunk != z) return;
+      // A prefix past the caller's bound: every member is a bad row, which
+      // its own workgroup writes.
+      if (pc.blocks > p.max_prefix_blocks) return;
+      const int pre = pc.blocks * BS;
+      const int npre = (pre + pt - 1) / pt;
+      if (part >= npre) return;
+      s = z;
+      slot = part;
+      r = token_range(pre, npre, part * pt, min(pre, part * pt + pt), false, wave, BS);
+      // Lane i < R checks member z + i: same group, and a context that holds
+      // the prefix (the same test its own workgroups make).
+      bool member = false;
+      int total = 0;
+      {
+        const int m = z + l16;
+        if (l16 < R && m < p.num_seqs && p.prefix_leader[m] == pc.leader) {
+          const SeqSplit sp = split_context(p, p.context_lens[m], pc.blocks);
+          member = !sp.bad;
+          total = sp.nprefix + sp.ntail;
+        }
+      }
+      const uint32_t members = static_cast<uint32_t>(__ballot(member)) & 0xffffu;
+      const int mi = l16 / G;
+      col_seq = (members >> mi) & 1u ? z + mi : -1;
+      col_total = __shfl(total, mi);
+      bool ids_bad;
+      my_id = load_page_ids(p, z, r, wave, lane, &ids_bad);
+      bad = ids_bad;
+      // Every member must name the same physical pages.
+      uint32_t differ = 0;
+      if (lane < r.nk) {
+        const int64_t j = r.pg0 + wave + lane * kWaves;
+#pragma unroll
+        for (int i = 1; i < R; ++i)
+          if (((members >> i) & 1u) &&
+              p.block_tables[(int64_t)(z + i) * p.max_blocks_per_seq + j] != my_id)
+            differ |= 1u << i;
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) differ |= __shfl_xor(differ, off);
+      col_bad = ((differ >> mi) & 1u) != 0;
+    } else {
+      // Sequence s's own workgroups: its tokens past the shared prefix.
+      s = (row - prefix_rows) / p.tail_parts;
+      part = (row - prefix_rows) % p.tail_parts;
+      const SeqSplit sp = split_context(p, p.context_lens[s], prefix_chunk(p, s).blocks);
+      if (part >= sp.ntail) return;
+      const int t0 = sp.prefix + part * pt;
+      r = token_range(sp.ctx, sp.nprefix + sp.ntail, t0, min(sp.ctx, t0 + pt), sp.bad, wave, BS);
+      bool ids_bad;
+      my_id = load_page_ids(p, s, r, wave, lane, &ids_bad);
+      bad = sp.bad || ids_bad;
+      col_seq = l16 < G ? s : -1;
+      col_total = sp.nprefix + sp.ntail;
+      slot = sp.nprefix + part;
+    }
+  }
   const int tok1 = r.tok1;
   const int nk = r.nk;
-  bool ids_bad;
-  const int my_id = load_page_ids(p, s, r, wave, lane, &ids_bad);
-  const bool bad = r.ctx_bad || ids_bad;
 
   // B operand of S^T = K Q^T: for bf16 caches lane holds Q[head l16][32c +
   // 8 g4 .. +7]; for fp8 caches, whose 16-byte K loads carry 16 columns, step
   // c = 2kk + h holds columns 64kk + 16 g4 + 8h .. +7 (the K operand uses the
-  // same column order, so the contraction is unchanged).  Zero for the padding
-  // heads l16 >= G.
+  // same column order, so the contraction is unchanged).  Zero for padding
+  // columns.
   bf16x8_t qb[NC];
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q) +
-                         ((int64_t)s * p.num_heads + (int64_t)kvh * G + (l16 < G ? l16 : 0)) * D;
+    const int q_seq = col_seq >= 0 ? col_seq : s;
+    const int q_head = kvh * G + (SHARED ? l16 % G : (l16 < G ? l16 : 0));
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)q_seq * p.num_heads + q_head) * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int col0 = kFp8 ? 64 * (c >> 1) + 16 * g4 + 8 * (c & 1) : 32 * c + 8 * g4;
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (l16 < G) v = *reinterpret_cast<const uint4*>(qp + col0);
+      if (col_seq >= 0) v = *reinterpret_cast<const uint4*>(qp + col0);
       qb[c] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -290,7 +385,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
 
   // One K and one V register buffer: the next page's V is requested as soon
   // as this page's V sits in LDS, the next K as soon as the QK products have
-  // consumed this page's K, so one page per wave is always in flight.
+  // consumed this page's K, so one page per wave is always in flight.  (Two
+  // buffer pairs, two pages in flight, measured no faster on any workload
+  // here and cost a wave per SIMD of occupancy.)
   if (!bad && nk > 0) {
     uint4 kr[NT][NKL], vr[NV];
     load_k(0, kr);
@@ -311,38 +408,94 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
 
   __syncthreads();  // every wave is done with its page buffer: reuse the LDS
   float* sm_acc = reinterpret_cast<float*>(smem);
-  float* sm_m = sm_acc + kWaves * G * D;
-  float* sm_l = sm_m + kWaves * G;
-  if (l16 < G) {
+  float* sm_m = sm_acc + kWaves * NCOL * D;
+  float* sm_l = sm_m + kWaves * NCOL;
+  if (l16 < NCOL) {
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sm_acc[(wave * G + l16) * D + 16 * m + 4 * g4 + j] = acc[m][j];
+      for (int j = 0; j < 4; ++j) sm_acc[(wave * NCOL + l16) * D + 16 * m + 4 * g4 + j] = acc[m][j];
     if (g4 == 0) {
-      sm_m[wave * G + l16] = bad ? 0.f : m_run;
-      sm_l[wave * G + l16] = bad ? __builtin_nanf("") : l_run;
+      sm_m[wave * NCOL + l16] = bad ? 0.f : m_run;
+      sm_l[wave * NCOL + l16] = bad || col_bad ? __builtin_nanf("") : l_run;
     }
   }
-  __syncthreads();
-  merge_waves_and_store<uint16_t, D, G>(p, sm_acc, sm_m, sm_l, s, kvh, part, r.nparts);
+  if constexpr (!SHARED) {
+    __syncthreads();
+    merge_waves_and_store<uint16_t, D, G>(p, sm_acc, sm_m, sm_l, s, kvh, part, r.nparts);
+  } else {
+    int* sm_seq = reinterpret_cast<int*>(sm_l + kWaves * NCOL);
+    int* sm_total = sm_seq + 16;
+    if (wave == 0 && g4 == 0) {
+      sm_seq[l16] = col_seq;
+      sm_total[l16] = col_total;
+    }
+    __syncthreads();
+    // Merge the waves per column; a sequence with one partition in all gets
+    // its final row, otherwise the partition slot.
+    for (int idx = tid; idx < NCOL * D; idx += kWaves * 64) {
+      const int c = idx / D;
+      const int d = idx % D;
+      const int seq = sm_seq[c];
+      if (seq < 0) continue;
+      float mm = -FLT_MAX;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm_m[w * NCOL + c]);
+      float ll = 0.f, aa = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float wt = fast_exp2(sm_m[w * NCOL + c] - mm);
+        ll += sm_l[w * NCOL + c] * wt;
+        aa += sm_acc[(w * NCOL + c) * D + d] * wt;
+      }
+      const int64_t sh = (int64_t)seq * p.num_heads + (int64_t)kvh * G + c % G;
+      if (sm_total[c] == 1) {
+        const float o = (ll == 0.f) ? 0.f : aa * p.v_scale / ll;
+        Elem<uint16_t>::store(static_cast<uint16_t*>(p.out) + sh * D + d, o);
+      } else {
+        const int64_t at = sh * p.max_parts + slot;
+        p.ws_acc[at * D + d] = aa;
+        if (d == 0) {
+          p.ws_ml[at * 2] = mm;
+          p.ws_ml[at * 2 + 1] = ll;
+        }
+      }
+    }
+  }
 }
 
-template <typename TC, int D, int BS, int G>
+template <typename TC, int D, int BS, int G, bool SHARED>
 hipError_t launch_t(const DecodeLaunch& a, const DecodeParams& p) {
-  dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
-  if (a.shared_pages)
-    hipLaunchKernelGGL((decode_partition_mfma_kernel<TC, D, BS, G, false>), grid, dim3(kWaves * 64), 0, a.stream, p);
-  else
-    hipLaunchKernelGGL((decode_partition_mfma_kernel<TC, D, BS, G, true>), grid, dim3(kWaves * 64), 0, a.stream, p);
+  const dim3 grid = SHARED ? dim3(a.num_seqs * (a.prefix_parts + a.tail_parts) * a.num_kv_heads, 1, 1)
+                          : dim3(a.grid_parts, a.num_kv_heads, a.num_seqs);
+  if constexpr (SHARED) {
+    hipLaunchKernelGGL((decode_partition_mfma_kernel<TC, D, BS, G, true, true>), grid, dim3(kWaves * 64), 0,
+                       a.stream, p);
+  } else if (a.shared_pages) {
+    hipLaunchKernelGGL((decode_partition_mfma_kernel<TC, D, BS, G, false, false>), grid, dim3(kWaves * 64), 0,
+                       a.stream, p);
+  } else {
+    hipLaunchKernelGGL((decode_partition_mfma_kernel<TC, D, BS, G, true, false>), grid, dim3(kWaves * 64), 0,
+                       a.stream, p);
+  }
   return hipGetLastError();
 }
 
 template <typename TC, int D, int BS>
 hipError_t by_group(const DecodeLaunch& a, const DecodeParams& p) {
+  if (a.prefix_leader != nullptr) {
+    switch (a.num_heads / a.num_kv_heads) {
+      case 1: return launch_t<TC, D, BS, 1, true>(a, p);
+      case 2: return launch_t<TC, D, BS, 2, true>(a, p);
+      case 4: return launch_t<TC, D, BS, 4, true>(a, p);
+      case 8: return launch_t<TC, D, BS, 8, true>(a, p);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (a.num_heads / a.num_kv_heads) {
-    case 2: return launch_t<TC, D, BS, 2>(a, p);
-    case 4: return launch_t<TC, D, BS, 4>(a, p);
-    case 8: return launch_t<TC, D, BS, 8>(a, p);
+    case 2: return launch_t<TC, D, BS, 2, false>(a, p);
+    case 4: return launch_t<TC, D, BS, 4, false>(a, p);
+    case 8: return launch_t<TC, D, BS, 8, false>(a, p);
     default: return hipErrorInvalidValue;
   }
 }

@@ -247,7 +247,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partition_valu_kernel(Deco
 
 template <typename TQ, typename TC, int D, int BS, int G>
 hipError_t launch_t(const DecodeLaunch& a, const DecodeParams& p) {
-  dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
+  dim3 grid(a.grid_parts, a.num_kv_heads, a.num_seqs);
   if (a.shared_pages)
     hipLaunchKernelGGL((decode_partition_valu_kernel<TQ, TC, D, BS, G, false>), grid, dim3(kWaves * 64), 0,
                        a.stream, p);

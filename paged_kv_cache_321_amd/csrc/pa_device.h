@@ -160,12 +160,22 @@ struct DecodeParams {
   int max_blocks_per_seq;
   int num_seqs;
   int num_heads;
+  int num_kv_heads;
   int num_blocks;
   int max_context_len;
   int partition_tokens;
   int max_parts;
   float scale_log2e;  // softmax scale * log2(e), times k_scale for fp8 caches
   float v_scale;      // multiplies the output (1 unless the cache holds fp8 codes)
+  // Shared-prefix decode only (prefix_leader == null otherwise).
+  const int32_t* prefix_leader;  // [num_seqs] first member of the sequence's group
+  const int32_t* prefix_blocks;  // [num_seqs] shared leading blocks, read at group leaders
+  int chunk_seqs;                // members one prefix workgroup serves (16 / G)
+  int block_size;
+  int max_prefix_blocks;         // caller's bound on prefix_blocks
+  int max_tail_len;              // caller's bound on context_len - shared prefix
+  int prefix_parts;              // grid rows per sequence for prefix partitions
+  int tail_parts;                // grid rows per sequence for the rest
 };
 
 // Sequence served by grid slot z (the caller may reorder dispatch); -1 if the
@@ -217,6 +227,80 @@ __device__ __forceinline__ int load_page_ids(const DecodeParams& p, int s, const
   return id;
 }
 
+// Shared-prefix decode.  Sequence s names the first member L of its group in
+// prefix_leader[s]; the group's members hold the same physical blocks in their
+// first prefix_blocks[L] table entries.  Members are served in chunks of
+// chunk_seqs consecutive sequences counted from L, and one workgroup reads each
+// shared page once for a whole chunk.  A sequence whose entry does not describe
+// such a chunk (L out of range or not its own leader, or the first sequence of
+// its chunk in another group) is served alone, which computes the same result.
+// Every kernel derives this from the same device values, so they agree.
+struct PrefixChunk {
+  int leader;  // the group's first member (s itself when served alone)
+  int chunk;   // first member of s's chunk (s itself when served alone)
+  int blocks;  // shared leading blocks, 0 = none
+};
+__device__ __forceinline__ PrefixChunk prefix_chunk(const DecodeParams& p, int s) {
+  PrefixChunk c{s, s, 0};
+  if (p.prefix_leader == nullptr) return c;
+  const int lead = p.prefix_leader[s];
+  if (lead < 0 || lead > s || p.prefix_leader[lead] != lead) return c;
+  const int first = lead + (s - lead) / p.chunk_seqs * p.chunk_seqs;
+  if (p.prefix_leader[first] != lead) return c;
+  const int nb = p.prefix_blocks[lead];
+  if (nb <= 0) return c;
+  c.leader = lead;
+  c.chunk = first;
+  c.blocks = nb;
+  return c;
+}
+// How a sequence's context is cut: the shared prefix [0, prefix) into nprefix
+// partitions (computed by its chunk's workgroups, partition slots 0 ..
+// nprefix-1), the rest [prefix, ctx) into ntail partitions (its own
+// workgroups, slots nprefix ..).  Without a prefix this is the plain
+// partitioning.  A bad row (context length out of range, shorter than the
+// declared prefix, or past the caller's prefix or tail bound) has one
+// partition and is written as NaN.
+struct SeqSplit {
+  int ctx, prefix, nprefix, ntail;
+  bool bad;
+};
+__device__ __forceinline__ SeqSplit split_context(const DecodeParams& p, int ctx, int prefix_blocks) {
+  SeqSplit r;
+  r.ctx = ctx;
+  const int64_t pre = (int64_t)prefix_blocks * p.block_size;
+  r.bad = ctx < 0 || ctx > p.max_context_len || pre > ctx;
+  if (p.prefix_leader != nullptr)  // the caller's bounds size the grid
+    r.bad = r.bad || prefix_blocks > p.max_prefix_blocks || ctx - pre > p.max_tail_len;
+  r.prefix = r.bad ? 0 : (int)pre;
+  const int pt = p.partition_tokens;
+  if (r.bad) {
+    r.nprefix = 0;
+    r.ntail = 1;
+  } else if (r.prefix == 0) {
+    r.nprefix = 0;
+    r.ntail = parts_for(ctx, pt);
+  } else {
+    r.nprefix = (r.prefix + pt - 1) / pt;
+    r.ntail = (ctx - r.prefix + pt - 1) / pt;
+  }
+  return r;
+}
+// Page range of the tokens [tok0, tok1) (tok0 a multiple of block_size) and
+// this wave's share of it.
+__device__ __forceinline__ PartitionRange token_range(int ctx, int nparts, int tok0, int tok1, bool bad,
+                                                      int wave, int block_size) {
+  PartitionRange r;
+  r.ctx = ctx;
+  r.ctx_bad = bad;
+  r.nparts = nparts;
+  r.tok0 = tok0;
+  r.tok1 = bad ? tok0 : tok1;
+  r.pg0 = tok0 / block_size;
+  r.npg = r.tok1 > r.tok0 ? (r.tok1 - r.tok0 + block_size - 1) / block_size : 0;
+  r.nk = r.npg > wave ? (r.npg - wave + kWaves - 1) / kWaves : 0;
+  return r;
+}
 // Epilogue: the kWaves partial states of each query head of the group sit in
 // LDS (sm_acc [kWaves][G][D], sm_m / sm_l [kWaves][G]); merge them with the
 // log-sum-exp rule and write either the final row (single partition) or the

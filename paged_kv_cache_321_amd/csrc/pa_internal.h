@@ -37,9 +37,19 @@ struct DecodeLaunch {
   float v_scale;
   int partition_tokens;  // resolved, > 0
   bool shared_pages;     // pages may be shared: default cache policy, else non-temporal
-  int max_parts;         // ceil(max_context_len / partition_tokens), >= 1
+  int grid_parts;        // ceil(max_context_len / partition_tokens), >= 1
+  int max_parts;         // partition slots per (sequence, head): grid_parts, or
+                         // prefix_parts + tail_parts with a shared prefix
   float* ws_ml;          // [S, H, max_parts, 2] (running max, running sum); null if max_parts == 1
   float* ws_acc;         // [S, H, max_parts, D] unnormalised outputs; null if max_parts == 1
+  // Shared-prefix decode (null for the plain decode): per-sequence group
+  // leader and shared leading blocks (read at leaders).
+  const int32_t* prefix_leader;
+  const int32_t* prefix_blocks;
+  int max_prefix_blocks;  // caller's bounds: prefix_blocks at leaders, context - prefix
+  int max_tail_len;
+  int prefix_parts;       // ceil(max_prefix_blocks * block_size / partition_tokens)
+  int tail_parts;         // ceil(max_tail_len / partition_tokens), >= 1
   hipStream_t stream;
 };
 
@@ -66,7 +76,8 @@ struct CopyLaunch {
 };
 
 // Default partition length (tokens) for a shape; a multiple of block_size.
-int default_partition_tokens(int dtype, int cache_dtype, int head_dim, int block_size, int group);
+int default_partition_tokens(int dtype, int cache_dtype, int head_dim, int block_size, int group,
+                             bool shared_prefix, int max_prefix_tokens);
 
 hipError_t launch_decode(const DecodeLaunch& a);
 hipError_t launch_reshape_and_cache(const ReshapeLaunch& a);

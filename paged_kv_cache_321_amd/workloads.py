@@ -42,14 +42,14 @@ from __future__ import annotations
 
 import math
 from dataclasses import dataclass, field
-from typing import Dict, List, Optional, Sequence
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 import torch
 
 from .block_pool import BlockPool, BlockTable, padded_rows
 
-__all__ = ["Spec", "Plan", "Inputs", "SPECS", "uniform_plan", "beam_plan",
+__all__ = ["Spec", "Plan", "Inputs", "SPECS", "uniform_plan", "beam_plan", "prefix_plan",
            "make_plan", "build_inputs", "make_inputs", "to_host_numpy",
            "TORCH_DTYPE"]
 
@@ -198,6 +198,46 @@ def beam_plan(groups: int, beams: int, prefix_len: int, tail_lo: int, tail_hi: i
     return Plan(block_size, nb, np.asarray(ctx, dtype=np.int32), rows, history,
                 np.arange(n, dtype=np.int64), np.asarray(slots, dtype=np.int64),
                 np.asarray(pairs, dtype=np.int64).reshape(-1, 2), shared)
+
+
+def prefix_plan(groups: Sequence[Tuple[int, Sequence[int]]], block_size: int,
+                gen: torch.Generator, pool_factor: float = 1.1) -> Plan:
+    """Groups of sequences forked from one prompt, consecutive in the batch.
+
+    ``groups`` lists ``(prefix_len, [context_len of each member])``; the first
+    member's ``prefix_len`` tokens (a multiple of ``block_size``) are shared by
+    the forks, each member then grows its own tail.  Every member whose context
+    extends past the prefix stores its newest token in a block of its own.
+    """
+    counts = []
+    for prefix_len, ctxs in groups:
+        if prefix_len % block_size or any(c < prefix_len for c in ctxs) or not ctxs:
+            raise ValueError("prefix must be whole blocks and no longer than any member")
+        pb = prefix_len // block_size
+        counts.append(pb + sum(BlockTable.blocks_for(int(c), block_size) - pb for c in ctxs))
+    nb = _pool_size(sum(counts), pool_factor, None)
+    pool = BlockPool(nb, torch.randperm(nb, generator=gen).tolist())
+    tables: List[BlockTable] = []
+    shared: List[int] = []
+    ctx: List[int] = []
+    for prefix_len, ctxs in groups:
+        first = BlockTable(pool, block_size)
+        first.ensure_tokens(prefix_len)
+        if len(ctxs) > 1:
+            shared.extend(first.blocks)
+        members = [first] + [first.fork() for _ in ctxs[1:]]
+        for t, c in zip(members, ctxs):
+            t.ensure_tokens(int(c))
+        tables.extend(members)
+        ctx.extend(int(c) for c in ctxs)
+    width = max(1, max(len(t.blocks) for t in tables))
+    rows = np.asarray(padded_rows([t.blocks for t in tables], width), dtype=np.int32)
+    prefix_of = [p for p, ctxs in groups for _ in ctxs]
+    seqs = [s for s in range(len(ctx)) if ctx[s] > prefix_of[s]]
+    slots = [tables[s].slot_of(ctx[s] - 1) for s in seqs]
+    return Plan(block_size, nb, np.asarray(ctx, dtype=np.int32), rows, rows.copy(),
+                np.asarray(seqs, dtype=np.int64), np.asarray(slots, dtype=np.int64),
+                np.zeros((0, 2), dtype=np.int64), shared)
 
 
 def make_plan(name: str, gen: torch.Generator, **kw) -> Plan:

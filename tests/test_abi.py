@@ -124,6 +124,70 @@ def test_workspace_size():
     assert ws(3, 8, 2, 64, 16, 2000, F32, FP8, 512) == bad
 
 
+def decode_shared(**kw):
+    a = dict(out=P, q=P, k=P, v=P, bt=P, mb=8, ctx=P, lead=P, nblk=P, S=2, H=8, Hkv=2, D=128,
+             BS=16, NB=32, maxctx=100, mpb=4, mtail=60, scale=0.1, dtype=BF16, cdtype=None, ks=0.5,
+             vs=0.5, pt=0, flags=0, ws=P, wsb=1 << 30)
+    a.update(kw)
+    cdtype = a["dtype"] if a["cdtype"] is None else a["cdtype"]
+    return LIB.pa_decode_shared_prefix(a["out"], a["q"], a["k"], a["v"], a["bt"], a["mb"], a["ctx"],
+                                       a["lead"], a["nblk"], a["S"], a["H"], a["Hkv"], a["D"],
+                                       a["BS"], a["NB"], a["maxctx"], a["mpb"], a["mtail"],
+                                       a["scale"], a["dtype"], cdtype, a["ks"], a["vs"], a["pt"],
+                                       a["flags"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=F32), UNSUP),            # the shared tile runs on bf16 matrix cores
+    (dict(dtype=F32, cdtype=F32, S=0), UNSUP),
+    (dict(flags=1), UNSUP),              # no flags
+    (dict(H=6, Hkv=2), UNSUP),
+    (dict(D=96), UNSUP),
+    (dict(lead=None), NULL),
+    (dict(nblk=None), NULL),
+    (dict(lead=P + 2), ALIGN),
+    (dict(nblk=P + 2), ALIGN),
+    (dict(ws=None), WS),                 # a prefix is declared: results are merged
+    (dict(wsb=16), WS),
+    (dict(ws=MIS), ALIGN),
+    (dict(S=70000, maxctx=10, mpb=0, mtail=10), UNSUP),
+    (dict(mpb=-1), SHAPE),
+    (dict(mtail=-1), SHAPE),
+    (dict(mpb=7), SHAPE),                # 7 * 16 > max_context_len
+    (dict(mtail=101), SHAPE),
+    (dict(mb=6), SHAPE),
+    (dict(pt=24), SHAPE),
+    (dict(cdtype=FP8, ks=0.0), VALUE),
+    (dict(S=0), OK),
+    (dict(S=0, lead=None, nblk=None, ws=None), OK),
+])
+def test_decode_shared_prefix_validation(kw, code):
+    assert decode_shared(**kw) == code
+
+
+def test_shared_prefix_workspace_size():
+    ws = LIB.pa_decode_shared_prefix_workspace_size
+    # Slots per (sequence, head): ceil(prefix bound / t) + max(1, ceil(tail bound / t)).
+    for maxctx, mpb, mtail, pt, parts in ((100, 4, 60, 512, 2), (2000, 64, 976, 512, 4),
+                                          (2000, 0, 2000, 512, 4), (2000, 125, 0, 512, 5)):
+        rows = 3 * 8 * parts
+        ml = (rows * 2 * 4 + 255) // 256 * 256
+        assert ws(3, 8, 2, 64, 16, maxctx, mpb, mtail, BF16, BF16, pt) == ml + rows * 64 * 4
+        assert ws(3, 8, 2, 64, 16, maxctx, mpb, mtail, BF16, FP8, pt) == ml + rows * 64 * 4
+    # Nothing to merge: no prefix and every context within one partition.
+    assert ws(3, 8, 2, 64, 16, 500, 0, 500, BF16, BF16, 512) == 0
+    # Default partition: a quarter of the longest prefix, a power of two in [256, 2048].
+    for mpb, pt in ((0, 256), (16, 256), (64, 256), (65, 512), (256, 1024), (4096, 2048)):
+        assert ws(1, 4, 4, 128, 16, 70000, mpb, 76, BF16, BF16, 0) == \
+            ws(1, 4, 4, 128, 16, 70000, mpb, 76, BF16, BF16, pt), mpb
+    assert ws(0, 8, 2, 64, 16, 100, 4, 60, BF16, BF16, 0) == 0
+    bad = ctypes.c_size_t(-1).value
+    assert ws(3, 8, 2, 64, 16, 2000, 4, 60, F32, F32, 512) == bad
+    assert ws(3, 8, 3, 64, 16, 2000, 4, 60, BF16, BF16, 512) == bad
+    assert ws(3, 8, 2, 64, 16, 2000, 126, 60, BF16, BF16, 512) == bad   # 126 * 16 > 2000
+    assert ws(3, 8, 2, 64, 16, 2000, 4, 2001, BF16, BF16, 512) == bad
+
+
 def reshape(**kw):
     a = dict(key=P, value=P, k=P, v=P, slots=P, T=4, NB=8, Hkv=2, BS=16, D=64, dtype=F32,
              cdtype=None, ks=1.0, vs=1.0)
