@@ -24,6 +24,9 @@ built from):
   through the block table, softmax over them, weighted sum of V),
   section 7 "模型实现 — 以 Llama 为例" (store the new token's K/V into the
   cache, then run paged attention).
+* [tbr8] sections "Chunked Prefill（分块预填充）" and "结合 Speculative
+  Decoding 加速" (several new tokens per sequence in one pass), see
+  ``multi_query``.
 
 Readings taken where the pages are silent or inconsistent (each is listed in
 the design notes of the repository as well):
@@ -74,6 +77,9 @@ __all__ = [
     "attend_one",
     "decode",
     "decode_rows",
+    "query_rows",
+    "query_position",
+    "multi_query",
 ]
 
 BF16 = "bf16"
@@ -360,3 +366,69 @@ def decode_rows(q_s: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
         out[i], w = attend_one(q64[h], k_ctx[kvh], v_ctx[kvh], float(np.float32(scale)))
         weights.append(w)
     return out, weights
+
+
+# --------------------------------------------------------------------------
+# Several new query tokens per sequence.  [tbr8] section "Chunked Prefill（分块
+# 预填充）": a long prompt is processed in chunks that are interleaved with
+# decoding requests; section "结合 Speculative Decoding 加速": a small draft
+# model proposes N tokens and the large model checks them all in one pass.
+# Reading (the pages give no formula): the K/V of a sequence's q_len new
+# tokens are already in the cache (stored by reshape_and_cache, as for
+# decode); the new tokens are the last q_len positions of its context; each
+# attends to every cached token at or before its own position (causal
+# attention, the rule that makes the chunked result equal the unchunked one).
+# --------------------------------------------------------------------------
+
+def query_rows(query_start: np.ndarray, s: int) -> tuple[int, int]:
+    """Rows [t0, t1) of q / out holding sequence s's queries (CSR offsets)."""
+    return int(query_start[s]), int(query_start[s + 1])
+
+
+def query_position(context_len: int, query_len: int, i: int) -> int:
+    """Position in its sequence of query i of a chunk of ``query_len`` new
+    tokens that end the sequence's ``context_len`` tokens."""
+    return context_len - query_len + i
+
+
+def multi_query(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                block_tables: np.ndarray, context_lens: np.ndarray,
+                query_start: np.ndarray, scale: float, dtype: str,
+                cache_dtype: str = None, k_scale: float = 1.0, v_scale: float = 1.0):
+    """Causal attention of each sequence's new query tokens over its paged cache.
+
+    q: [T, H, D] with sequence s's queries in rows query_rows(query_start, s);
+    caches [NB, Hkv, BS, D]; block_tables [S, MB]; context_lens [S] (cached
+    tokens, the new ones included); query_start [S + 1].  The query at
+    position p (``query_position``) gets softmax over tokens 0..p of
+    scale * q.k, applied to V.  A sequence with more queries than context
+    tokens is an error.  Returns out [T, H, D] float64 (rows of no sequence
+    stay zero).
+    """
+    num_rows, num_heads, head_dim = q.shape
+    num_kv_heads = k_cache.shape[1]
+    cache_dtype = dtype if cache_dtype is None else cache_dtype
+    scale64 = float(np.float32(scale))
+    q64 = widen(np.ascontiguousarray(q), dtype)
+    out = np.zeros((num_rows, num_heads, head_dim), dtype=np.float64)
+    for s in range(len(context_lens)):
+        t0, t1 = query_rows(query_start, s)
+        query_len = t1 - t0
+        context_len = int(context_lens[s])
+        if query_len == 0:
+            continue
+        if query_len > context_len:
+            raise ValueError(f"sequence {s}: {query_len} queries but {context_len} tokens")
+        k_ctx = widen(gather_context(k_cache, block_tables[s], context_len), cache_dtype)
+        v_ctx = widen(gather_context(v_cache, block_tables[s], context_len), cache_dtype)
+        if cache_dtype == FP8:
+            k_ctx = k_ctx * float(np.float32(k_scale))
+            v_ctx = v_ctx * float(np.float32(v_scale))
+        for i in range(query_len):
+            visible = query_position(context_len, query_len, i) + 1
+            for h in range(num_heads):
+                kvh = kv_head_for(h, num_heads, num_kv_heads)
+                out[t0 + i, h], _ = attend_one(q64[t0 + i, h], k_ctx[kvh, :visible],
+                                               v_ctx[kvh, :visible], scale64)
+    return out
+

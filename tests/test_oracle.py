@@ -383,13 +383,132 @@ def pin_fp8_reshape_and_decode():
     assert np.allclose(out, ref[0, :, 0].numpy(), rtol=0, atol=1e-12)
 
 
+# --------------------------------------------------------------------------
+# Several queries per sequence (chunked prefill, speculative verification)
+# --------------------------------------------------------------------------
+
+def mq_case(rng, h, hkv, d, seqs, bs=16):
+    """seqs: [(context_len, query_len)].  Dense K/V per sequence scattered into
+    one shuffled NaN-filled pool; the queries of all sequences stacked."""
+    need = [-(-c // bs) for c, _ in seqs]
+    nb = sum(need) + 3
+    ids = rng.permutation(nb)
+    kc = np.full((nb, hkv, bs, d), np.nan, dtype=np.float32)
+    vc = np.full_like(kc, np.nan)
+    tables = np.full((len(seqs), max(need + [1])), -1, dtype=np.int32)
+    dense = []
+    at = 0
+    for s, (c, _) in enumerate(seqs):
+        k = rng.standard_normal((hkv, c, d)).astype(np.float32)
+        v = rng.standard_normal((hkv, c, d)).astype(np.float32)
+        tables[s, :need[s]] = ids[at:at + need[s]]
+        at += need[s]
+        for t in range(c):
+            kc[tables[s, t // bs], :, t % bs, :] = k[:, t, :]
+            vc[tables[s, t // bs], :, t % bs, :] = v[:, t, :]
+        dense.append((k, v))
+    qs = np.concatenate([[0], np.cumsum([ql for _, ql in seqs])]).astype(np.int32)
+    q = rng.standard_normal((int(qs[-1]), h, d)).astype(np.float32)
+    ctx = np.array([c for c, _ in seqs], dtype=np.int32)
+    return q, dense, kc, vc, tables, ctx, qs
+
+
+MQ_CASES = [  # (H, Hkv, D, BS, [(context_len, query_len)])
+    (4, 4, 32, 16, [(10, 10), (37, 5), (1, 1), (50, 1), (20, 0)]),
+    (8, 2, 16, 16, [(33, 33), (70, 6), (16, 16)]),
+    (8, 1, 8, 4, [(9, 3), (5, 5), (12, 12)]),
+]
+
+
+def pin_mq_sdpa():
+    """Each chunk equals torch's SDPA (fp64) with the causal mask aligned to the
+    end of the context: query i may see tokens j <= L - q_len + i."""
+    rng = np.random.default_rng(31)
+    for h, hkv, d, bs, seqs in MQ_CASES:
+        q, dense, kc, vc, tables, ctx, qs = mq_case(rng, h, hkv, d, seqs, bs)
+        scale = float(np.float32(0.3))
+        out = op.multi_query(q, kc, vc, tables, ctx, qs, scale, op.F32)
+        g = h // hkv
+        for s, (c, ql) in enumerate(seqs):
+            if ql == 0:
+                continue
+            k, v = dense[s]
+            kt = torch.from_numpy(k).double().repeat_interleave(g, dim=0)[None]
+            vt = torch.from_numpy(v).double().repeat_interleave(g, dim=0)[None]
+            qt = torch.from_numpy(q[qs[s]:qs[s + 1]]).double().permute(1, 0, 2)[None]
+            allowed = torch.arange(c)[None, :] <= (c - ql + torch.arange(ql))[:, None]
+            ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=allowed,
+                                                                   scale=scale)
+            assert np.allclose(out[qs[s]:qs[s + 1]], ref[0].permute(1, 0, 2).numpy(), rtol=0,
+                               atol=1e-12), (h, hkv, s)
+
+
+def pin_mq_bruteforce():
+    rng = np.random.default_rng(32)
+    h, hkv, d, bs, seqs = 2, 1, 4, 2, [(5, 3), (3, 3), (4, 1)]
+    q, dense, kc, vc, tables, ctx, qs = mq_case(rng, h, hkv, d, seqs, bs)
+    scale = float(np.float32(0.5))
+    out = op.multi_query(q, kc, vc, tables, ctx, qs, scale, op.F32)
+    for s, (c, ql) in enumerate(seqs):
+        k, v = dense[s]
+        for i in range(ql):
+            seen = c - ql + i + 1   # tokens 0 .. c - ql + i
+            for hh in range(h):
+                ref = brute(q[qs[s] + i, hh], k[0][:seen], v[0][:seen], scale)
+                assert np.allclose(out[qs[s] + i, hh], ref, rtol=0, atol=1e-12), (s, i, hh)
+
+
+def pin_mq_last_query_is_decode():
+    """The last query of a chunk sits at position L - 1: plain decode."""
+    rng = np.random.default_rng(33)
+    for h, hkv, d, bs, seqs in MQ_CASES:
+        q, dense, kc, vc, tables, ctx, qs = mq_case(rng, h, hkv, d, seqs, bs)
+        out = op.multi_query(q, kc, vc, tables, ctx, qs, 0.25, op.F32)
+        for s, (c, ql) in enumerate(seqs):
+            if ql == 0:
+                continue
+            dec = op.decode(q[qs[s + 1] - 1][None], kc, vc, tables[s][None], ctx[s:s + 1], 0.25,
+                            op.F32)
+            assert np.allclose(out[qs[s + 1] - 1], dec[0], rtol=0, atol=1e-13)
+
+
+def pin_mq_chunking_invariance():
+    """Cutting a chunk in two (the first part at the shorter context) changes
+    nothing: the point of chunked prefill."""
+    rng = np.random.default_rng(34)
+    h, hkv, d, bs = 4, 2, 16, 4
+    q, dense, kc, vc, tables, ctx, qs = mq_case(rng, h, hkv, d, [(30, 12)], bs)
+    whole = op.multi_query(q, kc, vc, tables, ctx, qs, 0.3, op.F32)
+    for cut in (1, 5, 11):
+        first = op.multi_query(q[:cut], kc, vc, tables, np.array([30 - 12 + cut], np.int32),
+                               np.array([0, cut], np.int32), 0.3, op.F32)
+        second = op.multi_query(q[cut:], kc, vc, tables, ctx, np.array([0, 12 - cut], np.int32),
+                                0.3, op.F32)
+        assert np.allclose(np.concatenate([first, second]), whole, rtol=0, atol=1e-13), cut
+
+
+def pin_mq_causality():
+    """Changing the newest token's K/V changes only the last query's output."""
+    rng = np.random.default_rng(35)
+    h, hkv, d, bs = 4, 4, 8, 4
+    q, dense, kc, vc, tables, ctx, qs = mq_case(rng, h, hkv, d, [(13, 6)], bs)
+    before = op.multi_query(q, kc, vc, tables, ctx, qs, 0.3, op.F32)
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[tables[0, 12 // bs], :, 12 % bs, :] += 3.0
+    vc2[tables[0, 12 // bs], :, 12 % bs, :] -= 2.0
+    after = op.multi_query(q, kc2, vc2, tables, ctx, qs, 0.3, op.F32)
+    assert np.array_equal(after[:5], before[:5])
+    assert not np.allclose(after[5], before[5])
+
+
 PINS = [pin_bruteforce, pin_sdpa, pin_worked_tables, pin_block_counts, pin_kv_bytes,
         pin_ctx1_returns_v, pin_weights_sum_to_one, pin_q_zero_gives_mean,
         pin_constant_v, pin_shift_invariance, pin_block_permutation,
         pin_block_size_independent, pin_gqa_equals_repeated_mha,
         pin_nan_poison_ignored, pin_zero_context, pin_batch_invariance, pin_widen,
         pin_reshape_library, pin_reshape_roundtrip, pin_copy_blocks, pin_e4m3_table,
-        pin_e4m3_encode, pin_fp8_reshape_and_decode]
+        pin_e4m3_encode, pin_fp8_reshape_and_decode, pin_mq_sdpa, pin_mq_bruteforce,
+        pin_mq_last_query_is_decode, pin_mq_chunking_invariance, pin_mq_causality]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -499,6 +618,22 @@ def _e4m3_no_saturation(x):
 _ORIG_E4M3_VALUES = op.e4m3_values
 _ORIG_E4M3_ENCODE = op.e4m3_encode
 
+
+def _position_plus_one(context_len, query_len, i):
+    return context_len - query_len + i + 1
+
+
+def _position_unmasked(context_len, query_len, i):
+    return context_len - 1
+
+
+def _position_top_left(context_len, query_len, i):
+    return i
+
+
+def _rows_drop_last(query_start, s):
+    return int(query_start[s]), max(int(query_start[s]), int(query_start[s + 1]) - 1)
+
 MUTATIONS = {
     "e4m3_ties_away_from_even": ("e4m3_encode", _e4m3_ties_away),
     "e4m3_bias_8": ("e4m3_values", _e4m3_values_bias8),
@@ -513,6 +648,10 @@ MUTATIONS = {
     "bf16_widen_shift": ("widen", _widen_bad),
     "reshape_block_offset_swapped": ("reshape_and_cache", _reshape_swapped),
     "copy_blocks_k_only": ("copy_blocks", _copy_k_only),
+    "mq_causal_mask_one_late": ("query_position", _position_plus_one),
+    "mq_no_causal_mask": ("query_position", _position_unmasked),
+    "mq_causal_mask_top_left": ("query_position", _position_top_left),
+    "mq_query_rows_short": ("query_rows", _rows_drop_last),
 }
 
 
