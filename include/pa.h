@@ -263,6 +263,57 @@ int pa_decode_shared_prefix(void* out, const void* q,
                             int partition_tokens, int flags,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pa_multi_query_workspace_size -- bytes of device workspace pa_multi_query
+ * needs (0 when no context can need more than one partition); (size_t)-1 for
+ * arguments it would reject.  partition_tokens: 0 = default (1024 tokens).
+ */
+size_t pa_multi_query_workspace_size(int num_query_tokens, int num_heads, int num_kv_heads,
+                                     int head_dim, int block_size, int max_context_len,
+                                     int dtype, int cache_dtype, int partition_tokens);
+
+/*
+ * pa_multi_query -- causal attention of several new query tokens per sequence
+ * over the paged cache: a chunk of a long prompt processed between decode steps,
+ * or drafted tokens being verified.  ([tbr8] "Chunked Prefill（分块预填充）": a long
+ * prefill is cut into chunks interleaved with decoding; "结合 Speculative Decoding
+ * 加速": the large model checks N drafted tokens in one pass.)
+ *
+ * query_start: device int32 [num_seqs + 1]; sequence s owns rows
+ * query_start[s] .. query_start[s+1] - 1 of q and out ([num_query_tokens,
+ * num_heads, head_dim], bf16).  With n = its row count and L = context_lens[s]
+ * (cached tokens, the n new ones included: their K/V were stored with
+ * pa_reshape_and_cache), row query_start[s] + i is the token at position
+ * p = L - n + i and, for every query head h (kv head h / G),
+ *   out[row, h, :] = sum_{t <= p} softmax_t(scale * dot(q[row, h, :], K_t)) * V_t
+ * with K_t, V_t reached through block_tables as for pa_decode (E4M3 caches times
+ * k_scale / v_scale).  Accumulation in float32, output rounded to bf16 (RNE).
+ * A sequence with n == 1 is a decode step.
+ *
+ * dtype must be PA_BF16 (cache PA_BF16 or PA_FP8_E4M3); G = num_heads /
+ * num_kv_heads in {1, 2, 4, 8}; head_dim 64 or 128; block_size 16 or 32.
+ * max_query_len >= every n and max_context_len >= every L (host bounds that size
+ * the grid).  partition_tokens (0 = default 1024; else a positive multiple of
+ * block_size): a sequence whose n * G rows fit in 64 has its context cut into
+ * partitions of this many tokens, merged by a second kernel; longer chunks are
+ * not cut.  workspace: at least pa_multi_query_workspace_size(...) bytes,
+ * 16-byte aligned (NULL allowed when that is 0).
+ * Preconditions (device values): query_start ranges inside [0, num_query_tokens],
+ * non-decreasing, n <= max_query_len (a sequence breaking these is skipped and
+ * its rows are left unwritten; overlapping ranges give unspecified rows);
+ * n <= L <= max_context_len and table entries in [0, num_blocks) (rows of a
+ * sequence breaking these are NaN).  Rows of no sequence are left unwritten.
+ */
+int pa_multi_query(void* out, const void* q,
+                   const void* k_cache, const void* v_cache,
+                   const int32_t* block_tables, int max_blocks_per_seq,
+                   const int32_t* context_lens, const int32_t* query_start,
+                   int num_seqs, int num_query_tokens, int max_query_len,
+                   int num_heads, int num_kv_heads, int head_dim,
+                   int block_size, int num_blocks, int max_context_len,
+                   float scale, int dtype, int cache_dtype, float k_scale, float v_scale,
+                   int partition_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
 /* pa_status_string -- static, human-readable name of a status code. */
 const char* pa_status_string(int status);
 

@@ -27,7 +27,7 @@ STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
           -7: "PA_ERR_LAUNCH", -8: "PA_ERR_VALUE"}
 EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_workspace_size",
            "pa_decode", "pa_decode_shared_prefix_workspace_size", "pa_decode_shared_prefix",
-           "pa_status_string")
+           "pa_multi_query_workspace_size", "pa_multi_query", "pa_status_string")
 
 _c_int, _c_size, _c_float, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
 
@@ -61,6 +61,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                             [_c_float, _c_int, _c_int, _c_float, _c_float, _c_int,
                                              _c_int, _vp, _c_size, _vp])
     lib.pa_decode_shared_prefix.restype = _c_int
+    lib.pa_multi_query_workspace_size.argtypes = [_c_int] * 9
+    lib.pa_multi_query_workspace_size.restype = _c_size
+    lib.pa_multi_query.argtypes = ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp] + [_c_int] * 9 +
+                                   [_c_float, _c_int, _c_int, _c_float, _c_float, _c_int, _vp,
+                                    _c_size, _vp])
+    lib.pa_multi_query.restype = _c_int
     lib.pa_status_string.argtypes = [_c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     return lib
@@ -276,3 +282,55 @@ def pa_decode_shared_prefix(out: torch.Tensor, q: torch.Tensor, k_cache: torch.T
                                      float(v_scale), int(partition_tokens), 0, _ptr(workspace),
                                      ws_bytes, _stream(stream))
     _check(st, "pa_decode_shared_prefix")
+
+
+def pa_multi_query_workspace_size(num_query_tokens: int, num_heads: int, num_kv_heads: int,
+                                  head_dim: int, block_size: int, max_context_len: int, dtype: int,
+                                  partition_tokens: int = 0, cache_dtype: Optional[int] = None) -> int:
+    cache_dtype = dtype if cache_dtype is None else cache_dtype
+    n = LIB.pa_multi_query_workspace_size(num_query_tokens, num_heads, num_kv_heads, head_dim,
+                                          block_size, max_context_len, dtype, cache_dtype,
+                                          partition_tokens)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("pa_multi_query_workspace_size: arguments rejected by the library")
+    return n
+
+
+def pa_multi_query(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   block_tables: torch.Tensor, context_lens: torch.Tensor,
+                   query_start: torch.Tensor, scale: float, max_context_len: int,
+                   max_query_len: int, partition_tokens: int = 0,
+                   workspace: Optional[torch.Tensor] = None, stream=None, k_scale: float = 1.0,
+                   v_scale: float = 1.0) -> None:
+    """Causal attention of each sequence's new query tokens over the paged caches.
+
+    q, out [T, H, D] (bf16) hold sequence s's queries in rows
+    query_start[s] .. query_start[s + 1] - 1 (int32 device tensor [S + 1]); they
+    are the last positions of its context_lens[s] cached tokens.
+    """
+    for n, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                 ("block_tables", block_tables), ("context_lens", context_lens),
+                 ("query_start", query_start)):
+        _device_contig(n, t)
+    _need(all(t.dtype == torch.int32 for t in (block_tables, context_lens, query_start)),
+          "block_tables, context_lens and query_start must be int32")
+    _need(q.dtype == out.dtype and k_cache.dtype == v_cache.dtype, "element types differ")
+    t, h, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    s = context_lens.shape[0]
+    _need(d2 == d and out.shape == q.shape and v_cache.shape == k_cache.shape, "shape mismatch")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == s, "block_tables must be [S, MB]")
+    _need(query_start.shape == (s + 1,), "query_start must be [S + 1]")
+    code = _dtype_code(q)
+    ccode = _dtype_code(k_cache)
+    need = pa_multi_query_workspace_size(t, h, hkv, d, bs, max_context_len, code, partition_tokens,
+                                         ccode) if h > 0 and hkv > 0 and h % hkv == 0 else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = LIB.pa_multi_query(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                            block_tables.shape[1], _ptr(context_lens), _ptr(query_start), s, t,
+                            int(max_query_len), h, hkv, d, bs, nb, int(max_context_len),
+                            float(scale), code, ccode, float(k_scale), float(v_scale),
+                            int(partition_tokens), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "pa_multi_query")

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libpa.so")
 ARCH = "gfx950"
 
-SOURCES = ["pa_api.cpp", "pa_cache.hip", "pa_decode.hip", "pa_decode_valu.hip",
+SOURCES = ["pa_api.cpp", "pa_cache.hip", "pa_decode.hip", "pa_decode_valu.hip", "pa_multi_query.hip",
            "pa_decode_mfma.hip"]
 
 # Packed-fp32 VALU ops are switched off for all device code.

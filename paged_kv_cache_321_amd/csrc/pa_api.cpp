@@ -268,9 +268,117 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   return pa::launch_decode(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+struct MultiQuerySizes {
+  int status;
+  int partition_tokens;
+  int max_parts;
+  size_t ml_bytes;
+  size_t total;
+};
+
+MultiQuerySizes multi_query_sizes(int num_query_tokens, int num_heads, int num_kv_heads, int head_dim,
+                                  int block_size, int max_context_len, int dtype, int cache_dtype,
+                                  int partition_tokens) {
+  MultiQuerySizes z{PA_OK, 0, 1, 0, 0};
+  if (!value_dtype(dtype) || !cache_dtype_ok(cache_dtype)) { z.status = PA_ERR_DTYPE; return z; }
+  // The tiles run on bf16 matrix cores: a bf16 query over a bf16 or fp8 cache.
+  if (dtype != PA_BF16 || cache_dtype == PA_F32) { z.status = PA_ERR_UNSUPPORTED; return z; }
+  if (num_query_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_context_len < 0 || num_heads % num_kv_heads != 0) {
+    z.status = PA_ERR_SHAPE;
+    return z;
+  }
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size) ||
+      !supported_group(num_heads / num_kv_heads)) {
+    z.status = PA_ERR_UNSUPPORTED;
+    return z;
+  }
+  int pt = partition_tokens;
+  if (pt == 0) pt = pa::default_multi_query_partition_tokens(block_size);
+  if (pt < 0 || pt % block_size != 0) { z.status = PA_ERR_SHAPE; return z; }
+  z.partition_tokens = pt;
+  z.max_parts = max_context_len <= pt ? 1 : (max_context_len + pt - 1) / pt;
+  if (z.max_parts > 1) {
+    const uint64_t rows = (uint64_t)num_query_tokens * (uint64_t)num_heads * (uint64_t)z.max_parts;
+    const uint64_t ml = (rows * 2 * sizeof(float) + 255) / 256 * 256;
+    z.ml_bytes = (size_t)ml;
+    z.total = (size_t)(ml + rows * (uint64_t)head_dim * sizeof(float));
+  }
+  return z;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t pa_multi_query_workspace_size(int num_query_tokens, int num_heads, int num_kv_heads,
+                                     int head_dim, int block_size, int max_context_len, int dtype,
+                                     int cache_dtype, int partition_tokens) {
+  const MultiQuerySizes z = multi_query_sizes(num_query_tokens, num_heads, num_kv_heads, head_dim,
+                                              block_size, max_context_len, dtype, cache_dtype,
+                                              partition_tokens);
+  return z.status == PA_OK ? z.total : (size_t)-1;
+}
+
+int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                   const int32_t* query_start, int num_seqs, int num_query_tokens, int max_query_len,
+                   int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                   int max_context_len, float scale, int dtype, int cache_dtype, float k_scale,
+                   float v_scale, int partition_tokens, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  const MultiQuerySizes z = multi_query_sizes(num_query_tokens, num_heads, num_kv_heads, head_dim,
+                                              block_size, max_context_len, dtype, cache_dtype,
+                                              partition_tokens);
+  if (z.status != PA_OK) return z.status;
+  const bool fp8 = cache_dtype == PA_FP8_E4M3;
+  if (fp8 && (!good_scale(k_scale) || !good_scale(v_scale))) return PA_ERR_VALUE;
+  if (num_seqs < 0 || max_query_len < 0 || num_blocks <= 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size < max_context_len) return PA_ERR_SHAPE;
+  const int group = num_heads / num_kv_heads;
+  const int64_t row_blocks = ((int64_t)max_query_len * group + 63) / 64;
+  if (num_seqs == 0 || num_query_tokens == 0 || row_blocks == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+    return PA_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4))
+    return PA_ERR_ALIGN;
+  if ((int64_t)num_seqs * row_blocks * num_kv_heads * z.max_parts > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+  if (z.total > 0) {
+    if (!workspace || workspace_bytes < z.total) return PA_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
+  }
+  char* ws = static_cast<char*>(workspace);
+  pa::MultiQueryLaunch a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.num_seqs = num_seqs;
+  a.num_query_tokens = num_query_tokens;
+  a.max_query_len = max_query_len;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.scale = scale;
+  a.cache_dtype = cache_dtype;
+  a.k_scale = fp8 ? k_scale : 1.f;
+  a.v_scale = fp8 ? v_scale : 1.f;
+  a.partition_tokens = z.partition_tokens;
+  a.max_parts = z.max_parts;
+  a.max_row_blocks = (int)row_blocks;
+  a.ws_ml = z.total ? reinterpret_cast<float*>(ws) : nullptr;
+  a.ws_acc = z.total ? reinterpret_cast<float*>(ws + z.ml_bytes) : nullptr;
+  a.stream = static_cast<hipStream_t>(stream);
+  return pa::launch_multi_query(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,

@@ -34,50 +34,10 @@
 // denominator share the same reference, so the ratio is unchanged.
 
 #include "pa_device.h"
+#include "pa_mfma.h"
 
 namespace pa {
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef short s16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-// Orders this wave's LDS writes before its later LDS reads (and the reverse)
-// as seen by the compiler; the LDS unit serves one wave's requests in order.
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Two finite floats -> two bf16, round to nearest even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  typedef __bf16 pair_t __attribute__((ext_vector_type(2)));
-  const pair_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// Eight E4M3 codes -> eight bf16, exact (an E4M3 value has 3 mantissa bits),
-// with v_cvt_scalef32_pk_bf16_fp8 at scale 1 (checked on gfx950: exact for all
-// 256 codes in both halves).
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-template <bool kHigh>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHigh));
-}
-
-__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-  return make_uint4(fp8x2_to_bf16x2<false>(lo), fp8x2_to_bf16x2<true>(lo), fp8x2_to_bf16x2<false>(hi),
-                    fp8x2_to_bf16x2<true>(hi));
-}
-
-// 16-byte chunk c of LDS row `row` is stored at chunk c ^ swz(row).  One
-// transposed read (below) has each 16-lane group read 4 consecutive rows at
-// the same columns; the swizzle puts those 4 rows' 32-byte segments 2 chunks
-// apart, in distinct banks.
-__device__ __forceinline__ int swz(int row) { return 2 * (row & 3); }
 
 // TC: cache element type, bf16 bits (uint16_t) or E4M3 codes (uint8_t); the
 // query is bf16 either way and the products run on bf16 MFMA (E4M3 widens to
@@ -287,17 +247,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     }
     wave_lds_fence();
   };
-  // V^T operand through ds_read_b64_tr_b16 (checked on gfx950): in each group
-  // of 16 lanes, lane 4r + c receives element c of the 8-byte rows addressed
-  // by lanes r, r + 4, r + 8, r + 12.  Lane l16 addresses token tb + l16 / 4 at
-  // columns d0 + 4 (l16 % 4) .. +3, so it receives column d0 + l16 of tokens
-  // tb .. tb + 3: four k slots of the A operand in one instruction.
-  auto vt4 = [&](int tb, int d0) -> s16x4_t {
-    const int t = tb + (l16 >> 2);
-    const int d = d0 + 4 * (l16 & 3);
-    const unsigned char* a = vbuf + t * ROWB + (((d >> 3) ^ swz(t)) << 4) + ((d & 7) << 1);
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)a);
-  };
+  // V^T operand: four k slots per transposed LDS read (vt4 in pa_mfma.h).
+  auto vt4 = [&](int tb, int d0) -> s16x4_t { return pa::vt4<ROWB>(vbuf, l16, tb, d0); };
 
   auto scores = [&](const uint4 (&kr)[NT][NKL], f32x4_t (&st)[NT]) {
 #pragma unroll

@@ -75,11 +75,35 @@ struct CopyLaunch {
   hipStream_t stream;
 };
 
+struct MultiQueryLaunch {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  const int32_t* context_lens;
+  const int32_t* query_start;
+  int num_seqs, num_query_tokens, max_query_len;
+  int num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len;
+  float scale;
+  int cache_dtype;  // bf16 or fp8 (the query is bf16)
+  float k_scale, v_scale;
+  int partition_tokens;  // resolved, > 0
+  int max_parts;         // ceil(max_context_len / partition_tokens), >= 1
+  int max_row_blocks;    // ceil(max_query_len * G / 64)
+  float* ws_ml;          // [T, H, max_parts, 2]; null if max_parts == 1
+  float* ws_acc;         // [T, H, max_parts, D]; null if max_parts == 1
+  hipStream_t stream;
+};
+
 // Default partition length (tokens) for a shape; a multiple of block_size.
 int default_partition_tokens(int dtype, int cache_dtype, int head_dim, int block_size, int group,
                              bool shared_prefix, int max_prefix_tokens);
 
 hipError_t launch_decode(const DecodeLaunch& a);
+int default_multi_query_partition_tokens(int block_size);
+hipError_t launch_multi_query(const MultiQueryLaunch& a);
 hipError_t launch_reshape_and_cache(const ReshapeLaunch& a);
 hipError_t launch_copy_blocks(const CopyLaunch& a);
 

@@ -1,0 +1,462 @@
+// Multi-query paged attention on the matrix cores: several new query tokens per
+// sequence -- a chunk of a long prompt, or drafted tokens being verified --
+// each attending causally to the sequence's cached context ("详解vLLM推理引擎
+// 架构" (tbr8.org), sections "Chunked Prefill（分块预填充）" and "结合 Speculative
+// Decoding 加速").  The new tokens' K/V are already in the cache; query i of a
+// sequence with q_len new tokens and L cached tokens sits at position
+// L - q_len + i and sees tokens 0 .. L - q_len + i.
+//
+// Rows.  For one kv head, a sequence contributes q_len * G rows (row r is query
+// r / G with query head kvh * G + r % G).  A workgroup takes a block of 64 rows
+// and each of its 4 waves owns 16 of them as the 16 columns of
+//   S^T [tokens x rows] = K [tokens x D] . Q^T [D x rows],
+//   O^T [D x rows]     += V^T [D x tokens] . P^T [tokens x rows]
+// (the decode kernel's formulation), so one K/V step staged in LDS feeds 64
+// rows.  A step is 32 tokens: two 16-token pages or one 32-token page.  K sits
+// in LDS row-major with 16-byte chunks swizzled by the row, so the 16 rows one
+// A-operand read touches hit distinct banks; V sits in the transposed-read
+// layout of pa_mfma.h.  E4M3 caches are widened to bf16 (exactly) on the way
+// into LDS.  Each column keeps its own running max and sum, moved lazily (only
+// when a score exceeds the reference by more than 2^8).
+//
+// Partitions.  A sequence whose rows fit one block (speculative verification,
+// short chunks) would give too few workgroups on a long context, so its
+// context is cut into partitions of partition_tokens tokens whose
+// (max, sum, accumulator) triples the reduce kernel merges; a sequence with
+// more rows is parallel enough through its row blocks and is not cut.  The
+// rule depends on the sequence alone, so its result does not depend on the
+// rest of the batch.
+
+#include "pa_device.h"
+#include "pa_mfma.h"
+
+namespace pa {
+namespace {
+
+constexpr int kRowsPerBlock = kWaves * 16;
+constexpr int kStepTokens = 32;
+
+struct MultiQueryParams {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start;
+  float* ws_ml;
+  float* ws_acc;
+  int64_t block_stride;  // elements between consecutive physical blocks
+  int max_blocks_per_seq;
+  int num_seqs;
+  int num_query_tokens;
+  int num_heads;
+  int num_kv_heads;
+  int num_blocks;
+  int max_context_len;
+  int max_query_len;
+  int partition_tokens;
+  int max_parts;       // partition slots per row (grid and workspace)
+  int max_row_blocks;  // row blocks per sequence in the grid
+  float scale_log2e;   // softmax scale * log2(e), times k_scale for fp8 caches
+  float v_scale;       // multiplies the output (1 unless the cache holds fp8 codes)
+};
+
+// The work of row block `rbi` (in dispatch order) of sequence s.
+struct MqBlock {
+  int t0;       // first q / out row of the sequence
+  int qlen;     // new query tokens
+  int ctx;      // cached tokens, the new ones included
+  int rows;     // qlen * G
+  int rb;       // row block: rows rb * 64 .. rb * 64 + 63
+  int kv_end;   // tokens seen by the block's last query
+  int nparts;   // context partitions
+  bool skip;    // no such block, or an invalid query range: nothing is written
+  bool bad;     // bad context length: the block's rows are written as NaN
+};
+
+template <int G>
+__device__ __forceinline__ MqBlock mq_block(const MultiQueryParams& p, int s, int rbi) {
+  MqBlock b{};
+  const int t0 = p.query_start[s];
+  const int t1 = p.query_start[s + 1];
+  b.skip = t0 < 0 || t1 < t0 || t1 > p.num_query_tokens || t1 - t0 > p.max_query_len;
+  if (b.skip) return b;
+  b.t0 = t0;
+  b.qlen = t1 - t0;
+  b.rows = b.qlen * G;
+  const int nrb = (b.rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (rbi >= nrb) {
+    b.skip = true;
+    return b;
+  }
+  b.rb = nrb - 1 - rbi;  // later queries see more tokens: dispatch them first
+  b.ctx = p.context_lens[s];
+  b.bad = b.ctx < 0 || b.ctx > p.max_context_len || b.qlen > b.ctx;
+  b.nparts = 1;
+  if (b.bad) return b;
+  const int last_row = min(b.rows, (b.rb + 1) * kRowsPerBlock) - 1;
+  b.kv_end = b.ctx - b.qlen + last_row / G + 1;
+  if (nrb == 1 && b.kv_end > p.partition_tokens)
+    b.nparts = (b.kv_end + p.partition_tokens - 1) / p.partition_tokens;
+  return b;
+}
+
+template <typename TC, int D, int BS, int G>
+__global__ __launch_bounds__(kWaves * 64) void multi_query_kernel(MultiQueryParams p) {
+  constexpr bool kFp8 = sizeof(TC) == 1;
+  constexpr int PPS = kStepTokens / BS;      // pages per step
+  constexpr int NC = D / 32;                 // 32-wide steps of the QK contraction
+  constexpr int NM = D / 16;                 // 16-wide output tiles along D
+  constexpr int ROWB = D * 2;                // bytes of one bf16 row in LDS
+  constexpr int NCH = ROWB / 16;             // 16-byte bf16 chunks per row
+  constexpr int CCH = D * (int)sizeof(TC) / 16;  // 16-byte cache chunks per row
+  constexpr int CHUNKS = kStepTokens * CCH;  // 16-byte cache chunks per step (K or V)
+  constexpr int PER_T = (CHUNKS + kWaves * 64 - 1) / (kWaves * 64);
+  constexpr int TILEB = kStepTokens * ROWB;  // bytes of one step's K (or V) in LDS
+  static_assert(kStepTokens % BS == 0 && NCH >= 8, "tile shape");
+
+  int x = blockIdx.x;
+  const int kvh = x % p.num_kv_heads;
+  x /= p.num_kv_heads;
+  const int part = x % p.max_parts;
+  x /= p.max_parts;
+  const int rbi = x % p.max_row_blocks;
+  const int s = x / p.max_row_blocks;
+  const MqBlock b = mq_block<G>(p, s, rbi);
+  if (b.skip || part >= b.nparts) return;  // uniform over the workgroup
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int g4 = lane >> 4;
+
+  // This lane's row: column l16 of the wave's tile.
+  const int r = b.rb * kRowsPerBlock + wave * 16 + l16;
+  const bool row_ok = r < b.rows;
+  const int qi = row_ok ? r / G : 0;
+  const int head = kvh * G + (row_ok ? r % G : 0);
+  const int64_t qrow = b.t0 + qi;
+  const int last_seen = b.ctx - b.qlen + qi;  // the row sees tokens 0 .. last_seen
+
+  const int pt = p.partition_tokens;
+  const int tok0 = b.nparts > 1 ? part * pt : 0;
+  const int tok1 = b.bad ? tok0 : (b.nparts > 1 ? min(b.kv_end, tok0 + pt) : b.kv_end);
+  const int pg0 = tok0 / BS;
+  const int npg = tok1 > tok0 ? (tok1 - tok0 + BS - 1) / BS : 0;
+  const int nsteps = (npg + PPS - 1) / PPS;
+
+  // B operand of S^T: Q[row l16][32c + 8 g4 .. +7]; zero for rows past the block.
+  bf16x8_t qb[NC];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + (qrow * p.num_heads + head) * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (row_ok) v = *reinterpret_cast<const uint4*>(qp + 32 * c + 8 * g4);
+      qb[c] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  f32x4_t acc[NM];  // O^T[d = 16 m + 4 g4 + j][row l16]
+#pragma unroll
+  for (int m = 0; m < NM; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -FLT_MAX;  // running max of the row (same in its 4 lanes)
+  float l_run = 0.f;       // this lane's share of the running sum
+
+  __shared__ __attribute__((aligned(16))) unsigned char kt[TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char vt[TILEB];
+
+  const TC* kc = static_cast<const TC*>(p.k_cache) + (int64_t)kvh * BS * D;
+  const TC* vc = static_cast<const TC*>(p.v_cache) + (int64_t)kvh * BS * D;
+  const int32_t* table = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
+
+  // Physical ids of pages pg0 + base .. + 63, one per lane (ids outside the
+  // pool become 0 and mark the block bad).  Every wave holds the same ids.
+  int my_id = 0;
+  bool ids_bad = false;
+  auto load_ids = [&](int base) {
+    int id = 0;
+    bool badid = false;
+    if (base + lane < npg) {
+      id = table[pg0 + base + lane];
+      badid = id < 0 || id >= p.num_blocks;
+      if (badid) id = 0;
+    }
+    my_id = id;
+    ids_bad = ids_bad || __any(badid);
+  };
+
+  // One step's K and V chunks, PER_T per thread: chunk c is token c / CCH of
+  // the step, 16 bytes at chunk c % CCH of that token's cache row.
+  uint4 kreg[PER_T], vreg[PER_T];
+  auto load_step = [&](int st) {
+#pragma unroll
+    for (int u = 0; u < PER_T; ++u) {
+      const int c = tid + u * kWaves * 64;
+      const int tok = c / CCH;
+      const int pg = st * PPS + tok / BS;  // page of the partition
+      kreg[u] = vreg[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (c < CHUNKS && pg < npg) {
+        // The page is the same across each wave (a wave's chunks lie in one page).
+        const int64_t phys = __builtin_amdgcn_readlane(my_id, __builtin_amdgcn_readfirstlane(pg) & 63);
+        const int64_t off = phys * p.block_stride + (tok % BS) * D + (c % CCH) * (16 / (int)sizeof(TC));
+        kreg[u] = load_page16<true>(kc + off);
+        vreg[u] = load_page16<true>(vc + off);
+      }
+    }
+  };
+  // K rows at chunk ch ^ (token % NCH); V rows in the transposed-read layout.
+  // V rows past the partition end are zero, so nothing unread can reach the
+  // PV product (K rows there are masked out of the softmax).
+  auto stage_step = [&](int st) {
+#pragma unroll
+    for (int u = 0; u < PER_T; ++u) {
+      const int c = tid + u * kWaves * 64;
+      if (c >= CHUNKS) continue;
+      const int tok = c / CCH;
+      const int ch = c % CCH;
+      const bool keep = tok0 + (st * PPS) * BS + tok < tok1;
+      if constexpr (kFp8) {
+        const uint4 k0 = fp8x8_to_bf16x8(kreg[u].x, kreg[u].y), k1 = fp8x8_to_bf16x8(kreg[u].z, kreg[u].w);
+        uint4 v0 = fp8x8_to_bf16x8(vreg[u].x, vreg[u].y), v1 = fp8x8_to_bf16x8(vreg[u].z, vreg[u].w);
+        if (!keep) v0 = v1 = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(kt + tok * ROWB + (((2 * ch) ^ (tok % NCH)) << 4)) = k0;
+        *reinterpret_cast<uint4*>(kt + tok * ROWB + (((2 * ch + 1) ^ (tok % NCH)) << 4)) = k1;
+        *reinterpret_cast<uint4*>(vt + tok * ROWB + (((2 * ch) ^ swz(tok)) << 4)) = v0;
+        *reinterpret_cast<uint4*>(vt + tok * ROWB + (((2 * ch + 1) ^ swz(tok)) << 4)) = v1;
+      } else {
+        const uint4 v = keep ? vreg[u] : make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(kt + tok * ROWB + ((ch ^ (tok % NCH)) << 4)) = kreg[u];
+        *reinterpret_cast<uint4*>(vt + tok * ROWB + ((ch ^ swz(tok)) << 4)) = v;
+      }
+    }
+  };
+
+  auto compute_step = [&](int st) {
+    const int t_base = tok0 + st * kStepTokens;
+    // S^T for the step's two 16-token tiles.
+    f32x4_t sc[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      sc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int tok = 16 * tt + l16;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(kt + tok * ROWB + (((4 * c + g4) ^ (tok % NCH)) << 4));
+        sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qb[c], sc[tt], 0, 0, 0);
+      }
+    }
+    // Causal mask and online softmax: lane holds tokens 16 tt + 4 g4 + j.
+    float sv[2][4];
+    float mx = m_run;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = t_base + 16 * tt + 4 * g4 + j;
+        const bool valid = t < tok1 && t <= last_seen;
+        sv[tt][j] = valid ? sc[tt][j] * p.scale_log2e : -__builtin_inff();
+        mx = fmaxf(mx, sv[tt][j]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__any(mx > m_run + kRescaleLog2)) {
+      const float alpha = fast_exp2(m_run - mx);
+      m_run = mx;
+      l_run *= alpha;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) acc[m] *= alpha;
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sv[tt][j] = fast_exp2(sv[tt][j] - m_run);
+        ps += sv[tt][j];
+      }
+    l_run += ps;
+    // P^T as the B operand: k slot j of lane group g4 is token 4 g4 + j (j < 4)
+    // or 16 + 4 g4 + j - 4.
+    uint4 pbits;
+    pbits.x = pack_bf16x2(sv[0][0], sv[0][1]);
+    pbits.y = pack_bf16x2(sv[0][2], sv[0][3]);
+    pbits.z = pack_bf16x2(sv[1][0], sv[1][1]);
+    pbits.w = pack_bf16x2(sv[1][2], sv[1][3]);
+    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pbits);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const s16x4_t lo = vt4<ROWB>(vt, l16, 4 * g4, 16 * m);
+      const s16x4_t hi = vt4<ROWB>(vt, l16, 16 + 4 * g4, 16 * m);
+      const s16x8_t va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pb, acc[m], 0, 0, 0);
+    }
+  };
+
+  // Steps: the next step's chunks are loaded into registers while the current
+  // one is computed from LDS; two barriers per step hand the LDS tiles over.
+  if (nsteps > 0) {
+    load_ids(0);
+    load_step(0);
+    for (int st = 0; st < nsteps; ++st) {
+      __syncthreads();  // every wave is done with the previous step's tiles
+      stage_step(st);
+      __syncthreads();
+      if (st + 1 < nsteps) {
+        if (((st + 1) * PPS & 63) == 0) load_ids((st + 1) * PPS);
+        load_step(st + 1);
+      }
+      compute_step(st);
+    }
+  }
+  const bool bad = b.bad || ids_bad;
+
+  // The four lanes of a row each hold a share of its running sum.
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  const int64_t orow = qrow * p.num_heads + head;
+  if (b.nparts == 1) {
+    uint16_t* o = static_cast<uint16_t*>(p.out) + orow * D;
+    const float inv = l_run == 0.f ? 0.f : p.v_scale / l_run;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = bad ? __builtin_nanf("") : acc[m][j] * inv;
+      uint2 w;
+      w.x = f32_to_bf16_bits(v[0]) | (uint32_t)f32_to_bf16_bits(v[1]) << 16;
+      w.y = f32_to_bf16_bits(v[2]) | (uint32_t)f32_to_bf16_bits(v[3]) << 16;
+      *reinterpret_cast<uint2*>(o + 16 * m + 4 * g4) = w;
+    }
+  } else {
+    const int64_t slot = orow * p.max_parts + part;
+    float* a = p.ws_acc + slot * D;
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+      *reinterpret_cast<float4*>(a + 16 * m + 4 * g4) = make_float4(acc[m][0], acc[m][1], acc[m][2], acc[m][3]);
+    if (g4 == 0) {
+      p.ws_ml[slot * 2] = bad ? 0.f : m_run;
+      p.ws_ml[slot * 2 + 1] = bad ? __builtin_nanf("") : l_run;
+    }
+  }
+}
+
+// Merges the partitions of row blocks that were cut: one workgroup per (row
+// block, kv head), four threads per row, each owning D / 4 output columns.
+template <int D, int G>
+__global__ __launch_bounds__(kWaves * 64) void multi_query_reduce_kernel(MultiQueryParams p) {
+  constexpr int DQ = D / 4;
+  int x = blockIdx.x;
+  const int kvh = x % p.num_kv_heads;
+  x /= p.num_kv_heads;
+  const int rbi = x % p.max_row_blocks;
+  const int s = x / p.max_row_blocks;
+  const MqBlock b = mq_block<G>(p, s, rbi);
+  if (b.skip || b.nparts <= 1) return;  // written by the partition kernel
+  const int r = b.rb * kRowsPerBlock + threadIdx.x / 4;
+  if (r >= b.rows) return;
+  const int64_t orow = (int64_t)(b.t0 + r / G) * p.num_heads + kvh * G + r % G;
+  const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + orow * p.max_parts;
+  float mm = -FLT_MAX;
+  for (int q = 0; q < b.nparts; ++q) mm = fmaxf(mm, ml[q].x);
+  float ll = 0.f;
+  float aa[DQ];
+#pragma unroll
+  for (int e = 0; e < DQ; ++e) aa[e] = 0.f;
+  const int d0 = (threadIdx.x % 4) * DQ;
+  for (int q = 0; q < b.nparts; ++q) {
+    const float2 v = ml[q];
+    const float w = fast_exp2(v.x - mm);
+    ll += v.y * w;
+    const float4* a = reinterpret_cast<const float4*>(p.ws_acc + (orow * p.max_parts + q) * D + d0);
+#pragma unroll
+    for (int e = 0; e < DQ / 4; ++e) {
+      const float4 f = a[e];
+      aa[4 * e] += f.x * w;
+      aa[4 * e + 1] += f.y * w;
+      aa[4 * e + 2] += f.z * w;
+      aa[4 * e + 3] += f.w * w;
+    }
+  }
+  const float inv = ll == 0.f ? 0.f : p.v_scale / ll;
+  uint16_t* o = static_cast<uint16_t*>(p.out) + orow * D + d0;
+#pragma unroll
+  for (int e = 0; e < DQ / 2; ++e) {
+    const uint32_t w = f32_to_bf16_bits(aa[2 * e] * inv) | (uint32_t)f32_to_bf16_bits(aa[2 * e + 1] * inv) << 16;
+    *reinterpret_cast<uint32_t*>(o + 2 * e) = w;
+  }
+}
+
+template <typename TC, int D, int BS, int G>
+hipError_t launch_t(const MultiQueryLaunch& a, const MultiQueryParams& p) {
+  const int64_t blocks = (int64_t)a.num_seqs * a.max_row_blocks * a.num_kv_heads;
+  hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G>), dim3((unsigned)(blocks * a.max_parts)),
+                     dim3(kWaves * 64), 0, a.stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.max_parts <= 1) return e;
+  hipLaunchKernelGGL((multi_query_reduce_kernel<D, G>), dim3((unsigned)blocks), dim3(kWaves * 64), 0,
+                     a.stream, p);
+  return hipGetLastError();
+}
+
+template <typename TC, int D, int BS>
+hipError_t by_group(const MultiQueryLaunch& a, const MultiQueryParams& p) {
+  switch (a.num_heads / a.num_kv_heads) {
+    case 1: return launch_t<TC, D, BS, 1>(a, p);
+    case 2: return launch_t<TC, D, BS, 2>(a, p);
+    case 4: return launch_t<TC, D, BS, 4>(a, p);
+    case 8: return launch_t<TC, D, BS, 8>(a, p);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename TC, int D>
+hipError_t by_block(const MultiQueryLaunch& a, const MultiQueryParams& p) {
+  return a.block_size == 16 ? by_group<TC, D, 16>(a, p) : by_group<TC, D, 32>(a, p);
+}
+
+template <typename TC>
+hipError_t by_dim(const MultiQueryLaunch& a, const MultiQueryParams& p) {
+  return a.head_dim == 64 ? by_block<TC, 64>(a, p) : by_block<TC, 128>(a, p);
+}
+
+}  // namespace
+
+int default_multi_query_partition_tokens(int block_size) {
+  const int t = 1024;
+  return t - t % block_size;
+}
+
+hipError_t launch_multi_query(const MultiQueryLaunch& a) {
+  MultiQueryParams p;
+  p.out = a.out;
+  p.q = a.q;
+  p.k_cache = a.k_cache;
+  p.v_cache = a.v_cache;
+  p.block_tables = a.block_tables;
+  p.context_lens = a.context_lens;
+  p.query_start = a.query_start;
+  p.ws_ml = a.ws_ml;
+  p.ws_acc = a.ws_acc;
+  p.block_stride = (int64_t)a.num_kv_heads * a.block_size * a.head_dim;
+  p.max_blocks_per_seq = a.max_blocks_per_seq;
+  p.num_seqs = a.num_seqs;
+  p.num_query_tokens = a.num_query_tokens;
+  p.num_heads = a.num_heads;
+  p.num_kv_heads = a.num_kv_heads;
+  p.num_blocks = a.num_blocks;
+  p.max_context_len = a.max_context_len;
+  p.max_query_len = a.max_query_len;
+  p.partition_tokens = a.partition_tokens;
+  p.max_parts = a.max_parts;
+  p.max_row_blocks = a.max_row_blocks;
+  const bool fp8 = a.cache_dtype == kDtypeFp8;
+  p.scale_log2e = a.scale * kLog2e * (fp8 ? a.k_scale : 1.f);
+  p.v_scale = fp8 ? a.v_scale : 1.f;
+  return fp8 ? by_dim<uint8_t>(a, p) : by_dim<uint16_t>(a, p);
+}
+
+}  // namespace pa

@@ -25,6 +25,15 @@ type with round-to-nearest-even):
               beams whose last block already holds tokens find that block
               shared (reference count 2) and must copy it before the write.
 
+``specdec70b``  speculative verification: 32 sequences with contexts uniform
+              in [1024, 8192], each ending with 6 new tokens (the accepted
+              token and 5 drafts) whose K/V the step stores; 64 query heads
+              over 8 KV heads, head_dim 128, block_size 16.
+``chunked13b``  a chunked-prefill batch of 3136 query tokens: a 2048-token
+              chunk after 2048 cached tokens, a first chunk of 1024 tokens, and
+              64 decoding sequences (contexts uniform in [128, 4096]); 40
+              heads, head_dim 128, block_size 16 (LLaMA-13B shape).
+
 ``<name>_fp8``  the same workload with an fp8 (OCP E4M3) KV cache: history
               entries are N(0, 1) draws divided by the cache scale 1/64 and
               cast to float8_e4m3fn (torch's cast, clamped to +-448), new
@@ -50,6 +59,7 @@ import torch
 from .block_pool import BlockPool, BlockTable, padded_rows
 
 __all__ = ["Spec", "Plan", "Inputs", "SPECS", "uniform_plan", "beam_plan", "prefix_plan",
+           "multi_query_plan",
            "make_plan", "build_inputs", "make_inputs", "to_host_numpy",
            "TORCH_DTYPE"]
 
@@ -81,8 +91,10 @@ SPECS: Dict[str, Spec] = {
     "llama13b": Spec("llama13b", 40, 40, 128, 16, "bf16", seed=103),
     "gqa70b": Spec("gqa70b", 64, 8, 128, 32, "bf16", seed=104, q_std=0.5),
     "beam": Spec("beam", 32, 8, 128, 16, "bf16", seed=105),
+    "specdec70b": Spec("specdec70b", 64, 8, 128, 16, "bf16", seed=106),
+    "chunked13b": Spec("chunked13b", 40, 40, 128, 16, "bf16", seed=107),
 }
-for _base in ("llama7b", "llama13b", "gqa70b", "beam"):
+for _base in ("llama7b", "llama13b", "gqa70b", "beam", "specdec70b", "chunked13b"):
     _b = SPECS[_base]
     SPECS[_base + "_fp8"] = Spec(_base + "_fp8", _b.num_heads, _b.num_kv_heads, _b.head_dim,
                                  _b.block_size, _b.dtype, seed=_b.seed + 1000, q_std=_b.q_std,
@@ -102,6 +114,14 @@ class Plan:
     slot_mapping: np.ndarray            # int64 [T]
     block_pairs: np.ndarray             # int64 [P, 2] (src, dst)
     shared_prefix_blocks: List[int] = field(default_factory=list)
+    query_lens: Optional[np.ndarray] = None  # int32 [S] new queries per sequence (None: decode)
+
+    @property
+    def query_start(self) -> Optional[np.ndarray]:
+        """int32 [S + 1] CSR offsets of each sequence's query rows (multi-query plans)."""
+        if self.query_lens is None:
+            return None
+        return np.concatenate([[0], np.cumsum(self.query_lens)]).astype(np.int32)
 
     @property
     def num_seqs(self) -> int:
@@ -240,6 +260,35 @@ def prefix_plan(groups: Sequence[Tuple[int, Sequence[int]]], block_size: int,
                 np.zeros((0, 2), dtype=np.int64), shared)
 
 
+def multi_query_plan(context_lens: Sequence[int], query_lens: Sequence[int], block_size: int,
+                     gen: torch.Generator, pool_factor: float = 1.1) -> Plan:
+    """Independent sequences each ending with ``query_lens[s]`` new tokens.
+
+    The new tokens (positions ctx - q_len .. ctx - 1 of each sequence) are
+    stored by the step, sequence by sequence in position order, which is also
+    the order of the query rows.
+    """
+    ctx = [int(c) for c in context_lens]
+    qlens = [int(n) for n in query_lens]
+    if len(ctx) != len(qlens) or any(n > c or n < 0 for c, n in zip(ctx, qlens)):
+        raise ValueError("every sequence needs 0 <= query_len <= context_len")
+    per_seq = [BlockTable.blocks_for(c, block_size) for c in ctx]
+    nb = _pool_size(sum(per_seq), pool_factor, None)
+    pool = BlockPool(nb, torch.randperm(nb, generator=gen).tolist())
+    tables = []
+    for c in ctx:
+        t = BlockTable(pool, block_size)
+        t.ensure_tokens(c)
+        tables.append(t)
+    rows = np.asarray(padded_rows([t.blocks for t in tables], max(1, max(per_seq, default=1))),
+                      dtype=np.int32)
+    seqs = [s for s in range(len(ctx)) for _ in range(qlens[s])]
+    slots = [tables[s].slot_of(pos) for s in range(len(ctx)) for pos in range(ctx[s] - qlens[s], ctx[s])]
+    return Plan(block_size, nb, np.asarray(ctx, dtype=np.int32), rows, rows.copy(),
+                np.asarray(seqs, dtype=np.int64), np.asarray(slots, dtype=np.int64),
+                np.zeros((0, 2), dtype=np.int64), query_lens=np.asarray(qlens, dtype=np.int32))
+
+
 def make_plan(name: str, gen: torch.Generator, **kw) -> Plan:
     """The integer plan of a named workload (keyword overrides shrink it)."""
     spec = SPECS[name]
@@ -261,6 +310,18 @@ def make_plan(name: str, gen: torch.Generator, **kw) -> Plan:
         s = kw.pop("num_seqs", 16)
         c = kw.pop("context_len", 32768)
         plan = uniform_plan([c] * s, bs, gen, new_tokens=kw.pop("new_tokens", False))
+    elif name == "specdec70b":
+        s = kw.pop("num_seqs", 32)
+        lo, hi = kw.pop("ctx_range", (1024, 8192))
+        ctx = torch.randint(lo, hi + 1, (s,), generator=gen).tolist()
+        plan = multi_query_plan(ctx, [kw.pop("query_len", 6)] * s, bs, gen)
+    elif name == "chunked13b":
+        chunks = kw.pop("chunks", [(2048, 2048), (0, 1024)])  # (history, new tokens)
+        s = kw.pop("num_decodes", 64)
+        lo, hi = kw.pop("ctx_range", (128, 4096))
+        dec = torch.randint(lo, hi + 1, (s,), generator=gen).tolist()
+        plan = multi_query_plan([h + n for h, n in chunks] + dec, [n for _, n in chunks] + [1] * s,
+                                bs, gen)
     elif name == "beam":
         plan = beam_plan(kw.pop("groups", 32), kw.pop("beams", 4),
                          kw.pop("prefix_len", 1024), kw.pop("tail_lo", 1),
@@ -288,6 +349,7 @@ class Inputs:
     scale: float
     k_scale: float = 1.0         # fp8 caches only
     v_scale: float = 1.0
+    query_start: Optional[torch.Tensor] = None  # int32 [S + 1] (multi-query plans)
 
     @property
     def max_context_len(self) -> int:
@@ -323,11 +385,11 @@ def _history_mask(plan: Plan) -> np.ndarray:
     """[NB, BS] True where a slot holds a token before the step's writes."""
     mask = np.zeros((plan.num_blocks, plan.block_size), dtype=bool)
     written = {}
-    for s, slot in zip(plan.new_token_seqs.tolist(), plan.slot_mapping.tolist()):
-        written[s] = slot
+    for s in plan.new_token_seqs.tolist():
+        written[s] = written.get(s, 0) + 1
     bs = plan.block_size
     for s in range(plan.num_seqs):
-        n = int(plan.context_lens[s]) - (1 if s in written else 0)
+        n = int(plan.context_lens[s]) - written.get(s, 0)
         row = plan.history_tables[s]
         full, rest = divmod(n, bs)
         for j in range(full):
@@ -337,12 +399,15 @@ def _history_mask(plan: Plan) -> np.ndarray:
     return mask
 
 
-def build_inputs(spec: Spec, plan: Plan, device="cpu", poison: bool = True,
-                 num_seqs_q: Optional[int] = None) -> Inputs:
-    """Random tensors for ``plan`` on ``device`` (seeded by the spec)."""
+def build_inputs(spec: Spec, plan: Plan, device="cpu", poison: bool = True) -> Inputs:
+    """Random tensors for ``plan`` on ``device`` (seeded by the spec).
+
+    q has one row per sequence, or one per new query token for a multi-query
+    plan.
+    """
     gen = torch.Generator(device=device)
     gen.manual_seed(spec.seed * 7919 + 17)
-    s = plan.num_seqs
+    s = plan.num_seqs if plan.query_lens is None else int(plan.query_lens.sum())
     nb, bs = plan.num_blocks, plan.block_size
     hkv, d = spec.num_kv_heads, spec.head_dim
     q = _randn((s, spec.num_heads, d), gen, device, spec.q_std, spec.dtype)
@@ -373,6 +438,8 @@ def build_inputs(spec: Spec, plan: Plan, device="cpu", poison: bool = True,
         scale=float(np.float32(1.0 / math.sqrt(d))),
         k_scale=spec.kv_scale if spec.cache_dtype == "fp8" else 1.0,
         v_scale=spec.kv_scale if spec.cache_dtype == "fp8" else 1.0,
+        query_start=None if plan.query_lens is None
+        else torch.from_numpy(plan.query_start).to(device),
     )
 
 

@@ -75,6 +75,39 @@ def gpu_step_shared(x: Inputs, t: dict | None = None, partition_tokens: int = 0,
     return out, t
 
 
+def gpu_mq_step(x: Inputs, t: dict | None = None, partition_tokens: int = 0, max_query_len=None,
+                out: torch.Tensor | None = None):
+    """reshape_and_cache of the new tokens -> multi-query attention; returns (out, t)."""
+    t = on_device(x) if t is None else t
+    if "query_start" not in t:
+        t["query_start"] = x.query_start.to("cuda").clone()
+    if t["slot_mapping"].shape[0]:
+        binding.pa_reshape_and_cache(t["key"], t["value"], t["k_cache"], t["v_cache"],
+                                     t["slot_mapping"], k_scale=x.k_scale, v_scale=x.v_scale)
+    out = torch.empty_like(t["q"]) if out is None else out
+    mq = int(x.plan.query_lens.max()) if max_query_len is None else max_query_len
+    binding.pa_multi_query(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                           t["context_lens"], t["query_start"], x.scale, x.max_context_len, mq,
+                           partition_tokens=partition_tokens, k_scale=x.k_scale, v_scale=x.v_scale)
+    torch.cuda.synchronize()
+    return out, t
+
+
+def oracle_mq_step(x: Inputs):
+    """The same step on host copies with the oracle; returns (out64, kc, vc)."""
+    kc = to_host_numpy(x.k_cache).copy()
+    vc = to_host_numpy(x.v_cache).copy()
+    if x.slot_mapping.shape[0]:
+        op.reshape_and_cache(to_host_numpy(x.key), to_host_numpy(x.value), kc, vc,
+                             to_host_numpy(x.slot_mapping), src_dtype=x.spec.dtype,
+                             k_scale=x.k_scale, v_scale=x.v_scale)
+    out = op.multi_query(to_host_numpy(x.q), kc, vc, to_host_numpy(x.block_tables),
+                         to_host_numpy(x.context_lens), to_host_numpy(x.query_start), x.scale,
+                         x.spec.dtype, cache_dtype=x.spec.cache_dtype, k_scale=x.k_scale,
+                         v_scale=x.v_scale)
+    return out, kc, vc
+
+
 def oracle_step(x: Inputs, copy: bool = True, reshape: bool = True):
     """The same step on host copies with the oracle; returns (out64, kc, vc)."""
     kc = to_host_numpy(x.k_cache).copy()
@@ -155,3 +188,39 @@ def sampled_reference(x: Inputs, seqs):
     out = op.decode(q, kc, vc, tables, plan.context_lens[list(seqs)], x.scale, x.spec.dtype,
                     cache_dtype=x.spec.cache_dtype, k_scale=x.k_scale, v_scale=x.v_scale)
     return out, ids, kc, vc
+
+
+def sampled_mq_reference(x: Inputs, seqs):
+    """Oracle multi-query output for the rows of sequences ``seqs``.
+
+    Their blocks are copied to the host (before any GPU work), renumbered, the
+    sequences' new tokens stored by the oracle, and the oracle run on them.
+    Returns {s: out64 [q_len, H, D]}.
+    """
+    plan = x.plan
+    bs = plan.block_size
+    qs = plan.query_start
+    res = {}
+    for s in seqs:
+        nb = -(-int(plan.context_lens[s]) // bs)
+        ids = [int(b) for b in plan.block_tables[s][:nb]]
+        remap = {b: i for i, b in enumerate(ids)}
+        idx = torch.tensor(ids, dtype=torch.long, device=x.k_cache.device)
+        kc = to_host_numpy(x.k_cache.index_select(0, idx)).copy()
+        vc = to_host_numpy(x.v_cache.index_select(0, idx)).copy()
+        tok = [i for i, t in enumerate(plan.new_token_seqs.tolist()) if t == s]
+        if tok:
+            slots = [remap[int(plan.slot_mapping[i]) // bs] * bs + int(plan.slot_mapping[i]) % bs
+                     for i in tok]
+            ti = torch.tensor(tok, dtype=torch.long, device=x.key.device)
+            op.reshape_and_cache(to_host_numpy(x.key.index_select(0, ti)),
+                                 to_host_numpy(x.value.index_select(0, ti)), kc, vc,
+                                 np.array(slots, dtype=np.int64), src_dtype=x.spec.dtype,
+                                 k_scale=x.k_scale, v_scale=x.v_scale)
+        q = to_host_numpy(x.q[int(qs[s]):int(qs[s + 1])])
+        res[s] = op.multi_query(q, kc, vc, np.arange(nb, dtype=np.int32)[None],
+                                plan.context_lens[s:s + 1],
+                                np.array([0, int(qs[s + 1] - qs[s])], dtype=np.int32), x.scale,
+                                x.spec.dtype, cache_dtype=x.spec.cache_dtype, k_scale=x.k_scale,
+                                v_scale=x.v_scale)
+    return res

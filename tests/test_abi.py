@@ -188,6 +188,66 @@ def test_shared_prefix_workspace_size():
     assert ws(3, 8, 2, 64, 16, 2000, 4, 2001, BF16, BF16, 512) == bad
 
 
+def multi_query(**kw):
+    a = dict(out=P, q=P, k=P, v=P, bt=P, mb=8, ctx=P, qs=P, S=2, T=12, mq=6, H=8, Hkv=2, D=128,
+             BS=16, NB=32, maxctx=100, scale=0.1, dtype=BF16, cdtype=None, ks=0.5, vs=0.5, pt=0,
+             ws=None, wsb=0)
+    a.update(kw)
+    cdtype = a["dtype"] if a["cdtype"] is None else a["cdtype"]
+    return LIB.pa_multi_query(a["out"], a["q"], a["k"], a["v"], a["bt"], a["mb"], a["ctx"], a["qs"],
+                              a["S"], a["T"], a["mq"], a["H"], a["Hkv"], a["D"], a["BS"], a["NB"],
+                              a["maxctx"], a["scale"], a["dtype"], cdtype, a["ks"], a["vs"], a["pt"],
+                              a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=F32), UNSUP),            # bf16 matrix-core tiles only
+    (dict(dtype=BF16, cdtype=F32), UNSUP),
+    (dict(dtype=FP8), DTYPE),
+    (dict(cdtype=9), DTYPE),
+    (dict(H=6, Hkv=4), SHAPE),
+    (dict(H=32, Hkv=2), UNSUP),          # group of 16
+    (dict(D=96), UNSUP),
+    (dict(BS=8), UNSUP),
+    (dict(T=-1), SHAPE),
+    (dict(S=-1), SHAPE),
+    (dict(mq=-1), SHAPE),
+    (dict(maxctx=-1), SHAPE),
+    (dict(mb=6), SHAPE),                 # 6 * 16 < 100
+    (dict(NB=0), SHAPE),
+    (dict(pt=24), SHAPE),
+    (dict(pt=-16), SHAPE),
+    (dict(q=None), NULL),
+    (dict(qs=None), NULL),
+    (dict(ctx=None), NULL),
+    (dict(out=MIS), ALIGN),
+    (dict(qs=P + 2), ALIGN),
+    (dict(maxctx=3000, mb=200, pt=1024), WS),
+    (dict(maxctx=3000, mb=200, pt=1024, ws=P, wsb=16), WS),
+    (dict(maxctx=3000, mb=200, pt=1024, ws=MIS, wsb=1 << 30), ALIGN),
+    (dict(cdtype=FP8, ks=0.0), VALUE),
+    (dict(cdtype=FP8, vs=float("nan")), VALUE),
+    (dict(S=0), OK),                     # nothing to launch
+    (dict(T=0, q=None, out=None), OK),
+    (dict(mq=0), OK),
+])
+def test_multi_query_validation(kw, code):
+    assert multi_query(**kw) == code
+
+
+def test_multi_query_workspace_size():
+    ws = LIB.pa_multi_query_workspace_size
+    assert ws(12, 8, 2, 128, 16, 1024, BF16, BF16, 0) == 0   # one partition of 1024 (default)
+    rows = 12 * 8 * 3
+    ml = (rows * 2 * 4 + 255) // 256 * 256
+    assert ws(12, 8, 2, 128, 16, 2100, BF16, BF16, 1024) == ml + rows * 128 * 4
+    assert ws(12, 8, 2, 128, 16, 2100, BF16, FP8, 0) == ml + rows * 128 * 4
+    assert ws(12, 8, 2, 64, 32, 100, BF16, BF16, 32 * 300) == 0   # any multiple of the block
+    bad = ctypes.c_size_t(-1).value
+    assert ws(12, 8, 2, 128, 16, 2100, F32, F32, 0) == bad
+    assert ws(12, 8, 3, 128, 16, 2100, BF16, BF16, 0) == bad
+
+
 def reshape(**kw):
     a = dict(key=P, value=P, k=P, v=P, slots=P, T=4, NB=8, Hkv=2, BS=16, D=64, dtype=F32,
              cdtype=None, ks=1.0, vs=1.0)

@@ -152,6 +152,27 @@ def test_prefix_groups_of_forked_tables():
     assert lead == [0, 0, 0, 0] and nblk[0] == 3   # the partial fourth block is not shared
 
 
+def test_multi_query_plan_stores_the_last_positions():
+    plan = wl.multi_query_plan([5, 40, 33, 0], [3, 40, 1, 0], 16, torch.Generator().manual_seed(2))
+    assert len(set(plan.slot_mapping.tolist())) == len(plan.slot_mapping)
+    assert plan.query_start.tolist() == [0, 3, 43, 44, 44]
+    assert plan.new_token_seqs.tolist() == [0] * 3 + [1] * 40 + [2]
+    pos = [p for c, n in ((5, 3), (40, 40), (33, 1)) for p in range(c - n, c)]
+    seqs = plan.new_token_seqs.tolist()
+    for i, (s, p) in enumerate(zip(seqs, pos)):
+        assert plan.slot_mapping[i] == plan.block_tables[s][p // 16] * 16 + p % 16
+    # The slots about to be written hold no history (poisoned in correctness runs).
+    x = wl.build_inputs(wl.Spec("mq", 4, 2, 64, 16, "bf16", seed=1), plan)
+    kc = x.k_cache.float()
+    for slot in plan.slot_mapping.tolist():
+        assert torch.isnan(kc[slot // 16, :, slot % 16]).all()
+    b = plan.block_tables[0][0]
+    assert torch.isfinite(kc[b, :, :2]).all()   # positions 0, 1 of sequence 0 are history
+    assert x.q.shape[0] == 44 and x.query_start.tolist() == plan.query_start.tolist()
+    with pytest.raises(ValueError):
+        wl.multi_query_plan([4], [5], 16, torch.Generator())
+
+
 def test_llama13b_small_plan_shuffles_tokens():
     plan = wl.make_plan("llama13b", torch.Generator().manual_seed(3), num_seqs=8, context_len=64)
     _check_plan(plan)
