@@ -44,7 +44,14 @@ DESCRIPTION = {
             "U[1,256], H=32, Hkv=8, D=128, BS=16, bf16; copy_blocks + reshape_and_cache + pa_decode",
     "tiny": "tiny paged decode: 4 seqs ctx {1,17,33,100}, H=Hkv=4, D=64, BS=16, fp32",
 }
-for _n in ("llama7b", "llama13b", "gqa70b", "beam"):
+DESCRIPTION.update({
+    "specdec70b": "speculative verification, 70B GQA shape: 32 seqs, ctx U[1024,8192] ending with 6 new "
+                  "tokens each, H=64, Hkv=8, D=128, BS=16, bf16; reshape_and_cache + pa_multi_query",
+    "chunked13b": "chunked-prefill batch, LLaMA-13B shape: a 2048-token chunk after 2048 cached tokens, "
+                  "a first 1024-token chunk and 64 decodes (ctx U[128,4096]), 3136 query tokens, "
+                  "H=Hkv=40, D=128, BS=16, bf16; reshape_and_cache + pa_multi_query",
+})
+for _n in ("llama7b", "llama13b", "gqa70b", "beam", "specdec70b", "chunked13b"):
     DESCRIPTION[_n + "_fp8"] = DESCRIPTION[_n].replace(", bf16", ", bf16 query / fp8 E4M3 KV cache")
 # "+prefix": the same step with pa_decode_shared_prefix (each shared page read
 # once per chunk of sequences) in place of pa_decode.
@@ -59,7 +66,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama13b", choices=sorted(DESCRIPTION))
     ap.add_argument("--partition-tokens", type=int, default=0)
-    ap.add_argument("--others", default="llama7b,gqa70b,beam,beam+prefix,llama13b_fp8,gqa70b_fp8",
+    ap.add_argument("--others", default="llama7b,gqa70b,beam,beam+prefix,llama13b_fp8,gqa70b_fp8,"
+                                        "specdec70b,chunked13b",
                     help="comma list of extra workloads to report ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -70,14 +78,30 @@ def parse():
 
 
 def algorithmic_bytes(plan, spec) -> int:
-    """K and V read once + q read + out written + block-table entries + context lengths."""
+    """K and V read once + q read + out written + block-table entries + context lengths
+    (+ query offsets for a multi-query plan, whose q/out have one row per query token)."""
     e = 4 if spec.dtype == "f32" else 2
     ekv = {"f32": 4, "bf16": 2, "fp8": 1}[spec.cache_dtype]
     ctx = [int(c) for c in plan.context_lens]
     kv = sum(2 * spec.num_kv_heads * c * spec.head_dim * ekv for c in ctx)
-    qo = 2 * len(ctx) * spec.num_heads * spec.head_dim * e
+    rows = len(ctx) if plan.query_lens is None else int(plan.query_lens.sum())
+    qo = 2 * rows * spec.num_heads * spec.head_dim * e
+    if plan.query_lens is not None:
+        qo += 4 * (len(ctx) + 1)
     table = 4 * sum(-(-c // plan.block_size) for c in ctx)
     return kv + qo + table + 4 * len(ctx)
+
+
+def attention_flops(plan, spec) -> int:
+    """Multiply-adds x 2 of the causal attention: each query row at position p
+    and each query head does 2*D for q.k and 2*D for p*V over p + 1 tokens."""
+    total = 0
+    qlens = plan.query_lens if plan.query_lens is not None else [1] * plan.num_seqs
+    for c, n in zip(plan.context_lens.tolist(), list(qlens)):
+        c, n = int(c), int(n)
+        seen = sum(c - n + i + 1 for i in range(n))
+        total += 4 * spec.head_dim * spec.num_heads * seen
+    return total
 
 
 def decode_kernel_name(label, spec) -> str:
@@ -85,6 +109,8 @@ def decode_kernel_name(label, spec) -> str:
     group = spec.num_heads // spec.num_kv_heads
     cache = {"f32": "f32", "bf16": "bf16", "fp8": "fp8 E4M3"}[spec.cache_dtype]
     shape = f"D={spec.head_dim}, BS={spec.block_size}, G={group}"
+    if spec.recipe in ("specdec70b", "chunked13b") or label.startswith(("specdec70b", "chunked13b")):
+        return f"pa_multi_query: multi_query_kernel<{cache} cache, {shape}>"
     if label.endswith("+prefix"):
         return f"pa_decode_shared_prefix: decode_partition_mfma_kernel<{cache} cache, {shape}, shared>"
     if spec.dtype == "bf16" and group >= 2:
@@ -160,6 +186,13 @@ def run_workload(label, steps, warmup, partition_tokens, flush=False):
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if flush else None
     stream = torch.cuda.current_stream()
+    multi_query = plan.query_lens is not None
+    if multi_query:
+        ws_bytes = binding.pa_multi_query_workspace_size(
+            plan.num_seqs, int(plan.query_lens.sum()), spec.num_heads, spec.num_kv_heads, spec.head_dim,
+            plan.block_size, plan.max_context_len, code, partition_tokens, ccode)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+        max_q = int(plan.query_lens.max())
     has_pairs = plan.block_pairs.shape[0] > 0
     has_tokens = plan.slot_mapping.shape[0] > 0
     # Workloads whose sequences share physical blocks (beam prefixes) ask for
@@ -178,7 +211,12 @@ def run_workload(label, steps, warmup, partition_tokens, flush=False):
                                          stream=stream, k_scale=x.k_scale, v_scale=x.v_scale)
         if ev is not None:
             ev[0].record(stream)
-        if shared_prefix:
+        if multi_query:
+            binding.pa_multi_query(out, x.q, x.k_cache, x.v_cache, x.block_tables, x.context_lens,
+                                   x.query_start, x.scale, plan.max_context_len, max_q,
+                                   partition_tokens=partition_tokens, workspace=ws, stream=stream,
+                                   k_scale=x.k_scale, v_scale=x.v_scale)
+        elif shared_prefix:
             binding.pa_decode_shared_prefix(out, x.q, x.k_cache, x.v_cache, x.block_tables,
                                             x.context_lens, lead, nblk, x.scale,
                                             plan.max_context_len, bounds[0], bounds[1],
@@ -227,6 +265,8 @@ def run_workload(label, steps, warmup, partition_tokens, flush=False):
     med_decode_ms = decode_ms[len(decode_ms) // 2]
     nbytes = algorithmic_bytes(plan, spec)
     ubytes = unique_bytes(plan, spec)
+    flops = attention_flops(plan, spec)
+    ntok = int(plan.query_lens.sum()) if multi_query else plan.num_seqs
     res = {
         "workload": label,
         "description": DESCRIPTION[label],
@@ -234,10 +274,12 @@ def run_workload(label, steps, warmup, partition_tokens, flush=False):
         "total_context_tokens": int(sum(int(c) for c in plan.context_lens)),
         "ms_per_step": ms_per_step,
         "wall_ms_per_step": wall * 1e3 / steps if wall else None,
-        "tokens_per_s": plan.num_seqs / (ms_per_step / 1e3),
+        "tokens_per_s": ntok / (ms_per_step / 1e3),
         "decode_avg_us": avg_decode_ms * 1e3,
         "decode_median_us": med_decode_ms * 1e3,
-        "decode_tokens_per_s": plan.num_seqs / (avg_decode_ms / 1e3),
+        "decode_tokens_per_s": ntok / (avg_decode_ms / 1e3),
+        "attention_flops": flops,
+        "attention_TFLOPs": flops / (avg_decode_ms / 1e3) / 1e12,
         "decode_algorithmic_bytes": nbytes,
         "decode_GBps": nbytes / (avg_decode_ms / 1e3) / 1e9,
         "decode_frac_of_peak": nbytes / (avg_decode_ms / 1e3) / 1e9 / PEAK_GBPS,
@@ -247,7 +289,9 @@ def run_workload(label, steps, warmup, partition_tokens, flush=False):
         "new_tokens": int(plan.slot_mapping.shape[0]),
         "partition_tokens": partition_tokens,
         "shared_pages_flag": shared and not shared_prefix,
-        "decode_entry_point": "pa_decode_shared_prefix" if shared_prefix else "pa_decode",
+        "decode_entry_point": ("pa_multi_query" if multi_query else
+                               "pa_decode_shared_prefix" if shared_prefix else "pa_decode"),
+        "query_tokens": ntok,
         "cache": "cold (MALL flushed between steps)" if flush else "warm",
         "kv_cache_dtype": spec.cache_dtype,
     }

@@ -265,12 +265,15 @@ int pa_decode_shared_prefix(void* out, const void* q,
 
 /*
  * pa_multi_query_workspace_size -- bytes of device workspace pa_multi_query
- * needs (0 when no context can need more than one partition); (size_t)-1 for
- * arguments it would reject.  partition_tokens: 0 = default (1024 tokens).
+ * needs: the partitions of cut contexts and the list of work items it builds
+ * on the device each call (0 when there are no sequences or no query tokens);
+ * (size_t)-1 for arguments it would reject.  partition_tokens: 0 = default
+ * (1024 tokens).
  */
-size_t pa_multi_query_workspace_size(int num_query_tokens, int num_heads, int num_kv_heads,
-                                     int head_dim, int block_size, int max_context_len,
-                                     int dtype, int cache_dtype, int partition_tokens);
+size_t pa_multi_query_workspace_size(int num_seqs, int num_query_tokens, int num_heads,
+                                     int num_kv_heads, int head_dim, int block_size,
+                                     int max_context_len, int dtype, int cache_dtype,
+                                     int partition_tokens);
 
 /*
  * pa_multi_query -- causal attention of several new query tokens per sequence
@@ -293,11 +296,13 @@ size_t pa_multi_query_workspace_size(int num_query_tokens, int num_heads, int nu
  * dtype must be PA_BF16 (cache PA_BF16 or PA_FP8_E4M3); G = num_heads /
  * num_kv_heads in {1, 2, 4, 8}; head_dim 64 or 128; block_size 16 or 32.
  * max_query_len >= every n and max_context_len >= every L (host bounds that size
- * the grid).  partition_tokens (0 = default 1024; else a positive multiple of
- * block_size): a sequence whose n * G rows fit in 64 has its context cut into
- * partitions of this many tokens, merged by a second kernel; longer chunks are
- * not cut.  workspace: at least pa_multi_query_workspace_size(...) bytes,
- * 16-byte aligned (NULL allowed when that is 0).
+ * the grid).  A sequence with n == 1 is a decode step and runs through
+ * pa_decode's kernels (with their partitioning).  partition_tokens (0 = default
+ * 1024; else a positive multiple of block_size): a sequence with n > 1 whose
+ * n * G rows fit in 64 has its context cut into partitions of this many
+ * tokens, merged by a second kernel; longer chunks are not cut.
+ * workspace: at least pa_multi_query_workspace_size(...) bytes, 16-byte
+ * aligned.
  * Preconditions (device values): query_start ranges inside [0, num_query_tokens],
  * non-decreasing, n <= max_query_len (a sequence breaking these is skipped and
  * its rows are left unwritten; overlapping ranges give unspecified rows);

@@ -61,7 +61,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                             [_c_float, _c_int, _c_int, _c_float, _c_float, _c_int,
                                              _c_int, _vp, _c_size, _vp])
     lib.pa_decode_shared_prefix.restype = _c_int
-    lib.pa_multi_query_workspace_size.argtypes = [_c_int] * 9
+    lib.pa_multi_query_workspace_size.argtypes = [_c_int] * 10
     lib.pa_multi_query_workspace_size.restype = _c_size
     lib.pa_multi_query.argtypes = ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp] + [_c_int] * 9 +
                                    [_c_float, _c_int, _c_int, _c_float, _c_float, _c_int, _vp,
@@ -284,12 +284,13 @@ def pa_decode_shared_prefix(out: torch.Tensor, q: torch.Tensor, k_cache: torch.T
     _check(st, "pa_decode_shared_prefix")
 
 
-def pa_multi_query_workspace_size(num_query_tokens: int, num_heads: int, num_kv_heads: int,
-                                  head_dim: int, block_size: int, max_context_len: int, dtype: int,
-                                  partition_tokens: int = 0, cache_dtype: Optional[int] = None) -> int:
+def pa_multi_query_workspace_size(num_seqs: int, num_query_tokens: int, num_heads: int,
+                                  num_kv_heads: int, head_dim: int, block_size: int,
+                                  max_context_len: int, dtype: int, partition_tokens: int = 0,
+                                  cache_dtype: Optional[int] = None) -> int:
     cache_dtype = dtype if cache_dtype is None else cache_dtype
-    n = LIB.pa_multi_query_workspace_size(num_query_tokens, num_heads, num_kv_heads, head_dim,
-                                          block_size, max_context_len, dtype, cache_dtype,
+    n = LIB.pa_multi_query_workspace_size(num_seqs, num_query_tokens, num_heads, num_kv_heads,
+                                          head_dim, block_size, max_context_len, dtype, cache_dtype,
                                           partition_tokens)
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("pa_multi_query_workspace_size: arguments rejected by the library")
@@ -323,8 +324,9 @@ def pa_multi_query(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_
     _need(query_start.shape == (s + 1,), "query_start must be [S + 1]")
     code = _dtype_code(q)
     ccode = _dtype_code(k_cache)
-    need = pa_multi_query_workspace_size(t, h, hkv, d, bs, max_context_len, code, partition_tokens,
-                                         ccode) if h > 0 and hkv > 0 and h % hkv == 0 else 0
+    need = pa_multi_query_workspace_size(s, t, h, hkv, d, bs, max_context_len, code,
+                                         partition_tokens, ccode) \
+        if h > 0 and hkv > 0 and h % hkv == 0 else 0
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

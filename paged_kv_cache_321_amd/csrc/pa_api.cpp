@@ -258,6 +258,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.max_parts = z.max_parts;
   a.ws_ml = z.total ? reinterpret_cast<float*>(ws) : nullptr;
   a.ws_acc = z.total ? reinterpret_cast<float*>(ws + z.ml_bytes) : nullptr;
+  a.query_start = nullptr;
+  a.num_query_rows = 0;
   a.prefix_leader = shared_prefix ? prefix_leader : nullptr;
   a.prefix_blocks = shared_prefix ? prefix_blocks : nullptr;
   a.max_prefix_blocks = max_prefix_blocks;
@@ -268,23 +270,39 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   return pa::launch_decode(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+// Workspace of pa_multi_query: the decode kernels' partitions (sequences
+// with one query, indexed by sequence) followed by the multi-query
+// partitions (indexed by query row).
 struct MultiQuerySizes {
   int status;
   int partition_tokens;
   int max_parts;
   size_t ml_bytes;
   size_t total;
+  int decode_partition_tokens;
+  int decode_grid_parts;
+  size_t decode_ml_bytes;
+  size_t decode_bytes;  // offset of the multi-query area, 256-byte aligned
+  size_t parts_bytes;   // multi-query partition area (0 without cuts)
+  int64_t work_capacity;
+  size_t work_bytes;    // work list and its count, after the partition area
 };
 
-MultiQuerySizes multi_query_sizes(int num_query_tokens, int num_heads, int num_kv_heads, int head_dim,
-                                  int block_size, int max_context_len, int dtype, int cache_dtype,
-                                  int partition_tokens) {
-  MultiQuerySizes z{PA_OK, 0, 1, 0, 0};
+size_t partition_area(uint64_t rows, int head_dim, size_t* ml_bytes) {
+  const uint64_t ml = (rows * 2 * sizeof(float) + 255) / 256 * 256;
+  *ml_bytes = (size_t)ml;
+  return (size_t)((ml + rows * (uint64_t)head_dim * sizeof(float) + 255) / 256 * 256);
+}
+
+MultiQuerySizes multi_query_sizes(int num_seqs, int num_query_tokens, int num_heads, int num_kv_heads,
+                                  int head_dim, int block_size, int max_context_len, int dtype,
+                                  int cache_dtype, int partition_tokens) {
+  MultiQuerySizes z{PA_OK, 0, 1, 0, 0, 0, 1, 0, 0, 0, 0, 0};
   if (!value_dtype(dtype) || !cache_dtype_ok(cache_dtype)) { z.status = PA_ERR_DTYPE; return z; }
   // The tiles run on bf16 matrix cores: a bf16 query over a bf16 or fp8 cache.
   if (dtype != PA_BF16 || cache_dtype == PA_F32) { z.status = PA_ERR_UNSUPPORTED; return z; }
-  if (num_query_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-      max_context_len < 0 || num_heads % num_kv_heads != 0) {
+  if (num_seqs < 0 || num_query_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || max_context_len < 0 || num_heads % num_kv_heads != 0) {
     z.status = PA_ERR_SHAPE;
     return z;
   }
@@ -298,12 +316,22 @@ MultiQuerySizes multi_query_sizes(int num_query_tokens, int num_heads, int num_k
   if (pt < 0 || pt % block_size != 0) { z.status = PA_ERR_SHAPE; return z; }
   z.partition_tokens = pt;
   z.max_parts = max_context_len <= pt ? 1 : (max_context_len + pt - 1) / pt;
-  if (z.max_parts > 1) {
-    const uint64_t rows = (uint64_t)num_query_tokens * (uint64_t)num_heads * (uint64_t)z.max_parts;
-    const uint64_t ml = (rows * 2 * sizeof(float) + 255) / 256 * 256;
-    z.ml_bytes = (size_t)ml;
-    z.total = (size_t)(ml + rows * (uint64_t)head_dim * sizeof(float));
-  }
+  const int dpt = pa::default_partition_tokens(dtype, cache_dtype, head_dim, block_size,
+                                               num_heads / num_kv_heads, false, 0);
+  z.decode_partition_tokens = dpt;
+  z.decode_grid_parts = max_context_len <= dpt ? 1 : (max_context_len + dpt - 1) / dpt;
+  if (z.decode_grid_parts > 1)
+    z.decode_bytes = partition_area((uint64_t)num_seqs * num_heads * z.decode_grid_parts, head_dim,
+                                    &z.decode_ml_bytes);
+  if (z.max_parts > 1)
+    z.parts_bytes = partition_area((uint64_t)num_query_tokens * num_heads * z.max_parts, head_dim, &z.ml_bytes);
+  // Work items: every row block (at most T * G / 64 plus one partial block per
+  // sequence) or, for a sequence of one block, its partitions.
+  const int rpb = pa::multi_query_rows_per_block();
+  z.work_capacity = ((int64_t)num_query_tokens * (num_heads / num_kv_heads) + rpb - 1) / rpb +
+                    (int64_t)num_seqs * (z.max_parts + 1);
+  z.work_bytes = (size_t)((z.work_capacity * 8 + 4 + 255) / 256 * 256);
+  z.total = num_seqs > 0 && num_query_tokens > 0 ? z.decode_bytes + z.parts_bytes + z.work_bytes : 0;
   return z;
 }
 
@@ -311,12 +339,13 @@ MultiQuerySizes multi_query_sizes(int num_query_tokens, int num_heads, int num_k
 
 extern "C" {
 
-size_t pa_multi_query_workspace_size(int num_query_tokens, int num_heads, int num_kv_heads,
-                                     int head_dim, int block_size, int max_context_len, int dtype,
-                                     int cache_dtype, int partition_tokens) {
-  const MultiQuerySizes z = multi_query_sizes(num_query_tokens, num_heads, num_kv_heads, head_dim,
-                                              block_size, max_context_len, dtype, cache_dtype,
-                                              partition_tokens);
+size_t pa_multi_query_workspace_size(int num_seqs, int num_query_tokens, int num_heads,
+                                     int num_kv_heads, int head_dim, int block_size,
+                                     int max_context_len, int dtype, int cache_dtype,
+                                     int partition_tokens) {
+  const MultiQuerySizes z = multi_query_sizes(num_seqs, num_query_tokens, num_heads, num_kv_heads,
+                                              head_dim, block_size, max_context_len, dtype,
+                                              cache_dtype, partition_tokens);
   return z.status == PA_OK ? z.total : (size_t)-1;
 }
 
@@ -327,23 +356,26 @@ int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_
                    int max_context_len, float scale, int dtype, int cache_dtype, float k_scale,
                    float v_scale, int partition_tokens, void* workspace, size_t workspace_bytes,
                    void* stream) {
-  const MultiQuerySizes z = multi_query_sizes(num_query_tokens, num_heads, num_kv_heads, head_dim,
-                                              block_size, max_context_len, dtype, cache_dtype,
-                                              partition_tokens);
+  const MultiQuerySizes z = multi_query_sizes(num_seqs, num_query_tokens, num_heads, num_kv_heads,
+                                              head_dim, block_size, max_context_len, dtype,
+                                              cache_dtype, partition_tokens);
   if (z.status != PA_OK) return z.status;
   const bool fp8 = cache_dtype == PA_FP8_E4M3;
   if (fp8 && (!good_scale(k_scale) || !good_scale(v_scale))) return PA_ERR_VALUE;
-  if (num_seqs < 0 || max_query_len < 0 || num_blocks <= 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  if (max_query_len < 0 || num_blocks <= 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * block_size < max_context_len) return PA_ERR_SHAPE;
   const int group = num_heads / num_kv_heads;
-  const int64_t row_blocks = ((int64_t)max_query_len * group + 63) / 64;
+  const int rpb = pa::multi_query_rows_per_block();
+  const int64_t row_blocks = ((int64_t)max_query_len * group + rpb - 1) / rpb;
   if (num_seqs == 0 || num_query_tokens == 0 || row_blocks == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
     return PA_ERR_NULL;
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4))
     return PA_ERR_ALIGN;
-  if ((int64_t)num_seqs * row_blocks * num_kv_heads * z.max_parts > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+  if (z.work_capacity * num_kv_heads > 0x7fffffffLL || row_blocks > 0xffff || z.max_parts > 0xffff ||
+      num_seqs > kMaxGridYZ || num_kv_heads > kMaxGridYZ || num_heads > kMaxGridYZ)
+    return PA_ERR_UNSUPPORTED;
   if (z.total > 0) {
     if (!workspace || workspace_bytes < z.total) return PA_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
@@ -374,9 +406,52 @@ int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_
   a.partition_tokens = z.partition_tokens;
   a.max_parts = z.max_parts;
   a.max_row_blocks = (int)row_blocks;
-  a.ws_ml = z.total ? reinterpret_cast<float*>(ws) : nullptr;
-  a.ws_acc = z.total ? reinterpret_cast<float*>(ws + z.ml_bytes) : nullptr;
+  a.ws_ml = z.max_parts > 1 ? reinterpret_cast<float*>(ws + z.decode_bytes) : nullptr;
+  a.ws_acc = z.max_parts > 1 ? reinterpret_cast<float*>(ws + z.decode_bytes + z.ml_bytes) : nullptr;
+  a.work = ws + z.decode_bytes + z.parts_bytes;
+  a.work_count = reinterpret_cast<int*>(ws + z.decode_bytes + z.parts_bytes + z.work_capacity * 8);
+  a.work_capacity = (int)z.work_capacity;
   a.stream = static_cast<hipStream_t>(stream);
+  // Sequences with a single new query are decode steps: the decode kernels
+  // serve them (q / out row query_start[s]); the multi-query kernel skips them.
+  pa::DecodeLaunch d;
+  d.out = out;
+  d.q = q;
+  d.k_cache = k_cache;
+  d.v_cache = v_cache;
+  d.block_tables = block_tables;
+  d.max_blocks_per_seq = max_blocks_per_seq;
+  d.context_lens = context_lens;
+  d.seq_order = nullptr;
+  d.num_seqs = num_seqs;
+  d.num_heads = num_heads;
+  d.num_kv_heads = num_kv_heads;
+  d.head_dim = head_dim;
+  d.block_size = block_size;
+  d.num_blocks = num_blocks;
+  d.max_context_len = max_context_len;
+  d.scale = scale;
+  d.dtype = dtype;
+  d.cache_dtype = cache_dtype;
+  d.k_scale = a.k_scale;
+  d.v_scale = a.v_scale;
+  d.partition_tokens = z.decode_partition_tokens;
+  d.shared_pages = false;
+  d.grid_parts = z.decode_grid_parts;
+  d.max_parts = z.decode_grid_parts;
+  d.ws_ml = z.decode_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  d.ws_acc = z.decode_bytes ? reinterpret_cast<float*>(ws + z.decode_ml_bytes) : nullptr;
+  d.query_start = query_start;
+  d.num_query_rows = num_query_tokens;
+  d.prefix_leader = nullptr;
+  d.prefix_blocks = nullptr;
+  d.max_prefix_blocks = 0;
+  d.max_tail_len = 0;
+  d.prefix_parts = 0;
+  d.tail_parts = 1;
+  d.stream = a.stream;
+  if (pa::launch_decode(d) != hipSuccess) return PA_ERR_LAUNCH;
+  if (max_query_len < 2) return PA_OK;  // no sequence has more than one query
   return pa::launch_multi_query(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -24,8 +24,10 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams p) {
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   const int lane = threadIdx.x;
+  const int row = query_row(p, s);
+  if (row < 0) return;  // not a decode row of this call
   const SeqSplit sp = split_context(p, p.context_lens[s], prefix_chunk(p, s).blocks);
-  if (sp.bad) return;  // written as NaN by the partition kernel
+  if (sp.bad || sp.ctx < p.min_context) return;  // written as NaN by the partition kernel
   const int nparts = sp.nprefix + sp.ntail;
   if (nparts <= 1) return;  // written by the partition kernel
   const int64_t base = ((int64_t)s * p.num_heads + h) * p.max_parts;
@@ -62,7 +64,7 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams p) {
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const float o = (ll == 0.f) ? 0.f : aa[e] * p.v_scale / ll;
-    Elem<T>::store(static_cast<T*>(p.out) + ((int64_t)s * p.num_heads + h) * D + lane + 64 * e, o);
+    Elem<T>::store(static_cast<T*>(p.out) + ((int64_t)row * p.num_heads + h) * D + lane + 64 * e, o);
   }
 }
 
@@ -132,6 +134,9 @@ hipError_t launch_decode(const DecodeLaunch& a) {
   p.max_tail_len = a.max_tail_len;
   p.prefix_parts = a.prefix_parts;
   p.tail_parts = a.tail_parts;
+  p.query_start = a.query_start;
+  p.num_query_rows = a.num_query_rows;
+  p.min_context = a.query_start != nullptr ? 1 : 0;
   // Shared-prefix decode always runs on the matrix cores (one 16-column tile
   // holds the query heads of up to 16 / G sequences) and always merges.
   const bool shared = a.prefix_leader != nullptr;

@@ -82,6 +82,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   const int g4 = lane >> 4;
 
   int s;                 // sequence whose table row supplies the page ids
+  int qrow = 0;          // its q / out row (decode)
   PartitionRange r;
   int my_id;
   bool bad;              // this wave's pages cannot be read: its columns become NaN
@@ -93,6 +94,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     slot = part;
     s = sequence_of(p, blockIdx.z);
     if (s < 0) return;  // uniform over the workgroup
+    qrow = query_row(p, s);
+    if (qrow < 0) return;
     r = partition_range(p, s, part, wave, BS);
     if (part >= r.nparts) return;  // uniform over the workgroup
     bool ids_bad;
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   // columns.
   bf16x8_t qb[NC];
   {
-    const int q_seq = col_seq >= 0 ? col_seq : s;
+    const int q_seq = SHARED ? (col_seq >= 0 ? col_seq : s) : qrow;
     const int q_head = kvh * G + (SHARED ? l16 % G : (l16 < G ? l16 : 0));
     const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)q_seq * p.num_heads + q_head) * D;
 #pragma unroll
@@ -373,7 +376,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   }
   if constexpr (!SHARED) {
     __syncthreads();
-    merge_waves_and_store<uint16_t, D, G>(p, sm_acc, sm_m, sm_l, s, kvh, part, r.nparts);
+    merge_waves_and_store<uint16_t, D, G>(p, sm_acc, sm_m, sm_l, s, kvh, part, r.nparts, qrow);
   } else {
     int* sm_seq = reinterpret_cast<int*>(sm_l + kWaves * NCOL);
     int* sm_total = sm_seq + 16;

@@ -56,6 +56,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partition_valu_kernel(Deco
   const int kvh = blockIdx.y;
   const int s = sequence_of(p, blockIdx.z);
   if (s < 0) return;  // uniform over the workgroup
+  const int qrow = query_row(p, s);
+  if (qrow < 0) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -79,7 +81,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partition_valu_kernel(Deco
   float qf[G][VEC];
   uint32_t qw[G][4];
   {
-    const TQ* qb = static_cast<const TQ*>(p.q) + ((int64_t)s * p.num_heads + (int64_t)kvh * G) * D + col * VEC;
+    const TQ* qb = static_cast<const TQ*>(p.q) + ((int64_t)qrow * p.num_heads + (int64_t)kvh * G) * D + col * VEC;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partition_valu_kernel(Deco
     }
   }
   __syncthreads();
-  merge_waves_and_store<TQ, D, G>(p, sm_acc, sm_m, sm_l, s, kvh, part, r.nparts);
+  merge_waves_and_store<TQ, D, G>(p, sm_acc, sm_m, sm_l, s, kvh, part, r.nparts, qrow);
 }
 
 template <typename TQ, typename TC, int D, int BS, int G>

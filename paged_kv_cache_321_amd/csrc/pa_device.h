@@ -176,6 +176,12 @@ struct DecodeParams {
   int max_tail_len;              // caller's bound on context_len - shared prefix
   int prefix_parts;              // grid rows per sequence for prefix partitions
   int tail_parts;                // grid rows per sequence for the rest
+  // Decode rows of a multi-query batch (query_start == null otherwise): only
+  // sequences with exactly one new query are served, at q / out row
+  // query_start[s], and a context must hold that query (min_context = 1).
+  const int32_t* query_start;
+  int num_query_rows;
+  int min_context;
 };
 
 // Sequence served by grid slot z (the caller may reorder dispatch); -1 if the
@@ -186,6 +192,15 @@ __device__ __forceinline__ int sequence_of(const DecodeParams& p, int z) {
   return (s >= 0 && s < p.num_seqs) ? s : -1;
 }
 
+// q / out row of sequence s: s itself, or in a multi-query batch its one
+// query's row (-1: the sequence has another number of queries, or an invalid
+// range, and is not served by the decode kernels).
+__device__ __forceinline__ int query_row(const DecodeParams& p, int s) {
+  if (p.query_start == nullptr) return s;
+  const int t0 = p.query_start[s];
+  const int t1 = p.query_start[s + 1];
+  return (t1 - t0 == 1 && t0 >= 0 && t1 <= p.num_query_rows) ? t0 : -1;
+}
 __device__ __forceinline__ int parts_for(int ctx, int partition_tokens) {
   return ctx <= partition_tokens ? 1 : (ctx + partition_tokens - 1) / partition_tokens;
 }
@@ -202,7 +217,7 @@ __device__ __forceinline__ PartitionRange partition_range(const DecodeParams& p,
                                                           int wave, int block_size) {
   PartitionRange r;
   r.ctx = p.context_lens[s];
-  r.ctx_bad = r.ctx < 0 || r.ctx > p.max_context_len;
+  r.ctx_bad = r.ctx < p.min_context || r.ctx > p.max_context_len;
   r.nparts = r.ctx_bad ? 1 : parts_for(r.ctx, p.partition_tokens);
   r.tok0 = part * p.partition_tokens;
   r.tok1 = r.ctx_bad ? r.tok0 : min(r.ctx, r.tok0 + p.partition_tokens);
@@ -303,12 +318,13 @@ __device__ __forceinline__ PartitionRange token_range(int ctx, int nparts, int t
 }
 // Epilogue: the kWaves partial states of each query head of the group sit in
 // LDS (sm_acc [kWaves][G][D], sm_m / sm_l [kWaves][G]); merge them with the
-// log-sum-exp rule and write either the final row (single partition) or the
-// partition's (max, sum, accumulator) triple to the workspace.
+// log-sum-exp rule and write either the final row (single partition, at q /
+// out row `row`) or the partition's (max, sum, accumulator) triple to the
+// workspace (indexed by sequence).
 template <typename T, int D, int G>
 __device__ __forceinline__ void merge_waves_and_store(const DecodeParams& p, const float* sm_acc,
                                                       const float* sm_m, const float* sm_l, int s,
-                                                      int kvh, int part, int nparts) {
+                                                      int kvh, int part, int nparts, int row) {
   for (int idx = threadIdx.x; idx < G * D; idx += kWaves * 64) {
     const int g = idx / D;
     const int d = idx % D;
@@ -325,7 +341,7 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeParams& p, con
     const int64_t sh = (int64_t)s * p.num_heads + (int64_t)kvh * G + g;
     if (nparts == 1) {
       const float o = (ll == 0.f) ? 0.f : aa * p.v_scale / ll;
-      Elem<T>::store(static_cast<T*>(p.out) + sh * D + d, o);
+      Elem<T>::store(static_cast<T*>(p.out) + ((int64_t)row * p.num_heads + (int64_t)kvh * G + g) * D + d, o);
     } else {
       const int64_t slot = sh * p.max_parts + part;
       p.ws_acc[slot * D + d] = aa;

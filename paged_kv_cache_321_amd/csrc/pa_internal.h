@@ -46,6 +46,10 @@ struct DecodeLaunch {
   // leader and shared leading blocks (read at leaders).
   const int32_t* prefix_leader;
   const int32_t* prefix_blocks;
+  // Decode rows of a multi-query batch (null otherwise): sequences with one
+  // new query, at q / out row query_start[s].
+  const int32_t* query_start;
+  int num_query_rows;
   int max_prefix_blocks;  // caller's bounds: prefix_blocks at leaders, context - prefix
   int max_tail_len;
   int prefix_parts;       // ceil(max_prefix_blocks * block_size / partition_tokens)
@@ -91,9 +95,12 @@ struct MultiQueryLaunch {
   float k_scale, v_scale;
   int partition_tokens;  // resolved, > 0
   int max_parts;         // ceil(max_context_len / partition_tokens), >= 1
-  int max_row_blocks;    // ceil(max_query_len * G / 64)
+  int max_row_blocks;    // ceil(max_query_len * G / rows per block)
   float* ws_ml;          // [T, H, max_parts, 2]; null if max_parts == 1
   float* ws_acc;         // [T, H, max_parts, D]; null if max_parts == 1
+  void* work;            // work list: work_capacity 8-byte items (workspace)
+  int* work_count;       // (workspace)
+  int work_capacity;     // bound on the work items: the grid size per kv head
   hipStream_t stream;
 };
 
@@ -103,6 +110,7 @@ int default_partition_tokens(int dtype, int cache_dtype, int head_dim, int block
 
 hipError_t launch_decode(const DecodeLaunch& a);
 int default_multi_query_partition_tokens(int block_size);
+int multi_query_rows_per_block();
 hipError_t launch_multi_query(const MultiQueryLaunch& a);
 hipError_t launch_reshape_and_cache(const ReshapeLaunch& a);
 hipError_t launch_copy_blocks(const CopyLaunch& a);

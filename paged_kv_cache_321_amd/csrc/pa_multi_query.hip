@@ -19,6 +19,10 @@
 // into LDS.  Each column keeps its own running max and sum, moved lazily (only
 // when a score exceeds the reference by more than 2^8).
 //
+// Sequences with exactly one new query are decode steps; the entry point runs
+// them through the decode kernels (which stream their pages at the HBM rate)
+// and this kernel skips them.
+//
 // Partitions.  A sequence whose rows fit one block (speculative verification,
 // short chunks) would give too few workgroups on a long context, so its
 // context is cut into partitions of partition_tokens tokens whose
@@ -33,8 +37,9 @@
 namespace pa {
 namespace {
 
-constexpr int kRowsPerBlock = kWaves * 16;
-constexpr int kStepTokens = 32;
+constexpr int kMqWaves = 4;                   // waves per workgroup, 16 rows each
+constexpr int kRowsPerBlock = kMqWaves * 16;
+constexpr int kStepTokens = 32;               // tokens staged in LDS per step
 
 struct MultiQueryParams {
   void* out;
@@ -56,8 +61,11 @@ struct MultiQueryParams {
   int max_context_len;
   int max_query_len;
   int partition_tokens;
-  int max_parts;       // partition slots per row (grid and workspace)
-  int max_row_blocks;  // row blocks per sequence in the grid
+  int max_parts;       // partition slots per row (workspace)
+  int max_row_blocks;  // row blocks of the longest allowed chunk
+  int2* work;          // work items (sequence, row block index << 16 | partition)
+  int* work_count;     // number of work items
+  int work_capacity;   // items the list holds (the grid's bound)
   float scale_log2e;   // softmax scale * log2(e), times k_scale for fp8 caches
   float v_scale;       // multiplies the output (1 unless the cache holds fp8 codes)
 };
@@ -71,6 +79,7 @@ struct MqBlock {
   int rb;       // row block: rows rb * 64 .. rb * 64 + 63
   int kv_end;   // tokens seen by the block's last query
   int nparts;   // context partitions
+  int nrb;      // row blocks of the sequence
   bool skip;    // no such block, or an invalid query range: nothing is written
   bool bad;     // bad context length: the block's rows are written as NaN
 };
@@ -84,8 +93,13 @@ __device__ __forceinline__ MqBlock mq_block(const MultiQueryParams& p, int s, in
   if (b.skip) return b;
   b.t0 = t0;
   b.qlen = t1 - t0;
+  if (b.qlen == 1) {  // a decode row: served by the decode kernels
+    b.skip = true;
+    return b;
+  }
   b.rows = b.qlen * G;
   const int nrb = (b.rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  b.nrb = nrb;
   if (rbi >= nrb) {
     b.skip = true;
     return b;
@@ -103,7 +117,7 @@ __device__ __forceinline__ MqBlock mq_block(const MultiQueryParams& p, int s, in
 }
 
 template <typename TC, int D, int BS, int G>
-__global__ __launch_bounds__(kWaves * 64) void multi_query_kernel(MultiQueryParams p) {
+__global__ __launch_bounds__(kMqWaves * 64) void multi_query_kernel(MultiQueryParams p) {
   constexpr bool kFp8 = sizeof(TC) == 1;
   constexpr int PPS = kStepTokens / BS;      // pages per step
   constexpr int NC = D / 32;                 // 32-wide steps of the QK contraction
@@ -112,19 +126,20 @@ __global__ __launch_bounds__(kWaves * 64) void multi_query_kernel(MultiQueryPara
   constexpr int NCH = ROWB / 16;             // 16-byte bf16 chunks per row
   constexpr int CCH = D * (int)sizeof(TC) / 16;  // 16-byte cache chunks per row
   constexpr int CHUNKS = kStepTokens * CCH;  // 16-byte cache chunks per step (K or V)
-  constexpr int PER_T = (CHUNKS + kWaves * 64 - 1) / (kWaves * 64);
+  constexpr int PER_T = (CHUNKS + kMqWaves * 64 - 1) / (kMqWaves * 64);
+  constexpr int NTT = kStepTokens / 16;      // 16-token tiles per step
   constexpr int TILEB = kStepTokens * ROWB;  // bytes of one step's K (or V) in LDS
-  static_assert(kStepTokens % BS == 0 && NCH >= 8, "tile shape");
+  static_assert(kStepTokens % BS == 0 && kStepTokens % 32 == 0 && NCH >= 8, "tile shape");
 
-  int x = blockIdx.x;
-  const int kvh = x % p.num_kv_heads;
-  x /= p.num_kv_heads;
-  const int part = x % p.max_parts;
-  x /= p.max_parts;
-  const int rbi = x % p.max_row_blocks;
-  const int s = x / p.max_row_blocks;
+  const int kvh = blockIdx.x % p.num_kv_heads;
+  const int item = blockIdx.x / p.num_kv_heads;
+  if (item >= *p.work_count) return;  // uniform over the workgroup
+  const int2 w = p.work[item];
+  const int s = w.x;
+  const int rbi = w.y >> 16;
+  const int part = w.y & 0xffff;
   const MqBlock b = mq_block<G>(p, s, rbi);
-  if (b.skip || part >= b.nparts) return;  // uniform over the workgroup
+  if (b.skip || part >= b.nparts) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -132,7 +147,10 @@ __global__ __launch_bounds__(kWaves * 64) void multi_query_kernel(MultiQueryPara
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
 
-  // This lane's row: column l16 of the wave's tile.
+  // This lane's row: column l16 of the wave's tile.  A wave whose 16 rows
+  // all lie past the block's rows (a short chunk, a decoding sequence) only
+  // helps stage the tiles.
+  const bool wave_rows = b.rb * kRowsPerBlock + wave * 16 < b.rows;
   const int r = b.rb * kRowsPerBlock + wave * 16 + l16;
   const bool row_ok = r < b.rows;
   const int qi = row_ok ? r / G : 0;
@@ -194,7 +212,7 @@ __global__ __launch_bounds__(kWaves * 64) void multi_query_kernel(MultiQueryPara
   auto load_step = [&](int st) {
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
-      const int c = tid + u * kWaves * 64;
+      const int c = tid + u * kMqWaves * 64;
       const int tok = c / CCH;
       const int pg = st * PPS + tok / BS;  // page of the partition
       kreg[u] = vreg[u] = make_uint4(0u, 0u, 0u, 0u);
@@ -213,7 +231,7 @@ __global__ __launch_bounds__(kWaves * 64) void multi_query_kernel(MultiQueryPara
   auto stage_step = [&](int st) {
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
-      const int c = tid + u * kWaves * 64;
+      const int c = tid + u * kMqWaves * 64;
       if (c >= CHUNKS) continue;
       const int tok = c / CCH;
       const int ch = c % CCH;
@@ -236,10 +254,10 @@ __global__ __launch_bounds__(kWaves * 64) void multi_query_kernel(MultiQueryPara
 
   auto compute_step = [&](int st) {
     const int t_base = tok0 + st * kStepTokens;
-    // S^T for the step's two 16-token tiles.
-    f32x4_t sc[2];
+    // S^T for the step's 16-token tiles.
+    f32x4_t sc[NTT];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < NTT; ++tt) {
       sc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       const int tok = 16 * tt + l16;
 #pragma unroll
@@ -249,10 +267,10 @@ __global__ __launch_bounds__(kWaves * 64) void multi_query_kernel(MultiQueryPara
       }
     }
     // Causal mask and online softmax: lane holds tokens 16 tt + 4 g4 + j.
-    float sv[2][4];
+    float sv[NTT][4];
     float mx = m_run;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int t = t_base + 16 * tt + 4 * g4 + j;
@@ -271,27 +289,30 @@ __global__ __launch_bounds__(kWaves * 64) void multi_query_kernel(MultiQueryPara
     }
     float ps = 0.f;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         sv[tt][j] = fast_exp2(sv[tt][j] - m_run);
         ps += sv[tt][j];
       }
     l_run += ps;
-    // P^T as the B operand: k slot j of lane group g4 is token 4 g4 + j (j < 4)
-    // or 16 + 4 g4 + j - 4.
-    uint4 pbits;
-    pbits.x = pack_bf16x2(sv[0][0], sv[0][1]);
-    pbits.y = pack_bf16x2(sv[0][2], sv[0][3]);
-    pbits.z = pack_bf16x2(sv[1][0], sv[1][1]);
-    pbits.w = pack_bf16x2(sv[1][2], sv[1][3]);
-    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pbits);
+    // P^T as the B operand, two 16-token tiles per product: k slot j of lane
+    // group g4 is token 32 h + 4 g4 + j (j < 4) or 32 h + 16 + 4 g4 + j - 4.
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const s16x4_t lo = vt4<ROWB>(vt, l16, 4 * g4, 16 * m);
-      const s16x4_t hi = vt4<ROWB>(vt, l16, 16 + 4 * g4, 16 * m);
-      const s16x8_t va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pb, acc[m], 0, 0, 0);
+    for (int h = 0; h < NTT / 2; ++h) {
+      uint4 pbits;
+      pbits.x = pack_bf16x2(sv[2 * h][0], sv[2 * h][1]);
+      pbits.y = pack_bf16x2(sv[2 * h][2], sv[2 * h][3]);
+      pbits.z = pack_bf16x2(sv[2 * h + 1][0], sv[2 * h + 1][1]);
+      pbits.w = pack_bf16x2(sv[2 * h + 1][2], sv[2 * h + 1][3]);
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pbits);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const s16x4_t lo = vt4<ROWB>(vt, l16, 32 * h + 4 * g4, 16 * m);
+        const s16x4_t hi = vt4<ROWB>(vt, l16, 32 * h + 16 + 4 * g4, 16 * m);
+        const s16x8_t va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pb, acc[m], 0, 0, 0);
+      }
     }
   };
 
@@ -308,7 +329,7 @@ __global__ __launch_bounds__(kWaves * 64) void multi_query_kernel(MultiQueryPara
         if (((st + 1) * PPS & 63) == 0) load_ids((st + 1) * PPS);
         load_step(st + 1);
       }
-      compute_step(st);
+      if (wave_rows) compute_step(st);
     }
   }
   const bool bad = b.bad || ids_bad;
@@ -344,17 +365,57 @@ __global__ __launch_bounds__(kWaves * 64) void multi_query_kernel(MultiQueryPara
   }
 }
 
-// Merges the partitions of row blocks that were cut: one workgroup per (row
-// block, kv head), four threads per row, each owning D / 4 output columns.
+// The work list: one item per (sequence, row block) of every sequence with
+// more than one query, or per (sequence, partition) for a sequence whose rows
+// fit one block; ordered by sequence, a sequence's last row blocks (the ones
+// that see the most tokens) first.  One workgroup scans the sequences in
+// chunks of its size; items past the list's capacity (only possible when
+// query ranges overlap) are dropped.
+template <int G>
+__global__ __launch_bounds__(256) void multi_query_schedule_kernel(MultiQueryParams p) {
+  __shared__ int sums[256];
+  __shared__ int base;
+  const int tid = threadIdx.x;
+  if (tid == 0) base = 0;
+  __syncthreads();
+  for (int s0 = 0; s0 < p.num_seqs; s0 += 256) {
+    const int s = s0 + tid;
+    int n = 0;
+    bool single = false;
+    if (s < p.num_seqs) {
+      const MqBlock b = mq_block<G>(p, s, 0);
+      if (!b.skip) {
+        single = b.nrb == 1;
+        n = single ? b.nparts : b.nrb;
+      }
+    }
+    sums[tid] = n;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {  // inclusive scan
+      const int v = tid >= off ? sums[tid - off] : 0;
+      __syncthreads();
+      sums[tid] += v;
+      __syncthreads();
+    }
+    const int start = base + sums[tid] - n;
+    for (int i = 0; i < n && start + i < p.work_capacity; ++i)
+      p.work[start + i] = make_int2(s, single ? i : i << 16);
+    __syncthreads();  // every thread has read base
+    if (tid == 255) base += sums[255];
+    __syncthreads();
+  }
+  if (tid == 0) *p.work_count = min(base, p.work_capacity);
+}
+
+// Merges the partitions of sequences whose rows fit one block (the only ones
+// cut): one workgroup per (sequence, kv head), four threads per row, each
+// owning D / 4 output columns.
 template <int D, int G>
-__global__ __launch_bounds__(kWaves * 64) void multi_query_reduce_kernel(MultiQueryParams p) {
+__global__ __launch_bounds__(kMqWaves * 64) void multi_query_reduce_kernel(MultiQueryParams p) {
   constexpr int DQ = D / 4;
-  int x = blockIdx.x;
-  const int kvh = x % p.num_kv_heads;
-  x /= p.num_kv_heads;
-  const int rbi = x % p.max_row_blocks;
-  const int s = x / p.max_row_blocks;
-  const MqBlock b = mq_block<G>(p, s, rbi);
+  const int kvh = blockIdx.x % p.num_kv_heads;
+  const int s = blockIdx.x / p.num_kv_heads;
+  const MqBlock b = mq_block<G>(p, s, 0);
   if (b.skip || b.nparts <= 1) return;  // written by the partition kernel
   const int r = b.rb * kRowsPerBlock + threadIdx.x / 4;
   if (r >= b.rows) return;
@@ -392,13 +453,16 @@ __global__ __launch_bounds__(kWaves * 64) void multi_query_reduce_kernel(MultiQu
 
 template <typename TC, int D, int BS, int G>
 hipError_t launch_t(const MultiQueryLaunch& a, const MultiQueryParams& p) {
-  const int64_t blocks = (int64_t)a.num_seqs * a.max_row_blocks * a.num_kv_heads;
-  hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G>), dim3((unsigned)(blocks * a.max_parts)),
-                     dim3(kWaves * 64), 0, a.stream, p);
+  hipLaunchKernelGGL((multi_query_schedule_kernel<G>), dim3(1), dim3(256), 0, a.stream, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.max_parts <= 1) return e;
-  hipLaunchKernelGGL((multi_query_reduce_kernel<D, G>), dim3((unsigned)blocks), dim3(kWaves * 64), 0,
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G>),
+                     dim3((unsigned)((int64_t)a.work_capacity * a.num_kv_heads)), dim3(kMqWaves * 64), 0,
                      a.stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.max_parts <= 1) return e;
+  hipLaunchKernelGGL((multi_query_reduce_kernel<D, G>), dim3((unsigned)a.num_seqs * a.num_kv_heads),
+                     dim3(kMqWaves * 64), 0, a.stream, p);
   return hipGetLastError();
 }
 
@@ -424,6 +488,8 @@ hipError_t by_dim(const MultiQueryLaunch& a, const MultiQueryParams& p) {
 }
 
 }  // namespace
+
+int multi_query_rows_per_block() { return kRowsPerBlock; }
 
 int default_multi_query_partition_tokens(int block_size) {
   const int t = 1024;
@@ -453,6 +519,9 @@ hipError_t launch_multi_query(const MultiQueryLaunch& a) {
   p.partition_tokens = a.partition_tokens;
   p.max_parts = a.max_parts;
   p.max_row_blocks = a.max_row_blocks;
+  p.work = reinterpret_cast<int2*>(a.work);
+  p.work_count = a.work_count;
+  p.work_capacity = a.work_capacity;
   const bool fp8 = a.cache_dtype == kDtypeFp8;
   p.scale_log2e = a.scale * kLog2e * (fp8 ? a.k_scale : 1.f);
   p.v_scale = fp8 ? a.v_scale : 1.f;

@@ -222,9 +222,9 @@ def multi_query(**kw):
     (dict(ctx=None), NULL),
     (dict(out=MIS), ALIGN),
     (dict(qs=P + 2), ALIGN),
-    (dict(maxctx=3000, mb=200, pt=1024), WS),
-    (dict(maxctx=3000, mb=200, pt=1024, ws=P, wsb=16), WS),
-    (dict(maxctx=3000, mb=200, pt=1024, ws=MIS, wsb=1 << 30), ALIGN),
+    (dict(ws=None), WS),                 # the work list always lives in the workspace
+    (dict(ws=P, wsb=16), WS),
+    (dict(ws=MIS, wsb=1 << 30), ALIGN),
     (dict(cdtype=FP8, ks=0.0), VALUE),
     (dict(cdtype=FP8, vs=float("nan")), VALUE),
     (dict(S=0), OK),                     # nothing to launch
@@ -235,17 +235,36 @@ def test_multi_query_validation(kw, code):
     assert multi_query(**kw) == code
 
 
+def _area(rows, d):
+    ml = (rows * 2 * 4 + 255) // 256 * 256
+    return (ml + rows * d * 4 + 255) // 256 * 256
+
+
+def _work(s, t, g, parts):
+    cap = -(-t * g // 64) + s * (parts + 1)
+    return (cap * 8 + 4 + 255) // 256 * 256
+
+
 def test_multi_query_workspace_size():
     ws = LIB.pa_multi_query_workspace_size
-    assert ws(12, 8, 2, 128, 16, 1024, BF16, BF16, 0) == 0   # one partition of 1024 (default)
-    rows = 12 * 8 * 3
-    ml = (rows * 2 * 4 + 255) // 256 * 256
-    assert ws(12, 8, 2, 128, 16, 2100, BF16, BF16, 1024) == ml + rows * 128 * 4
-    assert ws(12, 8, 2, 128, 16, 2100, BF16, FP8, 0) == ml + rows * 128 * 4
-    assert ws(12, 8, 2, 64, 32, 100, BF16, BF16, 32 * 300) == 0   # any multiple of the block
+    # Contexts within one multi-query partition (1024) and one decode partition
+    # (4096 tokens on the matrix-core decode path at G = 4): the work list only.
+    assert ws(3, 12, 8, 2, 128, 16, 1024, BF16, BF16, 0) == _work(3, 12, 4, 1)
+    # Multi-query partitions: 3 slots per query row.
+    assert ws(3, 12, 8, 2, 128, 16, 2100, BF16, BF16, 1024) == _area(12 * 8 * 3, 128) + _work(3, 12, 4, 3)
+    assert ws(3, 12, 8, 2, 128, 16, 2100, BF16, FP8, 0) == _area(12 * 8 * 3, 128) + _work(3, 12, 4, 3)
+    # Decode rows too (a 5000-token context needs 2 decode partitions per sequence).
+    assert ws(3, 12, 8, 2, 128, 16, 5000, BF16, BF16, 0) == \
+        _area(3 * 8 * 2, 128) + _area(12 * 8 * 5, 128) + _work(3, 12, 4, 5)
+    # G = 1 decodes on the vector path: 2048-token partitions.
+    assert ws(3, 12, 8, 8, 64, 16, 2100, BF16, BF16, 4096) == _area(3 * 8 * 2, 64) + _work(3, 12, 1, 1)
+    assert ws(0, 12, 8, 2, 64, 32, 100, BF16, BF16, 0) == 0   # nothing to schedule
+    assert ws(3, 0, 8, 2, 64, 32, 100, BF16, BF16, 0) == 0
     bad = ctypes.c_size_t(-1).value
-    assert ws(12, 8, 2, 128, 16, 2100, F32, F32, 0) == bad
-    assert ws(12, 8, 3, 128, 16, 2100, BF16, BF16, 0) == bad
+    assert ws(3, 12, 8, 2, 128, 16, 2100, F32, F32, 0) == bad
+    assert ws(3, 12, 8, 3, 128, 16, 2100, BF16, BF16, 0) == bad
+    assert ws(-1, 12, 8, 2, 128, 16, 2100, BF16, BF16, 0) == bad
+    assert ws(3, 12, 8, 2, 64, 32, 100, BF16, BF16, 48) == bad     # not a multiple of the block
 
 
 def reshape(**kw):
