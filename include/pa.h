@@ -268,7 +268,7 @@ int pa_decode_shared_prefix(void* out, const void* q,
  * needs: the partitions of cut contexts and the list of work items it builds
  * on the device each call (0 when there are no sequences or no query tokens);
  * (size_t)-1 for arguments it would reject.  partition_tokens: 0 = default
- * (1024 tokens).
+ * (2048 tokens).
  */
 size_t pa_multi_query_workspace_size(int num_seqs, int num_query_tokens, int num_heads,
                                      int num_kv_heads, int head_dim, int block_size,
@@ -298,7 +298,7 @@ size_t pa_multi_query_workspace_size(int num_seqs, int num_query_tokens, int num
  * max_query_len >= every n and max_context_len >= every L (host bounds that size
  * the grid).  A sequence with n == 1 is a decode step and runs through
  * pa_decode's kernels (with their partitioning).  partition_tokens (0 = default
- * 1024; else a positive multiple of block_size): a sequence with n > 1 whose
+ * 2048; else a positive multiple of block_size): a sequence with n > 1 whose
  * n * G rows fit in 64 has its context cut into partitions of this many
  * tokens, merged by a second kernel; longer chunks are not cut.
  * workspace: at least pa_multi_query_workspace_size(...) bytes, 16-byte

@@ -492,7 +492,9 @@ hipError_t by_dim(const MultiQueryLaunch& a, const MultiQueryParams& p) {
 int multi_query_rows_per_block() { return kRowsPerBlock; }
 
 int default_multi_query_partition_tokens(int block_size) {
-  const int t = 1024;
+  // Measured on 6-query verification over 1-8K contexts (70B GQA shape):
+  // 1024 -> 160 us, 2048 -> 151 us, 4096 -> 224 us.
+  const int t = 2048;
   return t - t % block_size;
 }
 

@@ -247,15 +247,16 @@ def _work(s, t, g, parts):
 
 def test_multi_query_workspace_size():
     ws = LIB.pa_multi_query_workspace_size
-    # Contexts within one multi-query partition (1024) and one decode partition
-    # (4096 tokens on the matrix-core decode path at G = 4): the work list only.
-    assert ws(3, 12, 8, 2, 128, 16, 1024, BF16, BF16, 0) == _work(3, 12, 4, 1)
+    # Contexts within one multi-query partition (2048 by default) and one decode
+    # partition (4096 tokens on the matrix-core decode path at G = 4): the work
+    # list only.
+    assert ws(3, 12, 8, 2, 128, 16, 2048, BF16, BF16, 0) == _work(3, 12, 4, 1)
     # Multi-query partitions: 3 slots per query row.
     assert ws(3, 12, 8, 2, 128, 16, 2100, BF16, BF16, 1024) == _area(12 * 8 * 3, 128) + _work(3, 12, 4, 3)
-    assert ws(3, 12, 8, 2, 128, 16, 2100, BF16, FP8, 0) == _area(12 * 8 * 3, 128) + _work(3, 12, 4, 3)
+    assert ws(3, 12, 8, 2, 128, 16, 2100, BF16, FP8, 0) == _area(12 * 8 * 2, 128) + _work(3, 12, 4, 2)
     # Decode rows too (a 5000-token context needs 2 decode partitions per sequence).
     assert ws(3, 12, 8, 2, 128, 16, 5000, BF16, BF16, 0) == \
-        _area(3 * 8 * 2, 128) + _area(12 * 8 * 5, 128) + _work(3, 12, 4, 5)
+        _area(3 * 8 * 2, 128) + _area(12 * 8 * 3, 128) + _work(3, 12, 4, 3)
     # G = 1 decodes on the vector path: 2048-token partitions.
     assert ws(3, 12, 8, 8, 64, 16, 2100, BF16, BF16, 4096) == _area(3 * 8 * 2, 64) + _work(3, 12, 1, 1)
     assert ws(0, 12, 8, 2, 64, 32, 100, BF16, BF16, 0) == 0   # nothing to schedule
