@@ -77,6 +77,7 @@ __all__ = [
     "attend_one",
     "decode",
     "decode_rows",
+    "swap_blocks",
     "query_rows",
     "query_position",
     "multi_query",
@@ -267,6 +268,20 @@ def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray,
     for src, dst in pairs:
         k_cache[int(dst)] = k_src[int(src)]
         v_cache[int(dst)] = v_src[int(src)]
+
+
+def swap_blocks(src_k: np.ndarray, src_v: np.ndarray, dst_k: np.ndarray,
+                dst_v: np.ndarray, block_pairs: np.ndarray) -> None:
+    """Copy whole blocks from one pool to another, in place on the destination.
+
+    [tbr8] (the scheduler section) swaps a preempted request's KV cache out
+    to CPU memory and back in later; [luoboask] section 4 keeps such requests
+    in a SWAPPED queue.  For each (src, dst) pair, block dst of the destination
+    pool (K and V, every kv head and slot) becomes block src of the source pool.
+    """
+    for src, dst in np.asarray(block_pairs).reshape(-1, 2):
+        dst_k[int(dst)] = src_k[int(src)]
+        dst_v[int(dst)] = src_v[int(src)]
 
 
 # --------------------------------------------------------------------------

@@ -501,6 +501,27 @@ def pin_mq_causality():
     assert not np.allclose(after[5], before[5])
 
 
+def pin_swap_blocks():
+    """Swapping out then in restores the blocks; the rest of both pools is
+    untouched; the result equals a fancy-index copy."""
+    rng = np.random.default_rng(36)
+    dev_k = rng.standard_normal((20, 2, 4, 8)).astype(np.float32)
+    dev_v = rng.standard_normal((20, 2, 4, 8)).astype(np.float32)
+    host_k = np.full((6, 2, 4, 8), np.nan, dtype=np.float32)
+    host_v = host_k.copy()
+    out_pairs = np.array([[3, 0], [17, 4], [9, 1]], dtype=np.int64)
+    op.swap_blocks(dev_k, dev_v, host_k, host_v, out_pairs)
+    assert np.array_equal(host_k[[0, 4, 1]], dev_k[[3, 17, 9]])
+    assert np.array_equal(host_v[[0, 4, 1]], dev_v[[3, 17, 9]])
+    assert np.isnan(host_k[[2, 3, 5]]).all()
+    back_k, back_v = np.zeros_like(dev_k), np.zeros_like(dev_v)
+    op.swap_blocks(host_k, host_v, back_k, back_v, np.array([[0, 11], [4, 2], [1, 19]]))
+    assert np.array_equal(back_k[[11, 2, 19]], dev_k[[3, 17, 9]])
+    assert np.array_equal(back_v[[11, 2, 19]], dev_v[[3, 17, 9]])
+    others = [b for b in range(20) if b not in (11, 2, 19)]
+    assert not back_k[others].any() and not back_v[others].any()
+
+
 PINS = [pin_bruteforce, pin_sdpa, pin_worked_tables, pin_block_counts, pin_kv_bytes,
         pin_ctx1_returns_v, pin_weights_sum_to_one, pin_q_zero_gives_mean,
         pin_constant_v, pin_shift_invariance, pin_block_permutation,
@@ -508,7 +529,8 @@ PINS = [pin_bruteforce, pin_sdpa, pin_worked_tables, pin_block_counts, pin_kv_by
         pin_nan_poison_ignored, pin_zero_context, pin_batch_invariance, pin_widen,
         pin_reshape_library, pin_reshape_roundtrip, pin_copy_blocks, pin_e4m3_table,
         pin_e4m3_encode, pin_fp8_reshape_and_decode, pin_mq_sdpa, pin_mq_bruteforce,
-        pin_mq_last_query_is_decode, pin_mq_chunking_invariance, pin_mq_causality]
+        pin_mq_last_query_is_decode, pin_mq_chunking_invariance, pin_mq_causality,
+        pin_swap_blocks]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -619,6 +641,18 @@ _ORIG_E4M3_VALUES = op.e4m3_values
 _ORIG_E4M3_ENCODE = op.e4m3_encode
 
 
+def _swap_k_only(src_k, src_v, dst_k, dst_v, pairs):
+    for src, dst in np.asarray(pairs).reshape(-1, 2):
+        dst_k[int(dst)] = src_k[int(src)]
+
+
+def _swap_pair_reversed(src_k, src_v, dst_k, dst_v, pairs):
+    # reads each pair as (dst, src)
+    for dst, src in np.asarray(pairs).reshape(-1, 2):
+        dst_k[int(dst) % len(dst_k)] = src_k[int(src) % len(src_k)]
+        dst_v[int(dst) % len(dst_v)] = src_v[int(src) % len(src_v)]
+
+
 def _position_plus_one(context_len, query_len, i):
     return context_len - query_len + i + 1
 
@@ -652,6 +686,8 @@ MUTATIONS = {
     "mq_no_causal_mask": ("query_position", _position_unmasked),
     "mq_causal_mask_top_left": ("query_position", _position_top_left),
     "mq_query_rows_short": ("query_rows", _rows_drop_last),
+    "swap_k_only": ("swap_blocks", _swap_k_only),
+    "swap_pair_reversed": ("swap_blocks", _swap_pair_reversed),
 }
 
 
