@@ -53,6 +53,8 @@ DESCRIPTION.update({
 })
 for _n in ("llama7b", "llama13b", "gqa70b", "beam", "specdec70b", "chunked13b"):
     DESCRIPTION[_n + "_fp8"] = DESCRIPTION[_n].replace(", bf16", ", bf16 query / fp8 E4M3 KV cache")
+DESCRIPTION["swap13b"] = ("swap_blocks of 1024 random blocks of the LLaMA-13B-shaped pool (Hkv=40, BS=16, "
+                          "D=128, bf16: 320 KiB of K+V per block) to pinned host memory and back")
 # "+prefix": the same step with pa_decode_shared_prefix (each shared page read
 # once per chunk of sequences) in place of pa_decode.
 for _n in ("beam", "beam_fp8"):
@@ -64,10 +66,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama13b", choices=sorted(DESCRIPTION))
+    ap.add_argument("--workload", default="llama13b",
+                    choices=sorted(n for n in DESCRIPTION if n != "swap13b"))
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--others", default="llama7b,gqa70b,beam,beam+prefix,llama13b_fp8,gqa70b_fp8,"
-                                        "specdec70b,chunked13b",
+                                        "specdec70b,chunked13b,swap13b",
                     help="comma list of extra workloads to report ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -300,6 +303,49 @@ def run_workload(label, steps, warmup, partition_tokens, flush=False):
     return res, spec, plan
 
 
+PCIE_GBPS = 64.0  # PCIe 5.0 x16, one direction, published
+
+
+def run_swap(label, steps, warmup, blocks=1024):
+    """Swap-out (device -> pinned host) and swap-in of scattered blocks."""
+    import torch
+    from paged_kv_cache_321_amd import binding
+    from paged_kv_cache_321_amd import workloads as wl
+
+    x = wl.make_inputs("llama13b", device="cuda", poison=False)
+    nb = x.plan.num_blocks
+    shape = (blocks,) + tuple(x.k_cache.shape[1:])
+    host_k = torch.empty(shape, dtype=x.k_cache.dtype).pin_memory()
+    host_v = torch.empty(shape, dtype=x.k_cache.dtype).pin_memory()
+    g = torch.Generator().manual_seed(11)
+    dev_ids = torch.randperm(nb, generator=g)[:blocks]
+    host_ids = torch.randperm(blocks, generator=g)
+    out_pairs = torch.stack([dev_ids, host_ids], 1).to(torch.int64).to("cuda")
+    in_pairs = torch.stack([host_ids, dev_ids], 1).to(torch.int64).to("cuda")
+    stream = torch.cuda.current_stream()
+    res = {"workload": label, "description": DESCRIPTION[label], "blocks": blocks}
+    nbytes = 2 * blocks * x.k_cache[0].numel() * x.k_cache.element_size()
+    for what, args in (("out", (host_k, host_v, x.k_cache, x.v_cache, out_pairs)),
+                       ("in", (x.k_cache, x.v_cache, host_k, host_v, in_pairs))):
+        for _ in range(warmup):
+            binding.pa_swap_blocks(*args, stream=stream)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            binding.pa_swap_blocks(*args, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / steps * 1e3
+        res[f"swap_{what}_us"] = us
+        res[f"swap_{what}_GBps"] = nbytes / (us / 1e6) / 1e9
+        res[f"swap_{what}_frac_of_pcie"] = res[f"swap_{what}_GBps"] / PCIE_GBPS
+    res["bytes_per_direction"] = nbytes
+    del x, host_k, host_v
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(name, target_s):
     """The oracle, single-threaded, on a bounded sample of the workload."""
     import numpy as np
@@ -402,6 +448,9 @@ def main():
     head, spec, plan = run_workload(args.workload, args.steps, args.warmup, args.partition_tokens)
     others = []
     for name in [n for n in args.others.split(",") if n and n != args.workload]:
+        if name == "swap13b":
+            others.append(run_swap(name, min(args.steps, 10), min(args.warmup, 2)))
+            continue
         r, _, _ = run_workload(name, args.steps, args.warmup, args.partition_tokens)
         r["decode_traffic_bytes"] = measured_traffic(name)
         others.append(r)

@@ -129,6 +129,31 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs,
                    int block_size, int head_dim, int cache_dtype, void* stream);
 
 /*
+ * pa_swap_blocks -- copy whole cache blocks, K and V, from one pool to another:
+ * swap a preempted request's blocks out to host memory, or back in.
+ * ([tbr8] scheduler section: when GPU memory runs short, the KV cache of
+ * low-priority requests is swapped out to CPU memory and swapped back in
+ * later, with --swap-space setting the CPU memory for it; [luoboask] section 4
+ * "Scheduler": a SWAPPED queue whose requests are swapped back in when blocks
+ * are free.)
+ *
+ * For every pair p = (src, dst): dst_k_cache[dst] = src_k_cache[src] and
+ * dst_v_cache[dst] = src_v_cache[src] over all kv heads and slots (bit-exact);
+ * both pools have the [blocks, num_kv_heads, block_size, head_dim] layout of
+ * cache_dtype.  Either pool (and block_pairs) may live in host memory allocated
+ * pinned with hipHostMalloc: the copy kernel reads and writes it through its
+ * unified address, one launch for any number of scattered blocks.
+ * Preconditions: 0 <= src < num_src_blocks, 0 <= dst < num_dst_blocks (pairs
+ * outside are skipped); dst ids distinct; the pools do not overlap.
+ * num_pairs == 0 is a no-op.
+ */
+int pa_swap_blocks(void* dst_k_cache, void* dst_v_cache,
+                   const void* src_k_cache, const void* src_v_cache,
+                   const int64_t* block_pairs, int num_pairs,
+                   int num_src_blocks, int num_dst_blocks, int num_kv_heads,
+                   int block_size, int head_dim, int cache_dtype, void* stream);
+
+/*
  * pa_decode_workspace_size -- bytes of device workspace pa_decode needs for
  * these sizes.  Long contexts are cut into partitions of `partition_tokens`
  * tokens (0 = the library's default for this shape); each partition leaves a

@@ -27,7 +27,8 @@ STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
           -7: "PA_ERR_LAUNCH", -8: "PA_ERR_VALUE"}
 EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_workspace_size",
            "pa_decode", "pa_decode_shared_prefix_workspace_size", "pa_decode_shared_prefix",
-           "pa_multi_query_workspace_size", "pa_multi_query", "pa_status_string")
+           "pa_multi_query_workspace_size", "pa_multi_query", "pa_swap_blocks",
+           "pa_status_string")
 
 _c_int, _c_size, _c_float, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
 
@@ -67,6 +68,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                    [_c_float, _c_int, _c_int, _c_float, _c_float, _c_int, _vp,
                                     _c_size, _vp])
     lib.pa_multi_query.restype = _c_int
+    lib.pa_swap_blocks.argtypes = [_vp, _vp, _vp, _vp, _vp] + [_c_int] * 7 + [_vp]
+    lib.pa_swap_blocks.restype = _c_int
     lib.pa_status_string.argtypes = [_c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     return lib
@@ -336,3 +339,28 @@ def pa_multi_query(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_
                             float(scale), code, ccode, float(k_scale), float(v_scale),
                             int(partition_tokens), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "pa_multi_query")
+
+
+def pa_swap_blocks(dst_k_cache: torch.Tensor, dst_v_cache: torch.Tensor, src_k_cache: torch.Tensor,
+                   src_v_cache: torch.Tensor, block_pairs: torch.Tensor, stream=None) -> None:
+    """Copy whole blocks src_pool[src] -> dst_pool[dst] for block_pairs [P, 2] (int64).
+
+    Each pool is a device tensor or a pinned host tensor (``pin_memory=True``),
+    as is ``block_pairs``.
+    """
+    for n, t in (("dst_k_cache", dst_k_cache), ("dst_v_cache", dst_v_cache),
+                 ("src_k_cache", src_k_cache), ("src_v_cache", src_v_cache),
+                 ("block_pairs", block_pairs)):
+        _need(t.is_cuda or t.is_pinned(), f"{n} must be a device tensor or pinned host memory")
+        _need(t.is_contiguous(), f"{n} must be contiguous")
+    _need(block_pairs.dtype == torch.int64, "block_pairs must be int64")
+    _need(block_pairs.dim() == 2 and block_pairs.shape[1] == 2, "block_pairs must be [P, 2]")
+    _need(dst_k_cache.dtype == dst_v_cache.dtype == src_k_cache.dtype == src_v_cache.dtype,
+          "element types differ")
+    _need(dst_k_cache.shape == dst_v_cache.shape and src_k_cache.shape == src_v_cache.shape and
+          dst_k_cache.shape[1:] == src_k_cache.shape[1:], "pool shapes differ")
+    nbd, hkv, bs, d = dst_k_cache.shape
+    st = LIB.pa_swap_blocks(_ptr(dst_k_cache), _ptr(dst_v_cache), _ptr(src_k_cache), _ptr(src_v_cache),
+                            _ptr(block_pairs), block_pairs.shape[0], src_k_cache.shape[0], nbd, hkv,
+                            bs, d, _dtype_code(dst_k_cache), _stream(stream))
+    _check(st, "pa_swap_blocks")

@@ -176,6 +176,26 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs, int
   return pa::launch_copy_blocks(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+int pa_swap_blocks(void* dst_k_cache, void* dst_v_cache, const void* src_k_cache, const void* src_v_cache,
+                   const int64_t* block_pairs, int num_pairs, int num_src_blocks, int num_dst_blocks,
+                   int num_kv_heads, int block_size, int head_dim, int cache_dtype, void* stream) {
+  int st = cache_shape_status(num_dst_blocks, num_kv_heads, block_size, head_dim, cache_dtype);
+  if (st != PA_OK) return st;
+  if (num_src_blocks <= 0 || num_pairs < 0) return PA_ERR_SHAPE;
+  if (!dst_k_cache || !dst_v_cache || !src_k_cache || !src_v_cache) return PA_ERR_NULL;
+  if (num_pairs == 0) return PA_OK;
+  if (!block_pairs) return PA_ERR_NULL;
+  if (!aligned(dst_k_cache, 16) || !aligned(dst_v_cache, 16) || !aligned(src_k_cache, 16) ||
+      !aligned(src_v_cache, 16) || !aligned(block_pairs, 8))
+    return PA_ERR_ALIGN;
+  pa::CopyLaunch a{dst_k_cache, dst_v_cache, block_pairs, num_pairs, num_dst_blocks, num_kv_heads,
+                   block_size, head_dim, elem_bytes(cache_dtype), static_cast<hipStream_t>(stream)};
+  a.src_k_cache = src_k_cache;
+  a.src_v_cache = src_v_cache;
+  a.num_src_blocks = num_src_blocks;
+  return pa::launch_copy_blocks(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                                 int block_size, int max_context_len, int dtype, int cache_dtype,
                                 int partition_tokens) {

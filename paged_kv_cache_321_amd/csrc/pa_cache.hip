@@ -76,19 +76,23 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
   v_cache[dst] = encode16(value + src, v_inv);
 }
 
-// grid.x = pair, grid.y strides over the 16-byte chunks of a block.
-__global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_cache,
-                                                          uint4* __restrict__ v_cache,
+// Whole-block copies from one pool to another (or within one pool): grid.x
+// = pair, grid.y strides over the 16-byte chunks of a block.  Either pool may
+// be pinned host memory, which the kernel reads or writes through its unified
+// address (a swap to or from host memory).
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* dst_k, uint4* dst_v, const uint4* src_k,
+                                                          const uint4* src_v,
                                                           const int64_t* __restrict__ pairs,
-                                                          int64_t block_chunks, int num_blocks) {
+                                                          int64_t block_chunks, int num_src_blocks,
+                                                          int num_dst_blocks) {
   const int pr = blockIdx.x;
   const int64_t src = pairs[2 * (int64_t)pr];
   const int64_t dst = pairs[2 * (int64_t)pr + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  const uint4* ks = k_cache + src * block_chunks;
-  const uint4* vs = v_cache + src * block_chunks;
-  uint4* kd = k_cache + dst * block_chunks;
-  uint4* vd = v_cache + dst * block_chunks;
+  if (src < 0 || src >= num_src_blocks || dst < 0 || dst >= num_dst_blocks) return;
+  const uint4* ks = src_k + src * block_chunks;
+  const uint4* vs = src_v + src * block_chunks;
+  uint4* kd = dst_k + dst * block_chunks;
+  uint4* vd = dst_v + dst * block_chunks;
   for (int64_t c = (int64_t)blockIdx.y * blockDim.x + threadIdx.x; c < block_chunks;
        c += (int64_t)gridDim.y * blockDim.x) {
     const uint4 kk = ks[c];
@@ -139,7 +143,9 @@ hipError_t launch_copy_blocks(const CopyLaunch& a) {
   if (gy > 64) gy = 64;
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(a.num_pairs, static_cast<unsigned>(gy)), dim3(256), 0,
                      a.stream, static_cast<uint4*>(a.k_cache), static_cast<uint4*>(a.v_cache),
-                     a.block_pairs, block_chunks, a.num_blocks);
+                     static_cast<const uint4*>(a.src_k_cache ? a.src_k_cache : a.k_cache),
+                     static_cast<const uint4*>(a.src_v_cache ? a.src_v_cache : a.v_cache), a.block_pairs,
+                     block_chunks, a.src_k_cache ? a.num_src_blocks : a.num_blocks, a.num_blocks);
   return hipGetLastError();
 }
 

@@ -72,11 +72,14 @@ struct ReshapeLaunch {
 };
 
 struct CopyLaunch {
-  void* k_cache;
+  void* k_cache;  // destination pool (and source, for copy_blocks)
   void* v_cache;
   const int64_t* block_pairs;
   int num_pairs, num_blocks, num_kv_heads, block_size, head_dim, elem_bytes;
   hipStream_t stream;
+  const void* src_k_cache = nullptr;  // another source pool (swap_blocks), or null
+  const void* src_v_cache = nullptr;
+  int num_src_blocks = 0;
 };
 
 struct MultiQueryLaunch {

@@ -325,6 +325,32 @@ def test_copy_validation(kw, code):
     assert copy(**kw) == code
 
 
+def swap(**kw):
+    a = dict(dk=P, dv=P, sk=P, sv=P, pairs=P, n=3, nsrc=8, ndst=4, Hkv=2, BS=16, D=64, dtype=BF16)
+    a.update(kw)
+    return LIB.pa_swap_blocks(a["dk"], a["dv"], a["sk"], a["sv"], a["pairs"], a["n"], a["nsrc"],
+                              a["ndst"], a["Hkv"], a["BS"], a["D"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=9), DTYPE),
+    (dict(n=-1), SHAPE),
+    (dict(nsrc=0), SHAPE),
+    (dict(ndst=0), SHAPE),
+    (dict(D=96), UNSUP),
+    (dict(BS=8), UNSUP),
+    (dict(sk=None), NULL),
+    (dict(dv=None), NULL),
+    (dict(pairs=None), NULL),
+    (dict(sv=MIS), ALIGN),
+    (dict(pairs=P + 4), ALIGN),
+    (dict(n=0, pairs=None), OK),
+    (dict(n=0, pairs=None, dtype=FP8), OK),
+])
+def test_swap_validation(kw, code):
+    assert swap(**kw) == code
+
+
 def test_binding_raises_runtime_error_with_status():
     err = binding.PaError(SHAPE, "pa_decode")
     assert isinstance(err, RuntimeError) and "PA_ERR_SHAPE" in str(err)
