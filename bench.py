@@ -33,7 +33,8 @@ TRAFFIC_FILE = os.path.join(HERE, "profiles", "decode_traffic.json")
 # Sources that determine the decode kernels; the counter record is valid only
 # for the exact text it was measured on.
 KERNEL_SRCS = [os.path.join(HERE, "paged_kv_cache_321_amd", "csrc", n) for n in
-               ("pa_device.h", "pa_decode.hip", "pa_decode_valu.hip", "pa_decode_mfma.hip")]
+               ("pa_device.h", "pa_mfma.h", "pa_decode.hip", "pa_decode_valu.hip",
+                "pa_decode_mfma.hip", "pa_multi_query.hip")]
 
 DESCRIPTION = {
     "llama13b": "LLaMA-13B-shaped layer decode: 128 seqs x ctx 2048, H=Hkv=40, D=128, BS=16, bf16, "

@@ -207,7 +207,10 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_kernel(MultiQueryPa
   };
 
   // One step's K and V chunks, PER_T per thread: chunk c is token c / CCH of
-  // the step, 16 bytes at chunk c % CCH of that token's cache row.
+  // the step, 16 bytes at chunk c % CCH of that token's cache row.  Pages
+  // read by one workgroup only (a sequence of one row block) stream past the
+  // caches; the row blocks of a longer chunk share theirs through L2 / MALL.
+  const bool stream_pages = b.nrb == 1;
   uint4 kreg[PER_T], vreg[PER_T];
   auto load_step = [&](int st) {
 #pragma unroll
@@ -220,8 +223,13 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_kernel(MultiQueryPa
         // The page is the same across each wave (a wave's chunks lie in one page).
         const int64_t phys = __builtin_amdgcn_readlane(my_id, __builtin_amdgcn_readfirstlane(pg) & 63);
         const int64_t off = phys * p.block_stride + (tok % BS) * D + (c % CCH) * (16 / (int)sizeof(TC));
-        kreg[u] = load_page16<true>(kc + off);
-        vreg[u] = load_page16<true>(vc + off);
+        if (stream_pages) {
+          kreg[u] = load_page16<true>(kc + off);
+          vreg[u] = load_page16<true>(vc + off);
+        } else {
+          kreg[u] = load_page16<false>(kc + off);
+          vreg[u] = load_page16<false>(vc + off);
+        }
       }
     }
   };
