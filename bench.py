@@ -30,11 +30,10 @@ sys.path.insert(0, HERE)
 METRIC = "paged-attn decode tokens/s per layer + achieved HBM GB/s (% of peak), 1 GPU"
 PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "decode_traffic.json")
-# Sources that determine the decode kernels; the counter record is valid only
-# for the exact text it was measured on.
-KERNEL_SRCS = [os.path.join(HERE, "paged_kv_cache_321_amd", "csrc", n) for n in
-               ("pa_device.h", "pa_mfma.h", "pa_decode.hip", "pa_decode_valu.hip",
-                "pa_decode_mfma.hip", "pa_multi_query.hip")]
+# Sources that determine the attention kernels; a workload's counter record
+# is valid only for the exact text of the sources its kernels are built from.
+DECODE_SRCS = ("pa_device.h", "pa_mfma.h", "pa_decode.hip", "pa_decode_valu.hip", "pa_decode_mfma.hip")
+MULTI_QUERY_SRCS = DECODE_SRCS + ("pa_multi_query.hip",)
 
 DESCRIPTION = {
     "llama13b": "LLaMA-13B-shaped layer decode: 128 seqs x ctx 2048, H=Hkv=40, D=128, BS=16, bf16, "
@@ -140,9 +139,16 @@ def unique_bytes(plan, spec) -> int:
     return kv + qo + table + 4 * len(ctx)
 
 
-def kernel_hash() -> str:
+def kernel_sources(workload: str):
+    """Source files of the kernels a workload's attention call runs."""
+    names = MULTI_QUERY_SRCS if workload.split("_")[0].split("+")[0] in ("specdec70b", "chunked13b") \
+        else DECODE_SRCS
+    return [os.path.join(HERE, "paged_kv_cache_321_amd", "csrc", n) for n in names]
+
+
+def kernel_hash(workload: str) -> str:
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
+    for path in kernel_sources(workload):
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -156,7 +162,7 @@ def measured_traffic(workload: str):
     except (OSError, ValueError):
         return None
     entry = rec.get(workload)
-    if not entry or entry.get("kernel_sha256_16") != kernel_hash():
+    if not entry or entry.get("kernel_sha256_16") != kernel_hash(workload):
         return None
     return entry.get("bytes_per_launch")
 
