@@ -203,6 +203,8 @@ def run_workload(label, steps, warmup, partition_tokens, flush=False):
             plan.block_size, plan.max_context_len, code, partition_tokens, ccode)
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
         max_q = int(plan.query_lens.max())
+        # No single-query sequence in the batch: no decode launch.
+        tiles_only = int(plan.query_lens.min()) > 1
     has_pairs = plan.block_pairs.shape[0] > 0
     has_tokens = plan.slot_mapping.shape[0] > 0
     # Workloads whose sequences share physical blocks (beam prefixes) ask for
@@ -225,7 +227,7 @@ def run_workload(label, steps, warmup, partition_tokens, flush=False):
             binding.pa_multi_query(out, x.q, x.k_cache, x.v_cache, x.block_tables, x.context_lens,
                                    x.query_start, x.scale, plan.max_context_len, max_q,
                                    partition_tokens=partition_tokens, workspace=ws, stream=stream,
-                                   k_scale=x.k_scale, v_scale=x.v_scale)
+                                   k_scale=x.k_scale, v_scale=x.v_scale, tiles_only=tiles_only)
         elif shared_prefix:
             binding.pa_decode_shared_prefix(out, x.q, x.k_cache, x.v_cache, x.block_tables,
                                             x.context_lens, lead, nblk, x.scale,

@@ -61,6 +61,15 @@ extern "C" {
  * offers an fp8 KV cache without fixing the format; this is the reading used.) */
 typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
 
+/* pa_multi_query flags */
+enum {
+  /* Serve every sequence, single-query ones included, in the multi-query
+   * tiles instead of routing sequences with one new query through the decode
+   * kernels.  Saves the decode launch for batches that have no decode steps
+   * (speculative verification); never changes what is computed. */
+  PA_MULTI_QUERY_TILES_ONLY = 1
+};
+
 /* pa_decode flags */
 enum {
   /* Physical blocks may be shared by several sequences of the batch (prefix
@@ -322,7 +331,9 @@ size_t pa_multi_query_workspace_size(int num_seqs, int num_query_tokens, int num
  * num_kv_heads in {1, 2, 4, 8}; head_dim 64 or 128; block_size 16 or 32.
  * max_query_len >= every n and max_context_len >= every L (host bounds that size
  * the grid).  A sequence with n == 1 is a decode step and runs through
- * pa_decode's kernels (with their partitioning).  partition_tokens (0 = default
+ * pa_decode's kernels (with their partitioning) unless flags holds
+ * PA_MULTI_QUERY_TILES_ONLY (any other flag bit: PA_ERR_UNSUPPORTED).
+ * partition_tokens (0 = default
  * 2048; else a positive multiple of block_size): a sequence with n > 1 whose
  * n * G rows fit in 64 has its context cut into partitions of this many
  * tokens, merged by a second kernel; longer chunks are not cut.
@@ -342,7 +353,8 @@ int pa_multi_query(void* out, const void* q,
                    int num_heads, int num_kv_heads, int head_dim,
                    int block_size, int num_blocks, int max_context_len,
                    float scale, int dtype, int cache_dtype, float k_scale, float v_scale,
-                   int partition_tokens, void* workspace, size_t workspace_bytes, void* stream);
+                   int partition_tokens, int flags,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* pa_status_string -- static, human-readable name of a status code. */
 const char* pa_status_string(int status);

@@ -22,6 +22,7 @@ PA_F32 = 0
 PA_BF16 = 1
 PA_FP8_E4M3 = 2
 PA_DECODE_SHARED_PAGES = 1
+PA_MULTI_QUERY_TILES_ONLY = 1
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
           -4: "PA_ERR_UNSUPPORTED", -5: "PA_ERR_ALIGN", -6: "PA_ERR_WORKSPACE",
           -7: "PA_ERR_LAUNCH", -8: "PA_ERR_VALUE"}
@@ -65,8 +66,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_multi_query_workspace_size.argtypes = [_c_int] * 10
     lib.pa_multi_query_workspace_size.restype = _c_size
     lib.pa_multi_query.argtypes = ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp] + [_c_int] * 9 +
-                                   [_c_float, _c_int, _c_int, _c_float, _c_float, _c_int, _vp,
-                                    _c_size, _vp])
+                                   [_c_float, _c_int, _c_int, _c_float, _c_float, _c_int, _c_int,
+                                    _vp, _c_size, _vp])
     lib.pa_multi_query.restype = _c_int
     lib.pa_swap_blocks.argtypes = [_vp, _vp, _vp, _vp, _vp] + [_c_int] * 7 + [_vp]
     lib.pa_swap_blocks.restype = _c_int
@@ -305,12 +306,13 @@ def pa_multi_query(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_
                    query_start: torch.Tensor, scale: float, max_context_len: int,
                    max_query_len: int, partition_tokens: int = 0,
                    workspace: Optional[torch.Tensor] = None, stream=None, k_scale: float = 1.0,
-                   v_scale: float = 1.0) -> None:
+                   v_scale: float = 1.0, tiles_only: bool = False) -> None:
     """Causal attention of each sequence's new query tokens over the paged caches.
 
     q, out [T, H, D] (bf16) hold sequence s's queries in rows
     query_start[s] .. query_start[s + 1] - 1 (int32 device tensor [S + 1]); they
-    are the last positions of its context_lens[s] cached tokens.
+    are the last positions of its context_lens[s] cached tokens.  ``tiles_only``
+    sets PA_MULTI_QUERY_TILES_ONLY (no decode launch for single-query sequences).
     """
     for n, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
                  ("block_tables", block_tables), ("context_lens", context_lens),
@@ -337,7 +339,8 @@ def pa_multi_query(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_
                             block_tables.shape[1], _ptr(context_lens), _ptr(query_start), s, t,
                             int(max_query_len), h, hkv, d, bs, nb, int(max_context_len),
                             float(scale), code, ccode, float(k_scale), float(v_scale),
-                            int(partition_tokens), _ptr(workspace), ws_bytes, _stream(stream))
+                            int(partition_tokens), PA_MULTI_QUERY_TILES_ONLY if tiles_only else 0,
+                            _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "pa_multi_query")
 
 

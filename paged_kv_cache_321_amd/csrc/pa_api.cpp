@@ -374,8 +374,10 @@ int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_
                    const int32_t* query_start, int num_seqs, int num_query_tokens, int max_query_len,
                    int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
                    int max_context_len, float scale, int dtype, int cache_dtype, float k_scale,
-                   float v_scale, int partition_tokens, void* workspace, size_t workspace_bytes,
-                   void* stream) {
+                   float v_scale, int partition_tokens, int flags, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (flags & ~PA_MULTI_QUERY_TILES_ONLY) return PA_ERR_UNSUPPORTED;
+  const bool tiles_only = (flags & PA_MULTI_QUERY_TILES_ONLY) != 0;
   const MultiQuerySizes z = multi_query_sizes(num_seqs, num_query_tokens, num_heads, num_kv_heads,
                                               head_dim, block_size, max_context_len, dtype,
                                               cache_dtype, partition_tokens);
@@ -431,7 +433,9 @@ int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_
   a.work = ws + z.decode_bytes + z.parts_bytes;
   a.work_count = reinterpret_cast<int*>(ws + z.decode_bytes + z.parts_bytes + z.work_capacity * 8);
   a.work_capacity = (int)z.work_capacity;
+  a.decode_rows_elsewhere = !tiles_only;
   a.stream = static_cast<hipStream_t>(stream);
+  if (tiles_only) return pa::launch_multi_query(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
   // Sequences with a single new query are decode steps: the decode kernels
   // serve them (q / out row query_start[s]); the multi-query kernel skips them.
   pa::DecodeLaunch d;

@@ -104,6 +104,7 @@ struct MultiQueryLaunch {
   void* work;            // work list: work_capacity 8-byte items (workspace)
   int* work_count;       // (workspace)
   int work_capacity;     // bound on the work items: the grid size per kv head
+  bool decode_rows_elsewhere;  // single-query sequences go to the decode kernels
   hipStream_t stream;
 };
 

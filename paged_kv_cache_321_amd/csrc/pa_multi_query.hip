@@ -19,9 +19,9 @@
 // into LDS.  Each column keeps its own running max and sum, moved lazily (only
 // when a score exceeds the reference by more than 2^8).
 //
-// Sequences with exactly one new query are decode steps; the entry point runs
-// them through the decode kernels (which stream their pages at the HBM rate)
-// and this kernel skips them.
+// Sequences with exactly one new query are decode steps; unless told
+// otherwise, the entry point runs them through the decode kernels (which
+// stream their pages at the HBM rate) and this kernel skips them.
 //
 // Partitions.  A sequence whose rows fit one block (speculative verification,
 // short chunks) would give too few workgroups on a long context, so its
@@ -66,6 +66,7 @@ struct MultiQueryParams {
   int2* work;          // work items (sequence, row block index << 16 | partition)
   int* work_count;     // number of work items
   int work_capacity;   // items the list holds (the grid's bound)
+  int decode_rows_elsewhere;  // sequences with one query run in the decode kernels
   float scale_log2e;   // softmax scale * log2(e), times k_scale for fp8 caches
   float v_scale;       // multiplies the output (1 unless the cache holds fp8 codes)
 };
@@ -93,7 +94,7 @@ __device__ __forceinline__ MqBlock mq_block(const MultiQueryParams& p, int s, in
   if (b.skip) return b;
   b.t0 = t0;
   b.qlen = t1 - t0;
-  if (b.qlen == 1) {  // a decode row: served by the decode kernels
+  if (b.qlen == 1 && p.decode_rows_elsewhere) {  // a decode row: served by the decode kernels
     b.skip = true;
     return b;
   }
@@ -532,6 +533,7 @@ hipError_t launch_multi_query(const MultiQueryLaunch& a) {
   p.work = reinterpret_cast<int2*>(a.work);
   p.work_count = a.work_count;
   p.work_capacity = a.work_capacity;
+  p.decode_rows_elsewhere = a.decode_rows_elsewhere ? 1 : 0;
   const bool fp8 = a.cache_dtype == kDtypeFp8;
   p.scale_log2e = a.scale * kLog2e * (fp8 ? a.k_scale : 1.f);
   p.v_scale = fp8 ? a.v_scale : 1.f;

@@ -191,13 +191,13 @@ def test_shared_prefix_workspace_size():
 def multi_query(**kw):
     a = dict(out=P, q=P, k=P, v=P, bt=P, mb=8, ctx=P, qs=P, S=2, T=12, mq=6, H=8, Hkv=2, D=128,
              BS=16, NB=32, maxctx=100, scale=0.1, dtype=BF16, cdtype=None, ks=0.5, vs=0.5, pt=0,
-             ws=None, wsb=0)
+             flags=0, ws=None, wsb=0)
     a.update(kw)
     cdtype = a["dtype"] if a["cdtype"] is None else a["cdtype"]
     return LIB.pa_multi_query(a["out"], a["q"], a["k"], a["v"], a["bt"], a["mb"], a["ctx"], a["qs"],
                               a["S"], a["T"], a["mq"], a["H"], a["Hkv"], a["D"], a["BS"], a["NB"],
                               a["maxctx"], a["scale"], a["dtype"], cdtype, a["ks"], a["vs"], a["pt"],
-                              a["ws"], a["wsb"], None)
+                              a["flags"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -230,6 +230,8 @@ def multi_query(**kw):
     (dict(S=0), OK),                     # nothing to launch
     (dict(T=0, q=None, out=None), OK),
     (dict(mq=0), OK),
+    (dict(flags=2), UNSUP),
+    (dict(flags=1, S=0), OK),
 ])
 def test_multi_query_validation(kw, code):
     assert multi_query(**kw) == code

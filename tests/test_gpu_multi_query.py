@@ -64,6 +64,7 @@ def test_shapes(h, hkv, d, bs):
     x = shape_case(h, hkv, d, bs)
     check_mq(x)
     check_mq(x, partition_tokens=2 * bs)
+    check_mq(x, tiles_only=True)   # single-query sequences in the tiles as well
 
 
 @pytest.mark.parametrize("h,hkv,d,bs", [(8, 8, 128, 16), (64, 8, 128, 32), (16, 8, 64, 16),
