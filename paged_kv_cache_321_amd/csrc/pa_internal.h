@@ -1,5 +1,6 @@
 // Internal interface between the validating C entry points (pa_api.cpp) and
-// the kernel launchers (pa_kernels.hip).  Not part of the public ABI.
+// the kernel launchers (pa_cache.hip, pa_decode*.hip, pa_multi_query.hip).  Not part
+// of the public ABI.
 #ifndef PA_INTERNAL_H_
 #define PA_INTERNAL_H_
 
