@@ -67,7 +67,11 @@ enum {
    * tiles instead of routing sequences with one new query through the decode
    * kernels.  Saves the decode launch for batches that have no decode steps
    * (speculative verification); never changes what is computed. */
-  PA_MULTI_QUERY_TILES_ONLY = 1
+  PA_MULTI_QUERY_TILES_ONLY = 1,
+  /* Launch every kernel on the caller's stream.  By default the decode rows
+   * run on a second stream of the library's, beside the multi-query tiles;
+   * the results are the same bits either way. */
+  PA_MULTI_QUERY_ONE_STREAM = 2
 };
 
 /* pa_decode flags */
@@ -332,7 +336,17 @@ size_t pa_multi_query_workspace_size(int num_seqs, int num_query_tokens, int num
  * max_query_len >= every n and max_context_len >= every L (host bounds that size
  * the grid).  A sequence with n == 1 is a decode step and runs through
  * pa_decode's kernels (with their partitioning) unless flags holds
- * PA_MULTI_QUERY_TILES_ONLY (any other flag bit: PA_ERR_UNSUPPORTED).
+ * PA_MULTI_QUERY_TILES_ONLY (other flag bits than the two above:
+ * PA_ERR_UNSUPPORTED).
+ * Streams: when a batch has decode rows and longer chunks, the decode kernels
+ * (bound by the cache reads) run beside the multi-query kernels (bound by the
+ * matrix cores) on a side stream of the library's: one per device, created
+ * on the device's first such call (a caller that captures a graph makes one
+ * call before capturing), default priority, kept until the process ends.  It
+ * is forked from `stream` and joined back to it with events, so the call is
+ * ordered on `stream` like a single launch.  Calls on one device take turns
+ * on the side stream (a lock); PA_MULTI_QUERY_ONE_STREAM keeps every launch on
+ * `stream`.
  * partition_tokens (0 = default
  * 2048; else a positive multiple of block_size): a sequence with n > 1 whose
  * n * G rows fit in 64 has its context cut into partitions of this many

@@ -23,6 +23,7 @@ PA_BF16 = 1
 PA_FP8_E4M3 = 2
 PA_DECODE_SHARED_PAGES = 1
 PA_MULTI_QUERY_TILES_ONLY = 1
+PA_MULTI_QUERY_ONE_STREAM = 2
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
           -4: "PA_ERR_UNSUPPORTED", -5: "PA_ERR_ALIGN", -6: "PA_ERR_WORKSPACE",
           -7: "PA_ERR_LAUNCH", -8: "PA_ERR_VALUE"}
@@ -306,13 +307,15 @@ def pa_multi_query(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_
                    query_start: torch.Tensor, scale: float, max_context_len: int,
                    max_query_len: int, partition_tokens: int = 0,
                    workspace: Optional[torch.Tensor] = None, stream=None, k_scale: float = 1.0,
-                   v_scale: float = 1.0, tiles_only: bool = False) -> None:
+                   v_scale: float = 1.0, tiles_only: bool = False,
+                   one_stream: bool = False) -> None:
     """Causal attention of each sequence's new query tokens over the paged caches.
 
     q, out [T, H, D] (bf16) hold sequence s's queries in rows
     query_start[s] .. query_start[s + 1] - 1 (int32 device tensor [S + 1]); they
     are the last positions of its context_lens[s] cached tokens.  ``tiles_only``
-    sets PA_MULTI_QUERY_TILES_ONLY (no decode launch for single-query sequences).
+    sets PA_MULTI_QUERY_TILES_ONLY (no decode launch for single-query sequences),
+    ``one_stream`` PA_MULTI_QUERY_ONE_STREAM (no side stream for the decode rows).
     """
     for n, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
                  ("block_tables", block_tables), ("context_lens", context_lens),
@@ -339,7 +342,9 @@ def pa_multi_query(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_
                             block_tables.shape[1], _ptr(context_lens), _ptr(query_start), s, t,
                             int(max_query_len), h, hkv, d, bs, nb, int(max_context_len),
                             float(scale), code, ccode, float(k_scale), float(v_scale),
-                            int(partition_tokens), PA_MULTI_QUERY_TILES_ONLY if tiles_only else 0,
+                            int(partition_tokens),
+                            (PA_MULTI_QUERY_TILES_ONLY if tiles_only else 0)
+                            | (PA_MULTI_QUERY_ONE_STREAM if one_stream else 0),
                             _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "pa_multi_query")
 

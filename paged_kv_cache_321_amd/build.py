@@ -24,6 +24,10 @@ SOURCES = ["pa_api.cpp", "pa_cache.hip", "pa_decode.hip", "pa_decode_valu.hip", 
 
 # Packed-fp32 VALU ops are switched off for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# The multi-query kernel keeps its MFMA accumulators in ordinary VGPRs: with
+# the accumulation registers the compiler copies them out and back around
+# every loop iteration.
+SOURCE_FLAGS = {"pa_multi_query.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
                 "-I", INCLUDE, "-I", CSRC]
 
@@ -45,7 +49,7 @@ def _run(cmd):
 def _compile_cmd(cc: str, src: str, obj: str):
     cmd = [cc, *COMMON_FLAGS]
     if src.endswith(".hip"):
-        cmd += ["-x", "hip", *DEVICE_FLAGS]
+        cmd += ["-x", "hip", *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, [])]
     return cmd + ["-c", os.path.join(CSRC, src), "-o", obj]
 
 

@@ -8,6 +8,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <memory>
+#include <mutex>
+
 #include "pa_internal.h"
 
 namespace {
@@ -218,6 +221,38 @@ size_t pa_decode_shared_prefix_workspace_size(int num_seqs, int num_heads, int n
 
 namespace {
 
+// The side stream of pa_multi_query on the current device, with its fork and
+// join events; created on first use (null if HIP cannot create it, and the
+// call then keeps to the caller's stream).  Never destroyed: it lives as long
+// as the process.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr;
+  hipEvent_t join = nullptr;
+  std::mutex mu;  // one fork / launch / join sequence at a time
+};
+
+SideStream* side_stream() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex create_mu;
+  static std::unique_ptr<SideStream> per_device[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> hold(create_mu);
+  if (!per_device[dev]) {
+    auto s = std::make_unique<SideStream>();
+    if (hipStreamCreateWithFlags(&s->stream, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&s->fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&s->join, hipEventDisableTiming) != hipSuccess) {
+      if (s->fork) (void)hipEventDestroy(s->fork);
+      (void)hipStreamDestroy(s->stream);
+      return nullptr;
+    }
+    per_device[dev] = std::move(s);
+  }
+  return per_device[dev].get();
+}
+
 // Both decode entry points: validation, workspace carving, launch.  The
 // shared-prefix form passes its two per-sequence arrays (non-null).
 int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -376,8 +411,9 @@ int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_
                    int max_context_len, float scale, int dtype, int cache_dtype, float k_scale,
                    float v_scale, int partition_tokens, int flags, void* workspace,
                    size_t workspace_bytes, void* stream) {
-  if (flags & ~PA_MULTI_QUERY_TILES_ONLY) return PA_ERR_UNSUPPORTED;
+  if (flags & ~(PA_MULTI_QUERY_TILES_ONLY | PA_MULTI_QUERY_ONE_STREAM)) return PA_ERR_UNSUPPORTED;
   const bool tiles_only = (flags & PA_MULTI_QUERY_TILES_ONLY) != 0;
+  const bool one_stream = (flags & PA_MULTI_QUERY_ONE_STREAM) != 0;
   const MultiQuerySizes z = multi_query_sizes(num_seqs, num_query_tokens, num_heads, num_kv_heads,
                                               head_dim, block_size, max_context_len, dtype,
                                               cache_dtype, partition_tokens);
@@ -474,9 +510,25 @@ int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_
   d.prefix_parts = 0;
   d.tail_parts = 1;
   d.stream = a.stream;
-  if (pa::launch_decode(d) != hipSuccess) return PA_ERR_LAUNCH;
-  if (max_query_len < 2) return PA_OK;  // no sequence has more than one query
-  return pa::launch_multi_query(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+  if (max_query_len < 2)  // no sequence has more than one query
+    return pa::launch_decode(d) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+  SideStream* side = one_stream ? nullptr : side_stream();
+  if (!side) {
+    if (pa::launch_decode(d) != hipSuccess) return PA_ERR_LAUNCH;
+    return pa::launch_multi_query(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+  }
+  // Fork: the multi-query kernels (long workgroups, matrix-core bound) go
+  // first on the caller's stream, the decode kernels (cache-read bound) on
+  // the side stream; the join makes `stream` wait for both.
+  std::lock_guard<std::mutex> hold(side->mu);
+  if (hipEventRecord(side->fork, a.stream) != hipSuccess) return PA_ERR_LAUNCH;
+  if (hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess) return PA_ERR_LAUNCH;
+  d.stream = side->stream;
+  const bool mq_ok = pa::launch_multi_query(a) == hipSuccess;
+  const bool dec_ok = pa::launch_decode(d) == hipSuccess;
+  const bool join_ok = hipEventRecord(side->join, side->stream) == hipSuccess &&
+                       hipStreamWaitEvent(a.stream, side->join, 0) == hipSuccess;
+  return mq_ok && dec_ok && join_ok ? PA_OK : PA_ERR_LAUNCH;
 }
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -67,6 +67,42 @@ __device__ __forceinline__ s16x4_t vt4(const unsigned char* page, int l16, int t
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)a);
 }
 
+// 16 bytes per lane from global memory straight into LDS with gfx950's
+// global_load_lds_dwordx4: lane i writes lds_base + 16 i (checked on the
+// hardware), lds_base being wave-uniform.  The load counts in vmcnt like any
+// vector load.  It is issued from assembly so that the compiler, which cannot
+// tell which LDS bytes such a load writes, does not put a full vmcnt wait
+// before every later LDS read; callers order it with vm_wait and
+// block_barrier.  M0 is saved and restored around it.
+template <bool kNonTemporal>
+__device__ __forceinline__ void load_lds16(const void* g, uint32_t lds_base) {
+  uint32_t saved;
+  if constexpr (kNonTemporal)
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(g), "s"(lds_base) : "memory");
+  else
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(g), "s"(lds_base) : "memory");
+}
+
+// LDS byte address of a pointer into __shared__ memory, made wave-uniform.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p)));
+}
+
+// Waits until at most N of this wave's vector memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier after this wave's LDS reads have completed; no vmcnt
+// wait (loads still in flight into other LDS buffers stay in flight).
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 }  // namespace pa
 
 #endif  // PA_MFMA_H_

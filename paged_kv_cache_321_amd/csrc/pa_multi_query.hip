@@ -31,6 +31,8 @@
 // rule depends on the sequence alone, so its result does not depend on the
 // rest of the batch.
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_mfma.h"
 
@@ -117,8 +119,22 @@ __device__ __forceinline__ MqBlock mq_block(const MultiQueryParams& p, int s, in
   return b;
 }
 
+// Max over the four lanes l, l ^ 16, l ^ 32, l ^ 48 that hold one column of an
+// MFMA result: v_permlane32_swap exchanges the wave's 32-lane halves and
+// v_permlane16_swap the odd and even 16-lane rows (gfx950), both in the VALU.
+__device__ __forceinline__ float column_max(float x) {
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Sixteen zero bytes: the source of the LDS rows of tokens past a partition's
+// end, so that no unread cache bytes (possibly NaN) reach the PV product.
+__device__ const uint4 kZeroChunk = {0u, 0u, 0u, 0u};
+
 template <typename TC, int D, int BS, int G>
-__global__ __launch_bounds__(kMqWaves * 64) void multi_query_kernel(MultiQueryParams p) {
+__global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void multi_query_kernel(MultiQueryParams p) {
   constexpr bool kFp8 = sizeof(TC) == 1;
   constexpr int PPS = kStepTokens / BS;      // pages per step
   constexpr int NC = D / 32;                 // 32-wide steps of the QK contraction
@@ -130,7 +146,14 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_kernel(MultiQueryPa
   constexpr int PER_T = (CHUNKS + kMqWaves * 64 - 1) / (kMqWaves * 64);
   constexpr int NTT = kStepTokens / 16;      // 16-token tiles per step
   constexpr int TILEB = kStepTokens * ROWB;  // bytes of one step's K (or V) in LDS
+  // bf16 caches: a ring of three (K, V) stages filled by direct LDS loads two
+  // steps ahead; E4M3 caches: one stage, widened through registers.
+  constexpr int NSTAGE = kFp8 ? 1 : 3;
+  constexpr int WINDOW = 256;                // page ids held in registers (4 per lane)
   static_assert(kStepTokens % BS == 0 && kStepTokens % 32 == 0 && NCH >= 8, "tile shape");
+  static_assert(kFp8 || CHUNKS % (kMqWaves * 64) == 0, "a bf16 step is whole wave loads");
+  static_assert(CHUNKS % 64 == 0 && 64 / CCH <= BS, "a wave's chunks of a step lie in one page");
+  static_assert(WINDOW % PPS == 0, "a step's pages lie in one window");
 
   const int kvh = blockIdx.x % p.num_kv_heads;
   const int item = blockIdx.x / p.num_kv_heads;
@@ -144,7 +167,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_kernel(MultiQueryPa
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
 
@@ -174,6 +197,10 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_kernel(MultiQueryPa
     for (int c = 0; c < NC; ++c) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
       if (row_ok) v = *reinterpret_cast<const uint4*>(qp + 32 * c + 8 * g4);
+      // Consumed here, so that the compiler waits for the load before the
+      // step loop rather than at its first use inside it, where its wait
+      // would also drain the page loads in flight.
+      asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
       qb[c] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -184,46 +211,109 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_kernel(MultiQueryPa
   float m_run = -FLT_MAX;  // running max of the row (same in its 4 lanes)
   float l_run = 0.f;       // this lane's share of the running sum
 
-  __shared__ __attribute__((aligned(16))) unsigned char kt[TILEB];
-  __shared__ __attribute__((aligned(16))) unsigned char vt[TILEB];
+  // Stage i: K tile at ring + 2 i TILEB, V tile right after it.  K rows hold
+  // 16-byte chunk ch at position ch ^ (token % NCH); V rows are in the
+  // transposed-read layout (position ch ^ swz(token)).
+  __shared__ __attribute__((aligned(16))) unsigned char ring[NSTAGE * 2 * TILEB];
 
   const TC* kc = static_cast<const TC*>(p.k_cache) + (int64_t)kvh * BS * D;
   const TC* vc = static_cast<const TC*>(p.v_cache) + (int64_t)kvh * BS * D;
   const int32_t* table = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
 
-  // Physical ids of pages pg0 + base .. + 63, one per lane (ids outside the
-  // pool become 0 and mark the block bad).  Every wave holds the same ids.
-  int my_id = 0;
+  // Physical ids of pages pg0 + base .. + WINDOW - 1: lane i holds page
+  // base + 64 j + i in ids[j] (ids outside the pool become 0 and mark the
+  // block bad).  Every wave holds the same ids.
+  int ids[WINDOW / 64];
+  int ids_base = 0;
   bool ids_bad = false;
   auto load_ids = [&](int base) {
-    int id = 0;
+    // Entries past the partition's pages are read at its last page (npg > 0
+    // here), so the four loads go out together; they are then dropped.
+    int raw[WINDOW / 64];
+#pragma unroll
+    for (int j = 0; j < WINDOW / 64; ++j) raw[j] = table[pg0 + min(base + 64 * j + lane, npg - 1)];
     bool badid = false;
-    if (base + lane < npg) {
-      id = table[pg0 + base + lane];
-      badid = id < 0 || id >= p.num_blocks;
-      if (badid) id = 0;
+#pragma unroll
+    for (int j = 0; j < WINDOW / 64; ++j) {
+      const bool live = base + 64 * j + lane < npg;
+      const bool out_of_pool = raw[j] < 0 || raw[j] >= p.num_blocks;
+      badid = badid || (live && out_of_pool);
+      ids[j] = live && !out_of_pool ? raw[j] : 0;
     }
-    my_id = id;
+    ids_base = base;
     ids_bad = ids_bad || __any(badid);
   };
+  // Physical id of page pg of the partition (pg wave-uniform, inside the
+  // window).  Called with every lane active: the four reads take lane k % 64
+  // of registers written by the whole wave, and the choice among them is
+  // scalar (a per-lane select under a partial mask would leave that lane
+  // unwritten).
+  auto page_id = [&](int pg) -> int64_t {
+    const int k = __builtin_amdgcn_readfirstlane(pg - ids_base);
+    const int l = k & 63;
+    const int a0 = __builtin_amdgcn_readlane(ids[0], l);
+    const int a1 = __builtin_amdgcn_readlane(ids[1], l);
+    const int a2 = __builtin_amdgcn_readlane(ids[2], l);
+    const int a3 = __builtin_amdgcn_readlane(ids[3], l);
+    const int j = k >> 6;
+    return j == 0 ? a0 : j == 1 ? a1 : j == 2 ? a2 : a3;
+  };
+  static_assert(WINDOW / 64 == 4, "page_id selects among four registers");
 
-  // One step's K and V chunks, PER_T per thread: chunk c is token c / CCH of
-  // the step, 16 bytes at chunk c % CCH of that token's cache row.  Pages
-  // read by one workgroup only (a sequence of one row block) stream past the
-  // caches; the row blocks of a longer chunk share theirs through L2 / MALL.
+  // Pages read by one workgroup only (a sequence of one row block) stream
+  // past the caches; the row blocks of a longer chunk share theirs through
+  // L2 / MALL.
   const bool stream_pages = b.nrb == 1;
-  uint4 kreg[PER_T], vreg[PER_T];
+
+  // bf16: step st's K and V go straight from the cache into stage `stage`.
+  // Load u of wave w fills 64 consecutive 16-byte LDS slots, 64 / NCH whole
+  // rows of one page; each lane fetches the chunk its slot holds.
+  auto dma_step = [&](int st, int stage) {
+    unsigned char* kbuf = ring + stage * 2 * TILEB;
+#pragma unroll
+    for (int u = 0; u < PER_T; ++u) {
+      const int slot0 = (u * kMqWaves + wave) * 64;  // wave-uniform
+      const int row = (slot0 + lane) / NCH;
+      const int pos = (slot0 + lane) % NCH;
+      const int t = tok0 + st * kStepTokens + row;
+      // The page (past the partition's pages its id is 0) is looked up by the
+      // whole wave; lanes whose token lies past the partition end read zeros.
+      const int64_t base = page_id(st * PPS + slot0 / NCH / BS) * p.block_stride + (row % BS) * D;
+      const TC* kp = reinterpret_cast<const TC*>(&kZeroChunk);
+      const TC* vp = kp;
+      if (t < tok1) {
+        kp = kc + base + (pos ^ (row % NCH)) * 8;
+        vp = vc + base + (pos ^ swz(row)) * 8;
+      }
+      const uint32_t kdst = lds_address(kbuf + slot0 * 16);
+      const uint32_t vdst = lds_address(kbuf + TILEB + slot0 * 16);
+      if (stream_pages) {
+        load_lds16<true>(kp, kdst);
+        load_lds16<true>(vp, vdst);
+      } else {
+        load_lds16<false>(kp, kdst);
+        load_lds16<false>(vp, vdst);
+      }
+    }
+  };
+
+  // E4M3: one step's chunks, PER_T per thread (chunk c is token c / CCH of the
+  // step, 16 bytes at chunk c % CCH of its cache row), loaded into registers
+  // and widened into the single stage.  V rows past the partition end are
+  // zero.
+  uint4 kreg[kFp8 ? PER_T : 1], vreg[kFp8 ? PER_T : 1];
   auto load_step = [&](int st) {
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
       const int c = tid + u * kMqWaves * 64;
       const int tok = c / CCH;
       const int pg = st * PPS + tok / BS;  // page of the partition
+      // The page is the same across each wave (a wave's chunks lie in one
+      // page, CHUNKS is whole waves); looked up by the whole wave.
+      const int64_t phys = page_id(pg);
       kreg[u] = vreg[u] = make_uint4(0u, 0u, 0u, 0u);
       if (c < CHUNKS && pg < npg) {
-        // The page is the same across each wave (a wave's chunks lie in one page).
-        const int64_t phys = __builtin_amdgcn_readlane(my_id, __builtin_amdgcn_readfirstlane(pg) & 63);
-        const int64_t off = phys * p.block_stride + (tok % BS) * D + (c % CCH) * (16 / (int)sizeof(TC));
+        const int64_t off = phys * p.block_stride + (tok % BS) * D + (c % CCH) * 16;
         if (stream_pages) {
           kreg[u] = load_page16<true>(kc + off);
           vreg[u] = load_page16<true>(vc + off);
@@ -234,10 +324,9 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_kernel(MultiQueryPa
       }
     }
   };
-  // K rows at chunk ch ^ (token % NCH); V rows in the transposed-read layout.
-  // V rows past the partition end are zero, so nothing unread can reach the
-  // PV product (K rows there are masked out of the softmax).
   auto stage_step = [&](int st) {
+    unsigned char* kt = ring;
+    unsigned char* vt = ring + TILEB;
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
       const int c = tid + u * kMqWaves * 64;
@@ -245,23 +334,26 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_kernel(MultiQueryPa
       const int tok = c / CCH;
       const int ch = c % CCH;
       const bool keep = tok0 + (st * PPS) * BS + tok < tok1;
-      if constexpr (kFp8) {
-        const uint4 k0 = fp8x8_to_bf16x8(kreg[u].x, kreg[u].y), k1 = fp8x8_to_bf16x8(kreg[u].z, kreg[u].w);
-        uint4 v0 = fp8x8_to_bf16x8(vreg[u].x, vreg[u].y), v1 = fp8x8_to_bf16x8(vreg[u].z, vreg[u].w);
-        if (!keep) v0 = v1 = make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4*>(kt + tok * ROWB + (((2 * ch) ^ (tok % NCH)) << 4)) = k0;
-        *reinterpret_cast<uint4*>(kt + tok * ROWB + (((2 * ch + 1) ^ (tok % NCH)) << 4)) = k1;
-        *reinterpret_cast<uint4*>(vt + tok * ROWB + (((2 * ch) ^ swz(tok)) << 4)) = v0;
-        *reinterpret_cast<uint4*>(vt + tok * ROWB + (((2 * ch + 1) ^ swz(tok)) << 4)) = v1;
-      } else {
-        const uint4 v = keep ? vreg[u] : make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4*>(kt + tok * ROWB + ((ch ^ (tok % NCH)) << 4)) = kreg[u];
-        *reinterpret_cast<uint4*>(vt + tok * ROWB + ((ch ^ swz(tok)) << 4)) = v;
-      }
+      const uint4 k0 = fp8x8_to_bf16x8(kreg[u].x, kreg[u].y), k1 = fp8x8_to_bf16x8(kreg[u].z, kreg[u].w);
+      uint4 v0 = fp8x8_to_bf16x8(vreg[u].x, vreg[u].y), v1 = fp8x8_to_bf16x8(vreg[u].z, vreg[u].w);
+      if (!keep) v0 = v1 = make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(kt + tok * ROWB + (((2 * ch) ^ (tok % NCH)) << 4)) = k0;
+      *reinterpret_cast<uint4*>(kt + tok * ROWB + (((2 * ch + 1) ^ (tok % NCH)) << 4)) = k1;
+      *reinterpret_cast<uint4*>(vt + tok * ROWB + (((2 * ch) ^ swz(tok)) << 4)) = v0;
+      *reinterpret_cast<uint4*>(vt + tok * ROWB + (((2 * ch + 1) ^ swz(tok)) << 4)) = v1;
     }
   };
 
-  auto compute_step = [&](int st) {
+  // A step wholly below block_full_end needs no mask: every row of the
+  // block sees all of its tokens.  Such steps also take the row max of the
+  // raw scores and fold the scale into the exponent, which needs a positive
+  // scale.
+  const int block_first_qi = b.rb * kRowsPerBlock / G;
+  const int block_full_end = min(tok1, b.ctx - b.qlen + block_first_qi + 1);
+
+  auto compute_step = [&](int st, const unsigned char* kt, auto full_tag) {
+    constexpr bool kFull = decltype(full_tag)::value;
+    const unsigned char* vt = kt + TILEB;
     const int t_base = tok0 + st * kStepTokens;
     // S^T for the step's 16-token tiles.
     f32x4_t sc[NTT];
@@ -277,18 +369,27 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_kernel(MultiQueryPa
     }
     // Causal mask and online softmax: lane holds tokens 16 tt + 4 g4 + j.
     float sv[NTT][4];
-    float mx = m_run;
+    float mx;
+    if constexpr (kFull) {
+      float raw = sc[0][0];
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt)
+      for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = t_base + 16 * tt + 4 * g4 + j;
-        const bool valid = t < tok1 && t <= last_seen;
-        sv[tt][j] = valid ? sc[tt][j] * p.scale_log2e : -__builtin_inff();
-        mx = fmaxf(mx, sv[tt][j]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+        for (int j = 0; j < 4; ++j) raw = fmaxf(raw, sc[tt][j]);
+      mx = fmaxf(m_run, column_max(raw) * p.scale_log2e);
+    } else {
+      mx = m_run;
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = t_base + 16 * tt + 4 * g4 + j;
+          const bool valid = t < tok1 && t <= last_seen;
+          sv[tt][j] = valid ? sc[tt][j] * p.scale_log2e : -__builtin_inff();
+          mx = fmaxf(mx, sv[tt][j]);
+        }
+      mx = column_max(mx);
+    }
     if (__any(mx > m_run + kRescaleLog2)) {
       const float alpha = fast_exp2(m_run - mx);
       m_run = mx;
@@ -301,7 +402,10 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_kernel(MultiQueryPa
     for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        sv[tt][j] = fast_exp2(sv[tt][j] - m_run);
+        if constexpr (kFull)
+          sv[tt][j] = fast_exp2(fmaf(sc[tt][j], p.scale_log2e, -m_run));
+        else
+          sv[tt][j] = fast_exp2(sv[tt][j] - m_run);
         ps += sv[tt][j];
       }
     l_run += ps;
@@ -325,20 +429,56 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_kernel(MultiQueryPa
     }
   };
 
-  // Steps: the next step's chunks are loaded into registers while the current
-  // one is computed from LDS; two barriers per step hand the LDS tiles over.
+  // Steps.  The unmasked steps come first and run as a loop of their own;
+  // every wave passes the same barriers, so the split point is the
+  // workgroup's, set by its first row.
+  const int nfull = p.scale_log2e > 0.f ? min(nsteps, max(0, (block_full_end - tok0) / kStepTokens)) : 0;
   if (nsteps > 0) {
     load_ids(0);
-    load_step(0);
-    for (int st = 0; st < nsteps; ++st) {
-      __syncthreads();  // every wave is done with the previous step's tiles
-      stage_step(st);
-      __syncthreads();
-      if (st + 1 < nsteps) {
-        if (((st + 1) * PPS & 63) == 0) load_ids((st + 1) * PPS);
-        load_step(st + 1);
-      }
-      if (wave_rows) compute_step(st);
+    if constexpr (kFp8) {
+      // Registers hold the next step while the current one is computed from
+      // LDS; two barriers per step hand the single stage over.
+      load_step(0);
+      auto run_steps = [&](int st0, int st1, auto full_tag) {
+        for (int st = st0; st < st1; ++st) {
+          __syncthreads();  // every wave is done with the previous step's tiles
+          stage_step(st);
+          __syncthreads();
+          if (st + 1 < nsteps) {
+            if ((st + 1) * PPS - ids_base == WINDOW) load_ids((st + 1) * PPS);
+            load_step(st + 1);
+          }
+          if (wave_rows) compute_step(st, ring, full_tag);
+        }
+      };
+      run_steps(0, nfull, std::true_type{});
+      run_steps(nfull, nsteps, std::false_type{});
+    } else {
+      // Step st + 2 is loaded while step st is computed.  At the top of step
+      // st the wave waits until only step st + 1's loads are outstanding;
+      // the barrier then publishes step st's tiles and frees the stage of
+      // step st - 1, which the loads of step st + 2 reuse.
+      constexpr int kLoadsPerStep = 2 * PER_T;
+      dma_step(0, 0);
+      if (nsteps > 1) dma_step(1, 1);
+      auto run_steps = [&](int st0, int st1, auto full_tag) {
+        int stage = st0 % 3;
+        for (int st = st0; st < st1; ++st) {
+          if (st + 1 < nsteps)
+            vm_wait<kLoadsPerStep>();
+          else
+            vm_wait<0>();
+          block_barrier();
+          if (st + 2 < nsteps) {
+            if ((st + 2) * PPS - ids_base == WINDOW) load_ids((st + 2) * PPS);
+            dma_step(st + 2, stage == 0 ? 2 : stage - 1);
+          }
+          if (wave_rows) compute_step(st, ring + stage * 2 * TILEB, full_tag);
+          stage = stage == 2 ? 0 : stage + 1;
+        }
+      };
+      run_steps(0, nfull, std::true_type{});
+      run_steps(nfull, nsteps, std::false_type{});
     }
   }
   const bool bad = b.bad || ids_bad;

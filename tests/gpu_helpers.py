@@ -76,7 +76,7 @@ def gpu_step_shared(x: Inputs, t: dict | None = None, partition_tokens: int = 0,
 
 
 def gpu_mq_step(x: Inputs, t: dict | None = None, partition_tokens: int = 0, max_query_len=None,
-                out: torch.Tensor | None = None, tiles_only: bool = False):
+                out: torch.Tensor | None = None, tiles_only: bool = False, one_stream: bool = False):
     """reshape_and_cache of the new tokens -> multi-query attention; returns (out, t)."""
     t = on_device(x) if t is None else t
     if "query_start" not in t:
@@ -89,7 +89,7 @@ def gpu_mq_step(x: Inputs, t: dict | None = None, partition_tokens: int = 0, max
     binding.pa_multi_query(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
                            t["context_lens"], t["query_start"], x.scale, x.max_context_len, mq,
                            partition_tokens=partition_tokens, k_scale=x.k_scale, v_scale=x.v_scale,
-                           tiles_only=tiles_only)
+                           tiles_only=tiles_only, one_stream=one_stream)
     torch.cuda.synchronize()
     return out, t
 

@@ -230,8 +230,11 @@ def multi_query(**kw):
     (dict(S=0), OK),                     # nothing to launch
     (dict(T=0, q=None, out=None), OK),
     (dict(mq=0), OK),
-    (dict(flags=2), UNSUP),
+    (dict(flags=4), UNSUP),              # unknown flag bit
+    (dict(flags=-1), UNSUP),
     (dict(flags=1, S=0), OK),
+    (dict(flags=2, S=0), OK),
+    (dict(flags=3, S=0), OK),
 ])
 def test_multi_query_validation(kw, code):
     assert multi_query(**kw) == code
