@@ -240,12 +240,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
         uint4 a = fp8x8_to_bf16x8(vr[n].x, vr[n].y);
         uint4 b = fp8x8_to_bf16x8(vr[n].z, vr[n].w);
         if (!keep) a = b = make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4*>(vbuf + row * ROWB + (((2 * v_ch) ^ swz(row)) << 4)) = a;
-        *reinterpret_cast<uint4*>(vbuf + row * ROWB + (((2 * v_ch + 1) ^ swz(row)) << 4)) = b;
+        *reinterpret_cast<uint4*>(vbuf + row * ROWB + (((2 * v_ch) ^ swz<ROWB>(row)) << 4)) = a;
+        *reinterpret_cast<uint4*>(vbuf + row * ROWB + (((2 * v_ch + 1) ^ swz<ROWB>(row)) << 4)) = b;
       } else {
         uint4 v = vr[n];
         if (!keep) v = make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4*>(vbuf + row * ROWB + ((v_ch ^ swz(row)) << 4)) = v;
+        *reinterpret_cast<uint4*>(vbuf + row * ROWB + ((v_ch ^ swz<ROWB>(row)) << 4)) = v;
       }
     }
     wave_lds_fence();

@@ -48,11 +48,20 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
                     fp8x2_to_bf16x2<true>(hi));
 }
 
-// V page in LDS, read back transposed.  16-byte chunk c of row `row` is
-// stored at chunk c ^ swz(row).  One transposed read has each 16-lane group
-// read 4 consecutive rows at the same columns; the swizzle puts those 4 rows'
-// 32-byte segments 2 chunks apart, in distinct banks.
-__device__ __forceinline__ int swz(int row) { return 2 * (row & 3); }
+// V page in LDS (rows of ROWB = 128 or 256 bytes), read back transposed.
+// 16-byte chunk c of row `row` is stored at chunk c ^ swz<ROWB>(row).  In a
+// transposed read each 16-lane group reads 4 consecutive rows, and two such
+// groups 8 consecutive rows, at the same 32-byte column segment.  The
+// swizzle moves the segment by an even number of chunks so that, whether the
+// LDS serves 16 lanes over 32 banks or 32 lanes over 64 banks (4-byte banks)
+// per cycle, the rows served together hit distinct banks: 256-byte rows
+// (a whole 64-bank line) take 8 segment positions, 128-byte rows (half a
+// line, alternating halves) 4 positions spread over both parities.
+template <int ROWB>
+__device__ __forceinline__ int swz(int row) {
+  static_assert(ROWB == 128 || ROWB == 256, "128- or 256-byte rows");
+  return ROWB == 256 ? 2 * (row & 7) : 2 * ((row & 3) ^ ((row >> 2) & 1));
+}
 
 // Four k slots of the V^T A operand from a bf16 page of ROWB-byte rows, via
 // gfx950's ds_read_b64_tr_b16 (checked on the hardware): in each group of 16
@@ -63,7 +72,7 @@ template <int ROWB>
 __device__ __forceinline__ s16x4_t vt4(const unsigned char* page, int l16, int tb, int d0) {
   const int t = tb + (l16 >> 2);
   const int d = d0 + 4 * (l16 & 3);
-  const unsigned char* a = page + t * ROWB + (((d >> 3) ^ swz(t)) << 4) + ((d & 7) << 1);
+  const unsigned char* a = page + t * ROWB + (((d >> 3) ^ swz<ROWB>(t)) << 4) + ((d & 7) << 1);
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)a);
 }
 

@@ -119,6 +119,18 @@ __device__ __forceinline__ MqBlock mq_block(const MultiQueryParams& p, int s, in
   return b;
 }
 
+// K rows (ROWB bytes) in LDS: 16-byte chunk c of token `tok` is stored at
+// chunk c ^ kswz<ROWB>(tok).  One A-operand read has 16 lanes read 16
+// consecutive tokens at the same logical chunk; the swizzle gives them
+// distinct banks whether 8 or 16 lanes (32 or 64 4-byte banks) are served
+// per cycle: 256-byte rows take 16 chunk positions, 128-byte rows (alternating
+// bank halves) 8 positions distinct over each 8 tokens and each parity.
+template <int ROWB>
+__device__ __forceinline__ int kswz(int tok) {
+  static_assert(ROWB == 128 || ROWB == 256, "128- or 256-byte rows");
+  return ROWB == 256 ? (tok & 15) : ((tok & 7) ^ ((tok >> 3) & 1));
+}
+
 // Max over the four lanes l, l ^ 16, l ^ 32, l ^ 48 that hold one column of an
 // MFMA result: v_permlane32_swap exchanges the wave's 32-lane halves and
 // v_permlane16_swap the odd and even 16-lane rows (gfx950), both in the VALU.
@@ -212,8 +224,8 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   float l_run = 0.f;       // this lane's share of the running sum
 
   // Stage i: K tile at ring + 2 i TILEB, V tile right after it.  K rows hold
-  // 16-byte chunk ch at position ch ^ (token % NCH); V rows are in the
-  // transposed-read layout (position ch ^ swz(token)).
+  // 16-byte chunk ch at position ch ^ kswz<ROWB>(token); V rows are in the
+  // transposed-read layout (position ch ^ swz<ROWB>(token)).
   __shared__ __attribute__((aligned(16))) unsigned char ring[NSTAGE * 2 * TILEB];
 
   const TC* kc = static_cast<const TC*>(p.k_cache) + (int64_t)kvh * BS * D;
@@ -282,8 +294,8 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
       const TC* kp = reinterpret_cast<const TC*>(&kZeroChunk);
       const TC* vp = kp;
       if (t < tok1) {
-        kp = kc + base + (pos ^ (row % NCH)) * 8;
-        vp = vc + base + (pos ^ swz(row)) * 8;
+        kp = kc + base + (pos ^ kswz<ROWB>(row)) * 8;
+        vp = vc + base + (pos ^ swz<ROWB>(row)) * 8;
       }
       const uint32_t kdst = lds_address(kbuf + slot0 * 16);
       const uint32_t vdst = lds_address(kbuf + TILEB + slot0 * 16);
@@ -337,10 +349,10 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
       const uint4 k0 = fp8x8_to_bf16x8(kreg[u].x, kreg[u].y), k1 = fp8x8_to_bf16x8(kreg[u].z, kreg[u].w);
       uint4 v0 = fp8x8_to_bf16x8(vreg[u].x, vreg[u].y), v1 = fp8x8_to_bf16x8(vreg[u].z, vreg[u].w);
       if (!keep) v0 = v1 = make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4*>(kt + tok * ROWB + (((2 * ch) ^ (tok % NCH)) << 4)) = k0;
-      *reinterpret_cast<uint4*>(kt + tok * ROWB + (((2 * ch + 1) ^ (tok % NCH)) << 4)) = k1;
-      *reinterpret_cast<uint4*>(vt + tok * ROWB + (((2 * ch) ^ swz(tok)) << 4)) = v0;
-      *reinterpret_cast<uint4*>(vt + tok * ROWB + (((2 * ch + 1) ^ swz(tok)) << 4)) = v1;
+      *reinterpret_cast<uint4*>(kt + tok * ROWB + (((2 * ch) ^ kswz<ROWB>(tok)) << 4)) = k0;
+      *reinterpret_cast<uint4*>(kt + tok * ROWB + (((2 * ch + 1) ^ kswz<ROWB>(tok)) << 4)) = k1;
+      *reinterpret_cast<uint4*>(vt + tok * ROWB + (((2 * ch) ^ swz<ROWB>(tok)) << 4)) = v0;
+      *reinterpret_cast<uint4*>(vt + tok * ROWB + (((2 * ch + 1) ^ swz<ROWB>(tok)) << 4)) = v1;
     }
   };
 
@@ -363,7 +375,7 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
       const int tok = 16 * tt + l16;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(kt + tok * ROWB + (((4 * c + g4) ^ (tok % NCH)) << 4));
+        const uint4 ka = *reinterpret_cast<const uint4*>(kt + tok * ROWB + (((4 * c + g4) ^ kswz<ROWB>(tok)) << 4));
         sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qb[c], sc[tt], 0, 0, 0);
       }
     }
