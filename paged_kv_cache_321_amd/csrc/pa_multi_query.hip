@@ -145,7 +145,7 @@ __device__ __forceinline__ float column_max(float x) {
 // end, so that no unread cache bytes (possibly NaN) reach the PV product.
 __device__ const uint4 kZeroChunk = {0u, 0u, 0u, 0u};
 
-template <typename TC, int D, int BS, int G>
+template <typename TC, int D, int BS, int G, int STAGES>
 __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void multi_query_kernel(MultiQueryParams p) {
   constexpr bool kFp8 = sizeof(TC) == 1;
   constexpr int PPS = kStepTokens / BS;      // pages per step
@@ -158,14 +158,16 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   constexpr int PER_T = (CHUNKS + kMqWaves * 64 - 1) / (kMqWaves * 64);
   constexpr int NTT = kStepTokens / 16;      // 16-token tiles per step
   constexpr int TILEB = kStepTokens * ROWB;  // bytes of one step's K (or V) in LDS
-  // bf16 caches: a ring of three (K, V) stages filled by direct LDS loads two
-  // steps ahead; E4M3 caches: one stage, widened through registers.
-  constexpr int NSTAGE = kFp8 ? 1 : 3;
+  // bf16 caches: a ring of STAGES (K, V) stages filled by direct LDS loads
+  // STAGES - 1 steps ahead; E4M3 caches: one stage, widened through
+  // registers.
+  constexpr int NSTAGE = kFp8 ? 1 : STAGES;
   constexpr int WINDOW = 256;                // page ids held in registers (4 per lane)
   static_assert(kStepTokens % BS == 0 && kStepTokens % 32 == 0 && NCH >= 8, "tile shape");
   static_assert(kFp8 || CHUNKS % (kMqWaves * 64) == 0, "a bf16 step is whole wave loads");
   static_assert(CHUNKS % 64 == 0 && 64 / CCH <= BS, "a wave's chunks of a step lie in one page");
   static_assert(WINDOW % PPS == 0, "a step's pages lie in one window");
+  static_assert(kFp8 || (NSTAGE >= 2 && (NSTAGE - 1) * PPS <= WINDOW), "ring depth");
 
   const int kvh = blockIdx.x % p.num_kv_heads;
   const int item = blockIdx.x / p.num_kv_heads;
@@ -466,27 +468,28 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
       run_steps(0, nfull, std::true_type{});
       run_steps(nfull, nsteps, std::false_type{});
     } else {
-      // Step st + 2 is loaded while step st is computed.  At the top of step
-      // st the wave waits until only step st + 1's loads are outstanding;
-      // the barrier then publishes step st's tiles and frees the stage of
-      // step st - 1, which the loads of step st + 2 reuse.
+      // Step st + NSTAGE - 1 is loaded while step st is computed.  At the
+      // top of step st the wave waits until only the loads of the steps
+      // after st are outstanding (all of them in the last steps); the
+      // barrier then publishes step st's tiles and frees the stage of step
+      // st - 1, which the loads of step st + NSTAGE - 1 reuse.
+      constexpr int kAhead = NSTAGE - 1;
       constexpr int kLoadsPerStep = 2 * PER_T;
-      dma_step(0, 0);
-      if (nsteps > 1) dma_step(1, 1);
+      for (int st = 0; st < kAhead && st < nsteps; ++st) dma_step(st, st);
       auto run_steps = [&](int st0, int st1, auto full_tag) {
-        int stage = st0 % 3;
+        int stage = st0 % NSTAGE;
         for (int st = st0; st < st1; ++st) {
-          if (st + 1 < nsteps)
-            vm_wait<kLoadsPerStep>();
+          if (st + kAhead - 1 < nsteps)
+            vm_wait<(kAhead - 1) * kLoadsPerStep>();
           else
             vm_wait<0>();
           block_barrier();
-          if (st + 2 < nsteps) {
-            if ((st + 2) * PPS - ids_base == WINDOW) load_ids((st + 2) * PPS);
-            dma_step(st + 2, stage == 0 ? 2 : stage - 1);
+          if (st + kAhead < nsteps) {
+            if ((st + kAhead) * PPS - ids_base == WINDOW) load_ids((st + kAhead) * PPS);
+            dma_step(st + kAhead, stage == 0 ? NSTAGE - 1 : stage - 1);
           }
           if (wave_rows) compute_step(st, ring + stage * 2 * TILEB, full_tag);
-          stage = stage == 2 ? 0 : stage + 1;
+          stage = stage == NSTAGE - 1 ? 0 : stage + 1;
         }
       };
       run_steps(0, nfull, std::true_type{});
@@ -617,9 +620,22 @@ hipError_t launch_t(const MultiQueryLaunch& a, const MultiQueryParams& p) {
   hipLaunchKernelGGL((multi_query_schedule_kernel<G>), dim3(1), dim3(256), 0, a.stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G>),
-                     dim3((unsigned)((int64_t)a.work_capacity * a.num_kv_heads)), dim3(kMqWaves * 64), 0,
-                     a.stream, p);
+  // bf16 caches: when every sequence's rows fit one block (verification
+  // batches: each page is read by one workgroup, the kernel streams) a
+  // two-stage ring (32 KiB of LDS for D = 128) lets four workgroups share a
+  // CU; longer chunks, whose row blocks re-read pages from L2, take three
+  // stages (48 KiB, three workgroups per CU).  Measured on the 70B-shaped
+  // verification batch: 115 us against 126 us; on the chunked-prefill
+  // batch: 690 us against 651 us.
+  const dim3 grid((unsigned)((int64_t)a.work_capacity * a.num_kv_heads));
+  bool two_stages = false;
+  if constexpr (sizeof(TC) == 2) two_stages = a.max_row_blocks == 1;
+  if constexpr (sizeof(TC) == 2) {
+    if (two_stages)
+      hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G, 2>), grid, dim3(kMqWaves * 64), 0, a.stream, p);
+  }
+  if (!two_stages)
+    hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G, 3>), grid, dim3(kMqWaves * 64), 0, a.stream, p);
   e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   hipLaunchKernelGGL((multi_query_reduce_kernel<D, G>), dim3((unsigned)a.num_seqs * a.num_kv_heads),

@@ -67,6 +67,23 @@ def test_shapes(h, hkv, d, bs):
     check_mq(x, tiles_only=True)   # single-query sequences in the tiles as well
 
 
+@pytest.mark.parametrize("h,hkv,d,bs", SHAPES)
+def test_shapes_single_block(h, hkv, d, bs):
+    """Every sequence's rows fit one 64-row block (the verification case, run
+    with the two-stage ring for bf16 caches): query lengths up to 64 / G over
+    ragged contexts, with and without partitions."""
+    g = h // hkv
+    spec = wl.Spec(f"mq1b{h}x{hkv}x{d}x{bs}", h, hkv, d, bs, "bf16", seed=7 * h + d + bs)
+    qmax = 64 // g
+    qlens = [1, min(6, qmax), qmax, 2, 0, 3, qmax]
+    ctx = [1, 700, qmax + 40, 333, 50, 6 + 2 * bs + 1, qmax]
+    plan = wl.multi_query_plan(ctx, qlens, bs, torch.Generator().manual_seed(spec.seed))
+    x = wl.build_inputs(spec, plan)
+    check_mq(x)
+    check_mq(x, partition_tokens=2 * bs)
+    check_mq(x, tiles_only=True)
+
+
 @pytest.mark.parametrize("h,hkv,d,bs", [(8, 8, 128, 16), (64, 8, 128, 32), (16, 8, 64, 16),
                                         (32, 4, 128, 32)])
 def test_shapes_fp8(h, hkv, d, bs):
