@@ -150,6 +150,25 @@ def test_repeat_is_deterministic():
     assert np.array_equal(bits(a), bits(b))
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("h,hkv,d,bs", [(16, 8, 128, 16), (8, 8, 64, 32), (32, 4, 128, 32)])
+def test_long_context_page_window(h, hkv, d, bs, kv):
+    """A workgroup that walks more than 256 pages reloads its page-id window:
+    a chunk of two row blocks over a context of 256 pages and more (the
+    three-stage ring for bf16), and single-block sequences whose one partition
+    spans more than 256 pages (the two-stage ring)."""
+    g = h // hkv
+    spec = wl.Spec(f"mqlong{h}x{hkv}x{d}x{bs}{kv}", h, hkv, d, bs, "bf16", seed=5 * h + d + bs,
+                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0 if kv == "bf16" else 1.0 / 64)
+    long_ctx = 256 * bs + 700
+    plan = wl.multi_query_plan([long_ctx, 300], [64 // g + 1, 3], bs,
+                               torch.Generator().manual_seed(spec.seed))
+    check_mq(wl.build_inputs(spec, plan))
+    plan = wl.multi_query_plan([long_ctx, 2 * long_ctx, 40], [6, 64 // g, 1], bs,
+                               torch.Generator().manual_seed(spec.seed + 1))
+    check_mq(wl.build_inputs(spec, plan), partition_tokens=512 * bs)
+
+
 @pytest.mark.parametrize("name", ["specdec70b", "chunked13b", "specdec70b_fp8"])
 def test_full_size_sampled(name):
     """Full-size workloads in the benchmark's configuration; the oracle checks
