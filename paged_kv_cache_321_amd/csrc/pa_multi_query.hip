@@ -141,10 +141,6 @@ __device__ __forceinline__ float column_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Sixteen zero bytes: the source of the LDS rows of tokens past a partition's
-// end, so that no unread cache bytes (possibly NaN) reach the PV product.
-__device__ const uint4 kZeroChunk = {0u, 0u, 0u, 0u};
-
 template <typename TC, int D, int BS, int G, int STAGES>
 __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void multi_query_kernel(MultiQueryParams p) {
   constexpr bool kFp8 = sizeof(TC) == 1;
@@ -281,32 +277,38 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
 
   // bf16: step st's K and V go straight from the cache into stage `stage`.
   // Load u of wave w fills 64 consecutive 16-byte LDS slots, 64 / NCH whole
-  // rows of one page; each lane fetches the chunk its slot holds.
+  // rows of one page; each lane fetches the chunk its slot holds, at a byte
+  // offset inside the page that does not change along the walk.  The page is
+  // reached through a buffer descriptor whose record count ends at the
+  // partition's last token, so the rows past it read as zeros and no unread
+  // cache bytes (possibly NaN) reach the PV product.
+  uint32_t koff[PER_T], voff[PER_T];
+#pragma unroll
+  for (int u = 0; u < PER_T; ++u) {
+    const int slot = (u * kMqWaves + wave) * 64 + lane;
+    const int row = slot / NCH;
+    const int pos = slot % NCH;
+    koff[u] = (row % BS) * ROWB + ((pos ^ kswz<ROWB>(row)) << 4);
+    voff[u] = (row % BS) * ROWB + ((pos ^ swz<ROWB>(row)) << 4);
+  }
   auto dma_step = [&](int st, int stage) {
     unsigned char* kbuf = ring + stage * 2 * TILEB;
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
       const int slot0 = (u * kMqWaves + wave) * 64;  // wave-uniform
-      const int row = (slot0 + lane) / NCH;
-      const int pos = (slot0 + lane) % NCH;
-      const int t = tok0 + st * kStepTokens + row;
-      // The page (past the partition's pages its id is 0) is looked up by the
-      // whole wave; lanes whose token lies past the partition end read zeros.
-      const int64_t base = page_id(st * PPS + slot0 / NCH / BS) * p.block_stride + (row % BS) * D;
-      const TC* kp = reinterpret_cast<const TC*>(&kZeroChunk);
-      const TC* vp = kp;
-      if (t < tok1) {
-        kp = kc + base + (pos ^ kswz<ROWB>(row)) * 8;
-        vp = vc + base + (pos ^ swz<ROWB>(row)) * 8;
-      }
+      const int pg = st * PPS + slot0 / NCH / BS;     // page of the partition
+      const int64_t page = page_id(pg) * p.block_stride;
+      const int valid = min(max(tok1 - (tok0 + pg * BS), 0), BS);  // tokens of the page to read
+      const i32x4_t kr = raw_buffer(kc + page, valid * ROWB);
+      const i32x4_t vr = raw_buffer(vc + page, valid * ROWB);
       const uint32_t kdst = lds_address(kbuf + slot0 * 16);
       const uint32_t vdst = lds_address(kbuf + TILEB + slot0 * 16);
       if (stream_pages) {
-        load_lds16<true>(kp, kdst);
-        load_lds16<true>(vp, vdst);
+        buffer_load_lds16<true>(koff[u], kr, kdst);
+        buffer_load_lds16<true>(voff[u], vr, vdst);
       } else {
-        load_lds16<false>(kp, kdst);
-        load_lds16<false>(vp, vdst);
+        buffer_load_lds16<false>(koff[u], kr, kdst);
+        buffer_load_lds16<false>(voff[u], vr, vdst);
       }
     }
   };
