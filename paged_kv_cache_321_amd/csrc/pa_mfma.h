@@ -105,7 +105,7 @@ template <bool kNonTemporal>
 __device__ __forceinline__ void buffer_load_lds16(uint32_t voffset, i32x4_t rsrc, uint32_t lds_base) {
   uint32_t saved;
   if constexpr (kNonTemporal)
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds nt\n\ts_mov_b32 m0, %0"
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds\n\ts_mov_b32 m0, %0"
                  : "=&s"(saved) : "v"(voffset), "s"(rsrc), "s"(lds_base) : "memory");
   else
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_mov_b32 m0, %0"
