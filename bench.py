@@ -33,7 +33,7 @@ TRAFFIC_FILE = os.path.join(HERE, "profiles", "decode_traffic.json")
 # Sources that determine the attention kernels; a workload's counter record
 # is valid only for the exact text of the sources its kernels are built from.
 DECODE_SRCS = ("pa_device.h", "pa_mfma.h", "pa_decode.hip", "pa_decode_valu.hip", "pa_decode_mfma.hip")
-MULTI_QUERY_SRCS = DECODE_SRCS + ("pa_multi_query.hip",)
+MULTI_QUERY_SRCS = DECODE_SRCS + ("pa_lds_dma.h", "pa_multi_query.hip")
 
 DESCRIPTION = {
     "llama13b": "LLaMA-13B-shaped layer decode: 128 seqs x ctx 2048, H=Hkv=40, D=128, BS=16, bf16, "

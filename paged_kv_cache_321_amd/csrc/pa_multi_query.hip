@@ -34,6 +34,7 @@
 #include <type_traits>
 
 #include "pa_device.h"
+#include "pa_lds_dma.h"
 #include "pa_mfma.h"
 
 namespace pa {
