@@ -154,17 +154,22 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   constexpr int CHUNKS = kStepTokens * CCH;  // 16-byte cache chunks per step (K or V)
   constexpr int PER_T = (CHUNKS + kMqWaves * 64 - 1) / (kMqWaves * 64);
   constexpr int NTT = kStepTokens / 16;      // 16-token tiles per step
-  constexpr int TILEB = kStepTokens * ROWB;  // bytes of one step's K (or V) in LDS
-  // bf16 caches: a ring of STAGES (K, V) stages filled by direct LDS loads
-  // STAGES - 1 steps ahead; E4M3 caches: one stage, widened through
-  // registers.
-  constexpr int NSTAGE = kFp8 ? 1 : STAGES;
+  constexpr int TILEB = kStepTokens * ROWB;  // bytes of one step's bf16 K (or V) in LDS
+  constexpr int CROWB = D * (int)sizeof(TC);  // bytes of one cache row
+  constexpr int RTILEB = kStepTokens * CROWB; // bytes of one step's K (or V) as in the cache
+  // A ring of STAGES (K, V) stages filled by direct LDS loads STAGES - 1
+  // steps ahead.  bf16 caches land in the swizzled layouts the matrix cores
+  // read; E4M3 caches land as they are and each step is widened into one
+  // bf16 (K, V) tile after the ring.
+  constexpr int NSTAGE = STAGES;
+  constexpr int LDS_BYTES = NSTAGE * 2 * RTILEB + (kFp8 ? 2 * TILEB : 0);
   constexpr int WINDOW = 256;                // page ids held in registers (4 per lane)
   static_assert(kStepTokens % BS == 0 && kStepTokens % 32 == 0 && NCH >= 8, "tile shape");
   static_assert(kFp8 || CHUNKS % (kMqWaves * 64) == 0, "a bf16 step is whole wave loads");
+  static_assert(CHUNKS * 16 == RTILEB, "a step is CHUNKS 16-byte chunks");
   static_assert(CHUNKS % 64 == 0 && 64 / CCH <= BS, "a wave's chunks of a step lie in one page");
   static_assert(WINDOW % PPS == 0, "a step's pages lie in one window");
-  static_assert(kFp8 || (NSTAGE >= 2 && (NSTAGE - 1) * PPS <= WINDOW), "ring depth");
+  static_assert(NSTAGE >= 2 && (NSTAGE - 1) * PPS <= WINDOW, "ring depth");
 
   const int kvh = blockIdx.x % p.num_kv_heads;
   const int item = blockIdx.x / p.num_kv_heads;
@@ -222,10 +227,13 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   float m_run = -FLT_MAX;  // running max of the row (same in its 4 lanes)
   float l_run = 0.f;       // this lane's share of the running sum
 
-  // Stage i: K tile at ring + 2 i TILEB, V tile right after it.  K rows hold
-  // 16-byte chunk ch at position ch ^ kswz<ROWB>(token); V rows are in the
-  // transposed-read layout (position ch ^ swz<ROWB>(token)).
-  __shared__ __attribute__((aligned(16))) unsigned char ring[NSTAGE * 2 * TILEB];
+  // Stage i: K tile at ring + 2 i RTILEB, V tile right after it.  In the
+  // tiles the matrix cores read (the stages for bf16, the widened tile for
+  // E4M3), K rows hold 16-byte chunk ch at position ch ^ kswz<ROWB>(token)
+  // and V rows are in the transposed-read layout (position
+  // ch ^ swz<ROWB>(token)).
+  __shared__ __attribute__((aligned(16))) unsigned char ring[LDS_BYTES];
+  unsigned char* const wide = ring + NSTAGE * 2 * RTILEB;  // E4M3: the widened tile
 
   const TC* kc = static_cast<const TC*>(p.k_cache) + (int64_t)kvh * BS * D;
   const TC* vc = static_cast<const TC*>(p.v_cache) + (int64_t)kvh * BS * D;
@@ -276,34 +284,41 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   // L2 / MALL.
   const bool stream_pages = b.nrb == 1;
 
-  // bf16: step st's K and V go straight from the cache into stage `stage`.
-  // Load u of wave w fills 64 consecutive 16-byte LDS slots, 64 / NCH whole
-  // rows of one page; each lane fetches the chunk its slot holds, at a byte
-  // offset inside the page that does not change along the walk.  The page is
-  // reached through a buffer descriptor whose record count ends at the
-  // partition's last token, so the rows past it read as zeros and no unread
-  // cache bytes (possibly NaN) reach the PV product.
+  // Step st's K and V go straight from the cache into stage `stage`.  Load
+  // u of wave w fills 64 consecutive 16-byte LDS slots, 64 / CCH whole rows
+  // of one page; each lane fetches the chunk its slot holds (bf16: the
+  // swizzled position; E4M3: as stored), at a byte offset inside the page
+  // that does not change along the walk.  The page is reached through a
+  // buffer descriptor whose record count ends at the partition's last token,
+  // so the rows past it read as zeros and no unread cache bytes (possibly
+  // NaN) reach the PV product.
   uint32_t koff[PER_T], voff[PER_T];
 #pragma unroll
   for (int u = 0; u < PER_T; ++u) {
     const int slot = (u * kMqWaves + wave) * 64 + lane;
-    const int row = slot / NCH;
-    const int pos = slot % NCH;
-    koff[u] = (row % BS) * ROWB + ((pos ^ kswz<ROWB>(row)) << 4);
-    voff[u] = (row % BS) * ROWB + ((pos ^ swz<ROWB>(row)) << 4);
+    const int row = slot / CCH;
+    const int pos = slot % CCH;
+    if constexpr (kFp8) {
+      koff[u] = voff[u] = (row % BS) * CROWB + pos * 16;
+    } else {
+      koff[u] = (row % BS) * CROWB + ((pos ^ kswz<ROWB>(row)) << 4);
+      voff[u] = (row % BS) * CROWB + ((pos ^ swz<ROWB>(row)) << 4);
+    }
   }
+  constexpr int kLoadsPerStep = 2 * PER_T;  // per wave that loads (all, but for E4M3 at D = 64)
   auto dma_step = [&](int st, int stage) {
-    unsigned char* kbuf = ring + stage * 2 * TILEB;
+    unsigned char* kbuf = ring + stage * 2 * RTILEB;
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
       const int slot0 = (u * kMqWaves + wave) * 64;  // wave-uniform
-      const int pg = st * PPS + slot0 / NCH / BS;     // page of the partition
+      if (slot0 >= CHUNKS) continue;
+      const int pg = st * PPS + slot0 / CCH / BS;     // page of the partition
       const int64_t page = page_id(pg) * p.block_stride;
       const int valid = min(max(tok1 - (tok0 + pg * BS), 0), BS);  // tokens of the page to read
-      const i32x4_t kr = raw_buffer(kc + page, valid * ROWB);
-      const i32x4_t vr = raw_buffer(vc + page, valid * ROWB);
+      const i32x4_t kr = raw_buffer(kc + page, valid * CROWB);
+      const i32x4_t vr = raw_buffer(vc + page, valid * CROWB);
       const uint32_t kdst = lds_address(kbuf + slot0 * 16);
-      const uint32_t vdst = lds_address(kbuf + TILEB + slot0 * 16);
+      const uint32_t vdst = lds_address(kbuf + RTILEB + slot0 * 16);
       if (stream_pages) {
         buffer_load_lds16<true>(koff[u], kr, kdst);
         buffer_load_lds16<true>(voff[u], vr, vdst);
@@ -314,50 +329,26 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
     }
   };
 
-  // E4M3: one step's chunks, PER_T per thread (chunk c is token c / CCH of the
-  // step, 16 bytes at chunk c % CCH of its cache row), loaded into registers
-  // and widened into the single stage.  V rows past the partition end are
-  // zero.
-  uint4 kreg[kFp8 ? PER_T : 1], vreg[kFp8 ? PER_T : 1];
-  auto load_step = [&](int st) {
-#pragma unroll
-    for (int u = 0; u < PER_T; ++u) {
-      const int c = tid + u * kMqWaves * 64;
-      const int tok = c / CCH;
-      const int pg = st * PPS + tok / BS;  // page of the partition
-      // The page is the same across each wave (a wave's chunks lie in one
-      // page, CHUNKS is whole waves); looked up by the whole wave.
-      const int64_t phys = page_id(pg);
-      kreg[u] = vreg[u] = make_uint4(0u, 0u, 0u, 0u);
-      if (c < CHUNKS && pg < npg) {
-        const int64_t off = phys * p.block_stride + (tok % BS) * D + (c % CCH) * 16;
-        if (stream_pages) {
-          kreg[u] = load_page16<true>(kc + off);
-          vreg[u] = load_page16<true>(vc + off);
-        } else {
-          kreg[u] = load_page16<false>(kc + off);
-          vreg[u] = load_page16<false>(vc + off);
-        }
-      }
-    }
-  };
-  auto stage_step = [&](int st) {
-    unsigned char* kt = ring;
-    unsigned char* vt = ring + TILEB;
+  // E4M3: widen stage `stage` (16 codes per chunk, chunk c = token c / CCH,
+  // codes at 16 (c % CCH)) into the bf16 tile, two 16-byte chunks per chunk
+  // (exact; zero codes, the rows past the partition end, become +0).
+  auto widen_step = [&](int stage) {
+    const unsigned char* kq = ring + stage * 2 * RTILEB;
+    const unsigned char* vq = kq + RTILEB;
+    unsigned char* kt = wide;
+    unsigned char* vt = wide + TILEB;
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
       const int c = tid + u * kMqWaves * 64;
       if (c >= CHUNKS) continue;
       const int tok = c / CCH;
       const int ch = c % CCH;
-      const bool keep = tok0 + (st * PPS) * BS + tok < tok1;
-      const uint4 k0 = fp8x8_to_bf16x8(kreg[u].x, kreg[u].y), k1 = fp8x8_to_bf16x8(kreg[u].z, kreg[u].w);
-      uint4 v0 = fp8x8_to_bf16x8(vreg[u].x, vreg[u].y), v1 = fp8x8_to_bf16x8(vreg[u].z, vreg[u].w);
-      if (!keep) v0 = v1 = make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4*>(kt + tok * ROWB + (((2 * ch) ^ kswz<ROWB>(tok)) << 4)) = k0;
-      *reinterpret_cast<uint4*>(kt + tok * ROWB + (((2 * ch + 1) ^ kswz<ROWB>(tok)) << 4)) = k1;
-      *reinterpret_cast<uint4*>(vt + tok * ROWB + (((2 * ch) ^ swz<ROWB>(tok)) << 4)) = v0;
-      *reinterpret_cast<uint4*>(vt + tok * ROWB + (((2 * ch + 1) ^ swz<ROWB>(tok)) << 4)) = v1;
+      const uint4 kw = *reinterpret_cast<const uint4*>(kq + c * 16);
+      const uint4 vw = *reinterpret_cast<const uint4*>(vq + c * 16);
+      *reinterpret_cast<uint4*>(kt + tok * ROWB + (((2 * ch) ^ kswz<ROWB>(tok)) << 4)) = fp8x8_to_bf16x8(kw.x, kw.y);
+      *reinterpret_cast<uint4*>(kt + tok * ROWB + (((2 * ch + 1) ^ kswz<ROWB>(tok)) << 4)) = fp8x8_to_bf16x8(kw.z, kw.w);
+      *reinterpret_cast<uint4*>(vt + tok * ROWB + (((2 * ch) ^ swz<ROWB>(tok)) << 4)) = fp8x8_to_bf16x8(vw.x, vw.y);
+      *reinterpret_cast<uint4*>(vt + tok * ROWB + (((2 * ch + 1) ^ swz<ROWB>(tok)) << 4)) = fp8x8_to_bf16x8(vw.z, vw.w);
     }
   };
 
@@ -452,52 +443,38 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   const int nfull = p.scale_log2e > 0.f ? min(nsteps, max(0, (block_full_end - tok0) / kStepTokens)) : 0;
   if (nsteps > 0) {
     load_ids(0);
-    if constexpr (kFp8) {
-      // Registers hold the next step while the current one is computed from
-      // LDS; two barriers per step hand the single stage over.
-      load_step(0);
-      auto run_steps = [&](int st0, int st1, auto full_tag) {
-        for (int st = st0; st < st1; ++st) {
-          __syncthreads();  // every wave is done with the previous step's tiles
-          stage_step(st);
-          __syncthreads();
-          if (st + 1 < nsteps) {
-            if ((st + 1) * PPS - ids_base == WINDOW) load_ids((st + 1) * PPS);
-            load_step(st + 1);
-          }
-          if (wave_rows) compute_step(st, ring, full_tag);
+    // Step st + NSTAGE - 1 is loaded while step st is computed.  At the top
+    // of step st the wave waits until only the loads of the steps after st
+    // are outstanding (all of them in the last steps); the barrier then
+    // publishes step st's stage and frees the stage of step st - 1, which
+    // the loads of step st + NSTAGE - 1 reuse (for E4M3 also the widened
+    // tile, which a second barrier publishes).
+    constexpr int kAhead = NSTAGE - 1;
+    for (int st = 0; st < kAhead && st < nsteps; ++st) dma_step(st, st);
+    auto run_steps = [&](int st0, int st1, auto full_tag) {
+      int stage = st0 % NSTAGE;
+      for (int st = st0; st < st1; ++st) {
+        if (st + kAhead - 1 < nsteps)
+          vm_wait<(kAhead - 1) * kLoadsPerStep>();
+        else
+          vm_wait<0>();
+        block_barrier();
+        if (st + kAhead < nsteps) {
+          if ((st + kAhead) * PPS - ids_base == WINDOW) load_ids((st + kAhead) * PPS);
+          dma_step(st + kAhead, stage == 0 ? NSTAGE - 1 : stage - 1);
         }
-      };
-      run_steps(0, nfull, std::true_type{});
-      run_steps(nfull, nsteps, std::false_type{});
-    } else {
-      // Step st + NSTAGE - 1 is loaded while step st is computed.  At the
-      // top of step st the wave waits until only the loads of the steps
-      // after st are outstanding (all of them in the last steps); the
-      // barrier then publishes step st's tiles and frees the stage of step
-      // st - 1, which the loads of step st + NSTAGE - 1 reuse.
-      constexpr int kAhead = NSTAGE - 1;
-      constexpr int kLoadsPerStep = 2 * PER_T;
-      for (int st = 0; st < kAhead && st < nsteps; ++st) dma_step(st, st);
-      auto run_steps = [&](int st0, int st1, auto full_tag) {
-        int stage = st0 % NSTAGE;
-        for (int st = st0; st < st1; ++st) {
-          if (st + kAhead - 1 < nsteps)
-            vm_wait<(kAhead - 1) * kLoadsPerStep>();
-          else
-            vm_wait<0>();
+        const unsigned char* tiles = ring + stage * 2 * RTILEB;
+        if constexpr (kFp8) {
+          widen_step(stage);
           block_barrier();
-          if (st + kAhead < nsteps) {
-            if ((st + kAhead) * PPS - ids_base == WINDOW) load_ids((st + kAhead) * PPS);
-            dma_step(st + kAhead, stage == 0 ? NSTAGE - 1 : stage - 1);
-          }
-          if (wave_rows) compute_step(st, ring + stage * 2 * TILEB, full_tag);
-          stage = stage == NSTAGE - 1 ? 0 : stage + 1;
+          tiles = wide;
         }
-      };
-      run_steps(0, nfull, std::true_type{});
-      run_steps(nfull, nsteps, std::false_type{});
-    }
+        if (wave_rows) compute_step(st, tiles, full_tag);
+        stage = stage == NSTAGE - 1 ? 0 : stage + 1;
+      }
+    };
+    run_steps(0, nfull, std::true_type{});
+    run_steps(nfull, nsteps, std::false_type{});
   }
   const bool bad = b.bad || ids_bad;
 
@@ -623,21 +600,17 @@ hipError_t launch_t(const MultiQueryLaunch& a, const MultiQueryParams& p) {
   hipLaunchKernelGGL((multi_query_schedule_kernel<G>), dim3(1), dim3(256), 0, a.stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // bf16 caches: when every sequence's rows fit one block (verification
-  // batches: each page is read by one workgroup, the kernel streams) a
-  // two-stage ring (32 KiB of LDS for D = 128) lets four workgroups share a
-  // CU; longer chunks, whose row blocks re-read pages from L2, take three
-  // stages (48 KiB, three workgroups per CU).  Measured on the 70B-shaped
-  // verification batch: 115 us against 126 us; on the chunked-prefill
-  // batch: 690 us against 651 us.
+  // When every sequence's rows fit one block (verification batches: each
+  // page is read by one workgroup, the kernel streams) a two-stage ring
+  // (D = 128: 32 KiB of LDS for bf16, 16 + 16 KiB for E4M3 with its widened
+  // tile) lets four workgroups share a CU; longer chunks, whose row blocks
+  // re-read pages from L2, take three stages (48 KiB; E4M3 24 + 16 KiB).
+  // Measured on the 70B-shaped verification batch (bf16): 115 us against
+  // 126 us; on the chunked-prefill batch: 690 us against 651 us.
   const dim3 grid((unsigned)((int64_t)a.work_capacity * a.num_kv_heads));
-  bool two_stages = false;
-  if constexpr (sizeof(TC) == 2) two_stages = a.max_row_blocks == 1;
-  if constexpr (sizeof(TC) == 2) {
-    if (two_stages)
-      hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G, 2>), grid, dim3(kMqWaves * 64), 0, a.stream, p);
-  }
-  if (!two_stages)
+  if (a.max_row_blocks == 1)
+    hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G, 2>), grid, dim3(kMqWaves * 64), 0, a.stream, p);
+  else
     hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G, 3>), grid, dim3(kMqWaves * 64), 0, a.stream, p);
   e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
