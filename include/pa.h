@@ -305,8 +305,8 @@ int pa_decode_shared_prefix(void* out, const void* q,
  * pa_multi_query_workspace_size -- bytes of device workspace pa_multi_query
  * needs: the partitions of cut contexts and the list of work items it builds
  * on the device each call (0 when there are no sequences or no query tokens);
- * (size_t)-1 for arguments it would reject.  partition_tokens: 0 = default
- * (2048 tokens).
+ * (size_t)-1 for arguments it would reject.  partition_tokens: 0 = the
+ * default pa_multi_query picks for the same shape (see there).
  */
 size_t pa_multi_query_workspace_size(int num_seqs, int num_query_tokens, int num_heads,
                                      int num_kv_heads, int head_dim, int block_size,
@@ -347,10 +347,12 @@ size_t pa_multi_query_workspace_size(int num_seqs, int num_query_tokens, int num
  * ordered on `stream` like a single launch.  Calls on one device take turns
  * on the side stream (a lock); PA_MULTI_QUERY_ONE_STREAM keeps every launch on
  * `stream`.
- * partition_tokens (0 = default
- * 2048; else a positive multiple of block_size): a sequence with n > 1 whose
- * n * G rows fit in 64 has its context cut into partitions of this many
- * tokens, merged by a second kernel; longer chunks are not cut.
+ * partition_tokens (0 = chosen from the
+ * shape: the smallest of 512, 1024 and 2048 for which num_seqs * num_kv_heads
+ * * ceil(max_context_len / partition_tokens) <= 1024, else 2048; otherwise a
+ * positive multiple of block_size): a sequence with n > 1 whose n * G rows
+ * fit in 64 has its context cut into partitions of this many tokens, merged
+ * by a second kernel; longer chunks are not cut.
  * workspace: at least pa_multi_query_workspace_size(...) bytes, 16-byte
  * aligned.
  * Preconditions (device values): query_start ranges inside [0, num_query_tokens],

@@ -367,7 +367,7 @@ MultiQuerySizes multi_query_sizes(int num_seqs, int num_query_tokens, int num_he
     return z;
   }
   int pt = partition_tokens;
-  if (pt == 0) pt = pa::default_multi_query_partition_tokens(block_size);
+  if (pt == 0) pt = pa::default_multi_query_partition_tokens(block_size, num_seqs, num_kv_heads, max_context_len);
   if (pt < 0 || pt % block_size != 0) { z.status = PA_ERR_SHAPE; return z; }
   z.partition_tokens = pt;
   z.max_parts = max_context_len <= pt ? 1 : (max_context_len + pt - 1) / pt;

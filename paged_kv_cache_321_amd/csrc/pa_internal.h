@@ -114,7 +114,7 @@ int default_partition_tokens(int dtype, int cache_dtype, int head_dim, int block
                              bool shared_prefix, int max_prefix_tokens);
 
 hipError_t launch_decode(const DecodeLaunch& a);
-int default_multi_query_partition_tokens(int block_size);
+int default_multi_query_partition_tokens(int block_size, int num_seqs, int num_kv_heads, int max_context_len);
 int multi_query_rows_per_block();
 hipError_t launch_multi_query(const MultiQueryLaunch& a);
 hipError_t launch_reshape_and_cache(const ReshapeLaunch& a);

@@ -644,10 +644,18 @@ hipError_t by_dim(const MultiQueryLaunch& a, const MultiQueryParams& p) {
 
 int multi_query_rows_per_block() { return kRowsPerBlock; }
 
-int default_multi_query_partition_tokens(int block_size) {
-  // Measured on 6-query verification over 1-8K contexts (70B GQA shape):
-  // 1024 -> 160 us, 2048 -> 151 us, 4096 -> 224 us.
-  const int t = 2048;
+int default_multi_query_partition_tokens(int block_size, int num_seqs, int num_kv_heads, int max_context_len) {
+  // Each 32-token step of a workgroup costs about a microsecond of latency,
+  // so short partitions win while the grid is small and long ones (fewer
+  // partial results to merge) once it fills the chip: the smallest of 512,
+  // 1024 and 2048 tokens that keeps (sequence, kv head, partition) items
+  // within 1024, four per CU.  Measured on 6-query verification (70B GQA
+  // shape, contexts up to 8K): 2-8 sequences 41-56 us at 512 against 72-77
+  // at 2048; 16 sequences 75 us at 1024 against 94; 32 sequences 115 us at
+  // 2048 against 136 at 1024.
+  constexpr int64_t kTargetItems = 1024;
+  int t = 512;
+  while (t < 2048 && (int64_t)num_seqs * num_kv_heads * ((max_context_len + t - 1) / t) > kTargetItems) t *= 2;
   return t - t % block_size;
 }
 

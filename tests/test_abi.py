@@ -252,16 +252,27 @@ def _work(s, t, g, parts):
 
 def test_multi_query_workspace_size():
     ws = LIB.pa_multi_query_workspace_size
-    # Contexts within one multi-query partition (2048 by default) and one decode
-    # partition (4096 tokens on the matrix-core decode path at G = 4): the work
-    # list only.
-    assert ws(3, 12, 8, 2, 128, 16, 2048, BF16, BF16, 0) == _work(3, 12, 4, 1)
+    # Contexts within one multi-query partition and one decode partition (4096
+    # tokens on the matrix-core decode path at G = 4): the work list only.
+    assert ws(3, 12, 8, 2, 128, 16, 2048, BF16, BF16, 2048) == _work(3, 12, 4, 1)
     # Multi-query partitions: 3 slots per query row.
     assert ws(3, 12, 8, 2, 128, 16, 2100, BF16, BF16, 1024) == _area(12 * 8 * 3, 128) + _work(3, 12, 4, 3)
-    assert ws(3, 12, 8, 2, 128, 16, 2100, BF16, FP8, 0) == _area(12 * 8 * 2, 128) + _work(3, 12, 4, 2)
-    # Decode rows too (a 5000-token context needs 2 decode partitions per sequence).
+    # Default partitions for a small batch: 512 tokens (3 seqs x 2 kv heads x
+    # 5 partitions <= 1024 items), so 5 slots.
+    assert ws(3, 12, 8, 2, 128, 16, 2100, BF16, FP8, 0) == _area(12 * 8 * 5, 128) + _work(3, 12, 4, 5)
+    # Decode rows too (a 5000-token context needs 2 decode partitions per
+    # sequence; 10 multi-query partitions of 512).
     assert ws(3, 12, 8, 2, 128, 16, 5000, BF16, BF16, 0) == \
-        _area(3 * 8 * 2, 128) + _area(12 * 8 * 3, 128) + _work(3, 12, 4, 3)
+        _area(3 * 8 * 2, 128) + _area(12 * 8 * 10, 128) + _work(3, 12, 4, 10)
+    # Default partitions grow with the grid: 16 seqs x 8 kv heads over 8192
+    # tokens take 1024-token partitions (1024 items), 32 seqs 2048 (1024
+    # items), 64 seqs stay at 2048.
+    assert ws(16, 96, 64, 8, 128, 16, 8192, BF16, BF16, 0) == \
+        _area(16 * 64 * 2, 128) + _area(96 * 64 * 8, 128) + _work(16, 96, 8, 8)
+    assert ws(32, 192, 64, 8, 128, 16, 8192, BF16, BF16, 0) == \
+        _area(32 * 64 * 2, 128) + _area(192 * 64 * 4, 128) + _work(32, 192, 8, 4)
+    assert ws(64, 384, 64, 8, 128, 16, 8192, BF16, BF16, 0) == \
+        _area(64 * 64 * 2, 128) + _area(384 * 64 * 4, 128) + _work(64, 384, 8, 4)
     # G = 1 decodes on the vector path: 2048-token partitions.
     assert ws(3, 12, 8, 8, 64, 16, 2100, BF16, BF16, 4096) == _area(3 * 8 * 2, 64) + _work(3, 12, 1, 1)
     assert ws(0, 12, 8, 2, 64, 32, 100, BF16, BF16, 0) == 0   # nothing to schedule
