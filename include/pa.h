@@ -352,7 +352,9 @@ size_t pa_multi_query_workspace_size(int num_seqs, int num_query_tokens, int num
  * * ceil(max_context_len / partition_tokens) <= 1024, else 2048; otherwise a
  * positive multiple of block_size): a sequence with n > 1 whose n * G rows
  * fit in 64 has its context cut into partitions of this many tokens, merged
- * by a second kernel; longer chunks are not cut.
+ * by a second kernel; longer chunks are not cut.  The cut changes the
+ * rounding of a row's result, so a caller that needs rows bitwise
+ * independent of the rest of the batch passes a fixed partition_tokens.
  * workspace: at least pa_multi_query_workspace_size(...) bytes, 16-byte
  * aligned.
  * Preconditions (device values): query_start ranges inside [0, num_query_tokens],

@@ -27,9 +27,10 @@
 // short chunks) would give too few workgroups on a long context, so its
 // context is cut into partitions of partition_tokens tokens whose
 // (max, sum, accumulator) triples the reduce kernel merges; a sequence with
-// more rows is parallel enough through its row blocks and is not cut.  The
-// rule depends on the sequence alone, so its result does not depend on the
-// rest of the batch.
+// more rows is parallel enough through its row blocks and is not cut.  Given
+// partition_tokens, the cut depends on the sequence alone; the default
+// partition_tokens follows the batch's shape (its host-side bounds), so a
+// caller that needs rows bitwise independent of the batch fixes it.
 
 #include <type_traits>
 
