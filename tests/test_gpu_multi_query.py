@@ -207,3 +207,24 @@ def test_side_stream_same_bits_and_ordered():
     torch.cuda.synchronize()
     assert np.array_equal(bits(out), bits(one))
     assert np.array_equal(bits(seen), bits(one))
+
+
+def test_fixed_partitions_batch_invariant():
+    """With partition_tokens fixed, a sequence's rows are the same bits alone as
+    in a batch (the default partition size follows the batch shape, so this is
+    the caller's way to batch-invariant rows)."""
+    spec = wl.Spec("mqinv", 32, 8, 128, 16, "bf16", seed=91)
+    plan = wl.multi_query_plan([900, 2500, 40, 1300], [6, 5, 1, 30], 16, torch.Generator().manual_seed(4))
+    x = wl.build_inputs(spec, plan)
+    whole, t = gpu_mq_step(x, partition_tokens=256)
+    qs = x.query_start.tolist()
+    for s in (0, 1, 3):
+        rows = slice(qs[s], qs[s + 1])
+        q = t["q"][rows].contiguous()
+        alone = torch.empty_like(q)
+        binding.pa_multi_query(alone, q, t["k_cache"], t["v_cache"], t["block_tables"][s:s + 1].contiguous(),
+                               t["context_lens"][s:s + 1].contiguous(),
+                               torch.tensor([0, qs[s + 1] - qs[s]], dtype=torch.int32, device="cuda"),
+                               x.scale, x.max_context_len, qs[s + 1] - qs[s], partition_tokens=256)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(alone), bits(whole[rows])), s
