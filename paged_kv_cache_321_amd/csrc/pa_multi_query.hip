@@ -12,12 +12,15 @@
 //   S^T [tokens x rows] = K [tokens x D] . Q^T [D x rows],
 //   O^T [D x rows]     += V^T [D x tokens] . P^T [tokens x rows]
 // (the decode kernel's formulation), so one K/V step staged in LDS feeds 64
-// rows.  A step is 32 tokens: two 16-token pages or one 32-token page.  K sits
-// in LDS row-major with 16-byte chunks swizzled by the row, so the 16 rows one
-// A-operand read touches hit distinct banks; V sits in the transposed-read
-// layout of pa_mfma.h.  E4M3 caches are widened to bf16 (exactly) on the way
-// into LDS.  Each column keeps its own running max and sum, moved lazily (only
-// when a score exceeds the reference by more than 2^8).
+// rows.  A step is 32 tokens: two 16-token pages or one 32-token page.  Pages
+// go from the cache straight into a ring of two or three LDS stages (buffer
+// loads with the lds bit, one or two steps ahead).  bf16 chunks land where the
+// matrix cores read them: K row-major with 16-byte chunks swizzled by the
+// token, so the 16 rows one A-operand read touches hit distinct banks, and V
+// in the transposed-read layout of pa_mfma.h.  E4M3 codes land as stored and
+// each step is widened (exactly) into one bf16 tile in that layout.  Each
+// column keeps its own running max and sum, moved lazily (only when a score
+// exceeds the reference by more than 2^8).
 //
 // Sequences with exactly one new query are decode steps; unless told
 // otherwise, the entry point runs them through the decode kernels (which
