@@ -30,7 +30,9 @@
  *
  * Conventions shared by every entry point:
  *  - Every buffer pointer is a DEVICE pointer.  The caller owns every buffer;
- *    the library allocates nothing and keeps no global state.
+ *    the library allocates no memory.  Its only state is pa_multi_query's side
+ *    stream and two events per device, created on the device's first such
+ *    call and kept until the process ends (see pa_multi_query).
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *    null stream).  A return of PA_OK means the kernels were enqueued.
  *  - A negative return means nothing was launched, except PA_ERR_LAUNCH, which
