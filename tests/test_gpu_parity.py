@@ -351,6 +351,28 @@ def test_full_size_sampled(name):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("h,hkv,bs,kv", [(64, 8, 32, "bf16"), (64, 8, 32, "fp8"), (40, 40, 16, "bf16")])
+def test_long_contexts_sampled(h, hkv, bs, kv):
+    """Contexts of up to 128K tokens (4096-8192 pages per sequence, 32-64
+    partitions, many page-id windows), ragged, on both decode paths and an
+    E4M3 cache; the oracle checks every head of each sequence."""
+    torch.cuda.empty_cache()
+    spec = wl.Spec(f"long{h}x{hkv}x{bs}{kv}", h, hkv, 128, bs, "bf16", seed=h + bs,
+                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0 if kv == "bf16" else 1.0 / 64)
+    ctx = [131072, 65537] if hkv < h else [100001]
+    plan = wl.uniform_plan(ctx, bs, torch.Generator().manual_seed(spec.seed), new_tokens=True)
+    x = wl.build_inputs(spec, plan, device="cuda", poison=True)
+    seqs = list(range(len(ctx)))
+    ref, ids, kc, vc = sampled_reference(x, seqs)
+    resident = {n: getattr(x, n) for n in ("q", "k_cache", "v_cache", "key", "value",
+                                           "slot_mapping", "block_tables", "context_lens",
+                                           "block_pairs")}
+    out, t = gpu_step(x, t=resident)
+    assert_close(as_f64(out), ref, x.spec.dtype, spec.name)
+    del x, t, out
+    torch.cuda.empty_cache()
+
+
 # ----------------------------------------------------------------------------
 # swap_blocks: device pool <-> pinned host pool.
 # ----------------------------------------------------------------------------
