@@ -182,3 +182,26 @@ def test_full_size_sampled(name):
     assert torch.isfinite(out.float()).all()
     del x, t, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("h,hkv,bs,kv", [(32, 8, 16, "bf16"), (64, 8, 32, "fp8")])
+def test_long_prefix_sampled(h, hkv, bs, kv):
+    """A 48K-token prompt shared by 4 beams (the prefix cut into many
+    partitions, page-id windows reloaded), with ragged tails, next to an
+    unshared long sequence; every head of every sequence against the oracle."""
+    torch.cuda.empty_cache()
+    spec = wl.Spec(f"longpfx{h}x{hkv}x{bs}{kv}", h, hkv, 128, bs, "bf16", seed=3 * h + bs,
+                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0 if kv == "bf16" else 1.0 / 64)
+    p = 48 * 1024
+    groups = [(p, [p + 1, p + 77, p + 3 * bs, p + 500]), (0, [20000])]
+    plan = wl.prefix_plan(groups, bs, torch.Generator().manual_seed(spec.seed))
+    x = wl.build_inputs(spec, plan, device="cuda", poison=True)
+    seqs = list(range(plan.num_seqs))
+    ref, ids, kc, vc = sampled_reference(x, seqs)
+    resident = {n: getattr(x, n) for n in ("q", "k_cache", "v_cache", "key", "value",
+                                           "slot_mapping", "block_tables", "context_lens",
+                                           "block_pairs")}
+    out, t = gpu_step_shared(x, t=resident)
+    assert_close(as_f64(out), ref, x.spec.dtype, spec.name)
+    del x, t, out
+    torch.cuda.empty_cache()
