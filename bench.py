@@ -53,6 +53,13 @@ DESCRIPTION.update({
 })
 for _n in ("llama7b", "llama13b", "gqa70b", "beam", "specdec70b", "chunked13b"):
     DESCRIPTION[_n + "_fp8"] = DESCRIPTION[_n].replace(", bf16", ", bf16 query / fp8 E4M3 KV cache")
+# Two long sequences of the GQA 70B shape: too few (sequence, kv head,
+# partition) workgroups to fill the chip at the fixed partition length.
+# "+fill": the same step at the batch-shaped length (PA_PARTITION_FILL).
+FEW_SEQS = {"gqa70b_x2": "gqa70b", "gqa70b_fp8_x2": "gqa70b_fp8"}
+for _n, _b in FEW_SEQS.items():
+    DESCRIPTION[_n] = DESCRIPTION[_b].replace("16 seqs", "2 seqs") + ", fixed partitions"
+    DESCRIPTION[_n + "+fill"] = DESCRIPTION[_n].replace("fixed partitions", "batch-shaped partitions")
 DESCRIPTION["swap13b"] = ("swap_blocks of 1024 random blocks of the LLaMA-13B-shaped pool (Hkv=40, BS=16, "
                           "D=128, bf16: 320 KiB of K+V per block) to pinned host memory and back")
 # "+prefix": the same step with pa_decode_shared_prefix (each shared page read
@@ -70,7 +77,7 @@ def parse():
                     choices=sorted(n for n in DESCRIPTION if n != "swap13b"))
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--others", default="llama7b,gqa70b,beam,beam+prefix,llama13b_fp8,gqa70b_fp8,"
-                                        "specdec70b,chunked13b,swap13b",
+                                        "specdec70b,chunked13b,gqa70b_x2,gqa70b_x2+fill,swap13b",
                     help="comma list of extra workloads to report ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -175,7 +182,10 @@ def run_workload(label, steps, warmup, partition_tokens, flush=False):
 
     name, _, variant = label.partition("+")
     shared_prefix = variant == "prefix"
-    x = wl.make_inputs(name, device="cuda", poison=False)
+    if name in FEW_SEQS:
+        x = wl.make_inputs(FEW_SEQS[name], device="cuda", poison=False, num_seqs=2)
+    else:
+        x = wl.make_inputs(name, device="cuda", poison=False)
     spec, plan = x.spec, x.plan
     out = torch.empty_like(x.q)
     code = binding.PA_F32 if spec.dtype == "f32" else binding.PA_BF16
@@ -190,6 +200,10 @@ def run_workload(label, steps, warmup, partition_tokens, flush=False):
             plan.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_dim, plan.block_size,
             plan.max_context_len, bounds[0], bounds[1], code, partition_tokens, ccode)
     else:
+        if variant == "fill":
+            partition_tokens = binding.pa_decode_partition_tokens(
+                plan.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_dim, plan.block_size,
+                plan.max_context_len, code, ccode, policy=binding.PA_PARTITION_FILL)
         ws_bytes = binding.pa_decode_workspace_size(
             plan.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_dim, plan.block_size,
             plan.max_context_len, code, partition_tokens, ccode)
@@ -283,6 +297,7 @@ def run_workload(label, steps, warmup, partition_tokens, flush=False):
         "workload": label,
         "description": DESCRIPTION[label],
         "num_seqs": plan.num_seqs,
+        "partition_tokens": partition_tokens,
         "total_context_tokens": int(sum(int(c) for c in plan.context_lens)),
         "ms_per_step": ms_per_step,
         "wall_ms_per_step": wall * 1e3 / steps if wall else None,

@@ -168,6 +168,36 @@ int pa_swap_blocks(void* dst_k_cache, void* dst_v_cache,
                    int num_src_blocks, int num_dst_blocks, int num_kv_heads,
                    int block_size, int head_dim, int cache_dtype, void* stream);
 
+/* pa_decode_partition_tokens policies */
+enum {
+  /* The fixed length pa_decode uses for partition_tokens == 0: it depends on
+   * the shape only (dtypes, block size, heads per kv head), never on the
+   * batch, so a sequence's output does not depend on its batch. */
+  PA_PARTITION_FIXED = 0,
+  /* A length shaped to the batch: the fixed one, halved (down to 256 tokens)
+   * while the batch's sequences x kv heads x partitions would leave the chip
+   * short of workgroups.  Faster for a few long sequences (one 32K-token
+   * grouped-query sequence: about 2x); the same as the fixed length for full
+   * batches.  A sequence's output may then change, within float32
+   * accumulation rounding, when the batch around it changes. */
+  PA_PARTITION_FILL = 1
+};
+
+/*
+ * pa_decode_partition_tokens -- the partition length (tokens, a positive
+ * multiple of block_size) that `policy` picks for a pa_decode call of these
+ * sizes, to be passed as partition_tokens to pa_decode_workspace_size and
+ * pa_decode.  Host only: touches no device and no memory.  Returns a negative
+ * status for sizes pa_decode_workspace_size would reject, and
+ * PA_ERR_UNSUPPORTED for an unknown policy.
+ * (Splitting a long context over workgroups and merging their partial softmax
+ * results is the partitioning of [luoboask] section 3; the pages fix no
+ * partition length.)
+ */
+int pa_decode_partition_tokens(int num_seqs, int num_heads, int num_kv_heads,
+                               int head_dim, int block_size, int max_context_len,
+                               int dtype, int cache_dtype, int policy);
+
 /*
  * pa_decode_workspace_size -- bytes of device workspace pa_decode needs for
  * these sizes.  Long contexts are cut into partitions of `partition_tokens`

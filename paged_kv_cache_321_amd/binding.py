@@ -24,10 +24,13 @@ PA_FP8_E4M3 = 2
 PA_DECODE_SHARED_PAGES = 1
 PA_MULTI_QUERY_TILES_ONLY = 1
 PA_MULTI_QUERY_ONE_STREAM = 2
+PA_PARTITION_FIXED = 0
+PA_PARTITION_FILL = 1
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
           -4: "PA_ERR_UNSUPPORTED", -5: "PA_ERR_ALIGN", -6: "PA_ERR_WORKSPACE",
           -7: "PA_ERR_LAUNCH", -8: "PA_ERR_VALUE"}
-EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_workspace_size",
+EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_partition_tokens",
+           "pa_decode_workspace_size",
            "pa_decode", "pa_decode_shared_prefix_workspace_size", "pa_decode_shared_prefix",
            "pa_multi_query_workspace_size", "pa_multi_query", "pa_swap_blocks",
            "pa_status_string")
@@ -51,6 +54,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_reshape_and_cache.restype = _c_int
     lib.pa_copy_blocks.argtypes = [_vp, _vp, _vp] + [_c_int] * 6 + [_vp]
     lib.pa_copy_blocks.restype = _c_int
+    lib.pa_decode_partition_tokens.argtypes = [_c_int] * 9
+    lib.pa_decode_partition_tokens.restype = _c_int
     lib.pa_decode_workspace_size.argtypes = [_c_int] * 9
     lib.pa_decode_workspace_size.restype = _c_size
     lib.pa_decode.argtypes = ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp] + [_c_int] * 7 +
@@ -157,6 +162,18 @@ def pa_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_pairs: to
     st = LIB.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_pairs), block_pairs.shape[0],
                             nb, hkv, bs, d, _dtype_code(k_cache), _stream(stream))
     _check(st, "pa_copy_blocks")
+
+
+def pa_decode_partition_tokens(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                               block_size: int, max_context_len: int, dtype: int,
+                               cache_dtype: Optional[int] = None,
+                               policy: int = PA_PARTITION_FIXED) -> int:
+    """Partition length ``policy`` picks for a pa_decode call of these sizes."""
+    cache_dtype = dtype if cache_dtype is None else cache_dtype
+    t = LIB.pa_decode_partition_tokens(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                       max_context_len, dtype, cache_dtype, policy)
+    _check(t if t < 0 else 0, "pa_decode_partition_tokens")
+    return t
 
 
 def pa_decode_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,

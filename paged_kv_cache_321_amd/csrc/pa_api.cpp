@@ -25,6 +25,10 @@ bool good_scale(float s) { return isfinite(s) && s > 0.f; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Partitions of n tokens (n >= 0, t > 0), computed in 64 bits so that lengths
+// near INT_MAX do not overflow.
+int parts_of(int n, int t) { return n <= t ? 1 : (int)(((int64_t)n + t - 1) / t); }
+
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
 bool supported_block_size(int bs) { return bs == 16 || bs == 32; }
 bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
@@ -95,11 +99,11 @@ DecodeSizes decode_sizes(int num_seqs, int num_heads, int num_kv_heads, int head
                                    shared_prefix, max_prefix_blocks * block_size);
   if (pt < 0) { z.status = pt; return z; }
   z.partition_tokens = pt;
-  z.grid_parts = max_context_len <= pt ? 1 : (max_context_len + pt - 1) / pt;
+  z.grid_parts = parts_of(max_context_len, pt);
   z.max_parts = z.grid_parts;
   if (shared_prefix) {
     z.prefix_parts = (int)(((int64_t)max_prefix_blocks * block_size + pt - 1) / pt);
-    z.tail_parts = max_tail_len <= pt ? 1 : (max_tail_len + pt - 1) / pt;
+    z.tail_parts = parts_of(max_tail_len, pt);
     z.max_parts = z.prefix_parts + z.tail_parts;
     if ((int64_t)num_seqs * z.max_parts * num_kv_heads > 0x7fffffffLL) {  // one-dimensional grid
       z.status = PA_ERR_UNSUPPORTED;
@@ -197,6 +201,18 @@ int pa_swap_blocks(void* dst_k_cache, void* dst_v_cache, const void* src_k_cache
   a.src_v_cache = src_v_cache;
   a.num_src_blocks = num_src_blocks;
   return pa::launch_copy_blocks(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int pa_decode_partition_tokens(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                               int block_size, int max_context_len, int dtype, int cache_dtype,
+                               int policy) {
+  if (policy != PA_PARTITION_FIXED && policy != PA_PARTITION_FILL) return PA_ERR_UNSUPPORTED;
+  const DecodeSizes z = decode_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                     max_context_len, dtype, cache_dtype, 0, false);
+  if (z.status != PA_OK) return z.status;
+  if (policy == PA_PARTITION_FIXED) return z.partition_tokens;
+  return pa::fill_partition_tokens(dtype, cache_dtype, head_dim, block_size, num_heads / num_kv_heads,
+                                   num_seqs, num_kv_heads, max_context_len);
 }
 
 size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
@@ -370,11 +386,11 @@ MultiQuerySizes multi_query_sizes(int num_seqs, int num_query_tokens, int num_he
   if (pt == 0) pt = pa::default_multi_query_partition_tokens(block_size, num_seqs, num_kv_heads, max_context_len);
   if (pt < 0 || pt % block_size != 0) { z.status = PA_ERR_SHAPE; return z; }
   z.partition_tokens = pt;
-  z.max_parts = max_context_len <= pt ? 1 : (max_context_len + pt - 1) / pt;
+  z.max_parts = parts_of(max_context_len, pt);
   const int dpt = pa::default_partition_tokens(dtype, cache_dtype, head_dim, block_size,
                                                num_heads / num_kv_heads, false, 0);
   z.decode_partition_tokens = dpt;
-  z.decode_grid_parts = max_context_len <= dpt ? 1 : (max_context_len + dpt - 1) / dpt;
+  z.decode_grid_parts = parts_of(max_context_len, dpt);
   if (z.decode_grid_parts > 1)
     z.decode_bytes = partition_area((uint64_t)num_seqs * num_heads * z.decode_grid_parts, head_dim,
                                     &z.decode_ml_bytes);

@@ -102,6 +102,21 @@ int default_partition_tokens(int dtype, int /*cache_dtype*/, int /*head_dim*/, i
   return u - u % block_size;
 }
 
+int fill_partition_tokens(int dtype, int cache_dtype, int head_dim, int block_size, int group,
+                          int num_seqs, int num_kv_heads, int max_context_len) {
+  // Batch-shaped: start from the fixed length and halve it, down to 256
+  // tokens, while the partition grid (sequences x kv heads x partitions of the
+  // longest context) has fewer workgroups than the chip needs to stay busy.
+  // Measured on batches of 1..32 sequences of 4K..64K tokens: one workgroup
+  // per compute unit on the matrix-core path, four on the vector path, whose
+  // workgroups each stream one head and have less work in flight.
+  const int64_t target = use_mfma_path(dtype, group) ? 256 : 1024;
+  int t = default_partition_tokens(dtype, cache_dtype, head_dim, block_size, group, false, 0);
+  while (t > 256 && (int64_t)num_seqs * num_kv_heads * (((int64_t)max_context_len + t - 1) / t) < target)
+    t /= 2;
+  return t - t % block_size;
+}
+
 hipError_t launch_decode(const DecodeLaunch& a) {
   DecodeParams p;
   p.out = a.out;

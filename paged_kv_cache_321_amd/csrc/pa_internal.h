@@ -112,6 +112,9 @@ struct MultiQueryLaunch {
 // Default partition length (tokens) for a shape; a multiple of block_size.
 int default_partition_tokens(int dtype, int cache_dtype, int head_dim, int block_size, int group,
                              bool shared_prefix, int max_prefix_tokens);
+// Partition length shaped to a pa_decode batch (PA_PARTITION_FILL).
+int fill_partition_tokens(int dtype, int cache_dtype, int head_dim, int block_size, int group,
+                          int num_seqs, int num_kv_heads, int max_context_len);
 
 hipError_t launch_decode(const DecodeLaunch& a);
 int default_multi_query_partition_tokens(int block_size, int num_seqs, int num_kv_heads, int max_context_len);

@@ -659,7 +659,8 @@ int default_multi_query_partition_tokens(int block_size, int num_seqs, int num_k
   // 2048 against 136 at 1024.
   constexpr int64_t kTargetItems = 1024;
   int t = 512;
-  while (t < 2048 && (int64_t)num_seqs * num_kv_heads * ((max_context_len + t - 1) / t) > kTargetItems) t *= 2;
+  while (t < 2048 && (int64_t)num_seqs * num_kv_heads * (((int64_t)max_context_len + t - 1) / t) > kTargetItems)
+    t *= 2;
   return t - t % block_size;
 }
 

@@ -124,6 +124,113 @@ def test_workspace_size():
     assert ws(3, 8, 2, 64, 16, 2000, F32, FP8, 512) == bad
 
 
+def test_workspace_size_near_int_max():
+    # Partition counts of a 2^31 - 1 token bound are computed without overflow.
+    big = 2**31 - 1
+    ws = LIB.pa_decode_workspace_size
+    parts = -(-big // 2048)
+    rows = 2 * 8 * parts
+    ml = (rows * 2 * 4 + 255) // 256 * 256
+    assert ws(2, 8, 8, 64, 16, big, F32, F32, 2048) == ml + rows * 64 * 4
+    mq = LIB.pa_multi_query_workspace_size(1, 4, 8, 2, 128, 16, big, BF16, BF16, 2048)
+    assert mq == _area(1 * 8 * -(-big // 4096), 128) + _area(4 * 8 * -(-big // 2048), 128) + \
+        _work(1, 4, 4, -(-big // 2048))
+
+
+FIXED, FILL = binding.PA_PARTITION_FIXED, binding.PA_PARTITION_FILL
+
+
+def partition(S, H, Hkv, D, BS, maxctx, dtype=BF16, cdtype=None, policy=FIXED):
+    cdtype = dtype if cdtype is None else cdtype
+    return LIB.pa_decode_partition_tokens(S, H, Hkv, D, BS, maxctx, dtype, cdtype, policy)
+
+
+def test_partition_tokens_fixed_is_the_default():
+    # The fixed policy names the length partition_tokens = 0 selects: 4096 on
+    # the matrix-core path (bf16 query, G >= 2), 2048 on the vector path.
+    assert partition(1, 64, 8, 128, 16, 100) == 4096
+    assert partition(1, 64, 8, 128, 32, 100, cdtype=FP8) == 4096
+    assert partition(1, 40, 40, 128, 16, 100) == 2048
+    assert partition(1, 8, 2, 64, 16, 100, dtype=F32) == 2048
+    for S, H, Hkv, D, BS, maxctx, dt, cdt in [(3, 8, 2, 64, 16, 9000, F32, F32),
+                                              (5, 64, 8, 128, 16, 70000, BF16, BF16),
+                                              (2, 32, 32, 128, 32, 5000, BF16, FP8)]:
+        t = partition(S, H, Hkv, D, BS, maxctx, dt, cdt)
+        assert LIB.pa_decode_workspace_size(S, H, Hkv, D, BS, maxctx, dt, cdt, t) == \
+            LIB.pa_decode_workspace_size(S, H, Hkv, D, BS, maxctx, dt, cdt, 0)
+
+
+def _fill_rule(S, Hkv, maxctx, fixed, target):
+    # The documented rule written out: halve the fixed length (down to 256)
+    # while sequences x kv heads x partitions stays under the target.
+    t = fixed
+    while t > 256 and S * Hkv * -(-maxctx // t) < target:
+        t //= 2
+    return t
+
+
+@pytest.mark.parametrize("S,maxctx,want", [
+    (1, 32768, 1024),   # 8 kv heads x 32 partitions = 256 workgroups
+    (2, 32768, 2048),
+    (4, 32768, 4096),
+    (1, 4096, 256),     # the floor: 128 workgroups
+    (32, 4096, 4096),
+    (1, 131072, 4096),  # 8 x 32 = 256 already at the fixed length
+    (0, 4096, 256),
+    (1, 0, 256),
+])
+def test_partition_tokens_fill_matrix_core_path(S, maxctx, want):
+    assert partition(S, 64, 8, 128, 16, maxctx, policy=FILL) == want
+    assert partition(S, 64, 8, 128, 16, maxctx, cdtype=FP8, policy=FILL) == want
+
+
+@pytest.mark.parametrize("S,maxctx,want", [
+    (1, 4096, 256),     # 40 heads x 16 partitions = 640 < 1024 at the floor
+    (2, 4096, 256),
+    (4, 4096, 512),     # 4 x 40 x 8 = 1280
+    (1, 16384, 512),
+    (2, 16384, 1024),
+    (4, 16384, 2048),
+    (16, 4096, 2048),
+])
+def test_partition_tokens_fill_vector_path(S, maxctx, want):
+    assert partition(S, 40, 40, 128, 16, maxctx, policy=FILL) == want
+
+
+def test_partition_tokens_fill_properties():
+    cases = [(H, Hkv, D, BS, dt, cdt)
+             for H, Hkv in ((8, 8), (16, 8), (32, 8), (64, 8), (40, 40))
+             for D in (64, 128) for BS in (16, 32)
+             for dt, cdt in ((F32, F32), (BF16, BF16), (BF16, FP8))]
+    for H, Hkv, D, BS, dt, cdt in cases:
+        fixed = partition(1, H, Hkv, D, BS, 1000, dt, cdt)
+        target = 256 if dt == BF16 and H > Hkv else 1024
+        for maxctx in (1, 300, 4096, 20000, 131072, 2**31 - 1):
+            prev = 0
+            for S in (1, 2, 3, 8, 64, 1024):
+                t = partition(S, H, Hkv, D, BS, maxctx, dt, cdt, policy=FILL)
+                assert t == _fill_rule(S, Hkv, maxctx, fixed, target)
+                assert t % BS == 0 and 256 <= t <= fixed and t >= prev   # more sequences, never shorter
+                prev = t
+                assert LIB.pa_decode_workspace_size(S, H, Hkv, D, BS, maxctx, dt, cdt, t) != \
+                    ctypes.c_size_t(-1).value
+
+
+def test_partition_tokens_rejects():
+    assert partition(1, 64, 8, 128, 16, 100, policy=2) == UNSUP
+    assert partition(1, 64, 8, 128, 16, 100, policy=-1) == UNSUP
+    assert partition(1, 64, 6, 128, 16, 100) == SHAPE
+    assert partition(1, 64, 8, 96, 16, 100, policy=FILL) == UNSUP
+    assert partition(1, 64, 8, 128, 16, 100, dtype=FP8) == DTYPE
+    assert partition(1, 64, 8, 128, 16, 100, dtype=F32, cdtype=FP8) == UNSUP
+    assert partition(-1, 64, 8, 128, 16, 100, policy=FILL) == SHAPE
+    assert partition(1, 64, 8, 128, 16, -5) == SHAPE
+    with pytest.raises(binding.PaError):
+        binding.pa_decode_partition_tokens(1, 64, 6, 128, 16, 100, BF16)
+    assert binding.pa_decode_partition_tokens(2, 64, 8, 128, 16, 32768, BF16,
+                                              policy=FILL) == 2048
+
+
 def decode_shared(**kw):
     a = dict(out=P, q=P, k=P, v=P, bt=P, mb=8, ctx=P, lead=P, nblk=P, S=2, H=8, Hkv=2, D=128,
              BS=16, NB=32, maxctx=100, mpb=4, mtail=60, scale=0.1, dtype=BF16, cdtype=None, ks=0.5,

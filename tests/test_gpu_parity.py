@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from paged_kv_cache_321_amd import workloads as wl
+from paged_kv_cache_321_amd import binding, workloads as wl
 
 from gpu_helpers import (as_f64, assert_close, bits, gpu_step, on_device, oracle_step,
                          sampled_reference)
@@ -53,6 +53,27 @@ def test_partitions_llama7b_small(pt):
 @pytest.mark.parametrize("pt", [32, 1024])
 def test_partitions_gqa_small(pt):
     x = wl.make_inputs("gqa70b", **SMALL["gqa70b"])
+    check_case(x, partition_tokens=pt)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("gqa70b", dict(num_seqs=1, context_len=20000)),
+    ("gqa70b_fp8", dict(num_seqs=2, context_len=9000)),
+    ("llama13b", dict(num_seqs=2, context_len=5000)),
+    ("tiny", dict()),
+])
+def test_fill_partitions(name, kw):
+    """A few long sequences with the batch-shaped partition length
+    (PA_PARTITION_FILL): shorter partitions than the fixed ones, same result."""
+    x = wl.make_inputs(name, **kw)
+    sp = x.spec
+    code = {"f32": binding.PA_F32, "bf16": binding.PA_BF16}[sp.dtype]
+    ccode = binding.PA_FP8_E4M3 if sp.kv_dtype == "fp8" else code
+    args = (x.plan.num_seqs, sp.num_heads, sp.num_kv_heads, sp.head_dim, sp.block_size,
+            x.max_context_len, code, ccode)
+    pt = binding.pa_decode_partition_tokens(*args, policy=binding.PA_PARTITION_FILL)
+    fixed = binding.pa_decode_partition_tokens(*args)
+    assert pt <= fixed and (name == "tiny" or pt < fixed)
     check_case(x, partition_tokens=pt)
 
 
