@@ -53,13 +53,18 @@ DESCRIPTION.update({
 })
 for _n in ("llama7b", "llama13b", "gqa70b", "beam", "specdec70b", "chunked13b"):
     DESCRIPTION[_n + "_fp8"] = DESCRIPTION[_n].replace(", bf16", ", bf16 query / fp8 E4M3 KV cache")
-# Two long sequences of the GQA 70B shape: too few (sequence, kv head,
-# partition) workgroups to fill the chip at the fixed partition length.
-# "+fill": the same step at the batch-shaped length (PA_PARTITION_FILL).
-FEW_SEQS = {"gqa70b_x2": "gqa70b", "gqa70b_fp8_x2": "gqa70b_fp8"}
-for _n, _b in FEW_SEQS.items():
-    DESCRIPTION[_n] = DESCRIPTION[_b].replace("16 seqs", "2 seqs") + ", fixed partitions"
+# Variants of a workload's plan: (base workload, plan overrides).
+# Two long sequences of the GQA 70B shape have too few (sequence, kv head,
+# partition) workgroups to fill the chip at the fixed partition length;
+# "+fill" runs the same step at the batch-shaped length (PA_PARTITION_FILL).
+# Verification of 4 drafted tokens over an E4M3 cache (32 rows per sequence)
+# runs on the streaming multi-query kernel.
+VARIANTS = {"gqa70b_x2": ("gqa70b", {"num_seqs": 2}), "gqa70b_fp8_x2": ("gqa70b_fp8", {"num_seqs": 2}),
+            "specdec70b_fp8_q4": ("specdec70b_fp8", {"query_len": 4})}
+for _n in ("gqa70b_x2", "gqa70b_fp8_x2"):
+    DESCRIPTION[_n] = DESCRIPTION[VARIANTS[_n][0]].replace("16 seqs", "2 seqs") + ", fixed partitions"
     DESCRIPTION[_n + "+fill"] = DESCRIPTION[_n].replace("fixed partitions", "batch-shaped partitions")
+DESCRIPTION["specdec70b_fp8_q4"] = DESCRIPTION["specdec70b_fp8"].replace("6 new tokens", "4 new tokens")
 DESCRIPTION["swap13b"] = ("swap_blocks of 1024 random blocks of the LLaMA-13B-shaped pool (Hkv=40, BS=16, "
                           "D=128, bf16: 320 KiB of K+V per block) to pinned host memory and back")
 # "+prefix": the same step with pa_decode_shared_prefix (each shared page read
@@ -77,7 +82,7 @@ def parse():
                     choices=sorted(n for n in DESCRIPTION if n != "swap13b"))
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--others", default="llama7b,gqa70b,beam,beam+prefix,llama13b_fp8,gqa70b_fp8,"
-                                        "specdec70b,chunked13b,gqa70b_x2,gqa70b_x2+fill,swap13b",
+                                        "specdec70b,specdec70b_fp8_q4,chunked13b,gqa70b_x2,gqa70b_x2+fill,swap13b",
                     help="comma list of extra workloads to report ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -182,8 +187,8 @@ def run_workload(label, steps, warmup, partition_tokens, flush=False):
 
     name, _, variant = label.partition("+")
     shared_prefix = variant == "prefix"
-    if name in FEW_SEQS:
-        x = wl.make_inputs(FEW_SEQS[name], device="cuda", poison=False, num_seqs=2)
+    if name in VARIANTS:
+        x = wl.make_inputs(VARIANTS[name][0], device="cuda", poison=False, **VARIANTS[name][1])
     else:
         x = wl.make_inputs(name, device="cuda", poison=False)
     spec, plan = x.spec, x.plan

@@ -74,6 +74,8 @@ struct MultiQueryParams {
   int* work_count;     // number of work items
   int work_capacity;   // items the list holds (the grid's bound)
   int decode_rows_elsewhere;  // sequences with one query run in the decode kernels
+  int stream_rows;     // single-block sequences of at most this many rows run in the
+                       // streaming kernel (0: none), the others in the ring kernel
   float scale_log2e;   // softmax scale * log2(e), times k_scale for fp8 caches
   float v_scale;       // multiplies the output (1 unless the cache holds fp8 codes)
 };
@@ -184,6 +186,7 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   const int part = w.y & 0xffff;
   const MqBlock b = mq_block<G>(p, s, rbi);
   if (b.skip || part >= b.nparts) return;
+  if (b.nrb == 1 && b.rows <= p.stream_rows) return;  // the streaming kernel's
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -513,6 +516,314 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   }
 }
 
+// Verification rows over an E4M3 cache (a sequence of at most 32 rows) in
+// the decode kernel's layout instead of the LDS ring: each wave streams its own pages of
+// the partition (page pg0 + wave + 4 k) with one page in flight, K straight
+// from the cache into the A operand and V through a per-wave LDS page read
+// back transposed, and computes all of the sequence's rows as NCT 16-column
+// tiles of S^T = K Q^T and O^T += V^T P^T (the K and V^T operands are shared
+// by the tiles).  No barrier inside the walk: every wave's dependency chain
+// overlaps the others' loads, where the ring's per-step barriers (two for
+// E4M3, around the widening) expose it.
+// Column l16 of tile ct is row 16 ct + l16 (query r / G, head r % G) with its
+// own causal limit; the waves' partial states are merged through LDS, one tile
+// at a time, into the row (one partition) or its partition slot, which the
+// reduce kernel merges.  Needs the partition's pages to fit one page id per
+// lane and wave (partition_tokens <= 256 pages).
+template <typename TC, int D, int BS, int G, int NCT>
+__global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void multi_query_stream_kernel(MultiQueryParams p) {
+  constexpr bool kFp8 = sizeof(TC) == 1;
+  constexpr int NT = BS / 16;       // 16-token tiles per page
+  constexpr int NC = D / 32;        // 32-wide steps of the QK contraction
+  constexpr int NM = D / 16;        // 16-wide output tiles along head_dim
+  constexpr int ROWB = D * 2;       // bytes of one bf16 token row (LDS page)
+  constexpr int CROWB = D * (int)sizeof(TC);  // bytes of one cache token row
+  constexpr int CNCH = CROWB / 16;  // 16-byte cache chunks per row
+  constexpr int RPL = 64 / CNCH;    // rows per row-contiguous wave load of V
+  constexpr int NV = BS / RPL;      // V loads per lane per page
+  constexpr int NKL = kFp8 ? D / 64 : NC;  // K loads per 16-token tile
+  constexpr int PAGEB = BS * ROWB;  // bytes of one bf16 page in LDS
+  constexpr int EPI = (kMqWaves * 16 * D + 2 * kMqWaves * 16) * 4;
+  constexpr int SMEM = kMqWaves * PAGEB > EPI ? kMqWaves * PAGEB : EPI;
+  static_assert(NCT >= 1 && NCT * 16 <= kRowsPerBlock && BS % RPL == 0, "tile shape");
+
+  const int kvh = blockIdx.x % p.num_kv_heads;
+  const int item = blockIdx.x / p.num_kv_heads;
+  if (item >= *p.work_count) return;  // uniform over the workgroup
+  const int2 w = p.work[item];
+  const int s = w.x;
+  const int part = w.y & 0xffff;
+  const MqBlock b = mq_block<G>(p, s, w.y >> 16);
+  if (b.skip || part >= b.nparts || b.nrb != 1 || b.rows > p.stream_rows) return;  // the ring kernel's
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15;
+  const int g4 = lane >> 4;
+
+  const int pt = p.partition_tokens;
+  const int tok0 = b.nparts > 1 ? part * pt : 0;
+  const int tok1 = b.bad ? tok0 : (b.nparts > 1 ? min(b.kv_end, tok0 + pt) : b.kv_end);
+  const int pg0 = tok0 / BS;
+  const int npg = tok1 > tok0 ? (tok1 - tok0 + BS - 1) / BS : 0;
+  const int nk = npg > wave ? (npg - wave + kMqWaves - 1) / kMqWaves : 0;  // <= 64 (host bound)
+  // Pages every row sees in full: no mask.
+  const int full_end = min(tok1, b.ctx - b.qlen + 1);
+
+  // Physical id of this wave's page k in lane k (ids outside the pool become
+  // 0 and make the wave's results NaN).
+  int my_id = 0;
+  bool id_bad = false;
+  if (lane < nk) {
+    my_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + pg0 + wave + kMqWaves * lane];
+    id_bad = my_id < 0 || my_id >= p.num_blocks;
+    if (id_bad) my_id = 0;
+  }
+  const bool bad = b.bad || __any(id_bad);
+
+  // B operands (Q^T) of the tiles: for bf16 caches lane holds row l16's
+  // columns 32c + 8 g4 .. +7; for E4M3 caches, whose 16-byte K loads carry 16
+  // columns, step c = 2kk + h holds columns 64kk + 16 g4 + 8h .. +7 (the K
+  // operand takes the same order).  Zero for rows past the sequence's.
+  bf16x8_t qb[NCT][NC];
+  int lim[NCT];  // column l16 of tile ct sees tokens < lim[ct]
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int r = 16 * ct + l16;
+    const bool row_ok = r < b.rows;
+    const int qi = row_ok ? r / G : 0;
+    lim[ct] = row_ok ? min(tok1, b.ctx - b.qlen + qi + 1) : 0;
+    const uint16_t* qp =
+        static_cast<const uint16_t*>(p.q) + ((int64_t)(b.t0 + qi) * p.num_heads + kvh * G + (row_ok ? r % G : 0)) * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int col0 = kFp8 ? 64 * (c >> 1) + 16 * g4 + 8 * (c & 1) : 32 * c + 8 * g4;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (row_ok) v = *reinterpret_cast<const uint4*>(qp + col0);
+      qb[ct][c] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  f32x4_t acc[NCT][NM];  // O^T[d = 16 m + 4 g4 + j][row 16 ct + l16]
+  float m_run[NCT], l_run[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) acc[ct][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[ct] = -FLT_MAX;
+    l_run[ct] = 0.f;
+  }
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  unsigned char* vbuf = smem + wave * PAGEB;
+
+  const TC* kc = static_cast<const TC*>(p.k_cache) + (int64_t)kvh * BS * D;
+  const TC* vc = static_cast<const TC*>(p.v_cache) + (int64_t)kvh * BS * D;
+  const int k_off = l16 * D + (kFp8 ? 16 : 8) * g4;  // A operand: token l16
+  const int v_row = lane / CNCH;                     // row-contiguous V load
+  const int v_ch = lane % CNCH;
+  const int v_off = v_row * D + v_ch * (16 / (int)sizeof(TC));
+
+  auto load_k = [&](int k, uint4 (&kr)[NT][NKL]) {
+    const int64_t phys = __builtin_amdgcn_readlane(my_id, k);
+    const TC* kp = kc + phys * p.block_stride + k_off;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int c = 0; c < NKL; ++c) kr[tt][c] = load_page16<true>(kp + tt * 16 * D + (kFp8 ? 64 : 32) * c);
+  };
+  auto load_v = [&](int k, uint4 (&vr)[NV]) {
+    const int64_t phys = __builtin_amdgcn_readlane(my_id, k);
+    const TC* vp = vc + phys * p.block_stride + v_off;
+#pragma unroll
+    for (int n = 0; n < NV; ++n) vr[n] = load_page16<true>(vp + n * RPL * D);
+  };
+  // V page into LDS in the transposed-read layout; rows past the partition
+  // end become zeros, so unread cache bytes (possibly NaN) never reach PV.
+  auto stage_v = [&](int k, const uint4 (&vr)[NV]) {
+    const int t0 = (pg0 + wave + k * kMqWaves) * BS;
+    const bool whole = t0 + BS <= tok1;
+    wave_lds_fence();
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      const int row = n * RPL + v_row;
+      const bool keep = whole || t0 + row < tok1;
+      if constexpr (kFp8) {
+        uint4 lo = fp8x8_to_bf16x8(vr[n].x, vr[n].y);
+        uint4 hi = fp8x8_to_bf16x8(vr[n].z, vr[n].w);
+        if (!keep) lo = hi = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(vbuf + row * ROWB + (((2 * v_ch) ^ swz<ROWB>(row)) << 4)) = lo;
+        *reinterpret_cast<uint4*>(vbuf + row * ROWB + (((2 * v_ch + 1) ^ swz<ROWB>(row)) << 4)) = hi;
+      } else {
+        uint4 v = vr[n];
+        if (!keep) v = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(vbuf + row * ROWB + ((v_ch ^ swz<ROWB>(row)) << 4)) = v;
+      }
+    }
+    wave_lds_fence();
+  };
+
+  auto scores = [&](const uint4 (&kr)[NT][NKL], f32x4_t (&st)[NCT][NT]) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) st[ct][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        uint4 ka;
+        if constexpr (kFp8) {
+          const uint4& kw = kr[tt][c >> 1];
+          ka = (c & 1) ? fp8x8_to_bf16x8(kw.z, kw.w) : fp8x8_to_bf16x8(kw.x, kw.y);
+        } else {
+          ka = kr[tt][c];
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+          st[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qb[ct][c],
+                                                               st[ct][tt], 0, 0, 0);
+      }
+  };
+
+  auto softmax_pv = [&](int k, const f32x4_t (&st)[NCT][NT]) {
+    const int t0 = (pg0 + wave + k * kMqWaves) * BS;
+    const bool full = t0 + BS <= full_end;
+    // P^T of each tile (token 16 tt + 4 g4 + j of row l16 in this lane).
+    uint32_t pw[NCT][2 * NT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      float sv[NT][4];
+      float mx = m_run[ct];
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool valid = full || t0 + 16 * tt + 4 * g4 + j < lim[ct];
+          sv[tt][j] = valid ? st[ct][tt][j] * p.scale_log2e : -__builtin_inff();
+          mx = fmaxf(mx, sv[tt][j]);
+        }
+      mx = column_max(mx);
+      // Lazy rescaling (reference moves only when exceeded by more than
+      // 2^kRescaleLog2); a wave-uniform branch per tile.
+      if (__any(mx > m_run[ct] + kRescaleLog2)) {
+        const float alpha = fast_exp2(m_run[ct] - mx);
+        m_run[ct] = mx;
+        l_run[ct] *= alpha;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) acc[ct][m] *= alpha;
+      }
+      float ps = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sv[tt][j] = fast_exp2(sv[tt][j] - m_run[ct]);
+          ps += sv[tt][j];
+        }
+      l_run[ct] += ps;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        pw[ct][2 * tt] = pack_bf16x2(sv[tt][0], sv[tt][1]);
+        pw[ct][2 * tt + 1] = pack_bf16x2(sv[tt][2], sv[tt][3]);
+      }
+    }
+    // O^T += V^T P^T; each V^T read feeds every tile.
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      if constexpr (BS == 32) {
+        // k slot j of lane group g4: token 4 g4 + j (j < 4) or 16 + 4 g4 + j - 4.
+        const s16x4_t lo = vt4<ROWB>(vbuf, l16, 4 * g4, 16 * m);
+        const s16x4_t hi = vt4<ROWB>(vbuf, l16, 16 + 4 * g4, 16 * m);
+        const s16x8_t va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          const uint4 pbits = make_uint4(pw[ct][0], pw[ct][1], pw[ct][2], pw[ct][3]);
+          acc[ct][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va),
+                                                               __builtin_bit_cast(bf16x8_t, pbits), acc[ct][m], 0,
+                                                               0, 0);
+        }
+      } else {
+        const s16x4_t va = vt4<ROWB>(vbuf, l16, 4 * g4, 16 * m);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          const uint2 pbits = make_uint2(pw[ct][0], pw[ct][1]);
+          acc[ct][m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, __builtin_bit_cast(s16x4_t, pbits), acc[ct][m],
+                                                                 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // One K and one V register buffer per wave, as in the decode kernel: the
+  // next page's V is requested once this page's V sits in LDS, the next K
+  // once the QK products have consumed this page's K.
+  if (!bad && nk > 0) {
+    uint4 kr[NT][NKL], vr[NV];
+    load_k(0, kr);
+    load_v(0, vr);
+    for (int k = 0; k < nk; ++k) {
+      stage_v(k, vr);
+      if (k + 1 < nk) load_v(k + 1, vr);
+      f32x4_t st[NCT][NT];
+      scores(kr, st);
+      if (k + 1 < nk) load_k(k + 1, kr);
+      softmax_pv(k, st);
+    }
+  }
+
+  // Merge the waves' states tile by tile through LDS.
+  float* sm_acc = reinterpret_cast<float*>(smem);  // [kMqWaves][16][D]
+  float* sm_m = sm_acc + kMqWaves * 16 * D;          // [kMqWaves][16]
+  float* sm_l = sm_m + kMqWaves * 16;
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    if (16 * ct >= b.rows) break;  // uniform over the workgroup
+    float l = l_run[ct];
+    l += __shfl_xor(l, 16);  // the four lanes of a column each hold a share
+    l += __shfl_xor(l, 32);
+    __syncthreads();  // the page buffers (first tile) or the previous tile are done with
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm_acc[(wave * 16 + l16) * D + 16 * m + 4 * g4 + j] = acc[ct][m][j];
+    if (g4 == 0) {
+      sm_m[wave * 16 + l16] = bad ? 0.f : m_run[ct];
+      sm_l[wave * 16 + l16] = bad ? __builtin_nanf("") : l;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < 16 * D; idx += kMqWaves * 64) {
+      const int c = idx / D;
+      const int d = idx % D;
+      const int r = 16 * ct + c;
+      if (r >= b.rows) continue;
+      float mm = -FLT_MAX;
+#pragma unroll
+      for (int wv = 0; wv < kMqWaves; ++wv) mm = fmaxf(mm, sm_m[wv * 16 + c]);
+      float ll = 0.f, aa = 0.f;
+#pragma unroll
+      for (int wv = 0; wv < kMqWaves; ++wv) {
+        const float wt = fast_exp2(sm_m[wv * 16 + c] - mm);
+        ll += sm_l[wv * 16 + c] * wt;
+        aa += sm_acc[(wv * 16 + c) * D + d] * wt;
+      }
+      const int64_t orow = (int64_t)(b.t0 + r / G) * p.num_heads + kvh * G + r % G;
+      if (b.nparts == 1) {
+        const float o = ll == 0.f ? 0.f : aa * (p.v_scale / ll);
+        Elem<uint16_t>::store(static_cast<uint16_t*>(p.out) + orow * D + d, o);
+      } else {
+        const int64_t slot = orow * p.max_parts + part;
+        p.ws_acc[slot * D + d] = aa;
+        if (d == 0) {
+          p.ws_ml[slot * 2] = mm;
+          p.ws_ml[slot * 2 + 1] = ll;
+        }
+      }
+    }
+  }
+}
+
 // The work list: one item per (sequence, row block) of every sequence with
 // more than one query, or per (sequence, partition) for a sequence whose rows
 // fit one block; ordered by sequence, a sequence's last row blocks (the ones
@@ -600,24 +911,53 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_reduce_kernel(Multi
 }
 
 template <typename TC, int D, int BS, int G>
-hipError_t launch_t(const MultiQueryLaunch& a, const MultiQueryParams& p) {
+hipError_t launch_t(const MultiQueryLaunch& a, MultiQueryParams p) {
+  // E4M3 caches: sequences whose rows fit two 16-row tiles stream on the
+  // decode layout (multi_query_stream_kernel), when a partition holds at most
+  // 256 pages (one page id per lane and wave).  The choice depends on the
+  // sequence and the partition length alone, so with a fixed partition length
+  // a sequence's rows are the same bits in any batch.  Measured on the 70B
+  // verification shape, 32 sequences, default partitions: E4M3 with 1-4
+  // queries 72-83 us against 87-98 us on the ring; with 6 queries (three
+  // tiles) 119 against 106, and bf16 at every query length 117-144 against
+  // 104-120, so those stay on the ring.
+  constexpr int kStreamRows = sizeof(TC) == 1 ? 32 : 0;
+  p.stream_rows = a.partition_tokens <= 256 * BS ? kStreamRows : 0;
+  const int rows = a.max_query_len * G;  // rows of the longest sequence
   hipLaunchKernelGGL((multi_query_schedule_kernel<G>), dim3(1), dim3(256), 0, a.stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // When every sequence's rows fit one block (verification batches: each
-  // page is read by one workgroup, the kernel streams) a two-stage ring
-  // (D = 128: 32 KiB of LDS for bf16, 16 + 16 KiB for E4M3 with its widened
-  // tile) lets four workgroups share a CU; longer chunks, whose row blocks
-  // re-read pages from L2, take three stages (48 KiB; E4M3 24 + 16 KiB).
-  // Measured on the 70B-shaped verification batch (bf16): 115 us against
-  // 126 us; on the chunked-prefill batch: 690 us against 651 us.
   const dim3 grid((unsigned)((int64_t)a.work_capacity * a.num_kv_heads));
-  if (a.max_row_blocks == 1)
-    hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G, 2>), grid, dim3(kMqWaves * 64), 0, a.stream, p);
-  else
-    hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G, 3>), grid, dim3(kMqWaves * 64), 0, a.stream, p);
-  e = hipGetLastError();
-  if (e != hipSuccess || a.max_parts <= 1) return e;
+  // The ring kernel takes the other sequences, and runs when the batch can
+  // hold any.  When every sequence's rows fit one block (each page is read by
+  // one workgroup) a two-stage ring (D = 128: 32 KiB of LDS for bf16, 16 + 16
+  // KiB for E4M3 with its widened tile) lets four workgroups share a CU;
+  // longer chunks, whose row blocks re-read pages from L2, take three stages
+  // (48 KiB; E4M3 24 + 16 KiB).  Measured on the 70B-shaped verification
+  // batch (bf16): 115 us against 126 us; on the chunked-prefill batch: 690 us
+  // against 651 us.
+  if (rows > p.stream_rows) {
+    if (a.max_row_blocks == 1)
+      hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G, 2>), grid, dim3(kMqWaves * 64), 0, a.stream, p);
+    else
+      hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G, 3>), grid, dim3(kMqWaves * 64), 0, a.stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // After the ring kernel: on a chunked-prefill batch, which has no such
+  // sequence, its workgroups only look up their item and exit, and launched
+  // first they would wait for CU slots ahead of the ring kernel (50 us).
+  if constexpr (kStreamRows > 0) {
+    if (p.stream_rows > 0) {
+      if (rows <= 16)
+        hipLaunchKernelGGL((multi_query_stream_kernel<TC, D, BS, G, 1>), grid, dim3(kMqWaves * 64), 0, a.stream, p);
+      else
+        hipLaunchKernelGGL((multi_query_stream_kernel<TC, D, BS, G, 2>), grid, dim3(kMqWaves * 64), 0, a.stream, p);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  if (a.max_parts <= 1) return hipSuccess;
   hipLaunchKernelGGL((multi_query_reduce_kernel<D, G>), dim3((unsigned)a.num_seqs * a.num_kv_heads),
                      dim3(kMqWaves * 64), 0, a.stream, p);
   return hipGetLastError();
@@ -691,6 +1031,7 @@ hipError_t launch_multi_query(const MultiQueryLaunch& a) {
   p.work_count = a.work_count;
   p.work_capacity = a.work_capacity;
   p.decode_rows_elsewhere = a.decode_rows_elsewhere ? 1 : 0;
+  p.stream_rows = 0;  // set per shape by launch_t
   const bool fp8 = a.cache_dtype == kDtypeFp8;
   p.scale_log2e = a.scale * kLog2e * (fp8 ? a.k_scale : 1.f);
   p.v_scale = fp8 ? a.v_scale : 1.f;

@@ -69,9 +69,9 @@ def test_shapes(h, hkv, d, bs):
 
 @pytest.mark.parametrize("h,hkv,d,bs", SHAPES)
 def test_shapes_single_block(h, hkv, d, bs):
-    """Every sequence's rows fit one 64-row block (the verification case, run
-    with the two-stage ring for bf16 caches): query lengths up to 64 / G over
-    ragged contexts, with and without partitions."""
+    """Every sequence's rows fit one 64-row block: query lengths up to 64 / G
+    over ragged contexts, with and without partitions.  Sequences of more rows
+    than the streaming kernel takes run on the two-stage ring beside it."""
     g = h // hkv
     spec = wl.Spec(f"mq1b{h}x{hkv}x{d}x{bs}", h, hkv, d, bs, "bf16", seed=7 * h + d + bs)
     qmax = 64 // g
@@ -82,6 +82,53 @@ def test_shapes_single_block(h, hkv, d, bs):
     check_mq(x)
     check_mq(x, partition_tokens=2 * bs)
     check_mq(x, tiles_only=True)
+
+
+def stream_rows(kv):
+    """Rows of a sequence the streaming kernel takes (E4M3 caches only)."""
+    return 32 if kv == "fp8" else 0
+
+
+def stream_case(h, hkv, d, bs, cap, kv="bf16", seed=0):
+    """Sequences of at most `cap` rows (query lengths up to cap / G) over ragged
+    contexts, one of them a single query, one empty."""
+    g = h // hkv
+    spec = wl.Spec(f"mqs{h}x{hkv}x{d}x{bs}{kv}{cap}", h, hkv, d, bs, "bf16", seed=11 * h + d + bs + cap + seed,
+                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0 if kv == "bf16" else 1.0 / 64)
+    qmax = max(1, cap // g)
+    qlens = [qmax, 1, min(2, qmax), 0, qmax, max(1, qmax // 2)]
+    ctx = [qmax + 700, 333, 6 + 2 * bs + 1, 50, qmax, 2 * bs + qmax + 3]
+    plan = wl.multi_query_plan(ctx, qlens, bs, torch.Generator().manual_seed(spec.seed))
+    return wl.build_inputs(spec, plan)
+
+
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+@pytest.mark.parametrize("h,hkv,d,bs", SHAPES)
+def test_shapes_stream(h, hkv, d, bs, kv):
+    """Verification-shaped batches: at most 16, 32 and 48 rows per sequence,
+    with and without partitions, single queries in the tiles too.  Over an
+    E4M3 cache the first two run on the streaming kernel at one and two
+    16-row tiles, the third beside the ring kernel; bf16 runs on the ring."""
+    for cap in (16, 32, 48):
+        if cap < h // hkv:
+            continue
+        x = stream_case(h, hkv, d, bs, cap, kv=kv)
+        check_mq(x)
+        check_mq(x, partition_tokens=2 * bs)
+        check_mq(x, tiles_only=True)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_stream_partition_of_256_pages(kv):
+    """A partition of exactly 256 pages (64 per wave, the streaming kernel's
+    bound) and one page more, cut in two; the 48-row sequence beside them runs
+    on the ring."""
+    bs = 16
+    spec = wl.Spec(f"mqs256{kv}", 64, 8, 128, bs, "bf16", seed=77,
+                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0 if kv == "bf16" else 1.0 / 64)
+    plan = wl.multi_query_plan([256 * bs, 256 * bs + 5, 90], [4, 2, 6], bs,
+                               torch.Generator().manual_seed(8))
+    check_mq(wl.build_inputs(spec, plan), partition_tokens=256 * bs)
 
 
 @pytest.mark.parametrize("h,hkv,d,bs", [(8, 8, 128, 16), (64, 8, 128, 32), (16, 8, 64, 16),
@@ -169,12 +216,14 @@ def test_long_context_page_window(h, hkv, d, bs, kv):
     check_mq(wl.build_inputs(spec, plan), partition_tokens=512 * bs)
 
 
-@pytest.mark.parametrize("name", ["specdec70b", "chunked13b", "specdec70b_fp8"])
-def test_full_size_sampled(name):
+@pytest.mark.parametrize("name,kw", [("specdec70b", {}), ("chunked13b", {}), ("specdec70b_fp8", {}),
+                                     ("specdec70b_fp8", dict(query_len=4))])
+def test_full_size_sampled(name, kw):
     """Full-size workloads in the benchmark's configuration; the oracle checks
-    every row of a few sampled sequences (both chunks of the prefill batch)."""
+    every row of a few sampled sequences (both chunks of the prefill batch).
+    Four drafted tokens over the E4M3 cache (32 rows) stream."""
     torch.cuda.empty_cache()
-    x = wl.make_inputs(name, device="cuda", poison=True)
+    x = wl.make_inputs(name, device="cuda", poison=True, **kw)
     qs = x.query_start.tolist()
     seqs = [0, 1, len(qs) - 2] if name.startswith("chunked") else [0, 7, 31]
     refs = sampled_mq_reference(x, seqs)  # host copies taken before the GPU step
@@ -209,22 +258,30 @@ def test_side_stream_same_bits_and_ordered():
     assert np.array_equal(bits(seen), bits(one))
 
 
-def test_fixed_partitions_batch_invariant():
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_fixed_partitions_batch_invariant(kv):
     """With partition_tokens fixed, a sequence's rows are the same bits alone as
     in a batch (the default partition size follows the batch shape, so this is
-    the caller's way to batch-invariant rows)."""
-    spec = wl.Spec("mqinv", 32, 8, 128, 16, "bf16", seed=91)
-    plan = wl.multi_query_plan([900, 2500, 40, 1300], [6, 5, 1, 30], 16, torch.Generator().manual_seed(4))
+    the caller's way to batch-invariant rows).  Over an E4M3 cache the 24-,
+    20- and 12-row sequences stream (two tiles in the batch, the 12-row one
+    one tile alone) beside the 120-row one on the ring."""
+    spec = wl.Spec(f"mqinv{kv}", 32, 8, 128, 16, "bf16", seed=91,
+                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0 if kv == "bf16" else 1.0 / 64)
+    plan = wl.multi_query_plan([900, 2500, 40, 1300, 700], [6, 5, 1, 30, 3], 16,
+                               torch.Generator().manual_seed(4))
     x = wl.build_inputs(spec, plan)
     whole, t = gpu_mq_step(x, partition_tokens=256)
+    ref, _, _ = oracle_mq_step(x)
+    assert_close(as_f64(whole), ref, "bf16", spec.name)
     qs = x.query_start.tolist()
-    for s in (0, 1, 3):
+    for s in (0, 1, 3, 4):
         rows = slice(qs[s], qs[s + 1])
         q = t["q"][rows].contiguous()
         alone = torch.empty_like(q)
         binding.pa_multi_query(alone, q, t["k_cache"], t["v_cache"], t["block_tables"][s:s + 1].contiguous(),
                                t["context_lens"][s:s + 1].contiguous(),
                                torch.tensor([0, qs[s + 1] - qs[s]], dtype=torch.int32, device="cuda"),
-                               x.scale, x.max_context_len, qs[s + 1] - qs[s], partition_tokens=256)
+                               x.scale, x.max_context_len, qs[s + 1] - qs[s], partition_tokens=256,
+                               k_scale=x.k_scale, v_scale=x.v_scale)
         torch.cuda.synchronize()
         assert np.array_equal(bits(alone), bits(whole[rows])), s
