@@ -85,6 +85,8 @@ def parse():
                                         "specdec70b,specdec70b_fp8_q4,chunked13b,gqa70b_x2,gqa70b_x2+fill,swap13b",
                     help="comma list of extra workloads to report ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cache-ops", dest="cache_ops", action="store_false",
+                    help="skip the separate timing of reshape_and_cache and copy_blocks")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -375,6 +377,82 @@ def run_swap(label, steps, warmup, blocks=1024):
     return res
 
 
+def run_cache_ops(steps, warmup):
+    """The two cache writes alone, each call between its own pair of events.
+
+    reshape_and_cache of the LLaMA-13B-shaped step's 128 new tokens (bf16, and
+    encoded into an E4M3 cache), copy_blocks of the beam workload's
+    copy-on-write pairs, and copy_blocks of 1024 scattered LLaMA-13B-shaped
+    blocks.  Bytes are the data the op moves: every row or block read once and
+    written once (plus the slot or pair indices).
+    """
+    import torch
+    from paged_kv_cache_321_amd import binding
+    from paged_kv_cache_321_amd import workloads as wl
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        # A few milliseconds of GPU spin first, so every call below is queued
+        # before the GPU reaches it: the events then time the GPU, not the
+        # host's launch latency (these kernels take microseconds).
+        torch.cuda._sleep(5_000_000)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / steps * 1e3
+
+    res = []
+    for name in ("llama13b", "llama13b_fp8"):
+        x = wl.make_inputs(name, device="cuda", poison=False)
+        t = x.key.shape[0]
+        row = x.key[0].numel()
+        nbytes = t * row * 2 * (x.key.element_size() + x.k_cache.element_size()) + 8 * t
+        us = timed(lambda: binding.pa_reshape_and_cache(x.key, x.value, x.k_cache, x.v_cache,
+                                                        x.slot_mapping, stream=stream,
+                                                        k_scale=x.k_scale, v_scale=x.v_scale))
+        res.append({"op": "pa_reshape_and_cache", "workload": name, "new_tokens": t,
+                    "kv_cache_dtype": x.spec.cache_dtype, "avg_us": us, "bytes": nbytes,
+                    "GBps": nbytes / (us / 1e6) / 1e9})
+        del x
+    x = wl.make_inputs("beam", device="cuda", poison=False)
+    pairs = x.block_pairs
+    blk = x.k_cache[0].numel() * x.k_cache.element_size()
+    nbytes = pairs.shape[0] * 2 * 2 * blk + 16 * pairs.shape[0]
+    us = timed(lambda: binding.pa_copy_blocks(x.k_cache, x.v_cache, pairs, stream=stream))
+    res.append({"op": "pa_copy_blocks", "workload": "beam", "pairs": int(pairs.shape[0]),
+                "avg_us": us, "bytes": nbytes, "GBps": nbytes / (us / 1e6) / 1e9})
+    del x
+    x = wl.make_inputs("llama13b", device="cuda", poison=False)
+    g = torch.Generator().manual_seed(12)
+    ids = torch.randperm(x.plan.num_blocks, generator=g)[:2048]
+    pairs = torch.stack([ids[:1024], ids[1024:]], 1).to(torch.int64).to("cuda")
+    blk = x.k_cache[0].numel() * x.k_cache.element_size()
+    nbytes = 1024 * 2 * 2 * blk + 16 * 1024
+    us = timed(lambda: binding.pa_copy_blocks(x.k_cache, x.v_cache, pairs, stream=stream))
+    res.append({"op": "pa_copy_blocks", "workload": "1024 scattered LLaMA-13B-shaped blocks",
+                "pairs": 1024, "avg_us": us, "bytes": nbytes, "GBps": nbytes / (us / 1e6) / 1e9,
+                "frac_of_peak": nbytes / (us / 1e6) / 1e9 / PEAK_GBPS})
+    # The same bytes as one contiguous device-to-device copy: the rate a copy
+    # reaches on this GPU when nothing is scattered.
+    src = torch.empty(nbytes // 2, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    us = timed(lambda: dst.copy_(src))
+    res.append({"op": "contiguous device copy (torch copy_)", "bytes": 2 * src.numel(), "avg_us": us,
+                "GBps": 2 * src.numel() / (us / 1e6) / 1e9,
+                "frac_of_peak": 2 * src.numel() / (us / 1e6) / 1e9 / PEAK_GBPS})
+    del x, src, dst
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(name, target_s):
     """The oracle, single-threaded, on a bounded sample of the workload."""
     import numpy as np
@@ -487,6 +565,7 @@ def main():
             r2, _, _ = run_workload(name, args.steps, args.warmup, args.partition_tokens, flush=True)
             others.append(r2)
 
+    cache_ops = run_cache_ops(args.steps, args.warmup) if args.cache_ops else None
     traffic = measured_traffic(args.workload)
     roof = {
         "bound": "hbm",
@@ -530,6 +609,7 @@ def main():
                                         "decode_GBps", "decode_frac_of_peak")},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "cache_ops": cache_ops,
         "workloads": others,
     }
     print(json.dumps(line))

@@ -309,6 +309,34 @@ def test_copy_on_write_leaves_source_unchanged():
     assert np.array_equal(bits(t["k_cache"][rest]), bits(before_k[rest]))
 
 
+# Block shapes whose 16-byte chunk count is below one slice (64), not a
+# multiple of one (640 = 5 x 128), several slices (10240), and above the
+# grid's 64 slices per pair (131072: the stride loop wraps).
+@pytest.mark.parametrize("hkv,bs,d,dtype", [(1, 16, 64, torch.uint8), (5, 16, 64, torch.bfloat16),
+                                             (40, 16, 128, torch.bfloat16), (128, 32, 128, torch.float32)])
+def test_copy_blocks_bitwise_block_shapes(hkv, bs, d, dtype):
+    import oracle.paged_attention as op
+    g = torch.Generator().manual_seed(hkv * 1000 + bs + d)
+    nb = 12
+    shape = (nb, hkv, bs, d)
+    if dtype == torch.uint8:
+        k = torch.randint(0, 256, shape, generator=g, dtype=torch.uint8)
+        v = torch.randint(0, 256, shape, generator=g, dtype=torch.uint8)
+        kd, vd = k.view(torch.float8_e4m3fn).cuda(), v.view(torch.float8_e4m3fn).cuda()
+    else:
+        k = torch.randn(shape, generator=g).to(dtype)
+        v = torch.randn(shape, generator=g).to(dtype)
+        kd, vd = k.cuda(), v.cuda()
+    ids = torch.randperm(nb, generator=g)
+    pairs = torch.stack([ids[:5], ids[5:10]], 1).to(torch.int64)
+    binding.pa_copy_blocks(kd, vd, pairs.cuda())
+    torch.cuda.synchronize()
+    kc, vc = wl.to_host_numpy(k).copy(), wl.to_host_numpy(v).copy()
+    op.copy_blocks(kc, vc, pairs.numpy())
+    assert np.array_equal(bits(kd), bits(kc))
+    assert np.array_equal(bits(vd), bits(vc))
+
+
 def test_bad_device_values_give_nan_rows_only():
     x = wl.make_inputs("llama7b", num_seqs=4, ctx_range=(40, 300))
     t = on_device(x)
