@@ -1,0 +1,168 @@
+"""GPU decode against the oracle in regimes that seeded N(0, 1) inputs do not reach.
+
+Random normal K, V and q keep every score within a few units of the running
+maximum, so a kernel that skipped the max subtraction, moved its reference
+maximum wrongly, or merged partitions with the wrong exponents could still
+pass the ordinary parity cases.  Here:
+
+- scores tens of units apart (K scaled up): exp of the raw scores overflows
+  float32, and the partitions of one sequence have very different maxima;
+- a ramp along the logical token order, so that for about half the heads
+  every page raises the maximum by more than the kernels' lazy-rescale
+  threshold (2^8 in the weights), and for the others the first page dominates;
+- q = 0: every weight is equal, and the output is the mean of V over the
+  context (pinned against a direct mean as well as the oracle);
+- the same V row at every position: the output is that row (exactly on the
+  vector path, whose weights stay float32, up to the sign of zero, since a
+  sum of +0 and -0 is +0; within tolerance on the matrix-core path, which
+  rounds the weights to bf16 for the PV product).
+
+Each case runs on the vector path (MHA, fp32 and bf16), on the matrix-core
+path (grouped heads, bf16 query), and with an E4M3 cache, with one partition
+per sequence and with several.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_321_amd import workloads as wl
+
+from gpu_helpers import TOL, as_f64, assert_close, gpu_step, oracle_step
+
+pytestmark = pytest.mark.gpu
+
+# (label, H, Hkv, D, BS, dtype, cache dtype)
+PATHS = [
+    ("valu_f32", 4, 4, 64, 16, "f32", None),
+    ("valu_bf16", 8, 8, 128, 16, "bf16", None),
+    ("mfma_g8", 64, 8, 128, 32, "bf16", None),
+    ("mfma_g4", 32, 8, 128, 16, "bf16", None),
+    ("valu_fp8", 8, 8, 128, 16, "bf16", "fp8"),
+    ("mfma_fp8_g8", 64, 8, 128, 32, "bf16", "fp8"),
+]
+CTX = [1, 17, 255, 700, 1100]
+
+
+def make(label, h, hkv, d, bs, dtype, kv, seed):
+    spec = wl.Spec(f"inv_{label}", h, hkv, d, bs, dtype, seed=seed, kv_dtype=kv, kv_scale=1.0)
+    gen = torch.Generator().manual_seed(seed)
+    plan = wl.uniform_plan(CTX, bs, gen, new_tokens=False)
+    return wl.build_inputs(spec, plan)
+
+
+def set_cache(x, name, values: torch.Tensor):
+    """Store float32 ``values`` into cache ``name`` in its element type."""
+    old = getattr(x, name)
+    if old.dtype == torch.uint8 or old.dtype == torch.float8_e4m3fn:
+        new = values.clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+        new = new.view(torch.uint8) if old.dtype == torch.uint8 else new
+    else:
+        new = values.to(old.dtype)
+    setattr(x, name, new.contiguous())
+
+
+def positions(x):
+    """Logical position of every (block, slot) in use, -1 elsewhere: int64 [NB, BS]."""
+    bs = x.plan.block_size
+    pos = np.full((x.plan.num_blocks, bs), -1, dtype=np.int64)
+    for s, c in enumerate(x.plan.context_lens.tolist()):
+        for j in range(-(-c // bs)):
+            b = int(x.plan.block_tables[s, j])
+            pos[b] = j * bs + np.arange(bs)
+    return torch.from_numpy(pos)
+
+
+def cache_f32(t: torch.Tensor) -> torch.Tensor:
+    return (t.view(torch.float8_e4m3fn) if t.dtype == torch.uint8 else t).float()
+
+
+def check(x, pt):
+    out, _ = gpu_step(x, partition_tokens=pt, copy=False, reshape=False)
+    ref, _, _ = oracle_step(x, copy=False, reshape=False)
+    assert_close(as_f64(out), ref, x.spec.dtype, f"{x.spec.name} pt={pt}")
+    return out, ref
+
+
+@pytest.mark.parametrize("label,h,hkv,d,bs,dtype,kv", PATHS)
+@pytest.mark.parametrize("pt", [0, 256])
+def test_large_scores(label, h, hkv, d, bs, dtype, kv, pt):
+    x = make(label, h, hkv, d, bs, dtype, kv, seed=31 + h + d)
+    # Scores of standard deviation ~24 (up to ~100 units apart): exp of the
+    # raw scores overflows float32.
+    set_cache(x, "k_cache", cache_f32(x.k_cache) * 24.0)
+    check(x, pt)
+
+
+@pytest.mark.parametrize("label,h,hkv,d,bs,dtype,kv", PATHS)
+@pytest.mark.parametrize("pt", [0, 256])
+def test_ramp_moves_the_maximum_every_page(label, h, hkv, d, bs, dtype, kv, pt):
+    x = make(label, h, hkv, d, bs, dtype, kv, seed=57 + h + d)
+    g = torch.Generator().manual_seed(5)
+    w = torch.randn(hkv, d, generator=g)
+    w /= w.norm(dim=1, keepdim=True)
+    pos = positions(x).float()
+    # K_t += a t w: a head whose query has q.w ~ 1 gains ~0.5 (log units) per
+    # token, 8 to 16 per page.  E4M3 codes saturate at 448, so the ramp is
+    # gentler there (about 0.1 per token; the codes still span a wide range).
+    # float32 is held to 1e-5, and a score s carries a rounding error of about
+    # |s| sqrt(D) 2^-24 that moves its weight by as much: there the ramp spans
+    # about 25 units over the longest context, still past where exp of the
+    # raw scores would lose every digit of the early tokens' weights.
+    if kv is not None:
+        a = 1.2
+    elif dtype == "f32":
+        a = 0.18
+    else:
+        a = 0.5 * d ** 0.5
+    ramp = a * pos.clamp(min=0)[:, None, :, None] * w[None, :, None, :]
+    set_cache(x, "k_cache", cache_f32(x.k_cache) + ramp)
+    check(x, pt)
+
+
+@pytest.mark.parametrize("label,h,hkv,d,bs,dtype,kv", PATHS)
+@pytest.mark.parametrize("pt", [0, 256])
+def test_zero_query_gives_mean_of_v(label, h, hkv, d, bs, dtype, kv, pt):
+    x = make(label, h, hkv, d, bs, dtype, kv, seed=71 + h + d)
+    x.q = torch.zeros_like(x.q)
+    out, ref = check(x, pt)
+    # The property itself, from the cache directly.
+    vf = cache_f32(x.v_cache).double() * x.v_scale
+    group = h // hkv
+    for s, c in enumerate(x.plan.context_lens.tolist()):
+        nb = -(-c // bs)
+        rows = vf[torch.as_tensor(x.plan.block_tables[s, :nb].astype(np.int64))]  # [nb, Hkv, BS, D]
+        rows = rows.permute(1, 0, 2, 3).reshape(hkv, nb * bs, d)[:, :c]
+        mean = rows.mean(dim=1).repeat_interleave(group, dim=0).numpy()
+        assert np.allclose(ref[s], mean, atol=1e-12, rtol=1e-12)
+        atol, rtol = TOL[dtype]
+        assert np.all(np.abs(as_f64(out)[s] - mean) <= atol + rtol * np.abs(mean))
+
+
+@pytest.mark.parametrize("label,h,hkv,d,bs,dtype,kv", PATHS)
+@pytest.mark.parametrize("pt", [0, 256])
+def test_constant_v_gives_that_row(label, h, hkv, d, bs, dtype, kv, pt):
+    x = make(label, h, hkv, d, bs, dtype, kv, seed=89 + h + d)
+    g = torch.Generator().manual_seed(9)
+    row = torch.randn(hkv, d, generator=g) * 2.0
+    if kv is not None:  # a row the E4M3 codes hold exactly
+        row = row.to(torch.float8_e4m3fn).float()
+    pos = positions(x)
+    v = cache_f32(x.v_cache)
+    live = (pos >= 0)[:, None, :, None].expand_as(v)
+    set_cache(x, "v_cache", torch.where(live, row[None, :, None, :].expand_as(v), v))
+    out, _ = check(x, pt)
+    want = row.repeat_interleave(h // hkv, dim=0)  # [H, D]
+    if dtype == "bf16":
+        want = want.to(torch.bfloat16)
+    got = out.cpu()
+    vector_path = h == hkv or dtype == "f32"
+    for s in range(x.plan.num_seqs):
+        if vector_path and dtype == "bf16":
+            assert torch.equal(got[s].float(), want.float()), f"seq {s}"
+        elif vector_path:
+            assert torch.allclose(got[s], want, atol=0, rtol=1e-6), f"seq {s}"
+        else:
+            atol, rtol = TOL[dtype]
+            w64 = want.double()
+            assert torch.all((got[s].double() - w64).abs() <= atol + rtol * w64.abs()), f"seq {s}"
