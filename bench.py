@@ -399,7 +399,8 @@ def run_cache_ops(steps, warmup):
         # A few milliseconds of GPU spin first, so every call below is queued
         # before the GPU reaches it: the events then time the GPU, not the
         # host's launch latency (these kernels take microseconds).
-        torch.cuda._sleep(5_000_000)
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(5_000_000)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(steps)]
         for a, b in evs:
