@@ -225,3 +225,22 @@ def sampled_mq_reference(x: Inputs, seqs):
                                 x.spec.dtype, cache_dtype=x.spec.cache_dtype, k_scale=x.k_scale,
                                 v_scale=x.v_scale)
     return res
+
+
+def to_top_of_pool(plan, num_blocks):
+    """Renumber the plan's blocks into the last ids of a pool of ``num_blocks``."""
+    bs = plan.block_size
+    used = set(int(b) for b in plan.block_tables[plan.block_tables >= 0].ravel())
+    used |= set(int(b) for b in plan.history_tables[plan.history_tables >= 0].ravel())
+    used |= set(int(s) // bs for s in plan.slot_mapping)
+    remap = {b: num_blocks - 1 - i for i, b in enumerate(sorted(used))}
+
+    def table(t):
+        return np.where(t >= 0, np.vectorize(lambda b: remap.get(int(b), -1))(t), t).astype(np.int32)
+
+    plan.block_tables = table(plan.block_tables)
+    plan.history_tables = table(plan.history_tables)
+    plan.slot_mapping = np.array([remap[int(s) // bs] * bs + int(s) % bs for s in plan.slot_mapping],
+                                 dtype=np.int64)
+    plan.num_blocks = num_blocks
+    return plan

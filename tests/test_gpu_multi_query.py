@@ -13,7 +13,7 @@ from paged_kv_cache_321_amd import binding
 from paged_kv_cache_321_amd import workloads as wl
 
 from gpu_helpers import (as_f64, assert_close, bits, gpu_mq_step, gpu_step, on_device,
-                         oracle_mq_step, oracle_step, sampled_mq_reference)
+                         oracle_mq_step, oracle_step, sampled_mq_reference, to_top_of_pool)
 
 pytestmark = pytest.mark.gpu
 
@@ -285,3 +285,31 @@ def test_fixed_partitions_batch_invariant(kv):
                                k_scale=x.k_scale, v_scale=x.v_scale)
         torch.cuda.synchronize()
         assert np.array_equal(bits(alone), bits(whole[rows])), s
+
+
+@pytest.mark.parametrize("h,hkv,bs,kv", [(40, 40, 16, "bf16"), (64, 8, 32, "bf16"), (64, 8, 32, "fp8")])
+def test_pool_past_2g_elements(h, hkv, bs, kv):
+    """Every page of the batch lies past 2^31 elements of a 2.29e9-element
+    cache: the ring's buffer descriptors, the streaming kernel and the decode
+    rows all address it with 64-bit offsets."""
+    torch.cuda.empty_cache()
+    d = 128
+    per_block = hkv * bs * d
+    nb = (2_290_000_000 + per_block - 1) // per_block
+    spec = wl.Spec(f"mqbig{h}x{hkv}x{bs}{kv}", h, hkv, d, bs, "bf16", seed=h + bs + 5,
+                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0 if kv == "bf16" else 1.0 / 64)
+    plan = wl.multi_query_plan([700, 2049, 5000, 3000], [1, 6, 4, 100], bs,
+                               torch.Generator().manual_seed(spec.seed))
+    plan = to_top_of_pool(plan, nb)
+    assert int(plan.block_tables[plan.block_tables >= 0].min()) * per_block > 2 ** 31
+    x = wl.build_inputs(spec, plan, device="cuda", poison=True)
+    qs = x.query_start.tolist()
+    seqs = [0, 1, 2, 3]
+    refs = sampled_mq_reference(x, seqs)
+    out, t = gpu_mq_step(x, t={n: getattr(x, n) for n in ("q", "k_cache", "v_cache", "key",
+                                                            "value", "slot_mapping", "block_tables",
+                                                            "context_lens", "block_pairs")})
+    for s in seqs:
+        assert_close(as_f64(out[qs[s]:qs[s + 1]]), refs[s], "bf16", f"{spec.name} seq {s}")
+    del x, t, out
+    torch.cuda.empty_cache()

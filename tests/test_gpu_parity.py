@@ -15,7 +15,7 @@ import torch
 from paged_kv_cache_321_amd import binding, workloads as wl
 
 from gpu_helpers import (as_f64, assert_close, bits, gpu_step, on_device, oracle_step,
-                         sampled_reference)
+                         sampled_reference, to_top_of_pool)
 
 pytestmark = pytest.mark.gpu
 
@@ -456,3 +456,50 @@ def test_swap_out_and_in_bitwise(name):
     binding.pa_swap_blocks(t["k_cache"], t["v_cache"], host_k, host_v, in_pairs)
     torch.cuda.synchronize()
     assert np.array_equal(bits(t["k_cache"]), bits(dk)) and np.array_equal(bits(t["v_cache"]), bits(dv))
+
+
+# ----------------------------------------------------------------------------
+# Pools past 2^31 elements: every element offset into the caches needs 64 bits.
+# ----------------------------------------------------------------------------
+
+# (H, Hkv, BS, cache): pools of 2.29e9 elements per cache (4.6 GB bf16, 2.3 GB E4M3)
+BIG_POOLS = [(40, 40, 16, "bf16"), (64, 8, 32, "bf16"), (64, 8, 32, "fp8")]
+
+
+@pytest.mark.parametrize("h,hkv,bs,kv", BIG_POOLS)
+def test_pool_past_2g_elements(h, hkv, bs, kv):
+    torch.cuda.empty_cache()
+    d = 128
+    per_block = hkv * bs * d
+    nb = (2_290_000_000 + per_block - 1) // per_block
+    spec = wl.Spec(f"bigpool{h}x{hkv}x{bs}{kv}", h, hkv, d, bs, "bf16", seed=h + bs + 3,
+                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0 if kv == "bf16" else 1.0 / 64)
+    ctx = [1, 700, 2049, 5000]
+    plan = wl.uniform_plan(ctx, bs, torch.Generator().manual_seed(spec.seed), new_tokens=True)
+    plan = to_top_of_pool(plan, nb)
+    used_min = int(plan.block_tables[plan.block_tables >= 0].min())
+    assert used_min * per_block > 2 ** 31  # every page lies past 2^31 elements
+    x = wl.build_inputs(spec, plan, device="cuda", poison=True)
+    seqs = list(range(len(ctx)))
+    ref, ids, kc, vc = sampled_reference(x, seqs)
+    resident = {n: getattr(x, n) for n in ("q", "k_cache", "v_cache", "key", "value",
+                                           "slot_mapping", "block_tables", "context_lens",
+                                           "block_pairs")}
+    out, t = gpu_step(x, t=resident)
+    idx = torch.tensor(ids, device="cuda")
+    assert np.array_equal(bits(t["k_cache"].index_select(0, idx)), bits(kc))
+    assert np.array_equal(bits(t["v_cache"].index_select(0, idx)), bits(vc))
+    assert_close(as_f64(out), ref, x.spec.dtype, spec.name)
+    # copy_blocks from the top of the pool to a block just below 2^31 elements
+    # and to the block just below the used ones.
+    low = 2 ** 31 // per_block - 2
+    src = [int(plan.block_tables[3, 0]), int(plan.block_tables[2, 1])]
+    dst = [low, nb - 1 - len(ids) - 1]
+    pairs = torch.tensor(list(zip(src, dst)), dtype=torch.int64, device="cuda")
+    binding.pa_copy_blocks(t["k_cache"], t["v_cache"], pairs)
+    torch.cuda.synchronize()
+    for a, b in zip(src, dst):
+        assert np.array_equal(bits(t["k_cache"][b]), bits(t["k_cache"][a]))
+        assert np.array_equal(bits(t["v_cache"][b]), bits(t["v_cache"][a]))
+    del x, t, out, resident
+    torch.cuda.empty_cache()
