@@ -14,9 +14,14 @@
 namespace pa {
 namespace {
 
-// One wave per (head, sequence).  Lanes own partitions when reading the
-// (max, sum) pairs, so those loads are issued together; the weights of each
-// chunk of 64 partitions go through LDS to the lanes that own output columns.
+// One wave per (head, sequence).  Up to kFewParts partitions, every load of
+// the wave goes out at once: lane q reads the (max, sum) pair of partition q,
+// and each lane reads its output columns of every partition; the weights then
+// reach the column owners by shuffles.  More partitions take a loop that
+// reads the pairs 64 at a time and passes their weights through LDS.  Both
+// forms add the partitions in the same order, so they give the same bits.
+constexpr int kFewParts = 8;
+
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams p) {
   constexpr int E = D / 64;  // output columns per lane
@@ -32,31 +37,53 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams p) {
   if (nparts <= 1) return;  // written by the partition kernel
   const int64_t base = ((int64_t)s * p.num_heads + h) * p.max_parts;
   const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + base;
-  float mm = -FLT_MAX;
-  for (int q = lane; q < nparts; q += 64) mm = fmaxf(mm, ml[q].x);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off));
-  float ll = 0.f;
+  const float* acc = p.ws_acc + base * D + lane;
   float aa[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) aa[e] = 0.f;
-  const float* acc = p.ws_acc + base * D + lane;
-  for (int q0 = 0; q0 < nparts; q0 += 64) {
-    const int q = q0 + lane;
-    float w = 0.f;
-    if (q < nparts) {
-      const float2 v = ml[q];
-      w = fast_exp2(v.x - mm);
-      ll += v.y * w;
-    }
-    __syncthreads();
-    sw[lane] = w;
-    __syncthreads();
-    const int n = min(64, nparts - q0);
-    for (int j = 0; j < n; ++j) {
-      const float wj = sw[j];
+  float ll = 0.f;
+  if (nparts <= kFewParts) {
+    const float2 v = lane < nparts ? ml[lane] : make_float2(-FLT_MAX, 0.f);
+    float a[kFewParts][E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) aa[e] += acc[(int64_t)(q0 + j) * D + 64 * e] * wj;
+    for (int q = 0; q < kFewParts; ++q)
+#pragma unroll
+      for (int e = 0; e < E; ++e) a[q][e] = q < nparts ? acc[(int64_t)q * D + 64 * e] : 0.f;
+    float mm = v.x;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off));
+    const float w = lane < nparts ? fast_exp2(v.x - mm) : 0.f;
+    ll = v.y * w;
+#pragma unroll
+    for (int q = 0; q < kFewParts; ++q) {
+      const float wq = __shfl(w, q);
+      if (q < nparts) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) aa[e] += a[q][e] * wq;
+      }
+    }
+  } else {
+    float mm = -FLT_MAX;
+    for (int q = lane; q < nparts; q += 64) mm = fmaxf(mm, ml[q].x);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off));
+    for (int q0 = 0; q0 < nparts; q0 += 64) {
+      const int q = q0 + lane;
+      float w = 0.f;
+      if (q < nparts) {
+        const float2 v = ml[q];
+        w = fast_exp2(v.x - mm);
+        ll += v.y * w;
+      }
+      __syncthreads();
+      sw[lane] = w;
+      __syncthreads();
+      const int n = min(64, nparts - q0);
+      for (int j = 0; j < n; ++j) {
+        const float wj = sw[j];
+#pragma unroll
+        for (int e = 0; e < E; ++e) aa[e] += acc[(int64_t)(q0 + j) * D + 64 * e] * wj;
+      }
     }
   }
 #pragma unroll

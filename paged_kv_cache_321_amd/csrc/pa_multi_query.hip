@@ -867,47 +867,67 @@ __global__ __launch_bounds__(256) void multi_query_schedule_kernel(MultiQueryPar
 }
 
 // Merges the partitions of sequences whose rows fit one block (the only ones
-// cut): one workgroup per (sequence, kv head), four threads per row, each
-// owning D / 4 output columns.
+// cut): workgroup (sequence x kv head, c) takes rows 4c .. 4c + 3 of the
+// block, one wave per row, each lane owning D / 64 output columns.  Up to
+// kMqFewParts partitions every load of the wave goes out at once and the
+// weights reach the column owners by shuffles; more take a loop.  Either way
+// the partitions are added in order.
+constexpr int kMqFewParts = 8;
+
 template <int D, int G>
 __global__ __launch_bounds__(kMqWaves * 64) void multi_query_reduce_kernel(MultiQueryParams p) {
-  constexpr int DQ = D / 4;
+  constexpr int E = D / 64;
   const int kvh = blockIdx.x % p.num_kv_heads;
   const int s = blockIdx.x / p.num_kv_heads;
   const MqBlock b = mq_block<G>(p, s, 0);
   if (b.skip || b.nparts <= 1) return;  // written by the partition kernel
-  const int r = b.rb * kRowsPerBlock + threadIdx.x / 4;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.y * kMqWaves + (threadIdx.x >> 6);  // the row of this wave
   if (r >= b.rows) return;
   const int64_t orow = (int64_t)(b.t0 + r / G) * p.num_heads + kvh * G + r % G;
   const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + orow * p.max_parts;
-  float mm = -FLT_MAX;
-  for (int q = 0; q < b.nparts; ++q) mm = fmaxf(mm, ml[q].x);
+  const float* acc = p.ws_acc + orow * p.max_parts * D + lane;
+  const int n = b.nparts;
+  float aa[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) aa[e] = 0.f;
   float ll = 0.f;
-  float aa[DQ];
+  if (n <= kMqFewParts) {
+    const float2 v = lane < n ? ml[lane] : make_float2(-FLT_MAX, 0.f);
+    float a[kMqFewParts][E];
 #pragma unroll
-  for (int e = 0; e < DQ; ++e) aa[e] = 0.f;
-  const int d0 = (threadIdx.x % 4) * DQ;
-  for (int q = 0; q < b.nparts; ++q) {
-    const float2 v = ml[q];
-    const float w = fast_exp2(v.x - mm);
-    ll += v.y * w;
-    const float4* a = reinterpret_cast<const float4*>(p.ws_acc + (orow * p.max_parts + q) * D + d0);
+    for (int q = 0; q < kMqFewParts; ++q)
 #pragma unroll
-    for (int e = 0; e < DQ / 4; ++e) {
-      const float4 f = a[e];
-      aa[4 * e] += f.x * w;
-      aa[4 * e + 1] += f.y * w;
-      aa[4 * e + 2] += f.z * w;
-      aa[4 * e + 3] += f.w * w;
+      for (int e = 0; e < E; ++e) a[q][e] = q < n ? acc[(int64_t)q * D + 64 * e] : 0.f;
+    float mm = v.x;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off));
+    const float w = lane < n ? fast_exp2(v.x - mm) : 0.f;
+#pragma unroll
+    for (int q = 0; q < kMqFewParts; ++q) {
+      const float wq = __shfl(w, q);
+      const float lq = __shfl(v.y, q);
+      if (q < n) {
+        ll += lq * wq;
+#pragma unroll
+        for (int e = 0; e < E; ++e) aa[e] += a[q][e] * wq;
+      }
+    }
+  } else {
+    float mm = -FLT_MAX;
+    for (int q = 0; q < n; ++q) mm = fmaxf(mm, ml[q].x);
+    for (int q = 0; q < n; ++q) {
+      const float2 v = ml[q];
+      const float w = fast_exp2(v.x - mm);
+      ll += v.y * w;
+#pragma unroll
+      for (int e = 0; e < E; ++e) aa[e] += acc[(int64_t)q * D + 64 * e] * w;
     }
   }
   const float inv = ll == 0.f ? 0.f : p.v_scale / ll;
-  uint16_t* o = static_cast<uint16_t*>(p.out) + orow * D + d0;
+  uint16_t* o = static_cast<uint16_t*>(p.out) + orow * D + lane;
 #pragma unroll
-  for (int e = 0; e < DQ / 2; ++e) {
-    const uint32_t w = f32_to_bf16_bits(aa[2 * e] * inv) | (uint32_t)f32_to_bf16_bits(aa[2 * e + 1] * inv) << 16;
-    *reinterpret_cast<uint32_t*>(o + 2 * e) = w;
-  }
+  for (int e = 0; e < E; ++e) Elem<uint16_t>::store(o + 64 * e, aa[e] * inv);
 }
 
 template <typename TC, int D, int BS, int G>
@@ -958,7 +978,8 @@ hipError_t launch_t(const MultiQueryLaunch& a, MultiQueryParams p) {
     }
   }
   if (a.max_parts <= 1) return hipSuccess;
-  hipLaunchKernelGGL((multi_query_reduce_kernel<D, G>), dim3((unsigned)a.num_seqs * a.num_kv_heads),
+  hipLaunchKernelGGL((multi_query_reduce_kernel<D, G>),
+                     dim3((unsigned)a.num_seqs * a.num_kv_heads, kRowsPerBlock / kMqWaves),
                      dim3(kMqWaves * 64), 0, a.stream, p);
   return hipGetLastError();
 }
