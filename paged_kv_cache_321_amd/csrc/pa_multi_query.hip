@@ -867,50 +867,107 @@ __global__ __launch_bounds__(256) void multi_query_schedule_kernel(MultiQueryPar
 }
 
 // Merges the partitions of sequences whose rows fit one block (the only ones
-// cut): workgroup (sequence x kv head, c) takes rows 4c .. 4c + 3 of the
-// block, one wave per row, each lane owning D / 64 output columns.  Up to
-// kMqFewParts partitions every load of the wave goes out at once and the
-// weights reach the column owners by shuffles; more take a loop.  Either way
-// the partitions are added in order.
-constexpr int kMqFewParts = 8;
-
+// cut): one workgroup per (sequence, kv head), four threads per row, each
+// owning D / 4 output columns, a loop over the partitions.  Launched for
+// batches with longer chunks, on which most workgroups find nothing to merge
+// and exit at once: small workgroups keep that cheap.
 template <int D, int G>
 __global__ __launch_bounds__(kMqWaves * 64) void multi_query_reduce_kernel(MultiQueryParams p) {
-  constexpr int E = D / 64;
+  constexpr int DQ = D / 4;
+  const int kvh = blockIdx.x % p.num_kv_heads;
+  const int s = blockIdx.x / p.num_kv_heads;
+  const MqBlock b = mq_block<G>(p, s, 0);
+  if (b.skip || b.nparts <= 1) return;  // written by the partition kernel
+  const int r = b.rb * kRowsPerBlock + threadIdx.x / 4;
+  if (r >= b.rows) return;
+  const int64_t orow = (int64_t)(b.t0 + r / G) * p.num_heads + kvh * G + r % G;
+  const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + orow * p.max_parts;
+  float mm = -FLT_MAX;
+  for (int q = 0; q < b.nparts; ++q) mm = fmaxf(mm, ml[q].x);
+  float ll = 0.f;
+  float aa[DQ];
+#pragma unroll
+  for (int e = 0; e < DQ; ++e) aa[e] = 0.f;
+  const int d0 = (threadIdx.x % 4) * DQ;
+  for (int q = 0; q < b.nparts; ++q) {
+    const float2 v = ml[q];
+    const float w = fast_exp2(v.x - mm);
+    ll += v.y * w;
+    const float4* a = reinterpret_cast<const float4*>(p.ws_acc + (orow * p.max_parts + q) * D + d0);
+#pragma unroll
+    for (int e = 0; e < DQ / 4; ++e) {
+      const float4 f = a[e];
+      aa[4 * e] += f.x * w;
+      aa[4 * e + 1] += f.y * w;
+      aa[4 * e + 2] += f.z * w;
+      aa[4 * e + 3] += f.w * w;
+    }
+  }
+  const float inv = ll == 0.f ? 0.f : p.v_scale / ll;
+  uint16_t* o = static_cast<uint16_t*>(p.out) + orow * D + d0;
+#pragma unroll
+  for (int e = 0; e < DQ / 2; ++e) {
+    const uint32_t w = f32_to_bf16_bits(aa[2 * e] * inv) | (uint32_t)f32_to_bf16_bits(aa[2 * e + 1] * inv) << 16;
+    *reinterpret_cast<uint32_t*>(o + 2 * e) = w;
+  }
+}
+
+// The same merge for batches in which every sequence's rows fit one block
+// (speculative verification), where most sequences are cut: one workgroup of
+// 16 waves per (sequence, kv head), four rows per wave, 16 lanes per row, each
+// lane owning D / 16 consecutive output columns.  Up to kMqFewParts
+// partitions every load of the wave goes out at once and the weights reach
+// the column owners by shuffles within the row's 16 lanes; more take a loop.
+// Both kernels add the partitions in the same order with the same products,
+// so they give the same bits.
+constexpr int kMqFewParts = 8;
+constexpr int kMqReduceWaves = kRowsPerBlock / 4;
+
+template <int D, int G>
+__global__ __launch_bounds__(kMqReduceWaves * 64) void multi_query_reduce_rows_kernel(MultiQueryParams p) {
+  constexpr int C = D / 16;  // output columns per lane
   const int kvh = blockIdx.x % p.num_kv_heads;
   const int s = blockIdx.x / p.num_kv_heads;
   const MqBlock b = mq_block<G>(p, s, 0);
   if (b.skip || b.nparts <= 1) return;  // written by the partition kernel
   const int lane = threadIdx.x & 63;
-  const int r = blockIdx.y * kMqWaves + (threadIdx.x >> 6);  // the row of this wave
-  if (r >= b.rows) return;
+  const int j = lane & 15;                                   // lane within the row
+  const int r = (threadIdx.x >> 6) * 4 + (lane >> 4);        // the row
+  if (r >= b.rows) return;  // a row's 16 lanes leave together; shuffles stay within a row
   const int64_t orow = (int64_t)(b.t0 + r / G) * p.num_heads + kvh * G + r % G;
   const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + orow * p.max_parts;
-  const float* acc = p.ws_acc + orow * p.max_parts * D + lane;
+  const float* acc = p.ws_acc + orow * p.max_parts * D + j * C;
   const int n = b.nparts;
-  float aa[E];
+  float aa[C];
 #pragma unroll
-  for (int e = 0; e < E; ++e) aa[e] = 0.f;
+  for (int c = 0; c < C; ++c) aa[c] = 0.f;
   float ll = 0.f;
   if (n <= kMqFewParts) {
-    const float2 v = lane < n ? ml[lane] : make_float2(-FLT_MAX, 0.f);
-    float a[kMqFewParts][E];
+    const float2 v = j < n ? ml[j] : make_float2(-FLT_MAX, 0.f);
+    float4 a[kMqFewParts][C / 4];
 #pragma unroll
     for (int q = 0; q < kMqFewParts; ++q)
 #pragma unroll
-      for (int e = 0; e < E; ++e) a[q][e] = q < n ? acc[(int64_t)q * D + 64 * e] : 0.f;
+      for (int c = 0; c < C / 4; ++c)
+        a[q][c] = q < n ? *reinterpret_cast<const float4*>(acc + (int64_t)q * D + 4 * c)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
     float mm = v.x;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off));
-    const float w = lane < n ? fast_exp2(v.x - mm) : 0.f;
+    for (int off = 8; off >= 1; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off, 16));
+    const float w = j < n ? fast_exp2(v.x - mm) : 0.f;
 #pragma unroll
     for (int q = 0; q < kMqFewParts; ++q) {
-      const float wq = __shfl(w, q);
-      const float lq = __shfl(v.y, q);
+      const float wq = __shfl(w, q, 16);
+      const float lq = __shfl(v.y, q, 16);
       if (q < n) {
         ll += lq * wq;
 #pragma unroll
-        for (int e = 0; e < E; ++e) aa[e] += a[q][e] * wq;
+        for (int c = 0; c < C / 4; ++c) {
+          aa[4 * c] += a[q][c].x * wq;
+          aa[4 * c + 1] += a[q][c].y * wq;
+          aa[4 * c + 2] += a[q][c].z * wq;
+          aa[4 * c + 3] += a[q][c].w * wq;
+        }
       }
     }
   } else {
@@ -921,13 +978,20 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_reduce_kernel(Multi
       const float w = fast_exp2(v.x - mm);
       ll += v.y * w;
 #pragma unroll
-      for (int e = 0; e < E; ++e) aa[e] += acc[(int64_t)q * D + 64 * e] * w;
+      for (int c = 0; c < C / 4; ++c) {
+        const float4 f = *reinterpret_cast<const float4*>(acc + (int64_t)q * D + 4 * c);
+        aa[4 * c] += f.x * w;
+        aa[4 * c + 1] += f.y * w;
+        aa[4 * c + 2] += f.z * w;
+        aa[4 * c + 3] += f.w * w;
+      }
     }
   }
   const float inv = ll == 0.f ? 0.f : p.v_scale / ll;
-  uint16_t* o = static_cast<uint16_t*>(p.out) + orow * D + lane;
+  uint32_t* o = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.out) + orow * D + j * C);
 #pragma unroll
-  for (int e = 0; e < E; ++e) Elem<uint16_t>::store(o + 64 * e, aa[e] * inv);
+  for (int c = 0; c < C / 2; ++c)
+    o[c] = f32_to_bf16_bits(aa[2 * c] * inv) | (uint32_t)f32_to_bf16_bits(aa[2 * c + 1] * inv) << 16;
 }
 
 template <typename TC, int D, int BS, int G>
@@ -978,9 +1042,16 @@ hipError_t launch_t(const MultiQueryLaunch& a, MultiQueryParams p) {
     }
   }
   if (a.max_parts <= 1) return hipSuccess;
-  hipLaunchKernelGGL((multi_query_reduce_kernel<D, G>),
-                     dim3((unsigned)a.num_seqs * a.num_kv_heads, kRowsPerBlock / kMqWaves),
-                     dim3(kMqWaves * 64), 0, a.stream, p);
+  // Verification batches (every sequence one block) merge on the 16-wave
+  // kernel, whose loads go out in one round trip (70B verification shape:
+  // 4.7 us against 8.3); other batches, where most workgroups exit at once,
+  // on the small one (chunked prefill: 4.9 us against 13.7).
+  if (a.max_row_blocks == 1)
+    hipLaunchKernelGGL((multi_query_reduce_rows_kernel<D, G>), dim3((unsigned)a.num_seqs * a.num_kv_heads),
+                       dim3(kMqReduceWaves * 64), 0, a.stream, p);
+  else
+    hipLaunchKernelGGL((multi_query_reduce_kernel<D, G>), dim3((unsigned)a.num_seqs * a.num_kv_heads),
+                       dim3(kMqWaves * 64), 0, a.stream, p);
   return hipGetLastError();
 }
 
