@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+from concurrent.futures import ThreadPoolExecutor
 import json
 import math
 import os
@@ -305,6 +306,8 @@ def run_workload(label, steps, warmup, partition_tokens, flush=False, settle_s=0
     decode_ms.sort()
     avg_decode_ms = sum(decode_ms) / len(decode_ms)
     med_decode_ms = decode_ms[len(decode_ms) // 2]
+    p10_decode_ms = decode_ms[(len(decode_ms) - 1) // 10]
+    p90_decode_ms = decode_ms[(len(decode_ms) - 1) * 9 // 10]
     nbytes = algorithmic_bytes(plan, spec)
     ubytes = unique_bytes(plan, spec)
     flops = attention_flops(plan, spec)
@@ -320,6 +323,8 @@ def run_workload(label, steps, warmup, partition_tokens, flush=False, settle_s=0
         "tokens_per_s": ntok / (ms_per_step / 1e3),
         "decode_avg_us": avg_decode_ms * 1e3,
         "decode_median_us": med_decode_ms * 1e3,
+        "decode_p10_us": p10_decode_ms * 1e3,
+        "decode_p90_us": p90_decode_ms * 1e3,
         "decode_tokens_per_s": ntok / (avg_decode_ms / 1e3),
         "attention_flops": flops,
         "attention_TFLOPs": flops / (avg_decode_ms / 1e3) / 1e12,
@@ -464,7 +469,8 @@ def run_cache_ops(steps, warmup):
 
 
 def cpu_baseline(name, target_s):
-    """The oracle, single-threaded, on a bounded sample of the workload."""
+    """The oracle on a bounded sample of the workload: single-threaded, then
+    the same sequence-steps spread over a thread per available core."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
@@ -488,23 +494,36 @@ def cpu_baseline(name, target_s):
                      if len(tok) else None))
         if s >= 15:  # a bounded sample of sequences, cycled below
             break
+
+    def one(i):
+        """The oracle's step for sample item i: store the new token (if any), decode."""
+        kc0, vc0, q, nb, ctx, new = host[i % len(host)]
+        kc, vc = kc0.copy(), vc0.copy()
+        table = np.arange(nb, dtype=np.int32)[None]
+        t0 = time.perf_counter()
+        if new is not None:
+            pos = int(ctx[0]) - 1
+            op.reshape_and_cache(new[0], new[1], kc, vc, np.array([pos], dtype=np.int64))
+        op.decode(q, kc, vc, table, ctx, x.scale, spec.dtype)
+        return time.perf_counter() - t0, int(ctx[0])
+
     done = 0
     tokens = 0
     t_total = 0.0
     with threadpool_limits(limits=1):
         while t_total < target_s and done < 64 * len(host):
-            kc0, vc0, q, nb, ctx, new = host[done % len(host)]
-            kc, vc = kc0.copy(), vc0.copy()
-            table = np.arange(nb, dtype=np.int32)[None]
-            t0 = time.perf_counter()
-            # The oracle's step for this sequence: store its new token (if any), decode.
-            if new is not None:
-                pos = int(ctx[0]) - 1
-                op.reshape_and_cache(new[0], new[1], kc, vc, np.array([pos], dtype=np.int64))
-            op.decode(q, kc, vc, table, ctx, x.scale, spec.dtype)
-            t_total += time.perf_counter() - t0
-            tokens += int(ctx[0])
+            dt, c = one(done)
+            t_total += dt
+            tokens += c
             done += 1
+    # The same items over a pool of threads, one per available core (BLAS
+    # single-threaded inside each), timed by the wall clock around the pool.
+    cores = len(os.sched_getaffinity(0))
+    n_par = max(cores, min(64 * len(host), int(done * cores * 0.5)))
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=cores) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(one, range(n_par)))
+        t_par = time.perf_counter() - t0
     n_host = len(host)
     del x, host
     torch.cuda.empty_cache()
@@ -518,7 +537,10 @@ def cpu_baseline(name, target_s):
                   f"in total): reshape_and_cache of the new token + decode, fp64 NumPy oracle, "
                   f"one BLAS thread, {t_total:.1f} s",
         "seconds": t_total,
-        "host_cpus_available": len(os.sched_getaffinity(0)),
+        "threaded": {"value": n_par / t_par, "unit": "tokens/s", "cores": cores,
+                     "sample": f"{n_par} sequence-steps of the same sample over {cores} threads "
+                               f"(one BLAS thread each), {t_par:.1f} s wall"},
+        "host_cpus_available": cores,
         "cpu_model": _cpu_model(),
     }
 
@@ -616,8 +638,9 @@ def main():
             "new_tokens": head["new_tokens"],
             "parallelism": "single GPU",
         },
-        "decode": {k: head[k] for k in ("decode_avg_us", "decode_median_us", "decode_tokens_per_s",
-                                        "decode_GBps", "decode_frac_of_peak")},
+        "decode": {k: head[k] for k in ("decode_avg_us", "decode_median_us", "decode_p10_us",
+                                        "decode_p90_us", "decode_tokens_per_s", "decode_GBps",
+                                        "decode_frac_of_peak")},
         "roofline": roof,
         "cpu_baseline": cpu,
         "cache_ops": cache_ops,
