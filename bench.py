@@ -77,7 +77,7 @@ for _n in ("beam", "beam_fp8"):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama13b",
                     choices=sorted(n for n in DESCRIPTION if n != "swap13b"))
