@@ -17,8 +17,10 @@
 // loads with the lds bit, one or two steps ahead).  bf16 chunks land where the
 // matrix cores read them: K row-major with 16-byte chunks swizzled by the
 // token, so the 16 rows one A-operand read touches hit distinct banks, and V
-// in the transposed-read layout of pa_mfma.h.  E4M3 codes land as stored and
-// each step is widened (exactly) into one bf16 tile in that layout.  Each
+// in the transposed-read layout of pa_mfma.h.  E4M3 V codes land as stored
+// and each step is widened (exactly) into a bf16 tile in that layout; E4M3 K
+// codes at D = 128 land swizzled and the QK product widens them in registers
+// (at D = 64 they are widened into a tile like V).  Each
 // column keeps its own running max and sum, moved lazily (only when a score
 // exceeds the reference by more than 2^8).
 //
@@ -132,6 +134,13 @@ __device__ __forceinline__ MqBlock mq_block(const MultiQueryParams& p, int s, in
 // distinct banks whether 8 or 16 lanes (32 or 64 4-byte banks) are served
 // per cycle: 256-byte rows take 16 chunk positions, 128-byte rows (alternating
 // bank halves) 8 positions distinct over each 8 tokens and each parity.
+// E4M3 K codes at D = 128 (128-byte rows, 8 chunks) in the ring stage: chunk
+// c of token `tok` is stored at chunk c ^ kswz8(tok).  An operand read has 16
+// lanes read 8 bytes of 16 consecutive tokens at the same logical chunk; row
+// parity picks the bank half and the swizzle one of 8 positions, so the 32
+// lanes served together hit all 64 banks once.
+__device__ __forceinline__ int kswz8(int tok) { return (tok >> 1) & 7; }
+
 template <int ROWB>
 __device__ __forceinline__ int kswz(int tok) {
   static_assert(ROWB == 128 || ROWB == 256, "128- or 256-byte rows");
@@ -168,7 +177,10 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   // read; E4M3 caches land as they are and each step is widened into one
   // bf16 (K, V) tile after the ring.
   constexpr int NSTAGE = STAGES;
-  constexpr int LDS_BYTES = NSTAGE * 2 * RTILEB + (kFp8 ? 2 * TILEB : 0);
+  // E4M3 at D = 128: the QK product reads K codes straight from the stage
+  // (8 codes per lane, widened in registers), so only V is widened in LDS.
+  constexpr bool kKRaw = kFp8 && D == 128;
+  constexpr int LDS_BYTES = NSTAGE * 2 * RTILEB + (kFp8 ? (kKRaw ? 1 : 2) * TILEB : 0);
   constexpr int WINDOW = 256;                // page ids held in registers (4 per lane)
   static_assert(kStepTokens % BS == 0 && kStepTokens % 32 == 0 && NCH >= 8, "tile shape");
   static_assert(kFp8 || CHUNKS % (kMqWaves * 64) == 0, "a bf16 step is whole wave loads");
@@ -240,7 +252,8 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   // and V rows are in the transposed-read layout (position
   // ch ^ swz<ROWB>(token)).
   __shared__ __attribute__((aligned(16))) unsigned char ring[LDS_BYTES];
-  unsigned char* const wide = ring + NSTAGE * 2 * RTILEB;  // E4M3: the widened tile
+  unsigned char* const wide = ring + NSTAGE * 2 * RTILEB;  // E4M3: the widened tile(s)
+  unsigned char* const wide_v = wide + (kKRaw ? 0 : TILEB);  // E4M3: the widened V tile
 
   const TC* kc = static_cast<const TC*>(p.k_cache) + (int64_t)kvh * BS * D;
   const TC* vc = static_cast<const TC*>(p.v_cache) + (int64_t)kvh * BS * D;
@@ -293,8 +306,9 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
 
   // Step st's K and V go straight from the cache into stage `stage`.  Load
   // u of wave w fills 64 consecutive 16-byte LDS slots, 64 / CCH whole rows
-  // of one page; each lane fetches the chunk its slot holds (bf16: the
-  // swizzled position; E4M3: as stored), at a byte offset inside the page
+  // of one page; each lane fetches the chunk its slot holds (bf16 and E4M3 K
+  // at D = 128: the swizzled position; other E4M3: as stored), at a byte
+  // offset inside the page
   // that does not change along the walk.  The page is reached through a
   // buffer descriptor whose record count ends at the partition's last token,
   // so the rows past it read as zeros and no unread cache bytes (possibly
@@ -305,7 +319,12 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
     const int slot = (u * kMqWaves + wave) * 64 + lane;
     const int row = slot / CCH;
     const int pos = slot % CCH;
-    if constexpr (kFp8) {
+    if constexpr (kKRaw) {
+      // K codes: 16-byte chunk ch of token `row` at position ch ^ kswz8(row),
+      // so the 16 tokens of an 8-byte operand read hit distinct banks.
+      koff[u] = (row % BS) * CROWB + ((pos ^ kswz8(row)) << 4);
+      voff[u] = (row % BS) * CROWB + pos * 16;
+    } else if constexpr (kFp8) {
       koff[u] = voff[u] = (row % BS) * CROWB + pos * 16;
     } else {
       koff[u] = (row % BS) * CROWB + ((pos ^ kswz<ROWB>(row)) << 4);
@@ -343,17 +362,19 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
     const unsigned char* kq = ring + stage * 2 * RTILEB;
     const unsigned char* vq = kq + RTILEB;
     unsigned char* kt = wide;
-    unsigned char* vt = wide + TILEB;
+    unsigned char* vt = wide_v;
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
       const int c = tid + u * kMqWaves * 64;
       if (c >= CHUNKS) continue;
       const int tok = c / CCH;
       const int ch = c % CCH;
-      const uint4 kw = *reinterpret_cast<const uint4*>(kq + c * 16);
+      if constexpr (!kKRaw) {
+        const uint4 kw = *reinterpret_cast<const uint4*>(kq + c * 16);
+        *reinterpret_cast<uint4*>(kt + tok * ROWB + (((2 * ch) ^ kswz<ROWB>(tok)) << 4)) = fp8x8_to_bf16x8(kw.x, kw.y);
+        *reinterpret_cast<uint4*>(kt + tok * ROWB + (((2 * ch + 1) ^ kswz<ROWB>(tok)) << 4)) = fp8x8_to_bf16x8(kw.z, kw.w);
+      }
       const uint4 vw = *reinterpret_cast<const uint4*>(vq + c * 16);
-      *reinterpret_cast<uint4*>(kt + tok * ROWB + (((2 * ch) ^ kswz<ROWB>(tok)) << 4)) = fp8x8_to_bf16x8(kw.x, kw.y);
-      *reinterpret_cast<uint4*>(kt + tok * ROWB + (((2 * ch + 1) ^ kswz<ROWB>(tok)) << 4)) = fp8x8_to_bf16x8(kw.z, kw.w);
       *reinterpret_cast<uint4*>(vt + tok * ROWB + (((2 * ch) ^ swz<ROWB>(tok)) << 4)) = fp8x8_to_bf16x8(vw.x, vw.y);
       *reinterpret_cast<uint4*>(vt + tok * ROWB + (((2 * ch + 1) ^ swz<ROWB>(tok)) << 4)) = fp8x8_to_bf16x8(vw.z, vw.w);
     }
@@ -366,9 +387,10 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   const int block_first_qi = b.rb * kRowsPerBlock / G;
   const int block_full_end = min(tok1, b.ctx - b.qlen + block_first_qi + 1);
 
-  auto compute_step = [&](int st, const unsigned char* kt, auto full_tag) {
+  // kt: the step's K (bf16 tile, or for kKRaw the stage's raw codes); vt:
+  // its V tile in the transposed-read layout.
+  auto compute_step = [&](int st, const unsigned char* kt, const unsigned char* vt, auto full_tag) {
     constexpr bool kFull = decltype(full_tag)::value;
-    const unsigned char* vt = kt + TILEB;
     const int t_base = tok0 + st * kStepTokens;
     // S^T for the step's 16-token tiles.
     f32x4_t sc[NTT];
@@ -378,7 +400,15 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
       const int tok = 16 * tt + l16;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(kt + tok * ROWB + (((4 * c + g4) ^ kswz<ROWB>(tok)) << 4));
+        uint4 ka;
+        if constexpr (kKRaw) {
+          // Codes of columns 32 c + 8 g4 .. +7: half g4 % 2 of chunk 2 c + g4 / 2.
+          const uint2 w = *reinterpret_cast<const uint2*>(
+              kt + tok * CROWB + (((2 * c + (g4 >> 1)) ^ kswz8(tok)) << 4) + (g4 & 1) * 8);
+          ka = fp8x8_to_bf16x8(w.x, w.y);
+        } else {
+          ka = *reinterpret_cast<const uint4*>(kt + tok * ROWB + (((4 * c + g4) ^ kswz<ROWB>(tok)) << 4));
+        }
         sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qb[c], sc[tt], 0, 0, 0);
       }
     }
@@ -470,13 +500,15 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
           if ((st + kAhead) * PPS - ids_base == WINDOW) load_ids((st + kAhead) * PPS);
           dma_step(st + kAhead, stage == 0 ? NSTAGE - 1 : stage - 1);
         }
-        const unsigned char* tiles = ring + stage * 2 * RTILEB;
+        const unsigned char* kt = ring + stage * 2 * RTILEB;
+        const unsigned char* vt = kt + RTILEB;
         if constexpr (kFp8) {
           widen_step(stage);
           block_barrier();
-          tiles = wide;
+          if constexpr (!kKRaw) kt = wide;
+          vt = wide_v;
         }
-        if (wave_rows) compute_step(st, tiles, full_tag);
+        if (wave_rows) compute_step(st, kt, vt, full_tag);
         stage = stage == NSTAGE - 1 ? 0 : stage + 1;
       }
     };
