@@ -75,6 +75,8 @@ struct MultiQueryParams {
   int2* work;          // work items (sequence, row block index << 16 | partition)
   int* work_count;     // number of work items
   int work_capacity;   // items the list holds (the grid's bound)
+  int find_items;      // the workgroups find their own items (at most 64 sequences;
+                       // no list, no schedule launch)
   int decode_rows_elsewhere;  // sequences with one query run in the decode kernels
   int stream_rows;     // single-block sequences of at most this many rows run in the
                        // streaming kernel (0: none), the others in the ring kernel
@@ -126,6 +128,41 @@ __device__ __forceinline__ MqBlock mq_block(const MultiQueryParams& p, int s, in
   if (nrb == 1 && b.kv_end > p.partition_tokens)
     b.nparts = (b.kv_end + p.partition_tokens - 1) / p.partition_tokens;
   return b;
+}
+
+// Work item `item` of the list multi_query_schedule_kernel writes (the same
+// items in the same order), found by the workgroup itself when the batch has
+// at most 64 sequences: wave 0 counts the items of sequence `lane`, scans the
+// counts, and the lane whose range holds `item` publishes it through LDS.
+// Every thread of the workgroup calls it; false: no such item.
+template <int G>
+__device__ __forceinline__ bool find_item(const MultiQueryParams& p, int item, int2* w) {
+  __shared__ int2 found;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int n = 0;
+    bool single = false;
+    if (lane < p.num_seqs) {
+      const MqBlock b = mq_block<G>(p, lane, 0);
+      if (!b.skip) {
+        single = b.nrb == 1;
+        n = single ? b.nparts : b.nrb;
+      }
+    }
+    int incl = n;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    const int start = incl - n;
+    if (lane == 0) found = make_int2(-1, 0);
+    if (n > 0 && item >= start && item < start + n)
+      found = make_int2(lane, single ? item - start : (item - start) << 16);
+  }
+  __syncthreads();
+  *w = found;
+  return w->x >= 0;
 }
 
 // K rows (ROWB bytes) in LDS: 16-byte chunk c of token `tok` is stored at
@@ -191,8 +228,13 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
 
   const int kvh = blockIdx.x % p.num_kv_heads;
   const int item = blockIdx.x / p.num_kv_heads;
-  if (item >= *p.work_count) return;  // uniform over the workgroup
-  const int2 w = p.work[item];
+  int2 w;
+  if (p.find_items) {
+    if (!find_item<G>(p, item, &w)) return;  // uniform over the workgroup
+  } else {
+    if (item >= *p.work_count) return;  // uniform over the workgroup
+    w = p.work[item];
+  }
   const int s = w.x;
   const int rbi = w.y >> 16;
   const int part = w.y & 0xffff;
@@ -581,8 +623,13 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(2
 
   const int kvh = blockIdx.x % p.num_kv_heads;
   const int item = blockIdx.x / p.num_kv_heads;
-  if (item >= *p.work_count) return;  // uniform over the workgroup
-  const int2 w = p.work[item];
+  int2 w;
+  if (p.find_items) {
+    if (!find_item<G>(p, item, &w)) return;  // uniform over the workgroup
+  } else {
+    if (item >= *p.work_count) return;  // uniform over the workgroup
+    w = p.work[item];
+  }
   const int s = w.x;
   const int part = w.y & 0xffff;
   const MqBlock b = mq_block<G>(p, s, w.y >> 16);
@@ -1040,9 +1087,17 @@ hipError_t launch_t(const MultiQueryLaunch& a, MultiQueryParams p) {
   constexpr int kStreamRows = sizeof(TC) == 1 ? 32 : 0;
   p.stream_rows = a.partition_tokens <= 256 * BS ? kStreamRows : 0;
   const int rows = a.max_query_len * G;  // rows of the longest sequence
-  hipLaunchKernelGGL((multi_query_schedule_kernel<G>), dim3(1), dim3(256), 0, a.stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // Up to 64 sequences each workgroup finds its own work item (one wave's
+  // scan, no schedule launch: 70B verification shape, bf16, 107.6 -> 104.5
+  // us; E4M3 unchanged); larger batches get the list from the schedule
+  // kernel.  Same items either way.
+  p.find_items = a.num_seqs <= 64;
+  hipError_t e = hipSuccess;
+  if (!p.find_items) {
+    hipLaunchKernelGGL((multi_query_schedule_kernel<G>), dim3(1), dim3(256), 0, a.stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid((unsigned)((int64_t)a.work_capacity * a.num_kv_heads));
   // The ring kernel takes the other sequences, and runs when the batch can
   // hold any.  When every sequence's rows fit one block (each page is read by
