@@ -287,6 +287,40 @@ def test_fixed_partitions_batch_invariant(kv):
         assert np.array_equal(bits(alone), bits(whole[rows])), s
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_work_list_and_in_kernel_lookup_agree(kv):
+    """A verification batch of 80 sequences takes its work list from the
+    schedule kernel, a batch of at most 64 finds the items in the kernel: the
+    oracle checks the large batch, and 40 of its sequences run as a batch of
+    their own give the same bits (fixed partitions)."""
+    spec = wl.Spec(f"mqlist{kv}", 64, 8, 128, 16, "bf16", seed=93,
+                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0 if kv == "bf16" else 1.0 / 64)
+    g = torch.Generator().manual_seed(8)
+    n = 80
+    ctx = torch.randint(8, 600, (n,), generator=g).tolist()
+    qlen = torch.randint(2, 7, (n,), generator=g).tolist()
+    plan = wl.multi_query_plan(ctx, qlen, 16, g)
+    x = wl.build_inputs(spec, plan)
+    whole, t = gpu_mq_step(x, partition_tokens=128)
+    ref, _, _ = oracle_mq_step(x)
+    assert_close(as_f64(whole), ref, "bf16", spec.name)
+    qs = x.query_start.tolist()
+    sub = list(range(20, 60))
+    rows = torch.cat([torch.arange(qs[s], qs[s + 1]) for s in sub]).cuda()
+    starts = [0]
+    for s in sub:
+        starts.append(starts[-1] + qs[s + 1] - qs[s])
+    q = t["q"].index_select(0, rows).contiguous()
+    part = torch.empty_like(q)
+    binding.pa_multi_query(part, q, t["k_cache"], t["v_cache"], t["block_tables"][sub].contiguous(),
+                           t["context_lens"][sub].contiguous(),
+                           torch.tensor(starts, dtype=torch.int32, device="cuda"), x.scale,
+                           x.max_context_len, max(qlen), partition_tokens=128,
+                           k_scale=x.k_scale, v_scale=x.v_scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(part), bits(whole.index_select(0, rows)))
+
+
 @pytest.mark.parametrize("h,hkv,bs,kv", [(40, 40, 16, "bf16"), (64, 8, 32, "bf16"), (64, 8, 32, "fp8")])
 def test_pool_past_2g_elements(h, hkv, bs, kv):
     """Every page of the batch lies past 2^31 elements of a 2.29e9-element
