@@ -335,8 +335,10 @@ int pa_decode_shared_prefix(void* out, const void* q,
 
 /*
  * pa_multi_query_workspace_size -- bytes of device workspace pa_multi_query
- * needs: the partitions of cut contexts and the list of work items it builds
- * on the device each call (0 when there are no sequences or no query tokens);
+ * needs: the partitions of cut contexts and room for the list of work items
+ * it builds on the device each call for batches of more than 64 sequences
+ * (smaller batches find their items in the kernels; the size does not depend
+ * on that) (0 when there are no sequences or no query tokens);
  * (size_t)-1 for arguments it would reject.  partition_tokens: 0 = the
  * default pa_multi_query picks for the same shape (see there).
  */
