@@ -20,7 +20,9 @@ pass the ordinary parity cases.  Here:
 Each decode case runs on the vector path (MHA, fp32 and bf16), on the
 matrix-core path (grouped heads, bf16 query), and with an E4M3 cache, with one
 partition per sequence and with several; the first two regimes also run
-through multi-query attention and the shared-prefix decode.
+through multi-query attention and the shared-prefix decode.  The last tests
+run the same attention through two kernels (GQA against MHA with repeated kv
+heads; 32- against 16-token pages) and compare them with each other.
 """
 
 import numpy as np
@@ -281,3 +283,60 @@ def test_shared_prefix_ramp_moves_the_maximum_every_page(h, hkv, d, bs, kv, pt):
     tpos = new_decode_token_positions(x)
     x.key = (x.key.float() + a * tpos[:, None, None] * w[None]).to(x.key.dtype)
     check_shared(x, pt)
+
+
+# The same attention through different kernels: the vector kernel (MHA with
+# each kv head repeated G times) against the matrix-core kernel (GQA), and
+# 16-token against 32-token pages holding the same logical tokens.  Each side
+# is also held to the oracle.
+
+def _decode(x):
+    out, _ = gpu_step(x, copy=False, reshape=False)
+    return as_f64(out)
+
+
+@pytest.mark.parametrize("kv", [None, "fp8"])
+def test_gqa_equals_mha_with_repeated_kv_heads(kv):
+    h, hkv, d, bs = 32, 8, 128, 16
+    g = h // hkv
+    x = make(f"gqa{kv}", h, hkv, d, bs, "bf16", kv, seed=211)
+    y = make(f"mha{kv}", h, h, d, bs, "bf16", kv, seed=211)
+    y.q = x.q.clone()
+    y.k_cache = x.k_cache.repeat_interleave(g, dim=1).contiguous()
+    y.v_cache = x.v_cache.repeat_interleave(g, dim=1).contiguous()
+    y.block_tables, y.context_lens = x.block_tables.clone(), x.context_lens.clone()
+    y.plan = x.plan
+    a, b = _decode(x), _decode(y)
+    ref, _, _ = oracle_step(x, copy=False, reshape=False)
+    assert_close(a, ref, "bf16", "gqa")
+    assert_close(b, ref, "bf16", "mha")
+    atol, rtol = TOL["bf16"]
+    assert np.all(np.abs(a - b) <= atol + rtol * np.abs(b))
+
+
+@pytest.mark.parametrize("h,hkv,kv", [(8, 8, None), (64, 8, None), (64, 8, "fp8")])
+def test_block_size_16_and_32_agree(h, hkv, kv):
+    d = 128
+    x = make(f"bs32_{h}{kv}", h, hkv, d, 32, "bf16", kv, seed=223)
+    # Block b of 32 tokens becomes blocks 2b and 2b + 1 of 16.
+    nb = x.plan.num_blocks
+    y = make(f"bs16_{h}{kv}", h, hkv, d, 16, "bf16", kv, seed=223)
+    kc = x.k_cache.view(nb, hkv, 2, 16, d).permute(0, 2, 1, 3, 4).reshape(2 * nb, hkv, 16, d).contiguous()
+    vc = x.v_cache.view(nb, hkv, 2, 16, d).permute(0, 2, 1, 3, 4).reshape(2 * nb, hkv, 16, d).contiguous()
+    t32 = x.plan.block_tables
+    t16 = np.full((t32.shape[0], 2 * t32.shape[1]), -1, dtype=np.int32)
+    t16[:, 0::2] = np.where(t32 >= 0, 2 * t32, -1)
+    t16[:, 1::2] = np.where(t32 >= 0, 2 * t32 + 1, -1)
+    y.q, y.k_cache, y.v_cache = x.q.clone(), kc, vc
+    y.block_tables = torch.from_numpy(t16)
+    y.context_lens = x.context_lens.clone()
+    y.plan.block_tables = t16
+    y.plan.num_blocks = 2 * nb
+    a, b = _decode(x), _decode(y)
+    ref, _, _ = oracle_step(x, copy=False, reshape=False)
+    assert_close(a, ref, "bf16", "bs32")
+    ref16, _, _ = oracle_step(y, copy=False, reshape=False)
+    assert np.array_equal(ref16, ref)  # the oracle sees the same logical tokens
+    assert_close(b, ref, "bf16", "bs16")
+    atol, rtol = TOL["bf16"]
+    assert np.all(np.abs(a - b) <= atol + rtol * np.abs(b))
