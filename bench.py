@@ -525,6 +525,13 @@ def cpu_baseline(name, target_s):
         list(ex.map(one, range(n_par)))
         t_par = time.perf_counter() - t0
     n_host = len(host)
+    # K and V bytes each sequence-step reads, as counted for the GPU.
+    ekv = {"f32": 4, "bf16": 2, "fp8": 1}[spec.cache_dtype]
+
+    def kv_bytes(ctx_tokens):
+        return 2 * spec.num_kv_heads * spec.head_dim * ekv * ctx_tokens
+
+    par_tokens = sum(int(host[i % n_host][4][0]) for i in range(n_par))
     del x, host
     torch.cuda.empty_cache()
     return {
@@ -537,7 +544,9 @@ def cpu_baseline(name, target_s):
                   f"in total): reshape_and_cache of the new token + decode, fp64 NumPy oracle, "
                   f"one BLAS thread, {t_total:.1f} s",
         "seconds": t_total,
+        "GBps": kv_bytes(tokens) / t_total / 1e9,
         "threaded": {"value": n_par / t_par, "unit": "tokens/s", "cores": cores,
+                     "GBps": kv_bytes(par_tokens) / t_par / 1e9,
                      "sample": f"{n_par} sequence-steps of the same sample over {cores} threads "
                                f"(one BLAS thread each), {t_par:.1f} s wall"},
         "host_cpus_available": cores,
