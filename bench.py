@@ -60,12 +60,20 @@ for _n in ("llama7b", "llama13b", "gqa70b", "beam", "specdec70b", "chunked13b"):
 # "+fill" runs the same step at the batch-shaped length (PA_PARTITION_FILL).
 # Verification of 4 drafted tokens over an E4M3 cache (32 rows per sequence)
 # runs on the streaming multi-query kernel.
+# "chunked13b_chunks" keeps only the two prefill chunks of the chunked-prefill
+# batch (no decode rows, so no side-stream launch): the multi-query tile
+# kernel alone, compute-bound.
 VARIANTS = {"gqa70b_x2": ("gqa70b", {"num_seqs": 2}), "gqa70b_fp8_x2": ("gqa70b_fp8", {"num_seqs": 2}),
-            "specdec70b_fp8_q4": ("specdec70b_fp8", {"query_len": 4})}
+            "specdec70b_fp8_q4": ("specdec70b_fp8", {"query_len": 4}),
+            "chunked13b_chunks": ("chunked13b", {"num_decodes": 0}),
+            "chunked13b_fp8_chunks": ("chunked13b_fp8", {"num_decodes": 0})}
 for _n in ("gqa70b_x2", "gqa70b_fp8_x2"):
     DESCRIPTION[_n] = DESCRIPTION[VARIANTS[_n][0]].replace("16 seqs", "2 seqs") + ", fixed partitions"
     DESCRIPTION[_n + "+fill"] = DESCRIPTION[_n].replace("fixed partitions", "batch-shaped partitions")
 DESCRIPTION["specdec70b_fp8_q4"] = DESCRIPTION["specdec70b_fp8"].replace("6 new tokens", "4 new tokens")
+for _n in ("chunked13b", "chunked13b_fp8"):
+    DESCRIPTION[_n + "_chunks"] = DESCRIPTION[_n].replace(
+        " and 64 decodes (ctx U[128,4096]), 3136 query tokens", ", 3072 query tokens, no decodes")
 DESCRIPTION["swap13b"] = ("swap_blocks of 1024 random blocks of the LLaMA-13B-shaped pool (Hkv=40, BS=16, "
                           "D=128, bf16: 320 KiB of K+V per block) to pinned host memory and back")
 # "+prefix": the same step with pa_decode_shared_prefix (each shared page read
@@ -82,8 +90,9 @@ def parse():
     ap.add_argument("--workload", default="llama13b",
                     choices=sorted(n for n in DESCRIPTION if n != "swap13b"))
     ap.add_argument("--partition-tokens", type=int, default=0)
-    ap.add_argument("--others", default="llama7b,gqa70b,beam,beam+prefix,llama13b_fp8,gqa70b_fp8,"
-                                        "specdec70b,specdec70b_fp8_q4,chunked13b,gqa70b_x2,gqa70b_x2+fill,swap13b",
+    ap.add_argument("--others", default="tiny,llama7b,gqa70b,beam,beam+prefix,llama13b_fp8,gqa70b_fp8,"
+                                        "beam_fp8+prefix,specdec70b,specdec70b_fp8,specdec70b_fp8_q4,"
+                                        "chunked13b,chunked13b_chunks,gqa70b_x2,gqa70b_x2+fill,swap13b",
                     help="comma list of extra workloads to report ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cache-ops", dest="cache_ops", action="store_false",
@@ -138,8 +147,8 @@ def decode_kernel_name(label, spec) -> str:
 
 def unique_bytes(plan, spec) -> int:
     """Like algorithmic_bytes, but a physical block shared by several sequences
-    counts once (with the most tokens any of them uses from it)."""
-    e = 4 if spec.dtype == "f32" else 2
+    counts once (with the most tokens any of them uses from it): the K/V bytes
+    HBM has to deliver when each page is fetched once per call."""
     ekv = {"f32": 4, "bf16": 2, "fp8": 1}[spec.cache_dtype]
     bs = plan.block_size
     used = {}
@@ -148,10 +157,9 @@ def unique_bytes(plan, spec) -> int:
         for j in range(-(-c // bs)):
             b = int(plan.block_tables[s][j])
             used[b] = max(used.get(b, 0), min(bs, c - j * bs))
-    kv = 2 * spec.num_kv_heads * spec.head_dim * ekv * sum(used.values())
-    qo = 2 * len(ctx) * spec.num_heads * spec.head_dim * e
-    table = 4 * sum(-(-c // bs) for c in ctx)
-    return kv + qo + table + 4 * len(ctx)
+    kv_unique = 2 * spec.num_kv_heads * spec.head_dim * ekv * sum(used.values())
+    kv_logical = sum(2 * spec.num_kv_heads * c * spec.head_dim * ekv for c in ctx)
+    return algorithmic_bytes(plan, spec) - kv_logical + kv_unique
 
 
 def kernel_sources(workload: str):
@@ -329,10 +337,14 @@ def run_workload(label, steps, warmup, partition_tokens, flush=False, settle_s=0
         "attention_flops": flops,
         "attention_TFLOPs": flops / (avg_decode_ms / 1e3) / 1e12,
         "decode_algorithmic_bytes": nbytes,
-        "decode_GBps": nbytes / (avg_decode_ms / 1e3) / 1e9,
-        "decode_frac_of_peak": nbytes / (avg_decode_ms / 1e3) / 1e9 / PEAK_GBPS,
+        # The HBM rate counts each physical page once per call (unique bytes:
+        # a page that several sequences share is fetched from HBM once); the
+        # logical rate counts it once per sequence that reads it.  They are
+        # equal unless sequences share pages.
+        "decode_GBps": ubytes / (avg_decode_ms / 1e3) / 1e9,
+        "decode_frac_of_peak": ubytes / (avg_decode_ms / 1e3) / 1e9 / PEAK_GBPS,
         "decode_unique_bytes": ubytes,
-        "decode_unique_GBps": ubytes / (avg_decode_ms / 1e3) / 1e9,
+        "decode_logical_GBps": nbytes / (avg_decode_ms / 1e3) / 1e9,
         "copy_pairs": int(plan.block_pairs.shape[0]),
         "new_tokens": int(plan.slot_mapping.shape[0]),
         "partition_tokens": partition_tokens,
@@ -555,14 +567,22 @@ def cpu_baseline(name, target_s):
 
 
 def _cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo names it: the full "model name" field,
+    with the vendor and the family / model / stepping numbers beside it."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break  # the first processor's block is enough
+                k, _, v = line.partition(":")
+                fields[k.strip()] = v.strip()
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = fields.get("model name", "unknown")
+    ids = ", ".join(f"{k} {fields[k]}" for k in ("vendor_id", "cpu family", "model", "stepping")
+                    if k in fields)
+    return f"{name} ({ids})" if ids else name
 
 
 def copy_calibration():
@@ -576,6 +596,26 @@ def copy_calibration():
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
                       "launches": 3}))
+
+
+# The five configurations the metric is quoted on, by workload label.
+BASELINE_CONFIGS = {"tiny": 1, "llama7b": 2, "llama13b": 3, "gqa70b": 4, "beam": 5, "beam+prefix": 5}
+
+
+def baseline_summary(head, others):
+    """One short entry per run of a configuration of the metric: decode call
+    time, decode tokens/s, HBM GB/s (each page once) and its fraction of peak,
+    and the whole step's time."""
+    rows = []
+    for r in [head] + others:
+        cfg = BASELINE_CONFIGS.get(r.get("workload"))
+        if cfg is None:
+            continue
+        rows.append({"cfg": cfg, "w": r["workload"] + (" cold" if r["cache"].startswith("cold") else ""),
+                     "us": round(r["decode_avg_us"], 1), "tok_s": round(r["decode_tokens_per_s"]),
+                     "GBps": round(r["decode_GBps"]), "frac": round(r["decode_frac_of_peak"], 3),
+                     "step_us": round(r["ms_per_step"] * 1e3, 1)})
+    return sorted(rows, key=lambda e: e["cfg"])
 
 
 def main():
@@ -654,6 +694,9 @@ def main():
         "cpu_baseline": cpu,
         "cache_ops": cache_ops,
         "workloads": others,
+        # Last, so that the tail of the output holds it: the five configurations
+        # of the metric, one compact entry per run.
+        "configs": baseline_summary(head, others),
     }
     print(json.dumps(line))
 

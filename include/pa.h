@@ -368,7 +368,8 @@ size_t pa_multi_query_workspace_size(int num_seqs, int num_query_tokens, int num
  * dtype must be PA_BF16 (cache PA_BF16 or PA_FP8_E4M3); G = num_heads /
  * num_kv_heads in {1, 2, 4, 8}; head_dim 64 or 128; block_size 16 or 32.
  * max_query_len >= every n and max_context_len >= every L (host bounds that size
- * the grid).  A sequence with n == 1 is a decode step and runs through
+ * the grid); ceil(max_query_len * G / 64) and the number of partitions of
+ * max_context_len must each stay below 2^15 (else PA_ERR_UNSUPPORTED).  A sequence with n == 1 is a decode step and runs through
  * pa_decode's kernels (with their partitioning) unless flags holds
  * PA_MULTI_QUERY_TILES_ONLY (other flag bits than the two above:
  * PA_ERR_UNSUPPORTED).

@@ -447,7 +447,8 @@ int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4))
     return PA_ERR_ALIGN;
-  if (z.work_capacity * num_kv_heads > 0x7fffffffLL || row_blocks > 0xffff || z.max_parts > 0xffff ||
+  // Work items carry the row-block and partition indices in 16 bits each.
+  if (z.work_capacity * num_kv_heads > 0x7fffffffLL || row_blocks > 0x7fff || z.max_parts > 0x7fff ||
       num_seqs > kMaxGridYZ || num_kv_heads > kMaxGridYZ || num_heads > kMaxGridYZ)
     return PA_ERR_UNSUPPORTED;
   if (z.total > 0) {

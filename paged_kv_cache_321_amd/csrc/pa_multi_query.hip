@@ -98,6 +98,12 @@ struct MqBlock {
   bool bad;     // bad context length: the block's rows are written as NaN
 };
 
+// A work item's second word holds a row-block index in its upper 16 bits and
+// a partition index in the lower 16 (the host keeps both below 2^15).  The
+// word is packed and unpacked as unsigned, so no index reads back negative.
+__device__ __forceinline__ int pack_row_block(int rbi) { return (int)((uint32_t)rbi << 16); }
+__device__ __forceinline__ int row_block_of(int word) { return (int)((uint32_t)word >> 16); }
+
 template <int G>
 __device__ __forceinline__ MqBlock mq_block(const MultiQueryParams& p, int s, int rbi) {
   MqBlock b{};
@@ -158,7 +164,7 @@ __device__ __forceinline__ bool find_item(const MultiQueryParams& p, int item, i
     const int start = incl - n;
     if (lane == 0) found = make_int2(-1, 0);
     if (n > 0 && item >= start && item < start + n)
-      found = make_int2(lane, single ? item - start : (item - start) << 16);
+      found = make_int2(lane, single ? item - start : pack_row_block(item - start));
   }
   __syncthreads();
   *w = found;
@@ -236,7 +242,7 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
     w = p.work[item];
   }
   const int s = w.x;
-  const int rbi = w.y >> 16;
+  const int rbi = row_block_of(w.y);
   const int part = w.y & 0xffff;
   const MqBlock b = mq_block<G>(p, s, rbi);
   if (b.skip || part >= b.nparts) return;
@@ -632,7 +638,7 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(2
   }
   const int s = w.x;
   const int part = w.y & 0xffff;
-  const MqBlock b = mq_block<G>(p, s, w.y >> 16);
+  const MqBlock b = mq_block<G>(p, s, row_block_of(w.y));
   if (b.skip || part >= b.nparts || b.nrb != 1 || b.rows > p.stream_rows) return;  // the ring kernel's
 
   const int tid = threadIdx.x;
@@ -937,7 +943,7 @@ __global__ __launch_bounds__(256) void multi_query_schedule_kernel(MultiQueryPar
     }
     const int start = base + sums[tid] - n;
     for (int i = 0; i < n && start + i < p.work_capacity; ++i)
-      p.work[start + i] = make_int2(s, single ? i : i << 16);
+      p.work[start + i] = make_int2(s, single ? i : pack_row_block(i));
     __syncthreads();  // every thread has read base
     if (tid == 255) base += sums[255];
     __syncthreads();

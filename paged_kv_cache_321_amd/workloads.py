@@ -34,10 +34,14 @@ type with round-to-nearest-even):
               64 decoding sequences (contexts uniform in [128, 4096]); 40
               heads, head_dim 128, block_size 16 (LLaMA-13B shape).
 
-``<name>_fp8``  the same workload with an fp8 (OCP E4M3) KV cache: history
-              entries are N(0, 1) draws divided by the cache scale 1/64 and
-              cast to float8_e4m3fn (torch's cast, clamped to +-448), new
-              tokens stay bf16 and are encoded by reshape_and_cache.
+``<name>_fp8``  the same workload with an fp8 (OCP E4M3) KV cache and two
+              different scales, k_scale = 0.02 and v_scale = 0.03 (neither a
+              power of two, so a swapped pair or a division in place of the
+              multiplication by fl32(1 / scale) shows in the results):
+              history entries are N(0, 1) draws divided by their cache's
+              scale and cast to float8_e4m3fn (torch's cast, clamped to
+              +-448), new tokens stay bf16 and are encoded by
+              reshape_and_cache.
 
 Physical pools hold ceil(1.1 x blocks needed) blocks unless a size is given;
 blocks are handed out in the order of a seeded permutation, sequence by
@@ -58,12 +62,23 @@ import torch
 
 from .block_pool import BlockPool, BlockTable, padded_rows
 
-__all__ = ["Spec", "Plan", "Inputs", "SPECS", "uniform_plan", "beam_plan", "prefix_plan",
-           "multi_query_plan",
+__all__ = ["Spec", "FP8_K_SCALE", "FP8_V_SCALE", "fp8_scales", "Plan", "Inputs", "SPECS",
+           "uniform_plan", "beam_plan", "prefix_plan", "multi_query_plan",
            "make_plan", "build_inputs", "make_inputs", "to_host_numpy",
            "TORCH_DTYPE"]
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
+
+# Scales of the fp8 caches: distinct, and not powers of two.
+FP8_K_SCALE = 0.02
+FP8_V_SCALE = 0.03
+
+
+def fp8_scales(cache_dtype: Optional[str]) -> dict:
+    """Spec keyword arguments for the cache scales of ``cache_dtype``."""
+    if cache_dtype == "fp8":
+        return dict(k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
+    return dict(k_scale=1.0, v_scale=1.0)
 
 
 @dataclass(frozen=True)
@@ -77,7 +92,8 @@ class Spec:
     seed: int
     q_std: float = 1.0
     kv_dtype: Optional[str] = None   # cache element type (None: same as dtype)
-    kv_scale: float = 1.0            # fp8 caches: a code stands for value * kv_scale
+    k_scale: float = 1.0             # fp8 caches: a K code stands for value * k_scale,
+    v_scale: float = 1.0             # a V code for value * v_scale
     recipe: Optional[str] = None     # plan recipe (None: the name)
 
     @property
@@ -98,7 +114,7 @@ for _base in ("llama7b", "llama13b", "gqa70b", "beam", "specdec70b", "chunked13b
     _b = SPECS[_base]
     SPECS[_base + "_fp8"] = Spec(_base + "_fp8", _b.num_heads, _b.num_kv_heads, _b.head_dim,
                                  _b.block_size, _b.dtype, seed=_b.seed + 1000, q_std=_b.q_std,
-                                 kv_dtype="fp8", kv_scale=1.0 / 64, recipe=_base)
+                                 kv_dtype="fp8", recipe=_base, **fp8_scales("fp8"))
 
 
 @dataclass
@@ -412,8 +428,8 @@ def build_inputs(spec: Spec, plan: Plan, device="cpu", poison: bool = True) -> I
     hkv, d = spec.num_kv_heads, spec.head_dim
     q = _randn((s, spec.num_heads, d), gen, device, spec.q_std, spec.dtype)
     if spec.cache_dtype == "fp8":
-        k_cache = _fp8_codes((nb, hkv, bs, d), gen, device, spec.kv_scale)
-        v_cache = _fp8_codes((nb, hkv, bs, d), gen, device, spec.kv_scale)
+        k_cache = _fp8_codes((nb, hkv, bs, d), gen, device, spec.k_scale)
+        v_cache = _fp8_codes((nb, hkv, bs, d), gen, device, spec.v_scale)
     else:
         k_cache = _randn((nb, hkv, bs, d), gen, device, 1.0, spec.dtype, chunk_rows=256)
         v_cache = _randn((nb, hkv, bs, d), gen, device, 1.0, spec.dtype, chunk_rows=256)
@@ -436,8 +452,8 @@ def build_inputs(spec: Spec, plan: Plan, device="cpu", poison: bool = True) -> I
         context_lens=torch.from_numpy(plan.context_lens.copy()).to(device),
         block_pairs=torch.from_numpy(plan.block_pairs.copy()).to(device),
         scale=float(np.float32(1.0 / math.sqrt(d))),
-        k_scale=spec.kv_scale if spec.cache_dtype == "fp8" else 1.0,
-        v_scale=spec.kv_scale if spec.cache_dtype == "fp8" else 1.0,
+        k_scale=spec.k_scale if spec.cache_dtype == "fp8" else 1.0,
+        v_scale=spec.v_scale if spec.cache_dtype == "fp8" else 1.0,
         query_start=None if plan.query_lens is None
         else torch.from_numpy(plan.query_start).to(device),
     )

@@ -20,3 +20,14 @@ def _announce_gpu_case(request):
         sys.__stderr__.write(f"\n[gpu-case] {request.node.nodeid}\n")
         sys.__stderr__.flush()
     yield
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Worst |gpu - oracle| / (atol + rtol |oracle|) per checked label."""
+    helpers = sys.modules.get("gpu_helpers")
+    worst = getattr(helpers, "WORST_RATIO", None)
+    if not worst:
+        return
+    terminalreporter.write_line("worst err/bound per checked label (1.0 = at tolerance):")
+    for what, r in sorted(worst.items(), key=lambda kv: -kv[1]):
+        terminalreporter.write_line(f"  {r:7.4f}  {what}")

@@ -135,11 +135,18 @@ def bits(t) -> np.ndarray:
     return a.view({1: np.uint8, 2: np.uint16, 4: np.uint32}[a.dtype.itemsize])
 
 
+# Largest err / bound seen per label (the test log prints them at the end).
+WORST_RATIO: dict = {}
+
+
 def assert_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str = "") -> float:
     atol, rtol = TOL[dtype]
     assert np.isfinite(gpu).all(), f"{what}: non-finite GPU output"
     err = np.abs(gpu - ref)
     bound = atol + rtol * np.abs(ref)
+    if err.size:
+        ratio = float((err / bound).max())
+        WORST_RATIO[what] = max(ratio, WORST_RATIO.get(what, 0.0))
     bad = err > bound
     if bad.any():
         i = np.unravel_index(np.argmax(err - bound), err.shape)

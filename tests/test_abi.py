@@ -337,6 +337,9 @@ def multi_query(**kw):
     (dict(S=0), OK),                     # nothing to launch
     (dict(T=0, q=None, out=None), OK),
     (dict(mq=0), OK),
+    (dict(H=64, Hkv=8, mq=0x8000 * 8), UNSUP),   # 2^15 row blocks of 64 rows
+    (dict(H=64, Hkv=8, mq=0x7fff * 8), WS),      # the largest chunk accepted
+    (dict(maxctx=0x8000 * 16, mb=0x8000, pt=16), UNSUP),  # 2^15 partitions per row
     (dict(flags=4), UNSUP),              # unknown flag bit
     (dict(flags=-1), UNSUP),
     (dict(flags=1, S=0), OK),

@@ -44,6 +44,15 @@ def test_unique_bytes_count_shared_blocks_once():
     assert bench.unique_bytes(plan, spec) < bench.algorithmic_bytes(plan, spec)
     plan, spec = plan_of("llama7b")  # nothing shared
     assert bench.unique_bytes(plan, spec) == bench.algorithmic_bytes(plan, spec)
+    plan, spec = plan_of("specdec70b")  # one q/out row per query token
+    assert bench.unique_bytes(plan, spec) == bench.algorithmic_bytes(plan, spec)
+    # The beam workload: 32 prefixes of 64 blocks read once; every beam's
+    # tail blocks once; q/out, tables and lengths as counted per sequence.
+    plan, spec = plan_of("beam")
+    page = 2 * spec.num_kv_heads * spec.head_dim * 2       # K+V bytes per token
+    tails = sum(int(c) - 1024 for c in plan.context_lens)
+    other = bench.algorithmic_bytes(plan, spec) - page * sum(int(c) for c in plan.context_lens)
+    assert bench.unique_bytes(plan, spec) == page * (32 * 1024 + tails) + other
 
 
 def test_attention_flops_single_query_and_causal():

@@ -49,7 +49,7 @@ CTX = [1, 17, 255, 700, 1100]
 
 
 def make(label, h, hkv, d, bs, dtype, kv, seed):
-    spec = wl.Spec(f"inv_{label}", h, hkv, d, bs, dtype, seed=seed, kv_dtype=kv, kv_scale=1.0)
+    spec = wl.Spec(f"inv_{label}", h, hkv, d, bs, dtype, seed=seed, kv_dtype=kv, k_scale=1.0, v_scale=1.0)
     gen = torch.Generator().manual_seed(seed)
     plan = wl.uniform_plan(CTX, bs, gen, new_tokens=False)
     return wl.build_inputs(spec, plan)
@@ -182,7 +182,7 @@ MQ_SHAPES = [(8, 8, 128, 16), (16, 4, 64, 32), (64, 8, 128, 32)]
 
 def make_mq(h, hkv, d, bs, kv, seed):
     spec = wl.Spec(f"inv_mq{h}x{hkv}x{d}x{bs}{kv}", h, hkv, d, bs, "bf16", seed=seed,
-                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0)
+                   kv_dtype=None if kv == "bf16" else kv, k_scale=1.0, v_scale=1.0)
     g = h // hkv
     qlens = [1, 6, 17, 64 // g + 1, 100, 0, 3, 4]
     ctx = [1, 700, 17, 64 // g + 40, 333, 50, 3, 900]
@@ -238,7 +238,7 @@ SP_SHAPES = [(16, 8, 128, 32), (32, 8, 128, 16), (64, 8, 128, 32)]
 
 def make_shared(h, hkv, d, bs, kv, seed):
     spec = wl.Spec(f"inv_sp{h}x{hkv}x{d}x{bs}{kv}", h, hkv, d, bs, "bf16", seed=seed,
-                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0)
+                   kv_dtype=None if kv == "bf16" else kv, k_scale=1.0, v_scale=1.0)
     groups = [(4 * bs, [4 * bs, 4 * bs + 1, 5 * bs + 3, 9 * bs]),
               (20 * bs, [20 * bs + 1 + 7 * i for i in range(9)]),
               (0, [300]),

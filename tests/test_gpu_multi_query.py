@@ -45,7 +45,7 @@ def shape_case(h, hkv, d, bs, kv="bf16", seed=0):
     """Query lengths 1, 6, 17, 64/G+1 (two row blocks), 100 and 0, over
     contexts with and without history, ragged last pages."""
     spec = wl.Spec(f"mq{h}x{hkv}x{d}x{bs}{kv}", h, hkv, d, bs, "bf16", seed=13 * h + d + bs + seed,
-                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0 if kv == "bf16" else 1.0 / 64)
+                   kv_dtype=None if kv == "bf16" else kv, **wl.fp8_scales(kv))
     g = h // hkv
     qlens = [1, 6, 17, 64 // g + 1, 100, 0, 3, 6]
     ctx = [1, 700, 17, 64 // g + 40, 333, 50, 3, 6 + 2 * bs + 1]
@@ -94,7 +94,7 @@ def stream_case(h, hkv, d, bs, cap, kv="bf16", seed=0):
     contexts, one of them a single query, one empty."""
     g = h // hkv
     spec = wl.Spec(f"mqs{h}x{hkv}x{d}x{bs}{kv}{cap}", h, hkv, d, bs, "bf16", seed=11 * h + d + bs + cap + seed,
-                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0 if kv == "bf16" else 1.0 / 64)
+                   kv_dtype=None if kv == "bf16" else kv, **wl.fp8_scales(kv))
     qmax = max(1, cap // g)
     qlens = [qmax, 1, min(2, qmax), 0, qmax, max(1, qmax // 2)]
     ctx = [qmax + 700, 333, 6 + 2 * bs + 1, 50, qmax, 2 * bs + qmax + 3]
@@ -125,7 +125,7 @@ def test_stream_partition_of_256_pages(kv):
     on the ring."""
     bs = 16
     spec = wl.Spec(f"mqs256{kv}", 64, 8, 128, bs, "bf16", seed=77,
-                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0 if kv == "bf16" else 1.0 / 64)
+                   kv_dtype=None if kv == "bf16" else kv, **wl.fp8_scales(kv))
     plan = wl.multi_query_plan([256 * bs, 256 * bs + 5, 90], [4, 2, 6], bs,
                                torch.Generator().manual_seed(8))
     check_mq(wl.build_inputs(spec, plan), partition_tokens=256 * bs)
@@ -206,7 +206,7 @@ def test_long_context_page_window(h, hkv, d, bs, kv):
     spans more than 256 pages (the two-stage ring)."""
     g = h // hkv
     spec = wl.Spec(f"mqlong{h}x{hkv}x{d}x{bs}{kv}", h, hkv, d, bs, "bf16", seed=5 * h + d + bs,
-                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0 if kv == "bf16" else 1.0 / 64)
+                   kv_dtype=None if kv == "bf16" else kv, **wl.fp8_scales(kv))
     long_ctx = 256 * bs + 700
     plan = wl.multi_query_plan([long_ctx, 300], [64 // g + 1, 3], bs,
                                torch.Generator().manual_seed(spec.seed))
@@ -266,7 +266,7 @@ def test_fixed_partitions_batch_invariant(kv):
     20- and 12-row sequences stream (two tiles in the batch, the 12-row one
     one tile alone) beside the 120-row one on the ring."""
     spec = wl.Spec(f"mqinv{kv}", 32, 8, 128, 16, "bf16", seed=91,
-                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0 if kv == "bf16" else 1.0 / 64)
+                   kv_dtype=None if kv == "bf16" else kv, **wl.fp8_scales(kv))
     plan = wl.multi_query_plan([900, 2500, 40, 1300, 700], [6, 5, 1, 30, 3], 16,
                                torch.Generator().manual_seed(4))
     x = wl.build_inputs(spec, plan)
@@ -294,7 +294,7 @@ def test_work_list_and_in_kernel_lookup_agree(kv):
     oracle checks the large batch, and 40 of its sequences run as a batch of
     their own give the same bits (fixed partitions)."""
     spec = wl.Spec(f"mqlist{kv}", 64, 8, 128, 16, "bf16", seed=93,
-                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0 if kv == "bf16" else 1.0 / 64)
+                   kv_dtype=None if kv == "bf16" else kv, **wl.fp8_scales(kv))
     g = torch.Generator().manual_seed(8)
     n = 80
     ctx = torch.randint(8, 600, (n,), generator=g).tolist()
@@ -331,7 +331,7 @@ def test_pool_past_2g_elements(h, hkv, bs, kv):
     per_block = hkv * bs * d
     nb = (2_290_000_000 + per_block - 1) // per_block
     spec = wl.Spec(f"mqbig{h}x{hkv}x{bs}{kv}", h, hkv, d, bs, "bf16", seed=h + bs + 5,
-                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0 if kv == "bf16" else 1.0 / 64)
+                   kv_dtype=None if kv == "bf16" else kv, **wl.fp8_scales(kv))
     plan = wl.multi_query_plan([700, 2049, 5000, 3000], [1, 6, 4, 100], bs,
                                torch.Generator().manual_seed(spec.seed))
     plan = to_top_of_pool(plan, nb)

@@ -109,7 +109,7 @@ FP8_SHAPES = [
 @pytest.mark.parametrize("h,hkv,d,bs", FP8_SHAPES)
 def test_shapes_fp8(h, hkv, d, bs):
     spec = wl.Spec(f"fp8shape{h}x{hkv}x{d}x{bs}", h, hkv, d, bs, "bf16", seed=7 * h + d + bs,
-                   kv_dtype="fp8", kv_scale=1.0 / 64)
+                   kv_dtype="fp8", **wl.fp8_scales("fp8"))
     gen = torch.Generator().manual_seed(spec.seed)
     ctx = [0, 1, bs - 1, bs + 1, 3 * bs + 5, 700, 1100]
     plan = wl.uniform_plan(ctx, bs, gen, new_tokens=True)
@@ -118,10 +118,21 @@ def test_shapes_fp8(h, hkv, d, bs):
     check_case(x, partition_tokens=4 * bs)
 
 
+def _pow2_fp8(name, **kw):
+    """A workload of ``name`` whose fp8 caches use the scale 1/64 for K and V
+    (special values placed at a chosen code survive the scaling exactly)."""
+    base = wl.SPECS[name]
+    spec = wl.Spec(base.name + "_pow2", base.num_heads, base.num_kv_heads, base.head_dim,
+                   base.block_size, base.dtype, seed=base.seed, q_std=base.q_std,
+                   kv_dtype="fp8", k_scale=1.0 / 64, v_scale=1.0 / 64, recipe=base.recipe)
+    gen = torch.Generator().manual_seed(spec.seed)
+    return wl.build_inputs(spec, wl.make_plan(name, gen, **kw))
+
+
 def test_fp8_reshape_codes_exact():
     """E4M3 encoding of new rows: ties, subnormals, saturation, NaN, -0, random."""
     import oracle.paged_attention as op
-    x = wl.make_inputs("llama13b_fp8", num_seqs=6, context_len=40)
+    x = _pow2_fp8("llama13b_fp8", num_seqs=6, context_len=40)
     special = np.array([1.0625, 1.1875, 2.0 ** -10, 1.5 * 2.0 ** -9, 400.0, 432.0, 447.0, 448.0,
                         449.0, 464.0, 1e9, -1e9, 0.0, -0.0, 2.0 ** -12, -(2.0 ** -7),
                         0.015625 * 3.0, 1e-30], dtype=np.float32)
@@ -145,6 +156,65 @@ def test_fp8_reshape_codes_exact():
     assert_close(as_f64(out)[others], ref[others], "bf16", "fp8 rows")
 
 
+def _encode_rule_witnesses(scale):
+    """float32 values whose E4M3 code under x * fl32(1 / scale) differs from
+    the code of the correctly rounded quotient fl32(x / scale): a few next to
+    every midpoint between two E4M3 magnitudes where the two rules part."""
+    import oracle.paged_attention as op
+    s32 = np.float32(scale)
+    inv = op.e4m3_inverse_scale(scale)
+    mags = op.e4m3_values()[:0x7F]
+    found = []
+    for m in (mags[:-1] + mags[1:]) / 2:
+        x0 = np.float32(m * float(s32))
+        xs = (np.int32(x0.view(np.int32)) + np.arange(-200, 200, dtype=np.int32)).view(np.float32)
+        a = op.e4m3_encode(xs * inv)
+        b = op.e4m3_encode((xs / s32).astype(np.float32))
+        found.extend(xs[a != b][:2].tolist())
+    return np.array(found, dtype=np.float32)
+
+
+def test_fp8_encode_multiplies_by_rounded_inverse_scale():
+    """E4M3 codes of float32 rows at k_scale 0.02 and v_scale 0.03 (distinct,
+    not powers of two): bit-exact against the oracle's rule (binary32 product
+    with fl32(1 / scale)), with rows placed where a division by the scale, or
+    the other cache's scale, would give other codes."""
+    import oracle.paged_attention as op
+    spec = wl.Spec("fp8_encode_rule", 4, 2, 64, 16, "f32", seed=991, kv_dtype="fp8",
+                   **wl.fp8_scales("fp8"))
+    gen = torch.Generator().manual_seed(spec.seed)
+    plan = wl.uniform_plan([1, 17, 40, 33, 2, 64], 16, gen, new_tokens=True)
+    x = wl.build_inputs(spec, plan)
+    key, value = x.key.numpy().copy(), x.value.numpy().copy()
+    for arr, sc in ((key, x.k_scale), (value, x.v_scale)):
+        w = _encode_rule_witnesses(sc)
+        assert w.size >= 20, "too few witnesses of the encode rule"
+        w = np.concatenate([w, -w])
+        n = min(w.size, arr.size)
+        arr.reshape(-1)[:n] = w[:n]
+    x.key, x.value = torch.from_numpy(key), torch.from_numpy(value)
+    t = on_device(x)
+    binding.pa_reshape_and_cache(t["key"], t["value"], t["k_cache"], t["v_cache"],
+                                 t["slot_mapping"], k_scale=x.k_scale, v_scale=x.v_scale)
+    torch.cuda.synchronize()
+    kc, vc = bits(x.k_cache).copy(), bits(x.v_cache).copy()
+    op.reshape_and_cache(key, value, kc, vc, plan.slot_mapping, src_dtype="f32",
+                         k_scale=x.k_scale, v_scale=x.v_scale)
+    got_k, got_v = bits(t["k_cache"]), bits(t["v_cache"])
+    assert np.array_equal(got_k, kc) and np.array_equal(got_v, vc)
+    # The same rows under the division rule, and under swapped scales, differ.
+    for rule in ("divide", "swap"):
+        kd, vd = bits(x.k_cache).copy(), bits(x.v_cache).copy()
+        if rule == "divide":
+            kq = op.e4m3_encode((key / np.float32(x.k_scale)).astype(np.float32))
+            vq = op.e4m3_encode((value / np.float32(x.v_scale)).astype(np.float32))
+            op.reshape_and_cache(kq, vq, kd, vd, plan.slot_mapping)
+        else:
+            op.reshape_and_cache(key, value, kd, vd, plan.slot_mapping, src_dtype="f32",
+                                 k_scale=x.v_scale, v_scale=x.k_scale)
+        assert not np.array_equal(got_k, kd) and not np.array_equal(got_v, vd), rule
+
+
 @pytest.mark.parametrize("name", ["gqa70b_fp8", "llama7b_fp8"])
 def test_fp8_context_one_every_code_bitwise(name):
     """With one token the output is exactly code value * v_scale (a power of
@@ -152,7 +222,7 @@ def test_fp8_context_one_every_code_bitwise(name):
     import oracle.paged_attention as op
     kw = dict(num_seqs=2, context_len=1) if name == "gqa70b_fp8" else \
         dict(num_seqs=2, ctx_range=(1, 1))
-    x = wl.make_inputs(name, **kw)
+    x = _pow2_fp8(name, **kw)
     t = on_device(x)
     codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
     for s_ in range(x.plan.num_seqs):
@@ -407,7 +477,7 @@ def test_long_contexts_sampled(h, hkv, bs, kv):
     E4M3 cache; the oracle checks every head of each sequence."""
     torch.cuda.empty_cache()
     spec = wl.Spec(f"long{h}x{hkv}x{bs}{kv}", h, hkv, 128, bs, "bf16", seed=h + bs,
-                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0 if kv == "bf16" else 1.0 / 64)
+                   kv_dtype=None if kv == "bf16" else kv, **wl.fp8_scales(kv))
     ctx = [131072, 65537] if hkv < h else [100001]
     plan = wl.uniform_plan(ctx, bs, torch.Generator().manual_seed(spec.seed), new_tokens=True)
     x = wl.build_inputs(spec, plan, device="cuda", poison=True)
@@ -473,7 +543,7 @@ def test_pool_past_2g_elements(h, hkv, bs, kv):
     per_block = hkv * bs * d
     nb = (2_290_000_000 + per_block - 1) // per_block
     spec = wl.Spec(f"bigpool{h}x{hkv}x{bs}{kv}", h, hkv, d, bs, "bf16", seed=h + bs + 3,
-                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0 if kv == "bf16" else 1.0 / 64)
+                   kv_dtype=None if kv == "bf16" else kv, **wl.fp8_scales(kv))
     ctx = [1, 700, 2049, 5000]
     plan = wl.uniform_plan(ctx, bs, torch.Generator().manual_seed(spec.seed), new_tokens=True)
     plan = to_top_of_pool(plan, nb)

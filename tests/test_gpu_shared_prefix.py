@@ -44,7 +44,7 @@ def group_case(h, hkv, d, bs, kv="bf16", seed=0):
     with prefixes of 0 to 40 blocks, contexts equal to the prefix, one past
     it and ragged, plus unshared sequences."""
     spec = wl.Spec(f"grp{h}x{hkv}x{d}x{bs}{kv}", h, hkv, d, bs, "bf16", seed=11 * h + d + bs + seed,
-                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0 if kv == "bf16" else 1.0 / 64)
+                   kv_dtype=None if kv == "bf16" else kv, **wl.fp8_scales(kv))
     groups = [(4 * bs, [4 * bs, 4 * bs + 1, 5 * bs + 3, 9 * bs]),
               (0, [7]),
               (40 * bs, [40 * bs + 1 + 3 * i for i in range(17)]),
@@ -191,7 +191,7 @@ def test_long_prefix_sampled(h, hkv, bs, kv):
     unshared long sequence; every head of every sequence against the oracle."""
     torch.cuda.empty_cache()
     spec = wl.Spec(f"longpfx{h}x{hkv}x{bs}{kv}", h, hkv, 128, bs, "bf16", seed=3 * h + bs,
-                   kv_dtype=None if kv == "bf16" else kv, kv_scale=1.0 if kv == "bf16" else 1.0 / 64)
+                   kv_dtype=None if kv == "bf16" else kv, **wl.fp8_scales(kv))
     p = 48 * 1024
     groups = [(p, [p + 1, p + 77, p + 3 * bs, p + 500]), (0, [20000])]
     plan = wl.prefix_plan(groups, bs, torch.Generator().manual_seed(spec.seed))
