@@ -99,7 +99,9 @@ typedef enum pa_status {
                            /* an index buffer is not aligned to its element size*/
   PA_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required        */
   PA_ERR_LAUNCH = -7,      /* the HIP runtime reported an error after launch    */
-  PA_ERR_VALUE = -8        /* a scale of an fp8 cache is not finite and > 0     */
+  PA_ERR_VALUE = -8,       /* a scale of an fp8 cache is not finite and > 0     */
+  PA_ERR_SCRATCH = -9      /* pa_decode_noalloc: the call needs more workspace  */
+                           /* than the static scratch buffer holds              */
 } pa_status;
 
 /*
@@ -258,6 +260,39 @@ int pa_decode(void* out, const void* q,
               float scale, int dtype, int cache_dtype, float k_scale, float v_scale,
               int partition_tokens, int flags,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the static scratch buffer pa_decode_noalloc uses (32 MiB per GPU). */
+#define PA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate memory:
+ * code being captured into a HIP graph, tight serving loops, harnesses that
+ * forbid hipMalloc.  It takes pa_decode's arguments without the workspace and
+ * computes the same result with the same kernels (the same bits as pa_decode
+ * with the same partition_tokens); the partial results of cut contexts go to
+ * a static device buffer of PA_DECODE_NOALLOC_SCRATCH_BYTES bytes that the
+ * library holds on every GPU it runs on until the process ends.  The call
+ * allocates nothing: no hipMalloc, no hipFree, no allocating library routine.
+ *
+ * The buffer's device address is looked up on a GPU's first call that needs
+ * it, with that GPU current (the GPU holding the call's buffers must be the
+ * current device, as for every entry point).
+ * Errors: the statuses of pa_decode, and PA_ERR_SCRATCH (nothing launched)
+ * when pa_decode_workspace_size(...) for these arguments exceeds
+ * PA_DECODE_NOALLOC_SCRATCH_BYTES -- e.g. 32 sequences x 64 heads x 32K-token
+ * contexts at the default partitioning fit, 128 of them do not.
+ * All calls on one GPU share its buffer and nothing in it has to start at
+ * zero: calls that overlap on one GPU (on different streams, or from several
+ * threads) race on it and give unspecified results; serialise them.
+ */
+int pa_decode_noalloc(void* out, const void* q,
+                      const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, int max_blocks_per_seq,
+                      const int32_t* context_lens, const int32_t* seq_order,
+                      int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, int max_context_len,
+                      float scale, int dtype, int cache_dtype, float k_scale, float v_scale,
+                      int partition_tokens, int flags, void* stream);
 
 /*
  * pa_decode_shared_prefix_workspace_size -- bytes of device workspace

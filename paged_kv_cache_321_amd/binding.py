@@ -28,10 +28,12 @@ PA_PARTITION_FIXED = 0
 PA_PARTITION_FILL = 1
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
           -4: "PA_ERR_UNSUPPORTED", -5: "PA_ERR_ALIGN", -6: "PA_ERR_WORKSPACE",
-          -7: "PA_ERR_LAUNCH", -8: "PA_ERR_VALUE"}
+          -7: "PA_ERR_LAUNCH", -8: "PA_ERR_VALUE", -9: "PA_ERR_SCRATCH"}
+PA_DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20
 EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_partition_tokens",
            "pa_decode_workspace_size",
-           "pa_decode", "pa_decode_shared_prefix_workspace_size", "pa_decode_shared_prefix",
+           "pa_decode", "pa_decode_noalloc", "pa_decode_shared_prefix_workspace_size",
+           "pa_decode_shared_prefix",
            "pa_multi_query_workspace_size", "pa_multi_query", "pa_swap_blocks",
            "pa_status_string")
 
@@ -62,6 +64,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                               [_c_float, _c_int, _c_int, _c_float, _c_float, _c_int, _c_int, _vp,
                                _c_size, _vp])
     lib.pa_decode.restype = _c_int
+    lib.pa_decode_noalloc.argtypes = ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp] + [_c_int] * 7 +
+                                      [_c_float, _c_int, _c_int, _c_float, _c_float, _c_int, _c_int,
+                                       _vp])
+    lib.pa_decode_noalloc.restype = _c_int
     lib.pa_decode_shared_prefix_workspace_size.argtypes = [_c_int] * 11
     lib.pa_decode_shared_prefix_workspace_size.restype = _c_size
     lib.pa_decode_shared_prefix.argtypes = ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp] +
@@ -241,6 +247,38 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
                        PA_DECODE_SHARED_PAGES if shared_pages else 0,
                        _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "pa_decode")
+
+
+def pa_decode_noalloc(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                      scale: float, max_context_len: int, partition_tokens: int = 0, stream=None,
+                      shared_pages: bool = False, seq_order: Optional[torch.Tensor] = None,
+                      k_scale: float = 1.0, v_scale: float = 1.0) -> None:
+    """pa_decode without a workspace: the library's static scratch buffer
+    holds the partition results, and nothing is allocated here or in the
+    library.  Arguments as for ``pa_decode``."""
+    for n, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                 ("block_tables", block_tables), ("context_lens", context_lens)):
+        _device_contig(n, t)
+    _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
+          "block_tables and context_lens must be int32")
+    _need(q.dtype == out.dtype and k_cache.dtype == v_cache.dtype, "element types differ")
+    s, h, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    _need(d2 == d and out.shape == q.shape and v_cache.shape == k_cache.shape, "shape mismatch")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == s, "block_tables must be [S, MB]")
+    _need(context_lens.shape == (s,), "context_lens must be [S]")
+    if seq_order is not None:
+        _device_contig("seq_order", seq_order)
+        _need(seq_order.dtype == torch.int32 and seq_order.shape == (s,),
+              "seq_order must be int32 [S]")
+    st = LIB.pa_decode_noalloc(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                               block_tables.shape[1], _ptr(context_lens), _ptr(seq_order), s, h, hkv,
+                               d, bs, nb, int(max_context_len), float(scale), _dtype_code(q),
+                               _dtype_code(k_cache), float(k_scale), float(v_scale),
+                               int(partition_tokens), PA_DECODE_SHARED_PAGES if shared_pages else 0,
+                               _stream(stream))
+    _check(st, "pa_decode_noalloc")
 
 
 def pa_decode_shared_prefix_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int,

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libpa.so")
 ARCH = "gfx950"
 
 SOURCES = ["pa_api.cpp", "pa_cache.hip", "pa_decode.hip", "pa_decode_valu.hip", "pa_multi_query.hip",
-           "pa_decode_mfma.hip"]
+           "pa_decode_mfma.hip", "pa_noalloc.hip"]
 
 # Packed-fp32 VALU ops are switched off for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -138,6 +138,9 @@ const char* pa_status_string(int status) {
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: HIP reported an error after the launch";
     case PA_ERR_VALUE: return "PA_ERR_VALUE: an fp8 cache scale must be finite and > 0";
+    case PA_ERR_SCRATCH:
+      return "PA_ERR_SCRATCH: the call needs more workspace than the library's static scratch "
+             "buffer holds (PA_DECODE_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown pa status";
   }
 }
@@ -278,7 +281,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                 int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
                 int max_context_len, float scale, int dtype, int cache_dtype, float k_scale,
                 float v_scale, int partition_tokens, int flags, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                size_t workspace_bytes, void* stream, bool check_only = false) {
   const DecodeSizes z = decode_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                                      max_context_len, dtype, cache_dtype, partition_tokens, shared_prefix,
                                      max_prefix_blocks, max_tail_len);
@@ -297,6 +300,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     return PA_ERR_ALIGN;
   if (num_seqs > kMaxGridYZ || num_kv_heads > kMaxGridYZ || num_heads > kMaxGridYZ)
     return PA_ERR_UNSUPPORTED;
+  if (check_only) return PA_OK;  // every check but the workspace's passed
   if (z.total > 0) {
     if (!workspace || workspace_bytes < z.total) return PA_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
@@ -559,6 +563,25 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
                      block_size, num_blocks, max_context_len, scale, dtype, cache_dtype, k_scale,
                      v_scale, partition_tokens, flags, workspace, workspace_bytes, stream);
 }
+
+}  // extern "C"
+
+namespace pa {
+
+int decode_check(const void* out, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                 const int32_t* seq_order, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                 int block_size, int num_blocks, int max_context_len, int dtype, int cache_dtype,
+                 float k_scale, float v_scale, int partition_tokens, int flags) {
+  return decode_impl(const_cast<void*>(out), q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                     context_lens, seq_order, nullptr, nullptr, false, 0, 0, num_seqs, num_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, max_context_len, 1.f, dtype,
+                     cache_dtype, k_scale, v_scale, partition_tokens, flags, nullptr, 0, nullptr, true);
+}
+
+}  // namespace pa
+
+extern "C" {
 
 int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* block_tables, int max_blocks_per_seq,

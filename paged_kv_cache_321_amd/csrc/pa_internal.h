@@ -117,6 +117,13 @@ int fill_partition_tokens(int dtype, int cache_dtype, int head_dim, int block_si
                           int num_seqs, int num_kv_heads, int max_context_len);
 
 hipError_t launch_decode(const DecodeLaunch& a);
+// Every host check pa_decode makes on these arguments except the workspace's;
+// launches nothing and makes no HIP call.
+int decode_check(const void* out, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                 const int32_t* seq_order, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                 int block_size, int num_blocks, int max_context_len, int dtype, int cache_dtype,
+                 float k_scale, float v_scale, int partition_tokens, int flags);
 int default_multi_query_partition_tokens(int block_size, int num_seqs, int num_kv_heads, int max_context_len);
 int multi_query_rows_per_block();
 hipError_t launch_multi_query(const MultiQueryLaunch& a);

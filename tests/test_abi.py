@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pa.h")
 LIB = binding.LIB
 
-OK, NULL, SHAPE, DTYPE, UNSUP, ALIGN, WS, VALUE = 0, -1, -2, -3, -4, -5, -6, -8
+OK, NULL, SHAPE, DTYPE, UNSUP, ALIGN, WS, VALUE, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -8, -9
 F32, BF16, FP8 = 0, 1, 2
 
 # Host buffer standing in for device pointers: validation never dereferences.
@@ -488,3 +488,43 @@ def test_binding_raises_runtime_error_with_status():
 def test_longest_first_order():
     o = binding.longest_first([5, 9, 1, 9, 0], device="cpu").tolist()
     assert o == [1, 3, 0, 2, 4]
+
+
+def decode_noalloc(**kw):
+    a = dict(out=P, q=P, k=P, v=P, bt=P, mb=8, ctx=P, order=None, S=2, H=8, Hkv=2, D=128, BS=16,
+             NB=32, maxctx=100, scale=0.1, dtype=BF16, cdtype=None, ks=0.5, vs=0.5, pt=0, flags=0)
+    a.update(kw)
+    cdtype = a["dtype"] if a["cdtype"] is None else a["cdtype"]
+    return LIB.pa_decode_noalloc(a["out"], a["q"], a["k"], a["v"], a["bt"], a["mb"], a["ctx"],
+                                 a["order"], a["S"], a["H"], a["Hkv"], a["D"], a["BS"], a["NB"],
+                                 a["maxctx"], a["scale"], a["dtype"], cdtype, a["ks"], a["vs"], a["pt"],
+                                 a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), DTYPE),
+    (dict(H=6, Hkv=4), SHAPE),
+    (dict(D=96), UNSUP),
+    (dict(q=None), NULL),
+    (dict(out=MIS), ALIGN),
+    (dict(cdtype=FP8, ks=0.0), VALUE),
+    (dict(flags=2), UNSUP),
+    (dict(mb=6), SHAPE),
+    (dict(S=0), OK),
+    # 128 sequences x 64 heads x 8 partitions of 4096 tokens: 32.5 MiB of
+    # partition results, more than the 32 MiB buffer (rejected before any
+    # HIP call); with 64 sequences it would fit.
+    (dict(S=128, H=64, Hkv=8, maxctx=32768, mb=2048), SCRATCH),
+    (dict(S=1, H=8, Hkv=8, D=128, maxctx=1 << 20, mb=1 << 16, pt=16), SCRATCH),
+])
+def test_decode_noalloc_validation(kw, code):
+    assert decode_noalloc(**kw) == code
+
+
+def test_decode_noalloc_scratch_limit_matches_the_workspace_size():
+    ws = LIB.pa_decode_workspace_size
+    limit = binding.PA_DECODE_NOALLOC_SCRATCH_BYTES
+    assert ws(64, 64, 8, 128, 32, 32768, BF16, BF16, 0) <= limit < ws(128, 64, 8, 128, 32, 32768, BF16,
+                                                                        BF16, 0)
+    header = open(HEADER).read()
+    assert re.search(r"PA_DECODE_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)32 << 20\)", header)
