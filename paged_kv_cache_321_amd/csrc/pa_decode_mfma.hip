@@ -298,15 +298,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
 #pragma unroll
       for (int m = 0; m < NM; ++m) acc[m] *= alpha;
     }
-    float ps = 0.f;
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sv[tt][j] = fast_exp2(sv[tt][j] - m_run);
-        ps += sv[tt][j];
-      }
-    l_run += ps;
+      for (int j = 0; j < 4; ++j) sv[tt][j] = fast_exp2(sv[tt][j] - m_run);
+    // The weights are rounded to bf16 for the PV product; the running sum
+    // adds the same rounded weights, so numerator and denominator agree (a
+    // constant V row comes back exactly).
 
     if constexpr (BS == 32) {
       // P^T as the B operand: k slot j of lane group g4 is token 4 g4 + j
@@ -316,6 +314,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       pbits.y = pack_bf16x2(sv[0][2], sv[0][3]);
       pbits.z = pack_bf16x2(sv[1][0], sv[1][1]);
       pbits.w = pack_bf16x2(sv[1][2], sv[1][3]);
+      l_run += (bf16x2_sum(pbits.x) + bf16x2_sum(pbits.y)) + (bf16x2_sum(pbits.z) + bf16x2_sum(pbits.w));
       const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pbits);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
@@ -330,6 +329,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       uint2 pbits;
       pbits.x = pack_bf16x2(sv[0][0], sv[0][1]);
       pbits.y = pack_bf16x2(sv[0][2], sv[0][3]);
+      l_run += bf16x2_sum(pbits.x) + bf16x2_sum(pbits.y);
       const s16x4_t pb = __builtin_bit_cast(s16x4_t, pbits);
 #pragma unroll
       for (int m = 0; m < NM; ++m)

@@ -35,6 +35,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Sum of the two bf16 values packed in w (low half + high half), in float32:
+// the softmax weights as the PV product sees them, so that the running sum
+// (the denominator) adds exactly the weights the numerator was formed with.
+__device__ __forceinline__ float bf16x2_sum(uint32_t w) {
+  return __uint_as_float(w << 16) + __uint_as_float(w & 0xffff0000u);
+}
+
 // Eight E4M3 codes -> eight bf16, exact (an E4M3 value has 3 mantissa bits),
 // with v_cvt_scalef32_pk_bf16_fp8 at scale 1 (checked on gfx950: exact for all
 // 256 codes in both halves).

@@ -490,7 +490,6 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
 #pragma unroll
       for (int m = 0; m < NM; ++m) acc[m] *= alpha;
     }
-    float ps = 0.f;
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
@@ -499,11 +498,10 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
           sv[tt][j] = fast_exp2(fmaf(sc[tt][j], p.scale_log2e, -m_run));
         else
           sv[tt][j] = fast_exp2(sv[tt][j] - m_run);
-        ps += sv[tt][j];
       }
-    l_run += ps;
     // P^T as the B operand, two 16-token tiles per product: k slot j of lane
     // group g4 is token 32 h + 4 g4 + j (j < 4) or 32 h + 16 + 4 g4 + j - 4.
+    // The running sum adds the weights as rounded to bf16 for the product.
 #pragma unroll
     for (int h = 0; h < NTT / 2; ++h) {
       uint4 pbits;
@@ -511,6 +509,7 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
       pbits.y = pack_bf16x2(sv[2 * h][2], sv[2 * h][3]);
       pbits.z = pack_bf16x2(sv[2 * h + 1][0], sv[2 * h + 1][1]);
       pbits.w = pack_bf16x2(sv[2 * h + 1][2], sv[2 * h + 1][3]);
+      l_run += (bf16x2_sum(pbits.x) + bf16x2_sum(pbits.y)) + (bf16x2_sum(pbits.z) + bf16x2_sum(pbits.w));
       const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pbits);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
@@ -799,20 +798,19 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
         for (int m = 0; m < NM; ++m) acc[ct][m] *= alpha;
       }
-      float ps = 0.f;
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sv[tt][j] = fast_exp2(sv[tt][j] - m_run[ct]);
-          ps += sv[tt][j];
-        }
-      l_run[ct] += ps;
+        for (int j = 0; j < 4; ++j) sv[tt][j] = fast_exp2(sv[tt][j] - m_run[ct]);
+      // The running sum adds the weights as rounded to bf16 for the product.
+      float ps = 0.f;
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
         pw[ct][2 * tt] = pack_bf16x2(sv[tt][0], sv[tt][1]);
         pw[ct][2 * tt + 1] = pack_bf16x2(sv[tt][2], sv[tt][3]);
+        ps += bf16x2_sum(pw[ct][2 * tt]) + bf16x2_sum(pw[ct][2 * tt + 1]);
       }
+      l_run[ct] += ps;
     }
     // O^T += V^T P^T; each V^T read feeds every tile.
 #pragma unroll
