@@ -491,6 +491,7 @@ int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_
   a.work_count = reinterpret_cast<int*>(ws + z.decode_bytes + z.parts_bytes + z.work_capacity * 8);
   a.work_capacity = (int)z.work_capacity;
   a.decode_rows_elsewhere = !tiles_only;
+  a.beside_decode = false;
   a.stream = static_cast<hipStream_t>(stream);
   if (tiles_only) return pa::launch_multi_query(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
   // Sequences with a single new query are decode steps: the decode kernels
@@ -545,6 +546,7 @@ int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_
   if (hipEventRecord(side->fork, a.stream) != hipSuccess) return PA_ERR_LAUNCH;
   if (hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess) return PA_ERR_LAUNCH;
   d.stream = side->stream;
+  a.beside_decode = true;
   const bool mq_ok = pa::launch_multi_query(a) == hipSuccess;
   const bool dec_ok = pa::launch_decode(d) == hipSuccess;
   const bool join_ok = hipEventRecord(side->join, side->stream) == hipSuccess &&

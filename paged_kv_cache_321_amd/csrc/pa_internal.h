@@ -106,6 +106,7 @@ struct MultiQueryLaunch {
   int* work_count;       // (workspace)
   int work_capacity;     // bound on the work items: the grid size per kv head
   bool decode_rows_elsewhere;  // single-query sequences go to the decode kernels
+  bool beside_decode;          // the decode kernels run concurrently on another stream
   hipStream_t stream;
 };
 

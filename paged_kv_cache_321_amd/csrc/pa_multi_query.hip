@@ -90,7 +90,8 @@ struct MqBlock {
   int qlen;     // new query tokens
   int ctx;      // cached tokens, the new ones included
   int rows;     // qlen * G
-  int rb;       // row block: rows rb * 64 .. rb * 64 + 63
+  int rpb;      // rows per block: 64, or 128 for a sequence of more than 128 rows
+  int rb;       // row block: rows rb * rpb .. rb * rpb + rpb - 1
   int kv_end;   // tokens seen by the block's last query
   int nparts;   // context partitions
   int nrb;      // row blocks of the sequence
@@ -118,7 +119,12 @@ __device__ __forceinline__ MqBlock mq_block(const MultiQueryParams& p, int s, in
     return b;
   }
   b.rows = b.qlen * G;
-  const int nrb = (b.rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  // Long chunks take 128-row blocks (two 16-row tiles per wave: each K and
+  // V operand read from LDS feeds two products); sequences of at most 128
+  // rows keep 64-row blocks, so every sequence of one block has at most 64
+  // rows and only those are cut into partitions.
+  b.rpb = b.rows > 2 * kRowsPerBlock ? 2 * kRowsPerBlock : kRowsPerBlock;
+  const int nrb = (b.rows + b.rpb - 1) / b.rpb;
   b.nrb = nrb;
   if (rbi >= nrb) {
     b.skip = true;
@@ -129,7 +135,7 @@ __device__ __forceinline__ MqBlock mq_block(const MultiQueryParams& p, int s, in
   b.bad = b.ctx < 0 || b.ctx > p.max_context_len || b.qlen > b.ctx;
   b.nparts = 1;
   if (b.bad) return b;
-  const int last_row = min(b.rows, (b.rb + 1) * kRowsPerBlock) - 1;
+  const int last_row = min(b.rows, (b.rb + 1) * b.rpb) - 1;
   b.kv_end = b.ctx - b.qlen + last_row / G + 1;
   if (nrb == 1 && b.kv_end > p.partition_tokens)
     b.nparts = (b.kv_end + p.partition_tokens - 1) / p.partition_tokens;
@@ -200,8 +206,20 @@ __device__ __forceinline__ float column_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <typename TC, int D, int BS, int G, int STAGES>
-__global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void multi_query_kernel(MultiQueryParams p) {
+// Bytes of the ring kernel's LDS: STAGES (K, V) stages of one step as stored
+// in the cache, plus for E4M3 the widened bf16 tile(s) (V only at D = 128,
+// where the QK product widens K in registers).
+template <typename TC, int D, int STAGES>
+constexpr int ring_lds_bytes() {
+  constexpr int raw_tile = kStepTokens * D * (int)sizeof(TC);
+  constexpr int bf16_tile = kStepTokens * D * 2;
+  return STAGES * 2 * raw_tile + (sizeof(TC) == 1 ? (D == 128 ? 1 : 2) * bf16_tile : 0);
+}
+
+// NCT: 16-row tiles per wave (1: 64-row blocks, 2: 128-row blocks); the
+// kernel serves only the sequences whose blocks have its row count.
+template <typename TC, int D, int BS, int G, int STAGES, int NCT>
+__global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(NCT == 1 ? 4 : sizeof(TC) == 1 ? 2 : 3))) void multi_query_kernel(MultiQueryParams p) {
   constexpr bool kFp8 = sizeof(TC) == 1;
   constexpr int PPS = kStepTokens / BS;      // pages per step
   constexpr int NC = D / 32;                 // 32-wide steps of the QK contraction
@@ -223,8 +241,10 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   // E4M3 at D = 128: the QK product reads K codes straight from the stage
   // (8 codes per lane, widened in registers), so only V is widened in LDS.
   constexpr bool kKRaw = kFp8 && D == 128;
-  constexpr int LDS_BYTES = NSTAGE * 2 * RTILEB + (kFp8 ? (kKRaw ? 1 : 2) * TILEB : 0);
+  constexpr int LDS_BYTES = ring_lds_bytes<TC, D, NSTAGE>();
+  static_assert(LDS_BYTES == NSTAGE * 2 * RTILEB + (kFp8 ? (kKRaw ? 1 : 2) * TILEB : 0), "ring layout");
   constexpr int WINDOW = 256;                // page ids held in registers (4 per lane)
+  constexpr int RPB = kRowsPerBlock * NCT;   // rows per block
   static_assert(kStepTokens % BS == 0 && kStepTokens % 32 == 0 && NCH >= 8, "tile shape");
   static_assert(kFp8 || CHUNKS % (kMqWaves * 64) == 0, "a bf16 step is whole wave loads");
   static_assert(CHUNKS * 16 == RTILEB, "a step is CHUNKS 16-byte chunks");
@@ -245,7 +265,7 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   const int rbi = row_block_of(w.y);
   const int part = w.y & 0xffff;
   const MqBlock b = mq_block<G>(p, s, rbi);
-  if (b.skip || part >= b.nparts) return;
+  if (b.skip || part >= b.nparts || b.rpb != RPB) return;
   if (b.nrb == 1 && b.rows <= p.stream_rows) return;  // the streaming kernel's
 
   const int tid = threadIdx.x;
@@ -254,16 +274,23 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
 
-  // This lane's row: column l16 of the wave's tile.  A wave whose 16 rows
-  // all lie past the block's rows (a short chunk, a decoding sequence) only
-  // helps stage the tiles.
-  const bool wave_rows = b.rb * kRowsPerBlock + wave * 16 < b.rows;
-  const int r = b.rb * kRowsPerBlock + wave * 16 + l16;
-  const bool row_ok = r < b.rows;
-  const int qi = row_ok ? r / G : 0;
-  const int head = kvh * G + (row_ok ? r % G : 0);
-  const int64_t qrow = b.t0 + qi;
-  const int last_seen = b.ctx - b.qlen + qi;  // the row sees tokens 0 .. last_seen
+  // This lane's rows: column l16 of each of the wave's NCT tiles.  A wave
+  // whose rows all lie past the block's rows (a short chunk, a decoding
+  // sequence) only helps stage the tiles.
+  const int wrow0 = b.rb * RPB + wave * 16 * NCT;
+  const bool wave_rows = wrow0 < b.rows;
+  bool row_ok[NCT];
+  int head[NCT], last_seen[NCT];
+  int64_t qrow[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int r = wrow0 + 16 * ct + l16;
+    row_ok[ct] = r < b.rows;
+    const int qi = row_ok[ct] ? r / G : 0;
+    head[ct] = kvh * G + (row_ok[ct] ? r % G : 0);
+    qrow[ct] = b.t0 + qi;
+    last_seen[ct] = b.ctx - b.qlen + qi;  // the row sees tokens 0 .. last_seen
+  }
 
   const int pt = p.partition_tokens;
   const int tok0 = b.nparts > 1 ? part * pt : 0;
@@ -272,27 +299,36 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   const int npg = tok1 > tok0 ? (tok1 - tok0 + BS - 1) / BS : 0;
   const int nsteps = (npg + PPS - 1) / PPS;
 
-  // B operand of S^T: Q[row l16][32c + 8 g4 .. +7]; zero for rows past the block.
-  bf16x8_t qb[NC];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + (qrow * p.num_heads + head) * D;
+  // B operand of S^T: Q[row l16 of tile ct][32c + 8 g4 .. +7]; zero for rows
+  // past the block.
+  bf16x8_t qb[NCT][NC];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + (qrow[ct] * p.num_heads + head[ct]) * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (row_ok) v = *reinterpret_cast<const uint4*>(qp + 32 * c + 8 * g4);
+      if (row_ok[ct]) v = *reinterpret_cast<const uint4*>(qp + 32 * c + 8 * g4);
       // Consumed here, so that the compiler waits for the load before the
       // step loop rather than at its first use inside it, where its wait
       // would also drain the page loads in flight.
       asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
-      qb[c] = __builtin_bit_cast(bf16x8_t, v);
+      qb[ct][c] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
 
-  f32x4_t acc[NM];  // O^T[d = 16 m + 4 g4 + j][row l16]
+  f32x4_t acc[NCT][NM];  // O^T[d = 16 m + 4 g4 + j][row l16 of tile ct]
 #pragma unroll
-  for (int m = 0; m < NM; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -FLT_MAX;  // running max of the row (same in its 4 lanes)
-  float l_run = 0.f;       // this lane's share of the running sum
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int m = 0; m < NM; ++m) acc[ct][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run[NCT];  // running max of the row (same in its 4 lanes)
+  float l_run[NCT];  // this lane's share of the running sum
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    m_run[ct] = -FLT_MAX;
+    l_run[ct] = 0.f;
+  }
 
   // Stage i: K tile at ring + 2 i RTILEB, V tile right after it.  In the
   // tiles the matrix cores read (the stages for bf16, the widened tile for
@@ -432,7 +468,7 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   // block sees all of its tokens.  Such steps also take the row max of the
   // raw scores and fold the scale into the exponent, which needs a positive
   // scale.
-  const int block_first_qi = b.rb * kRowsPerBlock / G;
+  const int block_first_qi = b.rb * RPB / G;
   const int block_full_end = min(tok1, b.ctx - b.qlen + block_first_qi + 1);
 
   // kt: the step's K (bf16 tile, or for kKRaw the stage's raw codes); vt:
@@ -440,11 +476,13 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   auto compute_step = [&](int st, const unsigned char* kt, const unsigned char* vt, auto full_tag) {
     constexpr bool kFull = decltype(full_tag)::value;
     const int t_base = tok0 + st * kStepTokens;
-    // S^T for the step's 16-token tiles.
-    f32x4_t sc[NTT];
+    // S^T for the step's 16-token tiles; each K operand read feeds the NCT
+    // row tiles.
+    f32x4_t sc[NCT][NTT];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
-      sc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) sc[ct][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       const int tok = 16 * tt + l16;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -457,66 +495,81 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
         } else {
           ka = *reinterpret_cast<const uint4*>(kt + tok * ROWB + (((4 * c + g4) ^ kswz<ROWB>(tok)) << 4));
         }
-        sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qb[c], sc[tt], 0, 0, 0);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+          sc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qb[ct][c],
+                                                               sc[ct][tt], 0, 0, 0);
       }
     }
-    // Causal mask and online softmax: lane holds tokens 16 tt + 4 g4 + j.
-    float sv[NTT][4];
-    float mx;
-    if constexpr (kFull) {
-      float raw = sc[0][0];
+    // Causal mask and online softmax per tile: lane holds tokens 16 tt + 4 g4 + j.
+    // P^T of tile ct as the B operand, two 16-token tiles per product: k slot
+    // j of lane group g4 is token 32 h + 4 g4 + j (j < 4) or 32 h + 16 + 4 g4
+    // + j - 4.
+    uint4 pbits[NCT][NTT / 2];
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt)
+    for (int ct = 0; ct < NCT; ++ct) {
+      float sv[NTT][4];
+      float mx;
+      if constexpr (kFull) {
+        float raw = sc[ct][0][0];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) raw = fmaxf(raw, sc[tt][j]);
-      mx = fmaxf(m_run, column_max(raw) * p.scale_log2e);
-    } else {
-      mx = m_run;
+        for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) raw = fmaxf(raw, sc[ct][tt][j]);
+        mx = fmaxf(m_run[ct], column_max(raw) * p.scale_log2e);
+      } else {
+        mx = m_run[ct];
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int t = t_base + 16 * tt + 4 * g4 + j;
+            const bool valid = t < tok1 && t <= last_seen[ct];
+            sv[tt][j] = valid ? sc[ct][tt][j] * p.scale_log2e : -__builtin_inff();
+            mx = fmaxf(mx, sv[tt][j]);
+          }
+        mx = column_max(mx);
+      }
+      if (__any(mx > m_run[ct] + kRescaleLog2)) {
+        const float alpha = fast_exp2(m_run[ct] - mx);
+        m_run[ct] = mx;
+        l_run[ct] *= alpha;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) acc[ct][m] *= alpha;
+      }
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int t = t_base + 16 * tt + 4 * g4 + j;
-          const bool valid = t < tok1 && t <= last_seen;
-          sv[tt][j] = valid ? sc[tt][j] * p.scale_log2e : -__builtin_inff();
-          mx = fmaxf(mx, sv[tt][j]);
+          if constexpr (kFull)
+            sv[tt][j] = fast_exp2(fmaf(sc[ct][tt][j], p.scale_log2e, -m_run[ct]));
+          else
+            sv[tt][j] = fast_exp2(sv[tt][j] - m_run[ct]);
         }
-      mx = column_max(mx);
-    }
-    if (__any(mx > m_run + kRescaleLog2)) {
-      const float alpha = fast_exp2(m_run - mx);
-      m_run = mx;
-      l_run *= alpha;
+      // The running sum adds the weights as rounded to bf16 for the product.
 #pragma unroll
-      for (int m = 0; m < NM; ++m) acc[m] *= alpha;
-    }
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if constexpr (kFull)
-          sv[tt][j] = fast_exp2(fmaf(sc[tt][j], p.scale_log2e, -m_run));
-        else
-          sv[tt][j] = fast_exp2(sv[tt][j] - m_run);
+      for (int h = 0; h < NTT / 2; ++h) {
+        uint4& pb = pbits[ct][h];
+        pb.x = pack_bf16x2(sv[2 * h][0], sv[2 * h][1]);
+        pb.y = pack_bf16x2(sv[2 * h][2], sv[2 * h][3]);
+        pb.z = pack_bf16x2(sv[2 * h + 1][0], sv[2 * h + 1][1]);
+        pb.w = pack_bf16x2(sv[2 * h + 1][2], sv[2 * h + 1][3]);
+        l_run[ct] += (bf16x2_sum(pb.x) + bf16x2_sum(pb.y)) + (bf16x2_sum(pb.z) + bf16x2_sum(pb.w));
       }
-    // P^T as the B operand, two 16-token tiles per product: k slot j of lane
-    // group g4 is token 32 h + 4 g4 + j (j < 4) or 32 h + 16 + 4 g4 + j - 4.
-    // The running sum adds the weights as rounded to bf16 for the product.
+    }
+    // O^T += V^T P^T; each V^T operand read feeds the NCT row tiles.
 #pragma unroll
     for (int h = 0; h < NTT / 2; ++h) {
-      uint4 pbits;
-      pbits.x = pack_bf16x2(sv[2 * h][0], sv[2 * h][1]);
-      pbits.y = pack_bf16x2(sv[2 * h][2], sv[2 * h][3]);
-      pbits.z = pack_bf16x2(sv[2 * h + 1][0], sv[2 * h + 1][1]);
-      pbits.w = pack_bf16x2(sv[2 * h + 1][2], sv[2 * h + 1][3]);
-      l_run += (bf16x2_sum(pbits.x) + bf16x2_sum(pbits.y)) + (bf16x2_sum(pbits.z) + bf16x2_sum(pbits.w));
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pbits);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         const s16x4_t lo = vt4<ROWB>(vt, l16, 32 * h + 4 * g4, 16 * m);
         const s16x4_t hi = vt4<ROWB>(vt, l16, 32 * h + 16 + 4 * g4, 16 * m);
         const s16x8_t va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pb, acc[m], 0, 0, 0);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+          acc[ct][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va),
+                                                               __builtin_bit_cast(bf16x8_t, pbits[ct][h]),
+                                                               acc[ct][m], 0, 0, 0);
       }
     }
   };
@@ -564,33 +617,38 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   }
   const bool bad = b.bad || ids_bad;
 
-  // The four lanes of a row each hold a share of its running sum.
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  if (!row_ok) return;
-  const int64_t orow = qrow * p.num_heads + head;
-  if (b.nparts == 1) {
-    uint16_t* o = static_cast<uint16_t*>(p.out) + orow * D;
-    const float inv = l_run == 0.f ? 0.f : p.v_scale / l_run;
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      float v[4];
+  for (int ct = 0; ct < NCT; ++ct) {
+    // The four lanes of a row each hold a share of its running sum.
+    float l = l_run[ct];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (!row_ok[ct]) continue;
+    const int64_t orow = qrow[ct] * p.num_heads + head[ct];
+    if (b.nparts == 1) {
+      uint16_t* o = static_cast<uint16_t*>(p.out) + orow * D;
+      const float inv = l == 0.f ? 0.f : p.v_scale / l;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = bad ? __builtin_nanf("") : acc[m][j] * inv;
-      uint2 w;
-      w.x = f32_to_bf16_bits(v[0]) | (uint32_t)f32_to_bf16_bits(v[1]) << 16;
-      w.y = f32_to_bf16_bits(v[2]) | (uint32_t)f32_to_bf16_bits(v[3]) << 16;
-      *reinterpret_cast<uint2*>(o + 16 * m + 4 * g4) = w;
-    }
-  } else {
-    const int64_t slot = orow * p.max_parts + part;
-    float* a = p.ws_acc + slot * D;
+      for (int m = 0; m < NM; ++m) {
+        float v[4];
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
-      *reinterpret_cast<float4*>(a + 16 * m + 4 * g4) = make_float4(acc[m][0], acc[m][1], acc[m][2], acc[m][3]);
-    if (g4 == 0) {
-      p.ws_ml[slot * 2] = bad ? 0.f : m_run;
-      p.ws_ml[slot * 2 + 1] = bad ? __builtin_nanf("") : l_run;
+        for (int j = 0; j < 4; ++j) v[j] = bad ? __builtin_nanf("") : acc[ct][m][j] * inv;
+        uint2 w;
+        w.x = f32_to_bf16_bits(v[0]) | (uint32_t)f32_to_bf16_bits(v[1]) << 16;
+        w.y = f32_to_bf16_bits(v[2]) | (uint32_t)f32_to_bf16_bits(v[3]) << 16;
+        *reinterpret_cast<uint2*>(o + 16 * m + 4 * g4) = w;
+      }
+    } else {
+      const int64_t slot = orow * p.max_parts + part;
+      float* a = p.ws_acc + slot * D;
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+        *reinterpret_cast<float4*>(a + 16 * m + 4 * g4) =
+            make_float4(acc[ct][m][0], acc[ct][m][1], acc[ct][m][2], acc[ct][m][3]);
+      if (g4 == 0) {
+        p.ws_ml[slot * 2] = bad ? 0.f : m_run[ct];
+        p.ws_ml[slot * 2 + 1] = bad ? __builtin_nanf("") : l;
+      }
     }
   }
 }
@@ -961,7 +1019,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_reduce_kernel(Multi
   const int s = blockIdx.x / p.num_kv_heads;
   const MqBlock b = mq_block<G>(p, s, 0);
   if (b.skip || b.nparts <= 1) return;  // written by the partition kernel
-  const int r = b.rb * kRowsPerBlock + threadIdx.x / 4;
+  const int r = b.rb * b.rpb + threadIdx.x / 4;
   if (r >= b.rows) return;
   const int64_t orow = (int64_t)(b.t0 + r / G) * p.num_heads + kvh * G + r % G;
   const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + orow * p.max_parts;
@@ -1111,11 +1169,29 @@ hipError_t launch_t(const MultiQueryLaunch& a, MultiQueryParams p) {
   // (48 KiB; E4M3 24 + 16 KiB).  Measured on the 70B-shaped verification
   // batch (bf16): 115 us against 126 us; on the chunked-prefill batch: 690 us
   // against 651 us.
+  // Sequences of more than 128 rows run in 128-row blocks on the two-tile
+  // kernel, launched first (the longest workgroups); the one-tile kernel
+  // takes the rest.
+  //
+  // Beside the decode kernels (which need many waves in flight to keep HBM
+  // busy) the two-tile kernel asks for 64 KiB of LDS per workgroup instead of
+  // its 48, so at most two of its workgroups share a CU and the decode
+  // waves take the rest.  Measured on the chunked-prefill batch (2048- and
+  // 1024-token chunks beside 64 decodes, LLaMA-13B shape): 592 us against
+  // 681 us at three per CU; the chunks alone run at the same speed either way
+  // (194 us).
+  if (rows > 2 * kRowsPerBlock) {
+    constexpr int kRingBytes = ring_lds_bytes<TC, D, 3>();
+    const int pad = a.beside_decode && kRingBytes < 65536 ? 65536 - kRingBytes : 0;
+    hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G, 3, 2>), grid, dim3(kMqWaves * 64), pad, a.stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (rows > p.stream_rows) {
     if (a.max_row_blocks == 1)
-      hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G, 2>), grid, dim3(kMqWaves * 64), 0, a.stream, p);
+      hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G, 2, 1>), grid, dim3(kMqWaves * 64), 0, a.stream, p);
     else
-      hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G, 3>), grid, dim3(kMqWaves * 64), 0, a.stream, p);
+      hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G, 3, 1>), grid, dim3(kMqWaves * 64), 0, a.stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

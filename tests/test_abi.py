@@ -147,11 +147,11 @@ def partition(S, H, Hkv, D, BS, maxctx, dtype=BF16, cdtype=None, policy=FIXED):
 
 def test_partition_tokens_fixed_is_the_default():
     # The fixed policy names the length partition_tokens = 0 selects: 4096 on
-    # the matrix-core path (bf16 query, G >= 2), 2048 on the vector path.
+    # the matrix-core path (bf16 query, G >= 2) and on the vector path.
     assert partition(1, 64, 8, 128, 16, 100) == 4096
     assert partition(1, 64, 8, 128, 32, 100, cdtype=FP8) == 4096
-    assert partition(1, 40, 40, 128, 16, 100) == 2048
-    assert partition(1, 8, 2, 64, 16, 100, dtype=F32) == 2048
+    assert partition(1, 40, 40, 128, 16, 100) == 4096
+    assert partition(1, 8, 2, 64, 16, 100, dtype=F32) == 4096
     for S, H, Hkv, D, BS, maxctx, dt, cdt in [(3, 8, 2, 64, 16, 9000, F32, F32),
                                               (5, 64, 8, 128, 16, 70000, BF16, BF16),
                                               (2, 32, 32, 128, 32, 5000, BF16, FP8)]:
@@ -383,8 +383,10 @@ def test_multi_query_workspace_size():
         _area(32 * 64 * 2, 128) + _area(192 * 64 * 4, 128) + _work(32, 192, 8, 4)
     assert ws(64, 384, 64, 8, 128, 16, 8192, BF16, BF16, 0) == \
         _area(64 * 64 * 2, 128) + _area(384 * 64 * 4, 128) + _work(64, 384, 8, 4)
-    # G = 1 decodes on the vector path: 2048-token partitions.
-    assert ws(3, 12, 8, 8, 64, 16, 2100, BF16, BF16, 4096) == _area(3 * 8 * 2, 64) + _work(3, 12, 1, 1)
+    # G = 1 decodes on the vector path: 4096-token partitions.
+    assert ws(3, 12, 8, 8, 64, 16, 2100, BF16, BF16, 4096) == _work(3, 12, 1, 1)
+    assert ws(3, 12, 8, 8, 64, 16, 4200, BF16, BF16, 4096) == \
+        _area(3 * 8 * 2, 64) + _area(12 * 8 * 2, 64) + _work(3, 12, 1, 2)
     assert ws(0, 12, 8, 2, 64, 32, 100, BF16, BF16, 0) == 0   # nothing to schedule
     assert ws(3, 0, 8, 2, 64, 32, 100, BF16, BF16, 0) == 0
     bad = ctypes.c_size_t(-1).value
