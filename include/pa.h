@@ -29,10 +29,9 @@
  *   block_pairs     int64 [num_pairs, 2]; (src, dst) physical block ids
  *
  * Conventions shared by every entry point:
- *  - Every buffer pointer is a DEVICE pointer.  The caller owns every buffer;
- *    the library allocates no memory.  Its only state is pa_multi_query's side
- *    stream and two events per device, created on the device's first such
- *    call and kept until the process ends (see pa_multi_query).
+ *  - Every buffer pointer is a DEVICE pointer.  The caller owns every buffer
+ *    and every stream; the library allocates no device memory and keeps no
+ *    state between calls (pa_decode_noalloc's static scratch buffer aside).
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *    null stream).  A return of PA_OK means the kernels were enqueued.
  *  - A negative return means nothing was launched, except PA_ERR_LAUNCH, which
@@ -70,11 +69,33 @@ enum {
    * kernels.  Saves the decode launch for batches that have no decode steps
    * (speculative verification); never changes what is computed. */
   PA_MULTI_QUERY_TILES_ONLY = 1,
-  /* Launch every kernel on the caller's stream.  By default the decode rows
-   * run on a second stream of the library's, beside the multi-query tiles;
-   * the results are the same bits either way. */
+  /* Launch every kernel on the caller's stream, even when a side stream is
+   * given; the results are the same bits either way. */
   PA_MULTI_QUERY_ONE_STREAM = 2
 };
+
+/* A second stream for pa_multi_query, with the two events that fork it from
+ * and join it back to the caller's stream: HIP handles (hipStream_t,
+ * hipEvent_t) on one device, owned by the caller.  pa_side_stream_create
+ * makes them (a non-blocking stream of default priority, two events with
+ * timing disabled) and pa_side_stream_destroy releases them; a caller may also
+ * fill the fields with handles of its own.  One handle serves one call at a
+ * time: calls that overlap (from several host threads) need a handle each. */
+typedef struct pa_side_stream {
+  void* stream;
+  void* fork_event;
+  void* join_event;
+} pa_side_stream;
+
+/* pa_side_stream_create -- create the stream and events of *side on the
+ * current device.  PA_ERR_NULL for a null side, PA_ERR_LAUNCH if HIP fails
+ * (nothing is left allocated then). */
+int pa_side_stream_create(pa_side_stream* side);
+
+/* pa_side_stream_destroy -- destroy what pa_side_stream_create made (after the
+ * work queued on it is done, as for any HIP stream) and zero the fields.
+ * PA_ERR_NULL for a null side; null fields are skipped. */
+int pa_side_stream_destroy(pa_side_stream* side);
 
 /* pa_decode flags */
 enum {
@@ -408,15 +429,14 @@ size_t pa_multi_query_workspace_size(int num_seqs, int num_query_tokens, int num
  * pa_decode's kernels (with their partitioning) unless flags holds
  * PA_MULTI_QUERY_TILES_ONLY (other flag bits than the two above:
  * PA_ERR_UNSUPPORTED).
- * Streams: when a batch has decode rows and longer chunks, the decode kernels
- * (bound by the cache reads) run beside the multi-query kernels (bound by the
- * matrix cores) on a side stream of the library's: one per device, created
- * on the device's first such call (a caller that captures a graph makes one
- * call before capturing), default priority, kept until the process ends.  It
- * is forked from `stream` and joined back to it with events, so the call is
- * ordered on `stream` like a single launch.  Calls on one device take turns
- * on the side stream (a lock); PA_MULTI_QUERY_ONE_STREAM keeps every launch on
- * `stream`.
+ * Streams: when a batch has decode rows and longer chunks and `side` is not
+ * NULL, the decode kernels (bound by the cache reads) run on side->stream
+ * beside the multi-query kernels (bound by the matrix cores) on `stream`.
+ * side->stream is forked from `stream` and joined back to it with the two
+ * events, so the call is ordered on `stream` like a single launch.  With
+ * side == NULL or PA_MULTI_QUERY_ONE_STREAM every launch goes to `stream`.
+ * The side handle must be on the device of the call and serve no other call
+ * at the same time.
  * partition_tokens (0 = chosen from the
  * shape: the smallest of 512, 1024 and 2048 for which num_seqs * num_kv_heads
  * * ceil(max_context_len / partition_tokens) <= 1024, else 2048; otherwise a
@@ -442,7 +462,8 @@ int pa_multi_query(void* out, const void* q,
                    int block_size, int num_blocks, int max_context_len,
                    float scale, int dtype, int cache_dtype, float k_scale, float v_scale,
                    int partition_tokens, int flags,
-                   void* workspace, size_t workspace_bytes, void* stream);
+                   void* workspace, size_t workspace_bytes,
+                   const pa_side_stream* side, void* stream);
 
 /* pa_status_string -- static, human-readable name of a status code. */
 const char* pa_status_string(int status);

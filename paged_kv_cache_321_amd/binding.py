@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import threading
 from typing import Optional
 
 import torch
@@ -34,10 +35,27 @@ EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_partition_tokens
            "pa_decode_workspace_size",
            "pa_decode", "pa_decode_noalloc", "pa_decode_shared_prefix_workspace_size",
            "pa_decode_shared_prefix",
-           "pa_multi_query_workspace_size", "pa_multi_query", "pa_swap_blocks",
-           "pa_status_string")
+           "pa_multi_query_workspace_size", "pa_multi_query", "pa_side_stream_create",
+           "pa_side_stream_destroy", "pa_swap_blocks", "pa_status_string")
 
 _c_int, _c_size, _c_float, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
+
+
+class SideStream(ctypes.Structure):
+    """pa_side_stream: a second HIP stream and its fork / join events, owned by
+    whoever created it (``create`` / ``destroy`` call the library's helpers)."""
+
+    _fields_ = [("stream", ctypes.c_void_p), ("fork_event", ctypes.c_void_p),
+                ("join_event", ctypes.c_void_p)]
+
+    @classmethod
+    def create(cls) -> "SideStream":
+        side = cls()
+        _check(LIB.pa_side_stream_create(ctypes.byref(side)), "pa_side_stream_create")
+        return side
+
+    def destroy(self) -> None:
+        _check(LIB.pa_side_stream_destroy(ctypes.byref(self)), "pa_side_stream_destroy")
 
 
 class PaError(RuntimeError):
@@ -79,8 +97,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_multi_query_workspace_size.restype = _c_size
     lib.pa_multi_query.argtypes = ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp] + [_c_int] * 9 +
                                    [_c_float, _c_int, _c_int, _c_float, _c_float, _c_int, _c_int,
-                                    _vp, _c_size, _vp])
+                                    _vp, _c_size, _vp, _vp])
     lib.pa_multi_query.restype = _c_int
+    lib.pa_side_stream_create.argtypes = [_vp]
+    lib.pa_side_stream_create.restype = _c_int
+    lib.pa_side_stream_destroy.argtypes = [_vp]
+    lib.pa_side_stream_destroy.restype = _c_int
     lib.pa_swap_blocks.argtypes = [_vp, _vp, _vp, _vp, _vp] + [_c_int] * 7 + [_vp]
     lib.pa_swap_blocks.restype = _c_int
     lib.pa_status_string.argtypes = [_c_int]
@@ -357,13 +379,27 @@ def pa_multi_query_workspace_size(num_seqs: int, num_query_tokens: int, num_head
     return n
 
 
+# Side streams this binding made, one per device, for the calls that do not
+# pass their own; a lock keeps them to one call at a time.
+_SIDE = {}
+_SIDE_LOCK = threading.Lock()
+
+
+def _default_side(device: torch.device) -> SideStream:
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    if idx not in _SIDE:
+        with torch.cuda.device(idx):
+            _SIDE[idx] = SideStream.create()
+    return _SIDE[idx]
+
+
 def pa_multi_query(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                    block_tables: torch.Tensor, context_lens: torch.Tensor,
                    query_start: torch.Tensor, scale: float, max_context_len: int,
                    max_query_len: int, partition_tokens: int = 0,
                    workspace: Optional[torch.Tensor] = None, stream=None, k_scale: float = 1.0,
                    v_scale: float = 1.0, tiles_only: bool = False,
-                   one_stream: bool = False) -> None:
+                   one_stream: bool = False, side: Optional[SideStream] = None) -> None:
     """Causal attention of each sequence's new query tokens over the paged caches.
 
     q, out [T, H, D] (bf16) hold sequence s's queries in rows
@@ -371,6 +407,8 @@ def pa_multi_query(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_
     are the last positions of its context_lens[s] cached tokens.  ``tiles_only``
     sets PA_MULTI_QUERY_TILES_ONLY (no decode launch for single-query sequences),
     ``one_stream`` PA_MULTI_QUERY_ONE_STREAM (no side stream for the decode rows).
+    ``side``: the side stream for the decode rows (a ``SideStream``); by default
+    one this binding creates per device and keeps.
     """
     for n, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
                  ("block_tables", block_tables), ("context_lens", context_lens),
@@ -393,14 +431,26 @@ def pa_multi_query(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = LIB.pa_multi_query(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                            block_tables.shape[1], _ptr(context_lens), _ptr(query_start), s, t,
-                            int(max_query_len), h, hkv, d, bs, nb, int(max_context_len),
-                            float(scale), code, ccode, float(k_scale), float(v_scale),
-                            int(partition_tokens),
-                            (PA_MULTI_QUERY_TILES_ONLY if tiles_only else 0)
-                            | (PA_MULTI_QUERY_ONE_STREAM if one_stream else 0),
-                            _ptr(workspace), ws_bytes, _stream(stream))
+    shared_side = side is None and not one_stream
+    if shared_side:
+        side = _default_side(q.device)
+
+    def call():
+        return LIB.pa_multi_query(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                  block_tables.shape[1], _ptr(context_lens), _ptr(query_start), s, t,
+                                  int(max_query_len), h, hkv, d, bs, nb, int(max_context_len),
+                                  float(scale), code, ccode, float(k_scale), float(v_scale),
+                                  int(partition_tokens),
+                                  (PA_MULTI_QUERY_TILES_ONLY if tiles_only else 0)
+                                  | (PA_MULTI_QUERY_ONE_STREAM if one_stream else 0),
+                                  _ptr(workspace), ws_bytes,
+                                  None if side is None else ctypes.byref(side), _stream(stream))
+
+    if shared_side:
+        with _SIDE_LOCK:
+            st = call()
+    else:
+        st = call()
     _check(st, "pa_multi_query")
 
 

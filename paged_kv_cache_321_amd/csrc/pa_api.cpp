@@ -8,9 +8,6 @@
 #include <math.h>
 #include <stdint.h>
 
-#include <memory>
-#include <mutex>
-
 #include "pa_internal.h"
 
 namespace {
@@ -240,38 +237,6 @@ size_t pa_decode_shared_prefix_workspace_size(int num_seqs, int num_heads, int n
 
 namespace {
 
-// The side stream of pa_multi_query on the current device, with its fork and
-// join events; created on first use (null if HIP cannot create it, and the
-// call then keeps to the caller's stream).  Never destroyed: it lives as long
-// as the process.
-struct SideStream {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr;
-  hipEvent_t join = nullptr;
-  std::mutex mu;  // one fork / launch / join sequence at a time
-};
-
-SideStream* side_stream() {
-  constexpr int kMaxDevices = 64;
-  static std::mutex create_mu;
-  static std::unique_ptr<SideStream> per_device[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  std::lock_guard<std::mutex> hold(create_mu);
-  if (!per_device[dev]) {
-    auto s = std::make_unique<SideStream>();
-    if (hipStreamCreateWithFlags(&s->stream, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&s->fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&s->join, hipEventDisableTiming) != hipSuccess) {
-      if (s->fork) (void)hipEventDestroy(s->fork);
-      (void)hipStreamDestroy(s->stream);
-      return nullptr;
-    }
-    per_device[dev] = std::move(s);
-  }
-  return per_device[dev].get();
-}
-
 // Both decode entry points: validation, workspace carving, launch.  The
 // shared-prefix form passes its two per-sequence arrays (non-null).
 int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -430,8 +395,9 @@ int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_
                    int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
                    int max_context_len, float scale, int dtype, int cache_dtype, float k_scale,
                    float v_scale, int partition_tokens, int flags, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+                   size_t workspace_bytes, const pa_side_stream* side, void* stream) {
   if (flags & ~(PA_MULTI_QUERY_TILES_ONLY | PA_MULTI_QUERY_ONE_STREAM)) return PA_ERR_UNSUPPORTED;
+  if (side && (!side->stream || !side->fork_event || !side->join_event)) return PA_ERR_NULL;
   const bool tiles_only = (flags & PA_MULTI_QUERY_TILES_ONLY) != 0;
   const bool one_stream = (flags & PA_MULTI_QUERY_ONE_STREAM) != 0;
   const MultiQuerySizes z = multi_query_sizes(num_seqs, num_query_tokens, num_heads, num_kv_heads,
@@ -534,24 +500,52 @@ int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_
   d.stream = a.stream;
   if (max_query_len < 2)  // no sequence has more than one query
     return pa::launch_decode(d) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
-  SideStream* side = one_stream ? nullptr : side_stream();
-  if (!side) {
+  if (one_stream || !side) {
     if (pa::launch_decode(d) != hipSuccess) return PA_ERR_LAUNCH;
     return pa::launch_multi_query(a) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
   }
   // Fork: the multi-query kernels (long workgroups, matrix-core bound) go
   // first on the caller's stream, the decode kernels (cache-read bound) on
   // the side stream; the join makes `stream` wait for both.
-  std::lock_guard<std::mutex> hold(side->mu);
-  if (hipEventRecord(side->fork, a.stream) != hipSuccess) return PA_ERR_LAUNCH;
-  if (hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess) return PA_ERR_LAUNCH;
-  d.stream = side->stream;
+  const hipStream_t side_stream = static_cast<hipStream_t>(side->stream);
+  const hipEvent_t fork = static_cast<hipEvent_t>(side->fork_event);
+  const hipEvent_t join = static_cast<hipEvent_t>(side->join_event);
+  if (hipEventRecord(fork, a.stream) != hipSuccess) return PA_ERR_LAUNCH;
+  if (hipStreamWaitEvent(side_stream, fork, 0) != hipSuccess) return PA_ERR_LAUNCH;
+  d.stream = side_stream;
   a.beside_decode = true;
   const bool mq_ok = pa::launch_multi_query(a) == hipSuccess;
   const bool dec_ok = pa::launch_decode(d) == hipSuccess;
-  const bool join_ok = hipEventRecord(side->join, side->stream) == hipSuccess &&
-                       hipStreamWaitEvent(a.stream, side->join, 0) == hipSuccess;
+  const bool join_ok = hipEventRecord(join, side_stream) == hipSuccess &&
+                       hipStreamWaitEvent(a.stream, join, 0) == hipSuccess;
   return mq_ok && dec_ok && join_ok ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int pa_side_stream_create(pa_side_stream* side) {
+  if (!side) return PA_ERR_NULL;
+  hipStream_t st = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return PA_ERR_LAUNCH;
+  if (hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess) {
+    if (fork) (void)hipEventDestroy(fork);
+    (void)hipStreamDestroy(st);
+    return PA_ERR_LAUNCH;
+  }
+  side->stream = st;
+  side->fork_event = fork;
+  side->join_event = join;
+  return PA_OK;
+}
+
+int pa_side_stream_destroy(pa_side_stream* side) {
+  if (!side) return PA_ERR_NULL;
+  bool ok = true;
+  if (side->join_event) ok = hipEventDestroy(static_cast<hipEvent_t>(side->join_event)) == hipSuccess && ok;
+  if (side->fork_event) ok = hipEventDestroy(static_cast<hipEvent_t>(side->fork_event)) == hipSuccess && ok;
+  if (side->stream) ok = hipStreamDestroy(static_cast<hipStream_t>(side->stream)) == hipSuccess && ok;
+  side->stream = side->fork_event = side->join_event = nullptr;
+  return ok ? PA_OK : PA_ERR_LAUNCH;
 }
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

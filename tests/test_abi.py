@@ -298,13 +298,14 @@ def test_shared_prefix_workspace_size():
 def multi_query(**kw):
     a = dict(out=P, q=P, k=P, v=P, bt=P, mb=8, ctx=P, qs=P, S=2, T=12, mq=6, H=8, Hkv=2, D=128,
              BS=16, NB=32, maxctx=100, scale=0.1, dtype=BF16, cdtype=None, ks=0.5, vs=0.5, pt=0,
-             flags=0, ws=None, wsb=0)
+             flags=0, ws=None, wsb=0, side=None)
     a.update(kw)
     cdtype = a["dtype"] if a["cdtype"] is None else a["cdtype"]
+    side = None if a["side"] is None else ctypes.byref(a["side"])
     return LIB.pa_multi_query(a["out"], a["q"], a["k"], a["v"], a["bt"], a["mb"], a["ctx"], a["qs"],
                               a["S"], a["T"], a["mq"], a["H"], a["Hkv"], a["D"], a["BS"], a["NB"],
                               a["maxctx"], a["scale"], a["dtype"], cdtype, a["ks"], a["vs"], a["pt"],
-                              a["flags"], a["ws"], a["wsb"], None)
+                              a["flags"], a["ws"], a["wsb"], side, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -340,6 +341,8 @@ def multi_query(**kw):
     (dict(H=64, Hkv=8, mq=0x8000 * 8), UNSUP),   # 2^15 row blocks of 64 rows
     (dict(H=64, Hkv=8, mq=0x7fff * 8), WS),      # the largest chunk accepted
     (dict(maxctx=0x8000 * 16, mb=0x8000, pt=16), UNSUP),  # 2^15 partitions per row
+    (dict(side=binding.SideStream()), NULL),                # a side handle with null fields
+    (dict(side=binding.SideStream(P, P, None)), NULL),
     (dict(flags=4), UNSUP),              # unknown flag bit
     (dict(flags=-1), UNSUP),
     (dict(flags=1, S=0), OK),
@@ -530,3 +533,10 @@ def test_decode_noalloc_scratch_limit_matches_the_workspace_size():
                                                                         BF16, 0)
     header = open(HEADER).read()
     assert re.search(r"PA_DECODE_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)32 << 20\)", header)
+
+
+def test_side_stream_helpers_reject_null():
+    assert LIB.pa_side_stream_create(None) == NULL
+    assert LIB.pa_side_stream_destroy(None) == NULL
+    empty = binding.SideStream()
+    assert LIB.pa_side_stream_destroy(ctypes.byref(empty)) == OK   # null fields are skipped

@@ -237,23 +237,29 @@ def test_full_size_sampled(name, kw):
     torch.cuda.empty_cache()
 
 
-def test_side_stream_same_bits_and_ordered():
-    """Decode rows on the library's side stream give the bits of the one-stream
+@pytest.mark.parametrize("own_handle", [False, True])
+def test_side_stream_same_bits_and_ordered(own_handle):
+    """Decode rows on a side stream (the binding's per-device one, or a
+    handle the caller creates and destroys) give the bits of the one-stream
     launch, on a caller stream other than the default one, and work queued on
     that stream after the call sees the whole output (the join)."""
     x = wl.make_inputs("chunked13b", **SMALL["chunked13b"])
     one, t = gpu_mq_step(x, one_stream=True)
     ref, _, _ = oracle_mq_step(x)
     assert_close(as_f64(one), ref, "bf16", "one stream")
+    side = binding.SideStream.create() if own_handle else None
     caller = torch.cuda.Stream()
     out = torch.full_like(t["q"], float("nan"))
     torch.cuda.synchronize()
     with torch.cuda.stream(caller):
         binding.pa_multi_query(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
                                t["context_lens"], t["query_start"], x.scale, x.max_context_len,
-                               int(x.plan.query_lens.max()), stream=caller)
+                               int(x.plan.query_lens.max()), stream=caller, side=side)
         seen = out.clone()
     torch.cuda.synchronize()
+    if side is not None:
+        side.destroy()
+        assert side.stream is None and side.fork_event is None
     assert np.array_equal(bits(out), bits(one))
     assert np.array_equal(bits(seen), bits(one))
 
