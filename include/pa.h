@@ -350,9 +350,10 @@ size_t pa_decode_shared_prefix_workspace_size(int num_seqs, int num_heads, int n
  *                     <= every member's context length).  0 = no sharing.
  * Members are served in chunks of 16 / G consecutive sequences counted from L
  * (G = num_heads / num_kv_heads): one workgroup computes the shared part of a
- * chunk, so each shared page is read once per chunk; each sequence's tokens
- * past the prefix are read by its own workgroups; a merge kernel combines the
- * partial results.  An entry that does not describe such a chunk (L < 0, L > s,
+ * chunk, so each shared page is read once per chunk; a member's tokens past
+ * the prefix are read by one of its chunk's prefix workgroups when they fit one
+ * partition, else by its own workgroups; a merge kernel combines the partial
+ * results.  An entry that does not describe such a chunk (L < 0, L > s,
  * prefix_leader[L] != L, or the first sequence of s's chunk in another group)
  * makes s a sequence served alone (its prefix is 0), with the same result.
  *

@@ -102,7 +102,9 @@ DecodeSizes decode_sizes(int num_seqs, int num_heads, int num_kv_heads, int head
     z.prefix_parts = (int)(((int64_t)max_prefix_blocks * block_size + pt - 1) / pt);
     z.tail_parts = parts_of(max_tail_len, pt);
     z.max_parts = z.prefix_parts + z.tail_parts;
-    if ((int64_t)num_seqs * z.max_parts * num_kv_heads > 0x7fffffffLL) {  // one-dimensional grid
+    // One-dimensional grid: prefix rows for num_seqs rounded up to a whole
+    // number of chunks (at most 16 sequences), tail rows per sequence.
+    if (((int64_t)num_seqs + 15) * z.max_parts * num_kv_heads > 0x7fffffffLL) {
       z.status = PA_ERR_UNSUPPORTED;
       return z;
     }

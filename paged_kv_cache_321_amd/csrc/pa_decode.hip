@@ -31,7 +31,8 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams p) {
   const int lane = threadIdx.x;
   const int row = query_row(p, s);
   if (row < 0) return;  // not a decode row of this call
-  const SeqSplit sp = split_context(p, p.context_lens[s], prefix_chunk(p, s).blocks);
+  const PrefixChunk pc = prefix_chunk(p, s);
+  const SeqSplit sp = split_context(p, p.context_lens[s], pc.blocks, pc.blocks > 0 ? s - pc.chunk : -1);
   if (sp.bad || sp.ctx < p.min_context) return;  // written as NaN by the partition kernel
   const int nparts = sp.nprefix + sp.ntail;
   if (nparts <= 1) return;  // written by the partition kernel

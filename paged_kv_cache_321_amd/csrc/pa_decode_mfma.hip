@@ -54,7 +54,7 @@ namespace {
 // that the reduce kernel merges; the softmax algebra is the same as for one
 // sequence's partitions, since each column keeps its own running max and sum.
 template <typename TC, int D, int BS, int G, bool NONTEMPORAL, bool SHARED>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void decode_partition_mfma_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(SHARED && BS == 16 ? 4 : 3))) void decode_partition_mfma_kernel(DecodeParams p) {
   constexpr bool kFp8 = sizeof(TC) == 1;
   constexpr int NT = BS / 16;       // 16-token tiles per page
   constexpr int NC = D / 32;        // 32-wide steps of the QK contraction
@@ -90,6 +90,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   int col_total = 1;     // partitions of that sequence
   bool col_bad = false;  // that sequence's table disagrees with the chunk's (NaN row)
   int slot;              // partition slot of this workgroup's results (< max_parts)
+  // Shared prefix: the chunk members whose tokens past the prefix this
+  // workgroup reads after the prefix (bit i: member i), with their contexts.
+  uint32_t hosted = 0;
+  int member_ctx = 0;    // lane i < R: context length of member i
+  int chunk0 = 0;        // first sequence of the chunk
+  int pre_tokens = 0;    // shared prefix length
   if constexpr (!SHARED) {
     slot = part;
     s = sequence_of(p, blockIdx.z);
@@ -105,12 +111,19 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   } else {
     const int pt = p.partition_tokens;
     const int row = blockIdx.x / p.num_kv_heads;
-    const int prefix_rows = p.num_seqs * p.prefix_parts;
+    const int nwin = (p.num_seqs + R - 1) / R;
+    const int prefix_rows = R * nwin * p.prefix_parts;
     if (row < prefix_rows) {
-      // Prefix workgroup of the chunk that starts at sequence z.  Most rows
-      // are not chunk starts: that takes one load to see.
-      const int z = row / p.prefix_parts;
-      part = row % p.prefix_parts;
+      // Prefix workgroup of the chunk that starts at sequence z.  Rows come
+      // in R classes, z % R = 0 first: groups whose leaders sit at multiples
+      // of R (beams of equal width) have all their chunk starts in the first
+      // class, and the rows that are no chunk start (one load to see) come
+      // after them.
+      const int cls = row / (nwin * p.prefix_parts);
+      const int rem = row % (nwin * p.prefix_parts);
+      const int z = rem / p.prefix_parts * R + cls;
+      part = rem % p.prefix_parts;
+      if (z >= p.num_seqs) return;
       const int lead = p.prefix_leader[z];
       if (lead < 0 || lead > z || (z - lead) % R != 0) return;
       const PrefixChunk pc = prefix_chunk(p, z);
@@ -127,16 +140,22 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       // Lane i < R checks member z + i: same group, and a context that holds
       // the prefix (the same test its own workgroups make).
       bool member = false;
+      bool host = false;
       int total = 0;
       {
         const int m = z + l16;
         if (l16 < R && m < p.num_seqs && p.prefix_leader[m] == pc.leader) {
-          const SeqSplit sp = split_context(p, p.context_lens[m], pc.blocks);
+          const SeqSplit sp = split_context(p, p.context_lens[m], pc.blocks, l16);
           member = !sp.bad;
+          host = member && sp.folded && l16 % npre == part;
           total = sp.nprefix + sp.ntail;
+          member_ctx = sp.ctx;
         }
       }
       const uint32_t members = static_cast<uint32_t>(__ballot(member)) & 0xffffu;
+      hosted = static_cast<uint32_t>(__ballot(host)) & 0xffffu;
+      chunk0 = z;
+      pre_tokens = pre;
       const int mi = l16 / G;
       col_seq = (members >> mi) & 1u ? z + mi : -1;
       col_total = __shfl(total, mi);
@@ -160,8 +179,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       // Sequence s's own workgroups: its tokens past the shared prefix.
       s = (row - prefix_rows) / p.tail_parts;
       part = (row - prefix_rows) % p.tail_parts;
-      const SeqSplit sp = split_context(p, p.context_lens[s], prefix_chunk(p, s).blocks);
-      if (part >= sp.ntail) return;
+      const PrefixChunk pc = prefix_chunk(p, s);
+      const SeqSplit sp = split_context(p, p.context_lens[s], pc.blocks, pc.blocks > 0 ? s - pc.chunk : -1);
+      if (part >= sp.ntail) return;  // none, or folded into a prefix workgroup
       const int t0 = sp.prefix + part * pt;
       r = token_range(sp.ctx, sp.nprefix + sp.ntail, t0, min(sp.ctx, t0 + pt), sp.bad, wave, BS);
       bool ids_bad;
@@ -172,8 +192,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       slot = sp.nprefix + part;
     }
   }
-  const int tok1 = r.tok1;
-  const int nk = r.nk;
+  int tok1 = r.tok1;
+  int nk = r.nk;
+  bool col_on = true;  // this lane's column takes part in the current page range
 
   // B operand of S^T = K Q^T: for bf16 caches lane holds Q[head l16][32c +
   // 8 g4 .. +7]; for fp8 caches, whose 16-byte K loads carry 16 columns, step
@@ -282,7 +303,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bool valid = full || (t0 + 16 * tt + 4 * g4 + j < tok1);
+        const bool valid = col_on && (full || (t0 + 16 * tt + 4 * g4 + j < tok1));
         sv[tt][j] = valid ? st[tt][j] * p.scale_log2e : -__builtin_inff();
         mx = fmaxf(mx, sv[tt][j]);
       }
@@ -342,18 +363,36 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   // consumed this page's K, so one page per wave is always in flight.  (Two
   // buffer pairs, two pages in flight, measured no faster on any workload
   // here and cost a wave per SIMD of occupancy.)
-  if (!bad && nk > 0) {
-    uint4 kr[NT][NKL], vr[NV];
-    load_k(0, kr);
-    load_v(0, vr);
-    for (int k = 0; k < nk; ++k) {
-      stage_v(k, vr);
-      if (k + 1 < nk) load_v(k + 1, vr);
-      f32x4_t st[NT];
-      scores(kr, st);
-      if (k + 1 < nk) load_k(k + 1, kr);
-      softmax_pv(k, st);
+  // Page ranges: this workgroup's own, then (shared prefix) the tokens past
+  // the prefix of each member it hosts, from that member's table row, for
+  // that member's columns only (their running max and sum carry on).
+  bool walk = !bad;
+  for (;;) {
+    if (walk && nk > 0) {
+      uint4 kr[NT][NKL], vr[NV];
+      load_k(0, kr);
+      load_v(0, vr);
+      for (int k = 0; k < nk; ++k) {
+        stage_v(k, vr);
+        if (k + 1 < nk) load_v(k + 1, vr);
+        f32x4_t st[NT];
+        scores(kr, st);
+        if (k + 1 < nk) load_k(k + 1, kr);
+        softmax_pv(k, st);
+      }
     }
+    if (!SHARED || hosted == 0 || bad) break;
+    const int i = __builtin_ctz(hosted);
+    hosted &= hosted - 1;
+    const int ctx_i = __shfl(member_ctx, i);
+    r = token_range(ctx_i, 1, pre_tokens, ctx_i, false, wave, BS);
+    tok1 = r.tok1;
+    nk = r.nk;
+    bool ids_bad;
+    my_id = load_page_ids(p, chunk0 + i, r, wave, lane, &ids_bad);
+    col_on = l16 / G == i;
+    col_bad = col_bad || (ids_bad && col_on);  // the member's row becomes NaN
+    walk = !ids_bad;
   }
 
   // The four lanes of a head each hold a share of its running sum.
@@ -420,7 +459,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
 
 template <typename TC, int D, int BS, int G, bool SHARED>
 hipError_t launch_t(const DecodeLaunch& a, const DecodeParams& p) {
-  const dim3 grid = SHARED ? dim3(a.num_seqs * (a.prefix_parts + a.tail_parts) * a.num_kv_heads, 1, 1)
+  const int R = 16 / G;
+  const dim3 grid = SHARED ? dim3(((a.num_seqs + R - 1) / R * R * a.prefix_parts + a.num_seqs * a.tail_parts) *
+                                      a.num_kv_heads,
+                                  1, 1)
                           : dim3(a.grid_parts, a.num_kv_heads, a.num_seqs);
   if constexpr (SHARED) {
     hipLaunchKernelGGL((decode_partition_mfma_kernel<TC, D, BS, G, true, true>), grid, dim3(kWaves * 64), 0,

@@ -272,17 +272,23 @@ __device__ __forceinline__ PrefixChunk prefix_chunk(const DecodeParams& p, int s
 // How a sequence's context is cut: the shared prefix [0, prefix) into nprefix
 // partitions (computed by its chunk's workgroups, partition slots 0 ..
 // nprefix-1), the rest [prefix, ctx) into ntail partitions (its own
-// workgroups, slots nprefix ..).  Without a prefix this is the plain
-// partitioning.  A bad row (context length out of range, shorter than the
-// declared prefix, or past the caller's prefix or tail bound) has one
-// partition and is written as NaN.
+// workgroups, slots nprefix ..).  A chunk member (index `member` in its
+// chunk, -1 when served alone) whose rest fits one partition is folded: its
+// chunk's workgroup of prefix partition member % nprefix reads it too (for
+// that member's columns only), into the same slot, and ntail is 0.  Without
+// a prefix this is the plain partitioning.  A bad row (context length out of
+// range, shorter than the declared prefix, or past the caller's prefix or
+// tail bound) has one partition and is written as NaN.
 struct SeqSplit {
   int ctx, prefix, nprefix, ntail;
   bool bad;
+  bool folded;
 };
-__device__ __forceinline__ SeqSplit split_context(const DecodeParams& p, int ctx, int prefix_blocks) {
+__device__ __forceinline__ SeqSplit split_context(const DecodeParams& p, int ctx, int prefix_blocks,
+                                                  int member) {
   SeqSplit r;
   r.ctx = ctx;
+  r.folded = false;
   const int64_t pre = (int64_t)prefix_blocks * p.block_size;
   r.bad = ctx < 0 || ctx > p.max_context_len || pre > ctx;
   if (p.prefix_leader != nullptr)  // the caller's bounds size the grid
@@ -298,6 +304,8 @@ __device__ __forceinline__ SeqSplit split_context(const DecodeParams& p, int ctx
   } else {
     r.nprefix = (r.prefix + pt - 1) / pt;
     r.ntail = (ctx - r.prefix + pt - 1) / pt;
+    r.folded = member >= 0 && r.ntail == 1;
+    if (r.folded) r.ntail = 0;
   }
   return r;
 }
