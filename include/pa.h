@@ -300,8 +300,9 @@ int pa_decode(void* out, const void* q,
  * current device, as for every entry point).
  * Errors: the statuses of pa_decode, and PA_ERR_SCRATCH (nothing launched)
  * when pa_decode_workspace_size(...) for these arguments exceeds
- * PA_DECODE_NOALLOC_SCRATCH_BYTES -- e.g. 32 sequences x 64 heads x 32K-token
- * contexts at the default partitioning fit, 128 of them do not.
+ * PA_DECODE_NOALLOC_SCRATCH_BYTES -- e.g. at the default partitioning, 64
+ * sequences x 64 heads (8 kv heads) x 32K-token contexts in 16-token pages
+ * fit and 128 do not; in 32-token pages 128 fit and 256 do not.
  * All calls on one GPU share its buffer and nothing in it has to start at
  * zero: calls that overlap on one GPU (on different streams, or from several
  * threads) race on it and give unspecified results; serialise them.

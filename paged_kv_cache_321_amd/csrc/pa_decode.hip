@@ -114,16 +114,21 @@ static bool use_mfma_path(int dtype, int group) { return dtype == kDtypeBf16 && 
 int default_partition_tokens(int dtype, int /*cache_dtype*/, int /*head_dim*/, int block_size, int group,
                              bool shared_prefix, int max_prefix_tokens) {
   // Fixed lengths (never the batch size, so a sequence's result does not
-  // depend on the batch): 4096 tokens on both paths.  Fewer, longer
-  // workgroups measured faster on long GQA contexts, and on ragged MHA
-  // batches (64 sequences of 128..4096 tokens, LLaMA-7B shape: 314 us
-  // against 348 at 2048; 128 of 1000..8000: 1650 against 1799), and the
-  // same within 2% on uniform ones.
+  // depend on the batch): 4096 tokens on the vector path, 8192 on the
+  // matrix-core path (both capped at the 256 pages a partition can hold).
+  // Fewer, longer workgroups measured faster: on ragged MHA batches (64
+  // sequences of 128..4096 tokens, LLaMA-7B shape: 314 us against 348 at
+  // 2048; 128 of 1000..8000: 1650 against 1799), the same within 2% on
+  // uniform ones; on 16 GQA sequences of 32K tokens (70B shape, 32-token
+  // pages) 320 us against 327 at 4096 (bf16) and 167 against 175 (E4M3):
+  // 512 workgroups run in one round where 1024 need two at three per CU.
+  // Batches of a few long sequences take the batch-shaped length instead
+  // (PA_PARTITION_FILL).
   // Shared-prefix decode: a quarter of the longest shared prefix, rounded up
   // to a power of two within [256, 2048] -- each prefix is spread over about
   // four workgroups per kv head (measured best for 1024- and 4096-token
   // prefixes of 4-beam groups).
-  int t = 4096;
+  int t = use_mfma_path(dtype, group) ? 8192 : 4096;
   if (shared_prefix) {
     t = 256;
     while (t < 2048 && 4 * t < max_prefix_tokens) t *= 2;

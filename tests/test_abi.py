@@ -146,10 +146,12 @@ def partition(S, H, Hkv, D, BS, maxctx, dtype=BF16, cdtype=None, policy=FIXED):
 
 
 def test_partition_tokens_fixed_is_the_default():
-    # The fixed policy names the length partition_tokens = 0 selects: 4096 on
-    # the matrix-core path (bf16 query, G >= 2) and on the vector path.
+    # The fixed policy names the length partition_tokens = 0 selects: 8192 on
+    # the matrix-core path (bf16 query, G >= 2), 4096 on the vector path, both
+    # capped at 256 pages (4096 tokens of 16-token pages).
     assert partition(1, 64, 8, 128, 16, 100) == 4096
-    assert partition(1, 64, 8, 128, 32, 100, cdtype=FP8) == 4096
+    assert partition(1, 64, 8, 128, 32, 100, cdtype=FP8) == 8192
+    assert partition(1, 64, 8, 128, 32, 100) == 8192
     assert partition(1, 40, 40, 128, 16, 100) == 4096
     assert partition(1, 8, 2, 64, 16, 100, dtype=F32) == 4096
     for S, H, Hkv, D, BS, maxctx, dt, cdt in [(3, 8, 2, 64, 16, 9000, F32, F32),
@@ -529,8 +531,10 @@ def test_decode_noalloc_validation(kw, code):
 def test_decode_noalloc_scratch_limit_matches_the_workspace_size():
     ws = LIB.pa_decode_workspace_size
     limit = binding.PA_DECODE_NOALLOC_SCRATCH_BYTES
-    assert ws(64, 64, 8, 128, 32, 32768, BF16, BF16, 0) <= limit < ws(128, 64, 8, 128, 32, 32768, BF16,
+    assert ws(64, 64, 8, 128, 16, 32768, BF16, BF16, 0) <= limit < ws(128, 64, 8, 128, 16, 32768, BF16,
                                                                         BF16, 0)
+    assert ws(128, 64, 8, 128, 32, 32768, BF16, BF16, 0) <= limit < ws(256, 64, 8, 128, 32, 32768, BF16,
+                                                                         BF16, 0)
     header = open(HEADER).read()
     assert re.search(r"PA_DECODE_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)32 << 20\)", header)
 

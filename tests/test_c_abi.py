@@ -29,7 +29,7 @@ int main(void) {
   printf("%s\n", name(PA_OK));
   /* LLaMA-13B shape at 2048 tokens: one partition per sequence, no workspace. */
   printf("%zu\n", ws(128, 40, 40, 128, 16, 2048, PA_BF16, PA_BF16, 0));
-  /* GQA 70B shape at 32768 tokens: 8 partitions of 4096 tokens per sequence. */
+  /* GQA 70B shape at 32768 tokens: 4 partitions of 8192 tokens per sequence. */
   printf("%zu\n", ws(16, 64, 8, 128, 32, 32768, PA_BF16, PA_BF16, 0));
   /* Host validation: a null output pointer is refused before any GPU call. */
   printf("%d\n", decode(NULL, NULL, NULL, NULL, NULL, 128, NULL, NULL, 1, 8, 8, 128, 16, 64, 2048,
@@ -63,5 +63,5 @@ def test_c_program_uses_the_library(program):
     assert lines[0].startswith("PA_OK")
     assert int(lines[1]) == 0
     # (max, sum) pair and a D-float accumulator per (sequence, head, partition).
-    assert int(lines[2]) == 16 * 64 * 8 * (128 + 2) * 4
+    assert int(lines[2]) == 16 * 64 * 4 * (128 + 2) * 4
     assert int(lines[3]) == -1 and lines[4].startswith("PA_ERR_NULL")
