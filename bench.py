@@ -90,6 +90,8 @@ def parse():
     ap.add_argument("--workload", default="llama13b",
                     choices=sorted(n for n in DESCRIPTION if n != "swap13b"))
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--cold", action="store_true",
+                    help="flush the MALL between the timed steps of --workload (as for the beam cold rows)")
     ap.add_argument("--others", default="tiny,llama7b,gqa70b,beam,beam+prefix,llama13b_fp8,gqa70b_fp8,"
                                         "beam_fp8+prefix,specdec70b,specdec70b_fp8,specdec70b_fp8_q4,"
                                         "chunked13b,chunked13b_chunks,gqa70b_x2,gqa70b_x2+fill,swap13b",
@@ -633,7 +635,8 @@ def main():
         copy_calibration()
         return
 
-    head, spec, plan = run_workload(args.workload, args.steps, args.warmup, args.partition_tokens)
+    head, spec, plan = run_workload(args.workload, args.steps, args.warmup, args.partition_tokens,
+                                    flush=args.cold)
     others = []
     for name in [n for n in args.others.split(",") if n and n != args.workload]:
         if name == "swap13b":
