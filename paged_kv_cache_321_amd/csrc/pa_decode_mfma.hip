@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(SHA
       pbits.y = pack_bf16x2(sv[0][2], sv[0][3]);
       pbits.z = pack_bf16x2(sv[1][0], sv[1][1]);
       pbits.w = pack_bf16x2(sv[1][2], sv[1][3]);
-      l_run += (bf16x2_sum(pbits.x) + bf16x2_sum(pbits.y)) + (bf16x2_sum(pbits.z) + bf16x2_sum(pbits.w));
+      l_run = bf16x2_acc(pbits.w, bf16x2_acc(pbits.z, bf16x2_acc(pbits.y, bf16x2_acc(pbits.x, l_run))));
       const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pbits);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(SHA
       uint2 pbits;
       pbits.x = pack_bf16x2(sv[0][0], sv[0][1]);
       pbits.y = pack_bf16x2(sv[0][2], sv[0][3]);
-      l_run += bf16x2_sum(pbits.x) + bf16x2_sum(pbits.y);
+      l_run = bf16x2_acc(pbits.y, bf16x2_acc(pbits.x, l_run));
       const s16x4_t pb = __builtin_bit_cast(s16x4_t, pbits);
 #pragma unroll
       for (int m = 0; m < NM; ++m)

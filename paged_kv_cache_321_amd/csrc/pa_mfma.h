@@ -35,11 +35,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Sum of the two bf16 values packed in w (low half + high half), in float32:
-// the softmax weights as the PV product sees them, so that the running sum
-// (the denominator) adds exactly the weights the numerator was formed with.
-__device__ __forceinline__ float bf16x2_sum(uint32_t w) {
-  return __uint_as_float(w << 16) + __uint_as_float(w & 0xffff0000u);
+// c + the two bf16 values packed in w, in one v_dot2_f32_bf16 against (1, 1)
+// (the products are exact; one float32 rounding of the sum): the softmax
+// weights as the PV product sees them, so that the running sum (the
+// denominator) adds exactly the weights the numerator was formed with.
+__device__ __forceinline__ float bf16x2_acc(uint32_t w, float c) {
+  constexpr uint32_t kOnes = 0x3f803f80u;  // bf16 1.0 in both halves
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, kOnes), c,
+                                         false);
 }
 
 // Eight E4M3 codes -> eight bf16, exact (an E4M3 value has 3 mantissa bits),

@@ -209,30 +209,31 @@ __device__ __forceinline__ float column_max(float x) {
 // Bytes of the ring kernel's LDS: STAGES (K, V) stages of one step as stored
 // in the cache, plus for E4M3 the widened bf16 tile(s) (V only at D = 128,
 // where the QK product widens K in registers).
-template <typename TC, int D, int STAGES>
+template <typename TC, int D, int STAGES, int STEP = kStepTokens>
 constexpr int ring_lds_bytes() {
-  constexpr int raw_tile = kStepTokens * D * (int)sizeof(TC);
-  constexpr int bf16_tile = kStepTokens * D * 2;
+  constexpr int raw_tile = STEP * D * (int)sizeof(TC);
+  constexpr int bf16_tile = STEP * D * 2;
   return STAGES * 2 * raw_tile + (sizeof(TC) == 1 ? (D == 128 ? 1 : 2) * bf16_tile : 0);
 }
 
 // NCT: 16-row tiles per wave (1: 64-row blocks, 2: 128-row blocks); the
-// kernel serves only the sequences whose blocks have its row count.
-template <typename TC, int D, int BS, int G, int STAGES, int NCT>
+// kernel serves only the sequences whose blocks have its row count.  STEP:
+// tokens staged per step (32 or 64).
+template <typename TC, int D, int BS, int G, int STAGES, int NCT, int STEP = kStepTokens>
 __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(NCT == 1 ? 4 : sizeof(TC) == 1 ? 2 : 3))) void multi_query_kernel(MultiQueryParams p) {
   constexpr bool kFp8 = sizeof(TC) == 1;
-  constexpr int PPS = kStepTokens / BS;      // pages per step
+  constexpr int PPS = STEP / BS;             // pages per step
   constexpr int NC = D / 32;                 // 32-wide steps of the QK contraction
   constexpr int NM = D / 16;                 // 16-wide output tiles along D
   constexpr int ROWB = D * 2;                // bytes of one bf16 row in LDS
   constexpr int NCH = ROWB / 16;             // 16-byte bf16 chunks per row
   constexpr int CCH = D * (int)sizeof(TC) / 16;  // 16-byte cache chunks per row
-  constexpr int CHUNKS = kStepTokens * CCH;  // 16-byte cache chunks per step (K or V)
+  constexpr int CHUNKS = STEP * CCH;         // 16-byte cache chunks per step (K or V)
   constexpr int PER_T = (CHUNKS + kMqWaves * 64 - 1) / (kMqWaves * 64);
-  constexpr int NTT = kStepTokens / 16;      // 16-token tiles per step
-  constexpr int TILEB = kStepTokens * ROWB;  // bytes of one step's bf16 K (or V) in LDS
+  constexpr int NTT = STEP / 16;             // 16-token tiles per step
+  constexpr int TILEB = STEP * ROWB;         // bytes of one step's bf16 K (or V) in LDS
   constexpr int CROWB = D * (int)sizeof(TC);  // bytes of one cache row
-  constexpr int RTILEB = kStepTokens * CROWB; // bytes of one step's K (or V) as in the cache
+  constexpr int RTILEB = STEP * CROWB;       // bytes of one step's K (or V) as in the cache
   // A ring of STAGES (K, V) stages filled by direct LDS loads STAGES - 1
   // steps ahead.  bf16 caches land in the swizzled layouts the matrix cores
   // read; E4M3 caches land as they are and each step is widened into one
@@ -241,11 +242,11 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
   // E4M3 at D = 128: the QK product reads K codes straight from the stage
   // (8 codes per lane, widened in registers), so only V is widened in LDS.
   constexpr bool kKRaw = kFp8 && D == 128;
-  constexpr int LDS_BYTES = ring_lds_bytes<TC, D, NSTAGE>();
+  constexpr int LDS_BYTES = ring_lds_bytes<TC, D, NSTAGE, STEP>();
   static_assert(LDS_BYTES == NSTAGE * 2 * RTILEB + (kFp8 ? (kKRaw ? 1 : 2) * TILEB : 0), "ring layout");
   constexpr int WINDOW = 256;                // page ids held in registers (4 per lane)
   constexpr int RPB = kRowsPerBlock * NCT;   // rows per block
-  static_assert(kStepTokens % BS == 0 && kStepTokens % 32 == 0 && NCH >= 8, "tile shape");
+  static_assert(STEP % BS == 0 && STEP % 32 == 0 && NCH >= 8, "tile shape");
   static_assert(kFp8 || CHUNKS % (kMqWaves * 64) == 0, "a bf16 step is whole wave loads");
   static_assert(CHUNKS * 16 == RTILEB, "a step is CHUNKS 16-byte chunks");
   static_assert(CHUNKS % 64 == 0 && 64 / CCH <= BS, "a wave's chunks of a step lie in one page");
@@ -475,7 +476,7 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
   // its V tile in the transposed-read layout.
   auto compute_step = [&](int st, const unsigned char* kt, const unsigned char* vt, auto full_tag) {
     constexpr bool kFull = decltype(full_tag)::value;
-    const int t_base = tok0 + st * kStepTokens;
+    const int t_base = tok0 + st * STEP;
     // S^T for the step's 16-token tiles; each K operand read feeds the NCT
     // row tiles.
     f32x4_t sc[NCT][NTT];
@@ -554,7 +555,7 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
         pb.y = pack_bf16x2(sv[2 * h][2], sv[2 * h][3]);
         pb.z = pack_bf16x2(sv[2 * h + 1][0], sv[2 * h + 1][1]);
         pb.w = pack_bf16x2(sv[2 * h + 1][2], sv[2 * h + 1][3]);
-        l_run[ct] += (bf16x2_sum(pb.x) + bf16x2_sum(pb.y)) + (bf16x2_sum(pb.z) + bf16x2_sum(pb.w));
+        l_run[ct] = bf16x2_acc(pb.w, bf16x2_acc(pb.z, bf16x2_acc(pb.y, bf16x2_acc(pb.x, l_run[ct]))));
       }
     }
     // O^T += V^T P^T; each V^T operand read feeds the NCT row tiles.
@@ -577,7 +578,7 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
   // Steps.  The unmasked steps come first and run as a loop of their own;
   // every wave passes the same barriers, so the split point is the
   // workgroup's, set by its first row.
-  const int nfull = p.scale_log2e > 0.f ? min(nsteps, max(0, (block_full_end - tok0) / kStepTokens)) : 0;
+  const int nfull = p.scale_log2e > 0.f ? min(nsteps, max(0, (block_full_end - tok0) / STEP)) : 0;
   if (nsteps > 0) {
     load_ids(0);
     // Step st + NSTAGE - 1 is loaded while step st is computed.  At the top
@@ -861,14 +862,12 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
         for (int j = 0; j < 4; ++j) sv[tt][j] = fast_exp2(sv[tt][j] - m_run[ct]);
       // The running sum adds the weights as rounded to bf16 for the product.
-      float ps = 0.f;
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
         pw[ct][2 * tt] = pack_bf16x2(sv[tt][0], sv[tt][1]);
         pw[ct][2 * tt + 1] = pack_bf16x2(sv[tt][2], sv[tt][3]);
-        ps += bf16x2_sum(pw[ct][2 * tt]) + bf16x2_sum(pw[ct][2 * tt + 1]);
+        l_run[ct] = bf16x2_acc(pw[ct][2 * tt + 1], bf16x2_acc(pw[ct][2 * tt], l_run[ct]));
       }
-      l_run[ct] += ps;
     }
     // O^T += V^T P^T; each V^T read feeds every tile.
 #pragma unroll
