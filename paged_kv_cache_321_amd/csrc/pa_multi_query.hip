@@ -244,14 +244,12 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
   constexpr bool kKRaw = kFp8 && D == 128;
   constexpr int LDS_BYTES = ring_lds_bytes<TC, D, NSTAGE, STEP>();
   static_assert(LDS_BYTES == NSTAGE * 2 * RTILEB + (kFp8 ? (kKRaw ? 1 : 2) * TILEB : 0), "ring layout");
-  constexpr int WINDOW = 256;                // page ids held in registers (4 per lane)
   constexpr int RPB = kRowsPerBlock * NCT;   // rows per block
   static_assert(STEP % BS == 0 && STEP % 32 == 0 && NCH >= 8, "tile shape");
   static_assert(kFp8 || CHUNKS % (kMqWaves * 64) == 0, "a bf16 step is whole wave loads");
   static_assert(CHUNKS * 16 == RTILEB, "a step is CHUNKS 16-byte chunks");
   static_assert(CHUNKS % 64 == 0 && 64 / CCH <= BS, "a wave's chunks of a step lie in one page");
-  static_assert(WINDOW % PPS == 0, "a step's pages lie in one window");
-  static_assert(NSTAGE >= 2 && (NSTAGE - 1) * PPS <= WINDOW, "ring depth");
+  static_assert(NSTAGE >= 2, "ring depth");
 
   const int kvh = blockIdx.x % p.num_kv_heads;
   const int item = blockIdx.x / p.num_kv_heads;
@@ -344,46 +342,24 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
   const TC* vc = static_cast<const TC*>(p.v_cache) + (int64_t)kvh * BS * D;
   const int32_t* table = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
 
-  // Physical ids of pages pg0 + base .. + WINDOW - 1: lane i holds page
-  // base + 64 j + i in ids[j] (ids outside the pool become 0 and mark the
-  // block bad).  Every wave holds the same ids.
-  int ids[WINDOW / 64];
-  int ids_base = 0;
+  // Physical page ids come from the block table through scalar loads: the
+  // table is read-only here, so a wave-uniform index into the constant
+  // address space reads it through the scalar cache, and those loads count
+  // in lgkmcnt, apart from the page loads' vmcnt.  The ids of the next step
+  // to be loaded are read at the end of the step before (the barrier at the
+  // top of each step waits for them), so the scalar work of issuing a step
+  // is a short chain without lane reads.  Entries past the partition's pages
+  // are read at its last page and dropped; an id outside the pool reads page
+  // 0 and marks the block bad (every wave checks every page of the step, so
+  // the flag is the same in all of them).
+  using const_i32 = const __attribute__((address_space(4))) int32_t;
+  const_i32* const ctable = reinterpret_cast<const_i32*>(reinterpret_cast<uintptr_t>(table + pg0));
+  int nid[PPS];  // ids of the pages of the next step to load
   bool ids_bad = false;
-  auto load_ids = [&](int base) {
-    // Entries past the partition's pages are read at its last page (npg > 0
-    // here), so the four loads go out together; they are then dropped.
-    int raw[WINDOW / 64];
+  auto read_ids = [&](int st) {
 #pragma unroll
-    for (int j = 0; j < WINDOW / 64; ++j) raw[j] = table[pg0 + min(base + 64 * j + lane, npg - 1)];
-    bool badid = false;
-#pragma unroll
-    for (int j = 0; j < WINDOW / 64; ++j) {
-      const bool live = base + 64 * j + lane < npg;
-      const bool out_of_pool = raw[j] < 0 || raw[j] >= p.num_blocks;
-      badid = badid || (live && out_of_pool);
-      ids[j] = live && !out_of_pool ? raw[j] : 0;
-    }
-    ids_base = base;
-    ids_bad = ids_bad || __any(badid);
+    for (int q = 0; q < PPS; ++q) nid[q] = ctable[min(st * PPS + q, npg - 1)];
   };
-  // Physical id of page pg of the partition (pg wave-uniform, inside the
-  // window).  Called with every lane active: the four reads take lane k % 64
-  // of registers written by the whole wave, and the choice among them is
-  // scalar (a per-lane select under a partial mask would leave that lane
-  // unwritten).
-  auto page_id = [&](int pg) -> int64_t {
-    const int k = __builtin_amdgcn_readfirstlane(pg - ids_base);
-    const int l = k & 63;
-    const int a0 = __builtin_amdgcn_readlane(ids[0], l);
-    const int a1 = __builtin_amdgcn_readlane(ids[1], l);
-    const int a2 = __builtin_amdgcn_readlane(ids[2], l);
-    const int a3 = __builtin_amdgcn_readlane(ids[3], l);
-    const int j = k >> 6;
-    return j == 0 ? a0 : j == 1 ? a1 : j == 2 ? a2 : a3;
-  };
-  static_assert(WINDOW / 64 == 4, "page_id selects among four registers");
-
   // Pages read by one workgroup only (a sequence of one row block) stream
   // past the caches; the row blocks of a longer chunk share theirs through
   // L2 / MALL.
@@ -417,19 +393,38 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
     }
   }
   constexpr int kLoadsPerStep = 2 * PER_T;  // per wave that loads (all, but for E4M3 at D = 64)
+  // Bytes between consecutive physical pages: below 2^32 (the host bounds
+  // the kv heads by 65535), so a page's offset is one 32 x 32-bit product.
+  const uint32_t page_bytes = (uint32_t)p.block_stride * (uint32_t)sizeof(TC);
+  const uint64_t kbase = reinterpret_cast<uint64_t>(kc);
+  const uint64_t vbase = reinterpret_cast<uint64_t>(vc);
+  const uint32_t ring_lds = lds_address(ring);
+  // Loads step st's pages (ids in nid) into stage `stage`.
   auto dma_step = [&](int st, int stage) {
-    unsigned char* kbuf = ring + stage * 2 * RTILEB;
+    int id[PPS];
+#pragma unroll
+    for (int q = 0; q < PPS; ++q) {
+      const bool live = st * PPS + q < npg;
+      const bool out_of_pool = nid[q] < 0 || nid[q] >= p.num_blocks;
+      ids_bad = ids_bad || (live && out_of_pool);
+      id[q] = live && !out_of_pool ? nid[q] : 0;
+    }
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
       const int slot0 = (u * kMqWaves + wave) * 64;  // wave-uniform
       if (slot0 >= CHUNKS) continue;
-      const int pg = st * PPS + slot0 / CCH / BS;     // page of the partition
-      const int64_t page = page_id(pg) * p.block_stride;
+      const int q = slot0 / CCH / BS;                 // page of the step
+      int pid = id[0];
+#pragma unroll
+      for (int r = 1; r < PPS; ++r)
+        if (q == r) pid = id[r];
+      const int pg = st * PPS + q;                    // page of the partition
+      const uint64_t page = (uint64_t)(uint32_t)pid * page_bytes;
       const int valid = min(max(tok1 - (tok0 + pg * BS), 0), BS);  // tokens of the page to read
-      const i32x4_t kr = raw_buffer(kc + page, valid * CROWB);
-      const i32x4_t vr = raw_buffer(vc + page, valid * CROWB);
-      const uint32_t kdst = lds_address(kbuf + slot0 * 16);
-      const uint32_t vdst = lds_address(kbuf + RTILEB + slot0 * 16);
+      const i32x4_t kr = raw_buffer(reinterpret_cast<const void*>(kbase + page), valid * CROWB);
+      const i32x4_t vr = raw_buffer(reinterpret_cast<const void*>(vbase + page), valid * CROWB);
+      const uint32_t kdst = ring_lds + stage * 2 * RTILEB + slot0 * 16;
+      const uint32_t vdst = kdst + RTILEB;
       if (stream_pages) {
         buffer_load_lds16<true>(koff[u], kr, kdst);
         buffer_load_lds16<true>(voff[u], vr, vdst);
@@ -580,7 +575,7 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
   // workgroup's, set by its first row.
   const int nfull = p.scale_log2e > 0.f ? min(nsteps, max(0, (block_full_end - tok0) / STEP)) : 0;
   if (nsteps > 0) {
-    load_ids(0);
+    read_ids(0);
     // Step st + NSTAGE - 1 is loaded while step st is computed.  At the top
     // of step st the wave waits until only the loads of the steps after st
     // are outstanding (all of them in the last steps); the barrier then
@@ -588,7 +583,10 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
     // the loads of step st + NSTAGE - 1 reuse (for E4M3 also the widened
     // tile, which a second barrier publishes).
     constexpr int kAhead = NSTAGE - 1;
-    for (int st = 0; st < kAhead && st < nsteps; ++st) dma_step(st, st);
+    for (int st = 0; st < kAhead && st < nsteps; ++st) {
+      dma_step(st, st);
+      if (st + 1 < nsteps) read_ids(st + 1);
+    }
     auto run_steps = [&](int st0, int st1, auto full_tag) {
       int stage = st0 % NSTAGE;
       for (int st = st0; st < st1; ++st) {
@@ -597,10 +595,7 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
         else
           vm_wait<0>();
         block_barrier();
-        if (st + kAhead < nsteps) {
-          if ((st + kAhead) * PPS - ids_base == WINDOW) load_ids((st + kAhead) * PPS);
-          dma_step(st + kAhead, stage == 0 ? NSTAGE - 1 : stage - 1);
-        }
+        if (st + kAhead < nsteps) dma_step(st + kAhead, stage == 0 ? NSTAGE - 1 : stage - 1);
         const unsigned char* kt = ring + stage * 2 * RTILEB;
         const unsigned char* vt = kt + RTILEB;
         if constexpr (kFp8) {
@@ -610,6 +605,7 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
           vt = wide_v;
         }
         if (wave_rows) compute_step(st, kt, vt, full_tag);
+        if (st + kAhead + 1 < nsteps) read_ids(st + kAhead + 1);
         stage = stage == NSTAGE - 1 ? 0 : stage + 1;
       }
     };
