@@ -199,11 +199,21 @@ __device__ __forceinline__ int kswz(int tok) {
 // Max over the four lanes l, l ^ 16, l ^ 32, l ^ 48 that hold one column of an
 // MFMA result: v_permlane32_swap exchanges the wave's 32-lane halves and
 // v_permlane16_swap the odd and even 16-lane rows (gfx950), both in the VALU.
+// The maxima take v_max_f32 directly: for fmaxf the compiler first quiets
+// each input it cannot prove canonical (a lane swap's result, a running max),
+// one instruction per input; scores are never signalling NaNs, so the plain
+// instruction gives the same values.
+__device__ __forceinline__ float max_of(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 __device__ __forceinline__ float column_max(float x) {
   const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  x = max_of(__uint_as_float(h[0]), __uint_as_float(h[1]));
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_of(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Bytes of the ring kernel's LDS: STAGES (K, V) stages of one step as stored
@@ -400,7 +410,7 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
   const uint64_t vbase = reinterpret_cast<uint64_t>(vc);
   const uint32_t ring_lds = lds_address(ring);
   // Loads step st's pages (ids in nid) into stage `stage`.
-  auto dma_step = [&](int st, int stage) {
+  auto dma_step = [&](int st, int stage) __attribute__((always_inline)) {
     int id[PPS];
 #pragma unroll
     for (int q = 0; q < PPS; ++q) {
@@ -438,7 +448,7 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
   // E4M3: widen stage `stage` (16 codes per chunk, chunk c = token c / CCH,
   // codes at 16 (c % CCH)) into the bf16 tile, two 16-byte chunks per chunk
   // (exact; zero codes, the rows past the partition end, become +0).
-  auto widen_step = [&](int stage) {
+  auto widen_step = [&](int stage) __attribute__((always_inline)) {
     const unsigned char* kq = ring + stage * 2 * RTILEB;
     const unsigned char* vq = kq + RTILEB;
     unsigned char* kt = wide;
@@ -469,7 +479,8 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
 
   // kt: the step's K (bf16 tile, or for kKRaw the stage's raw codes); vt:
   // its V tile in the transposed-read layout.
-  auto compute_step = [&](int st, const unsigned char* kt, const unsigned char* vt, auto full_tag) {
+  auto compute_step = [&](int st, const unsigned char* kt, const unsigned char* vt, auto full_tag)
+                          __attribute__((always_inline)) {
     constexpr bool kFull = decltype(full_tag)::value;
     const int t_base = tok0 + st * STEP;
     // S^T for the step's 16-token tiles; each K operand read feeds the NCT
@@ -512,7 +523,7 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
         for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
           for (int j = 0; j < 4; ++j) raw = fmaxf(raw, sc[ct][tt][j]);
-        mx = fmaxf(m_run[ct], column_max(raw) * p.scale_log2e);
+        mx = max_of(m_run[ct], column_max(raw) * p.scale_log2e);
       } else {
         mx = m_run[ct];
 #pragma unroll
@@ -573,7 +584,10 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
   // Steps.  The unmasked steps come first and run as a loop of their own;
   // every wave passes the same barriers, so the split point is the
   // workgroup's, set by its first row.
-  const int nfull = p.scale_log2e > 0.f ? min(nsteps, max(0, (block_full_end - tok0) / STEP)) : 0;
+  // (A whole number of ring rounds, so that both loops start at stage 0; the
+  // full steps past it take the masked path, which handles them too.)
+  const int nfull =
+      p.scale_log2e > 0.f ? min(nsteps, max(0, (block_full_end - tok0) / STEP)) / NSTAGE * NSTAGE : 0;
   if (nsteps > 0) {
     read_ids(0);
     // Step st + NSTAGE - 1 is loaded while step st is computed.  At the top
@@ -587,26 +601,40 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
       dma_step(st, st);
       if (st + 1 < nsteps) read_ids(st + 1);
     }
-    auto run_steps = [&](int st0, int st1, auto full_tag) {
-      int stage = st0 % NSTAGE;
-      for (int st = st0; st < st1; ++st) {
-        if (st + kAhead - 1 < nsteps)
-          vm_wait<(kAhead - 1) * kLoadsPerStep>();
-        else
-          vm_wait<0>();
+    // Step st on ring stage S (a constant, so every LDS address of the step
+    // is a per-lane base plus an immediate offset).
+    auto step = [&](int st, auto stage_c, auto full_tag) __attribute__((always_inline)) {
+      constexpr int S = decltype(stage_c)::value;
+      if (st + kAhead - 1 < nsteps)
+        vm_wait<(kAhead - 1) * kLoadsPerStep>();
+      else
+        vm_wait<0>();
+      block_barrier();
+      if (st + kAhead < nsteps) dma_step(st + kAhead, (S + NSTAGE - 1) % NSTAGE);
+      const unsigned char* kt = ring + S * 2 * RTILEB;
+      const unsigned char* vt = kt + RTILEB;
+      if constexpr (kFp8) {
+        widen_step(S);
         block_barrier();
-        if (st + kAhead < nsteps) dma_step(st + kAhead, stage == 0 ? NSTAGE - 1 : stage - 1);
-        const unsigned char* kt = ring + stage * 2 * RTILEB;
-        const unsigned char* vt = kt + RTILEB;
-        if constexpr (kFp8) {
-          widen_step(stage);
-          block_barrier();
-          if constexpr (!kKRaw) kt = wide;
-          vt = wide_v;
+        if constexpr (!kKRaw) kt = wide;
+        vt = wide_v;
+      }
+      if (wave_rows) compute_step(st, kt, vt, full_tag);
+      if (st + kAhead + 1 < nsteps) read_ids(st + kAhead + 1);
+    };
+    // Steps st0 .. st1 - 1, st0 a multiple of NSTAGE: whole ring rounds.
+    auto run_steps = [&](int st0, int st1, auto full_tag) {
+      static_assert(NSTAGE == 2 || NSTAGE == 3, "ring rounds of two or three stages");
+      for (int st = st0; st < st1;) {
+        step(st, std::integral_constant<int, 0>{}, full_tag);
+        if (++st == st1) break;
+        step(st, std::integral_constant<int, 1>{}, full_tag);
+        ++st;
+        if constexpr (NSTAGE == 3) {
+          if (st == st1) break;
+          step(st, std::integral_constant<int, 2>{}, full_tag);
+          ++st;
         }
-        if (wave_rows) compute_step(st, kt, vt, full_tag);
-        if (st + kAhead + 1 < nsteps) read_ids(st + kAhead + 1);
-        stage = stage == NSTAGE - 1 ? 0 : stage + 1;
       }
     };
     run_steps(0, nfull, std::true_type{});
