@@ -124,9 +124,43 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(SHA
       const int z = rem / p.prefix_parts * R + cls;
       part = rem % p.prefix_parts;
       if (z >= p.num_seqs) return;
+      // The prologue's reads are dependent (leader, then the chunk, then the
+      // members and the page ids), and under the walk's load each level costs
+      // microseconds.  Rows of the first class (the chunk starts of groups
+      // that sit at multiples of R, e.g. beams) therefore issue every read
+      // that needs z alone at once: the leader entry, the prefix length at z
+      // (the chunk's own when z leads its group), the members' leader entries
+      // and contexts, and the page ids of the partition and the members'
+      // entries for the same pages as if the prefix filled it.  Each is used
+      // only where the checks below would have read it.  Other rows read one
+      // level at a time.
+      const bool spec = cls == 0;
+      const int m = z + l16;
+      const bool m_in = l16 < R && m < p.num_seqs;
+      const int spec_lanes = (pt / BS + kWaves - 1) / kWaves;  // pages per wave of a full partition
+      const int64_t jspec = (int64_t)part * (pt / BS) + wave + lane * kWaves;
+      const bool j_in = lane < spec_lanes && jspec < p.max_blocks_per_seq;
       const int lead = p.prefix_leader[z];
+      int z_blocks = 0, m_lead = -1, m_ctx = 0, spec_id = 0;
+      int other[R > 1 ? R - 1 : 1] = {};
+      if (spec) {
+        z_blocks = p.prefix_blocks[z];
+        if (m_in) {
+          m_lead = p.prefix_leader[m];
+          m_ctx = p.context_lens[m];
+        }
+        if (j_in) {
+          spec_id = p.block_tables[(int64_t)z * p.max_blocks_per_seq + jspec];
+#pragma unroll
+          for (int i = 1; i < R; ++i)
+            if (z + i < p.num_seqs) other[i - 1] = p.block_tables[(int64_t)(z + i) * p.max_blocks_per_seq + jspec];
+        }
+      }
       if (lead < 0 || lead > z || (z - lead) % R != 0) return;
-      const PrefixChunk pc = prefix_chunk(p, z);
+      // A leader's own chunk: prefix_chunk's reads are the leader entry and
+      // the prefix length at z, both in hand.
+      const PrefixChunk pc =
+          spec && lead == z ? PrefixChunk{z, z, z_blocks > 0 ? z_blocks : 0} : prefix_chunk(p, z);
       if (pc.blocks == 0 || pc.chunk != z) return;
       // A prefix past the caller's bound: every member is a bad row, which
       // its own workgroup writes.
@@ -142,15 +176,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(SHA
       bool member = false;
       bool host = false;
       int total = 0;
-      {
-        const int m = z + l16;
-        if (l16 < R && m < p.num_seqs && p.prefix_leader[m] == pc.leader) {
-          const SeqSplit sp = split_context(p, p.context_lens[m], pc.blocks, l16);
-          member = !sp.bad;
-          host = member && sp.folded && l16 % npre == part;
-          total = sp.nprefix + sp.ntail;
-          member_ctx = sp.ctx;
-        }
+      if (!spec && m_in) {
+        m_lead = p.prefix_leader[m];
+        m_ctx = p.context_lens[m];
+      }
+      if (m_in && m_lead == pc.leader) {
+        const SeqSplit sp = split_context(p, m_ctx, pc.blocks, l16);
+        member = !sp.bad;
+        host = member && sp.folded && l16 % npre == part;
+        total = sp.nprefix + sp.ntail;
+        member_ctx = sp.ctx;
       }
       const uint32_t members = static_cast<uint32_t>(__ballot(member)) & 0xffffu;
       hosted = static_cast<uint32_t>(__ballot(host)) & 0xffffu;
@@ -160,17 +195,29 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(SHA
       col_seq = (members >> mi) & 1u ? z + mi : -1;
       col_total = __shfl(total, mi);
       bool ids_bad;
-      my_id = load_page_ids(p, z, r, wave, lane, &ids_bad);
+      if (spec) {
+        // The partition's pages are the first r.nk <= spec_lanes of each wave's.
+        bool badid = false;
+        my_id = 0;
+        if (lane < r.nk) {
+          badid = spec_id < 0 || spec_id >= p.num_blocks;
+          my_id = badid ? 0 : spec_id;
+        }
+        ids_bad = __any(badid);
+      } else {
+        my_id = load_page_ids(p, z, r, wave, lane, &ids_bad);
+      }
       bad = ids_bad;
       // Every member must name the same physical pages.
       uint32_t differ = 0;
       if (lane < r.nk) {
         const int64_t j = r.pg0 + wave + lane * kWaves;
 #pragma unroll
-        for (int i = 1; i < R; ++i)
-          if (((members >> i) & 1u) &&
-              p.block_tables[(int64_t)(z + i) * p.max_blocks_per_seq + j] != my_id)
-            differ |= 1u << i;
+        for (int i = 1; i < R; ++i) {
+          if (!((members >> i) & 1u)) continue;
+          const int e = spec ? other[i - 1] : p.block_tables[(int64_t)(z + i) * p.max_blocks_per_seq + j];
+          if (e != my_id) differ |= 1u << i;
+        }
       }
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) differ |= __shfl_xor(differ, off);
