@@ -80,6 +80,8 @@ struct MultiQueryParams {
   int decode_rows_elsewhere;  // sequences with one query run in the decode kernels
   int stream_rows;     // single-block sequences of at most this many rows run in the
                        // streaming kernel (0: none), the others in the ring kernel
+  int one_ring;        // the two-tile ring kernel takes the 64-row blocks too (the
+                       // one-tile kernel is not launched)
   float scale_log2e;   // softmax scale * log2(e), times k_scale for fp8 caches
   float v_scale;       // multiplies the output (1 unless the cache holds fp8 codes)
 };
@@ -226,9 +228,10 @@ constexpr int ring_lds_bytes() {
   return STAGES * 2 * raw_tile + (sizeof(TC) == 1 ? (D == 128 ? 1 : 2) * bf16_tile : 0);
 }
 
-// NCT: 16-row tiles per wave (1: 64-row blocks, 2: 128-row blocks); the
-// kernel serves only the sequences whose blocks have its row count.  STEP:
-// tokens staged per step (32 or 64).
+// NCT: 16-row tiles per wave (1: 64-row blocks, 2: 128-row blocks, and the
+// 64-row ones too when it is the batch's only ring launch); the kernel serves
+// only the sequences whose blocks it takes.  STEP: tokens staged per step (32
+// or 64).
 template <typename TC, int D, int BS, int G, int STAGES, int NCT, int STEP = kStepTokens>
 __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(NCT == 1 ? 4 : sizeof(TC) == 1 ? 2 : 3))) void multi_query_kernel(MultiQueryParams p) {
   constexpr bool kFp8 = sizeof(TC) == 1;
@@ -274,7 +277,11 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
   const int rbi = row_block_of(w.y);
   const int part = w.y & 0xffff;
   const MqBlock b = mq_block<G>(p, s, rbi);
-  if (b.skip || part >= b.nparts || b.rpb != RPB) return;
+  if (b.skip || part >= b.nparts) return;
+  // The two-tile kernel takes 128-row blocks, and the 64-row ones when it is
+  // the only ring launch (its waves 0 and 1 then hold the rows); the one-tile
+  // kernel takes 64-row blocks.
+  if (b.rpb != RPB && !(NCT == 2 && p.one_ring && b.rpb == kRowsPerBlock)) return;
   if (b.nrb == 1 && b.rows <= p.stream_rows) return;  // the streaming kernel's
 
   const int tid = threadIdx.x;
@@ -286,15 +293,16 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
   // This lane's rows: column l16 of each of the wave's NCT tiles.  A wave
   // whose rows all lie past the block's rows (a short chunk, a decoding
   // sequence) only helps stage the tiles.
-  const int wrow0 = b.rb * RPB + wave * 16 * NCT;
-  const bool wave_rows = wrow0 < b.rows;
+  const int rows_end = min(b.rows, (b.rb + 1) * b.rpb);  // past the block's last row
+  const int wrow0 = b.rb * b.rpb + wave * 16 * NCT;
+  const bool wave_rows = wrow0 < rows_end;
   bool row_ok[NCT];
   int head[NCT], last_seen[NCT];
   int64_t qrow[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
     const int r = wrow0 + 16 * ct + l16;
-    row_ok[ct] = r < b.rows;
+    row_ok[ct] = r < rows_end;
     const int qi = row_ok[ct] ? r / G : 0;
     head[ct] = kvh * G + (row_ok[ct] ? r % G : 0);
     qrow[ct] = b.t0 + qi;
@@ -474,7 +482,7 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
   // block sees all of its tokens.  Such steps also take the row max of the
   // raw scores and fold the scale into the exponent, which needs a positive
   // scale.
-  const int block_first_qi = b.rb * RPB / G;
+  const int block_first_qi = b.rb * b.rpb / G;
   const int block_full_end = min(tok1, b.ctx - b.qlen + block_first_qi + 1);
 
   // kt: the step's K (bf16 tile, or for kKRaw the stage's raw codes); vt:
@@ -1203,14 +1211,20 @@ hipError_t launch_t(const MultiQueryLaunch& a, MultiQueryParams p) {
   // 1024-token chunks beside 64 decodes, LLaMA-13B shape): 592 us against
   // 681 us at three per CU; the chunks alone run at the same speed either way
   // (194 us).
-  if (rows > 2 * kRowsPerBlock) {
+  // With a sequence of 128-row blocks in the batch the two-tile kernel is the
+  // only ring launch: it also takes the 64-row blocks (two of its waves hold
+  // their rows), so no second grid of workgroups that look up their item and
+  // exit (chunk-only prefill batch, back-to-back calls: 164.6 -> 160.2 us,
+  // E4M3 236.7 -> 232.0 us).
+  p.one_ring = rows > 2 * kRowsPerBlock;
+  if (p.one_ring) {
     constexpr int kRingBytes = ring_lds_bytes<TC, D, 3>();
     const int pad = a.beside_decode && kRingBytes < 65536 ? 65536 - kRingBytes : 0;
     hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G, 3, 2>), grid, dim3(kMqWaves * 64), pad, a.stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (rows > p.stream_rows) {
+  if (!p.one_ring && rows > p.stream_rows) {
     // Verification rows over an E4M3 cache take 64-token steps: the step's
     // fixed costs (barriers, issuing the page loads, the waits) are shared by
     // twice the tokens, in a 48 KiB ring.  Measured on the 70B verification
@@ -1322,6 +1336,7 @@ hipError_t launch_multi_query(const MultiQueryLaunch& a) {
   p.work_capacity = a.work_capacity;
   p.decode_rows_elsewhere = a.decode_rows_elsewhere ? 1 : 0;
   p.stream_rows = 0;  // set per shape by launch_t
+  p.one_ring = 0;
   const bool fp8 = a.cache_dtype == kDtypeFp8;
   p.scale_log2e = a.scale * kLog2e * (fp8 ? a.k_scale : 1.f);
   p.v_scale = fp8 ? a.v_scale : 1.f;
