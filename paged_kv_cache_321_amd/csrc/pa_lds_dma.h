@@ -33,16 +33,17 @@ __device__ __forceinline__ i32x4_t raw_buffer(const void* base, uint32_t bytes) 
 // load counts in vmcnt like any vector load.  It is issued from assembly so
 // that the compiler, which cannot tell which LDS bytes such a load writes,
 // does not put a full vmcnt wait before every later LDS read; callers order
-// it with vm_wait and block_barrier.  M0 is saved and restored around it.
+// it with vm_wait and block_barrier.  lds_base is an M0 operand, so the
+// compiler writes M0 right before the instruction and knows it holds that
+// value; the nop is the wait state an M0 write needs before such a load.
 template <bool kNonTemporal>
 __device__ __forceinline__ void buffer_load_lds16(uint32_t voffset, i32x4_t rsrc, uint32_t lds_base) {
-  uint32_t saved;
   if constexpr (kNonTemporal)
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "v"(voffset), "s"(rsrc), "s"(lds_base) : "memory");
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+                 :: "v"(voffset), "s"(rsrc), "{m0}"(lds_base) : "memory");
   else
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "v"(voffset), "s"(rsrc), "s"(lds_base) : "memory");
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voffset), "s"(rsrc), "{m0}"(lds_base) : "memory");
 }
 
 // LDS byte address of a pointer into __shared__ memory, made wave-uniform.

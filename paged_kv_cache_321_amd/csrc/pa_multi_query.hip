@@ -232,8 +232,13 @@ constexpr int ring_lds_bytes() {
 // 64-row ones too when it is the batch's only ring launch); the kernel serves
 // only the sequences whose blocks it takes.  STEP: tokens staged per step (32
 // or 64).
+// Register targets: four waves per SIMD for one tile (the 64-token E4M3
+// kernel needs more than 128 registers and runs at two waves; held to three it
+// measured no faster), three for two tiles.  The two-tile E4M3 kernel, asked for two, took
+// 180 registers; at three it takes 168 with a few values spilled outside the
+// step loops (chunk-only prefill batch over E4M3: 230 -> 199 us).
 template <typename TC, int D, int BS, int G, int STAGES, int NCT, int STEP = kStepTokens>
-__global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(NCT == 1 ? 4 : sizeof(TC) == 1 ? 2 : 3))) void multi_query_kernel(MultiQueryParams p) {
+__global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(NCT == 1 ? 4 : 3))) void multi_query_kernel(MultiQueryParams p) {
   constexpr bool kFp8 = sizeof(TC) == 1;
   constexpr int PPS = STEP / BS;             // pages per step
   constexpr int NC = D / 32;                 // 32-wide steps of the QK contraction
@@ -287,6 +292,7 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(wave >= 0 && wave < kMqWaves);
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
 
@@ -367,14 +373,17 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
   // to be loaded are read at the end of the step before (the barrier at the
   // top of each step waits for them), so the scalar work of issuing a step
   // is a short chain without lane reads.  Entries past the partition's pages
-  // are read at its last page and dropped; an id outside the pool reads page
-  // 0 and marks the block bad (every wave checks every page of the step, so
-  // the flag is the same in all of them).
+  // are read at its last page (and none of their bytes is loaded).  An id
+  // outside the pool reads the pool's last page and marks the block bad:
+  // every wave keeps the largest id of the walk, as an unsigned number (so a
+  // negative id is larger than any page), over every page of every step, so
+  // the flag is the same in all of them.
   using const_i32 = const __attribute__((address_space(4))) int32_t;
   const_i32* const ctable = reinterpret_cast<const_i32*>(reinterpret_cast<uintptr_t>(table + pg0));
   int nid[PPS];  // ids of the pages of the next step to load
-  bool ids_bad = false;
-  auto read_ids = [&](int st) {
+  uint32_t id_max = 0;
+  const uint32_t id_last = static_cast<uint32_t>(p.num_blocks) - 1u;  // num_blocks >= 1
+  auto read_ids = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < PPS; ++q) nid[q] = ctable[min(st * PPS + q, npg - 1)];
   };
@@ -417,38 +426,61 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
   const uint64_t kbase = reinterpret_cast<uint64_t>(kc);
   const uint64_t vbase = reinterpret_cast<uint64_t>(vc);
   const uint32_t ring_lds = lds_address(ring);
-  // Loads step st's pages (ids in nid) into stage `stage`.
+  // Loads step st's pages (ids in nid) into stage `stage`.  Load u of wave w
+  // fills LDS slots (u kMqWaves + w) 64 .. +63, which hold page
+  // (u kMqWaves + w) 64 / (CCH BS) of the step: the same page for every wave
+  // when a page takes at least one load per wave, else a page that also
+  // depends on the wave (wave_page for u = 0).
+  const int wave_page = wave * 64 / (CCH * BS);
   auto dma_step = [&](int st, int stage) __attribute__((always_inline)) {
-    int id[PPS];
+    uint32_t id[PPS];
 #pragma unroll
     for (int q = 0; q < PPS; ++q) {
-      const bool live = st * PPS + q < npg;
-      const bool out_of_pool = nid[q] < 0 || nid[q] >= p.num_blocks;
-      ids_bad = ids_bad || (live && out_of_pool);
-      id[q] = live && !out_of_pool ? nid[q] : 0;
+      const uint32_t raw = static_cast<uint32_t>(nid[q]);
+      id_max = max(id_max, raw);
+      id[q] = min(raw, id_last);
     }
+    // Tokens of the partition from this step on: every page of the step is
+    // whole unless this is its last step.
+    const int rem = tok1 - tok0 - st * STEP;
+    i32x4_t kr[PER_T], vr[PER_T];
+    uint32_t kdst[PER_T];
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
       const int slot0 = (u * kMqWaves + wave) * 64;  // wave-uniform
       if (slot0 >= CHUNKS) continue;
-      const int q = slot0 / CCH / BS;                 // page of the step
-      int pid = id[0];
-#pragma unroll
-      for (int r = 1; r < PPS; ++r)
-        if (q == r) pid = id[r];
-      const int pg = st * PPS + q;                    // page of the partition
-      const uint64_t page = (uint64_t)(uint32_t)pid * page_bytes;
-      const int valid = min(max(tok1 - (tok0 + pg * BS), 0), BS);  // tokens of the page to read
-      const i32x4_t kr = raw_buffer(reinterpret_cast<const void*>(kbase + page), valid * CROWB);
-      const i32x4_t vr = raw_buffer(reinterpret_cast<const void*>(vbase + page), valid * CROWB);
-      const uint32_t kdst = ring_lds + stage * 2 * RTILEB + slot0 * 16;
-      const uint32_t vdst = kdst + RTILEB;
-      if (stream_pages) {
-        buffer_load_lds16<true>(koff[u], kr, kdst);
-        buffer_load_lds16<true>(voff[u], vr, vdst);
+      int q;  // page of the step
+      uint32_t pid;
+      if constexpr (CCH * BS >= kMqWaves * 64) {
+        q = u * kMqWaves * 64 / (CCH * BS);
+        pid = id[q];
       } else {
-        buffer_load_lds16<false>(koff[u], kr, kdst);
-        buffer_load_lds16<false>(voff[u], vr, vdst);
+        q = u * (kMqWaves * 64 / (CCH * BS)) + wave_page;
+        pid = id[0];
+#pragma unroll
+        for (int r = 1; r < PPS; ++r)
+          if (q == r) pid = id[r];
+      }
+      const uint64_t page = static_cast<uint64_t>(pid) * page_bytes;
+      uint32_t bytes = BS * CROWB;
+      if (rem < STEP) bytes = static_cast<uint32_t>(min(max(rem - q * BS, 0), BS)) * CROWB;
+      kr[u] = raw_buffer(reinterpret_cast<const void*>(kbase + page), bytes);
+      vr[u] = raw_buffer(reinterpret_cast<const void*>(vbase + page), bytes);
+      kdst[u] = ring_lds + stage * 2 * RTILEB + slot0 * 16;
+    }
+    if (stream_pages) {
+#pragma unroll
+      for (int u = 0; u < PER_T; ++u) {
+        if ((u * kMqWaves + wave) * 64 >= CHUNKS) continue;
+        buffer_load_lds16<true>(koff[u], kr[u], kdst[u]);
+        buffer_load_lds16<true>(voff[u], vr[u], kdst[u] + RTILEB);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < PER_T; ++u) {
+        if ((u * kMqWaves + wave) * 64 >= CHUNKS) continue;
+        buffer_load_lds16<false>(koff[u], kr[u], kdst[u]);
+        buffer_load_lds16<false>(voff[u], vr[u], kdst[u] + RTILEB);
       }
     }
   };
@@ -487,8 +519,28 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
 
   // kt: the step's K (bf16 tile, or for kKRaw the stage's raw codes); vt:
   // its V tile in the transposed-read layout.
-  auto compute_step = [&](int st, const unsigned char* kt, const unsigned char* vt, auto full_tag)
-                          __attribute__((always_inline)) {
+  // The K operand of 16-token tile tt and contraction step c (for kKRaw the
+  // raw codes, widened at the product).
+  using KRead = std::conditional_t<kKRaw, uint2, uint4>;
+  auto read_k = [&](const unsigned char* kt, int tt, int c) __attribute__((always_inline)) {
+    const int tok = 16 * tt + l16;
+    if constexpr (kKRaw)
+      // Codes of columns 32 c + 8 g4 .. +7: half g4 % 2 of chunk 2 c + g4 / 2.
+      return *reinterpret_cast<const uint2*>(kt + tok * CROWB + (((2 * c + (g4 >> 1)) ^ kswz8(tok)) << 4) +
+                                             (g4 & 1) * 8);
+    else
+      return *reinterpret_cast<const uint4*>(kt + tok * ROWB + (((4 * c + g4) ^ kswz<ROWB>(tok)) << 4));
+  };
+  // The first token tile's K operands are read right after the step's
+  // barrier, before the page loads are issued, so that their LDS round trip
+  // overlaps that scalar work (the E4M3 kernels at D = 64 read K from the
+  // widened tile, after the widening).  Measured against no such reads: the
+  // chunk-only prefill batch 158 -> 147 us (bf16) and 198 -> 184 us (E4M3),
+  // the 70B verification shape 87.4 -> 81.8 us (E4M3) and 101.8 -> 100.4 us
+  // (bf16); two of the four operands gave about half of that.
+  constexpr int KPRE = kFp8 && !kKRaw ? 0 : NC;
+  auto compute_step = [&](int st, const unsigned char* kt, const unsigned char* vt, auto full_tag,
+                          const KRead* kpre) __attribute__((always_inline)) {
     constexpr bool kFull = decltype(full_tag)::value;
     const int t_base = tok0 + st * STEP;
     // S^T for the step's 16-token tiles; each K operand read feeds the NCT
@@ -498,18 +550,14 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
     for (int tt = 0; tt < NTT; ++tt) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) sc[ct][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const int tok = 16 * tt + l16;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
+        const KRead kr = tt == 0 && c < KPRE ? kpre[c] : read_k(kt, tt, c);
         uint4 ka;
-        if constexpr (kKRaw) {
-          // Codes of columns 32 c + 8 g4 .. +7: half g4 % 2 of chunk 2 c + g4 / 2.
-          const uint2 w = *reinterpret_cast<const uint2*>(
-              kt + tok * CROWB + (((2 * c + (g4 >> 1)) ^ kswz8(tok)) << 4) + (g4 & 1) * 8);
-          ka = fp8x8_to_bf16x8(w.x, w.y);
-        } else {
-          ka = *reinterpret_cast<const uint4*>(kt + tok * ROWB + (((4 * c + g4) ^ kswz<ROWB>(tok)) << 4));
-        }
+        if constexpr (kKRaw)
+          ka = fp8x8_to_bf16x8(kr.x, kr.y);
+        else
+          ka = kr;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
           sc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qb[ct][c],
@@ -618,16 +666,21 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
       else
         vm_wait<0>();
       block_barrier();
-      if (st + kAhead < nsteps) dma_step(st + kAhead, (S + NSTAGE - 1) % NSTAGE);
       const unsigned char* kt = ring + S * 2 * RTILEB;
       const unsigned char* vt = kt + RTILEB;
+      KRead kpre[KPRE > 0 ? KPRE : 1];
+      if (wave_rows) {
+#pragma unroll
+        for (int c = 0; c < KPRE; ++c) kpre[c] = read_k(kt, 0, c);
+      }
+      if (st + kAhead < nsteps) dma_step(st + kAhead, (S + NSTAGE - 1) % NSTAGE);
       if constexpr (kFp8) {
         widen_step(S);
         block_barrier();
         if constexpr (!kKRaw) kt = wide;
         vt = wide_v;
       }
-      if (wave_rows) compute_step(st, kt, vt, full_tag);
+      if (wave_rows) compute_step(st, kt, vt, full_tag, kpre);
       if (st + kAhead + 1 < nsteps) read_ids(st + kAhead + 1);
     };
     // Steps st0 .. st1 - 1, st0 a multiple of NSTAGE: whole ring rounds.
@@ -648,7 +701,7 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
     run_steps(0, nfull, std::true_type{});
     run_steps(nfull, nsteps, std::false_type{});
   }
-  const bool bad = b.bad || ids_bad;
+  const bool bad = b.bad || id_max > id_last;
 
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
@@ -1230,10 +1283,13 @@ hipError_t launch_t(const MultiQueryLaunch& a, MultiQueryParams p) {
     // twice the tokens, in a 48 KiB ring.  Measured on the 70B verification
     // shape (6 queries): 32 sequences 89.9 against 95.4 us, 8 sequences 40.1
     // against 41.2, 64 sequences 169.9 against 173.6.
-    if (a.max_row_blocks == 1 && sizeof(TC) == 1)
-      hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G, 2, 1, 2 * kStepTokens>), grid, dim3(kMqWaves * 64), 0,
-                         a.stream, p);
-    else if (a.max_row_blocks == 1)
+    if constexpr (sizeof(TC) == 1) {
+      if (a.max_row_blocks == 1)
+        hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G, 2, 1, 2 * kStepTokens>), grid, dim3(kMqWaves * 64), 0,
+                           a.stream, p);
+      else
+        hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G, 3, 1>), grid, dim3(kMqWaves * 64), 0, a.stream, p);
+    } else if (a.max_row_blocks == 1)
       hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G, 2, 1>), grid, dim3(kMqWaves * 64), 0, a.stream, p);
     else
       hipLaunchKernelGGL((multi_query_kernel<TC, D, BS, G, 3, 1>), grid, dim3(kMqWaves * 64), 0, a.stream, p);
