@@ -452,8 +452,11 @@ size_t pa_multi_query_workspace_size(int num_seqs, int num_query_tokens, int num
  * Preconditions (device values): query_start ranges inside [0, num_query_tokens],
  * non-decreasing, n <= max_query_len (a sequence breaking these is skipped and
  * its rows are left unwritten; overlapping ranges give unspecified rows);
- * n <= L <= max_context_len and table entries in [0, num_blocks) (rows of a
- * sequence breaking these are NaN).  Rows of no sequence are left unwritten.
+ * n <= L <= max_context_len (all rows of a sequence breaking these are NaN)
+ * and table entries in [0, num_blocks) for the pages of the context (a bad
+ * entry makes NaN every row that attends to its page, and possibly other rows
+ * of the same sequence: those that share the bad row's block of 64 or 128
+ * rows).  Rows of no sequence are left unwritten.
  */
 int pa_multi_query(void* out, const void* q,
                    const void* k_cache, const void* v_cache,

@@ -169,12 +169,17 @@ def test_chunking_matches_one_pass():
     assert_close(as_f64(whole), ref, "bf16", "whole")
 
 
-def test_bad_device_values():
-    x = shape_case(32, 8, 128, 16)
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_bad_device_values(kv):
+    """Page ids past the pool and negative ones (ring kernel; for E4M3 the
+    24-row sequence runs on the streaming kernel), too few tokens, invalid
+    query ranges."""
+    x = shape_case(32, 8, 128, 16, kv=kv)
     t = on_device(x)
     t["query_start"] = x.query_start.to("cuda").clone()
     qs = x.query_start.tolist()
-    t["block_tables"][1, 3] = x.plan.num_blocks + 7   # bad page id: sequence 1's rows NaN
+    t["block_tables"][1, 3] = x.plan.num_blocks + 7   # page id past the pool: sequence 1's rows NaN
+    t["block_tables"][2, 0] = -5                      # negative id of a page every row reads: NaN
     t["context_lens"][4] = 99                         # 100 queries > 99 tokens: rows NaN
     sentinel = torch.full_like(t["q"], 7.0)
     t["query_start"][7] = qs[7] + 1000                # sequences 6 and 7: invalid ranges, unwritten
@@ -182,11 +187,11 @@ def test_bad_device_values():
     o = out.float()
     ref, _, _ = oracle_mq_step(x)
     rows = lambda s: list(range(qs[s], qs[s + 1]))
-    for s in (1, 4):
+    for s in (1, 2, 4):
         assert torch.isnan(o[rows(s)]).all(), s
     for s in (6, 7):
         assert (o[rows(s)] == 7.0).all(), s
-    keep = rows(0) + rows(2) + rows(3)
+    keep = rows(0) + rows(3)
     assert_close(as_f64(out)[keep], ref[keep], "bf16", "rows keeping the preconditions")
 
 
