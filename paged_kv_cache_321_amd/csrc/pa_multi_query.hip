@@ -610,10 +610,13 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
       for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+          // Masked steps take the same product as unmasked ones for the
+          // tokens they keep, so which loop runs a step never changes a bit.
+          const float e = fast_exp2(fmaf(sc[ct][tt][j], p.scale_log2e, -m_run[ct]));
           if constexpr (kFull)
-            sv[tt][j] = fast_exp2(fmaf(sc[ct][tt][j], p.scale_log2e, -m_run[ct]));
+            sv[tt][j] = e;
           else
-            sv[tt][j] = fast_exp2(sv[tt][j] - m_run[ct]);
+            sv[tt][j] = sv[tt][j] == -__builtin_inff() ? 0.f : e;
         }
       // The running sum adds the weights as rounded to bf16 for the product.
 #pragma unroll
