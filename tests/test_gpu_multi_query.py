@@ -270,18 +270,22 @@ def test_side_stream_same_bits_and_ordered(own_handle):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
-def test_fixed_partitions_batch_invariant(kv):
+@pytest.mark.parametrize("pt", [256, 160])
+def test_fixed_partitions_batch_invariant(kv, pt):
     """With partition_tokens fixed, a sequence's rows are the same bits alone as
     in a batch (the default partition size follows the batch shape, so this is
     the caller's way to batch-invariant rows).  Over an E4M3 cache the 24-,
     20- and 12-row sequences stream (two tiles in the batch, the 12-row one
-    one tile alone) beside the 120-row one on the ring."""
+    one tile alone) beside the 120-row one on the ring.  In the batch the
+    other sequences run on the three-stage ring, alone on the two-stage one,
+    which split a partition of 8 (or 5) steps differently between unmasked and
+    masked steps."""
     spec = wl.Spec(f"mqinv{kv}", 32, 8, 128, 16, "bf16", seed=91,
                    kv_dtype=None if kv == "bf16" else kv, **wl.fp8_scales(kv))
     plan = wl.multi_query_plan([900, 2500, 40, 1300, 700], [6, 5, 1, 30, 3], 16,
                                torch.Generator().manual_seed(4))
     x = wl.build_inputs(spec, plan)
-    whole, t = gpu_mq_step(x, partition_tokens=256)
+    whole, t = gpu_mq_step(x, partition_tokens=pt)
     ref, _, _ = oracle_mq_step(x)
     assert_close(as_f64(whole), ref, "bf16", spec.name)
     qs = x.query_start.tolist()
@@ -292,7 +296,7 @@ def test_fixed_partitions_batch_invariant(kv):
         binding.pa_multi_query(alone, q, t["k_cache"], t["v_cache"], t["block_tables"][s:s + 1].contiguous(),
                                t["context_lens"][s:s + 1].contiguous(),
                                torch.tensor([0, qs[s + 1] - qs[s]], dtype=torch.int32, device="cuda"),
-                               x.scale, x.max_context_len, qs[s + 1] - qs[s], partition_tokens=256,
+                               x.scale, x.max_context_len, qs[s + 1] - qs[s], partition_tokens=pt,
                                k_scale=x.k_scale, v_scale=x.v_scale)
         torch.cuda.synchronize()
         assert np.array_equal(bits(alone), bits(whole[rows])), s
