@@ -46,6 +46,20 @@ __device__ __forceinline__ void buffer_load_lds16(uint32_t voffset, i32x4_t rsrc
                  :: "v"(voffset), "s"(rsrc), "{m0}"(lds_base) : "memory");
 }
 
+// The same with a wave-uniform byte offset in the scalar offset operand:
+// lanes read base + soffset + voffset, and soffset + voffset is what the
+// range check compares with the record count (checked on the hardware: with
+// a one-page record count every lane past the first page read zeros).
+template <bool kNonTemporal>
+__device__ __forceinline__ void buffer_load_lds16(uint32_t voffset, i32x4_t rsrc, uint32_t soffset, uint32_t lds_base) {
+  if constexpr (kNonTemporal)
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen nt lds"
+                 :: "v"(voffset), "s"(rsrc), "s"(soffset), "{m0}"(lds_base) : "memory");
+  else
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :: "v"(voffset), "s"(rsrc), "s"(soffset), "{m0}"(lds_base) : "memory");
+}
+
 // LDS byte address of a pointer into __shared__ memory, made wave-uniform.
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return __builtin_amdgcn_readfirstlane(

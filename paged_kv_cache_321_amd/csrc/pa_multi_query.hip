@@ -438,6 +438,17 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
   // when a page takes at least one load per wave, else a page that also
   // depends on the wave (wave_page for u = 0).
   const int wave_page = wave * 64 / (CCH * BS);
+  // A cache of less than 4 GiB is one descriptor per cache for the whole
+  // walk, its record count the bytes from this kv head's first page to the
+  // cache's end: a whole page is reached through the load's scalar offset
+  // (which the range check counts too).  Pages of a partition's last step,
+  // whose rows past the partition must read as zeros, and larger caches take
+  // a descriptor per page.
+  const uint64_t pool_bytes = static_cast<uint64_t>(static_cast<uint32_t>(p.num_blocks)) * page_bytes;
+  const bool small_pool = pool_bytes < (1ull << 32);
+  const uint32_t pool_records = static_cast<uint32_t>(pool_bytes) - static_cast<uint32_t>(kvh * BS * CROWB);
+  const i32x4_t kpool = raw_buffer(kc, pool_records);
+  const i32x4_t vpool = raw_buffer(vc, pool_records);
   auto dma_step = [&](int st, int stage) __attribute__((always_inline)) {
     uint32_t id[PPS];
 #pragma unroll
@@ -449,6 +460,42 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
     // Tokens of the partition from this step on: every page of the step is
     // whole unless this is its last step.
     const int rem = tok1 - tok0 - st * STEP;
+    if (small_pool && rem >= STEP) {
+      uint32_t soff[PER_T], kdst[PER_T];
+#pragma unroll
+      for (int u = 0; u < PER_T; ++u) {
+        const int slot0 = (u * kMqWaves + wave) * 64;
+        if (slot0 >= CHUNKS) continue;
+        uint32_t pid;
+        if constexpr (CCH * BS >= kMqWaves * 64) {
+          pid = id[u * kMqWaves * 64 / (CCH * BS)];
+        } else {
+          const int q = u * (kMqWaves * 64 / (CCH * BS)) + wave_page;
+          pid = id[0];
+#pragma unroll
+          for (int r = 1; r < PPS; ++r)
+            if (q == r) pid = id[r];
+        }
+        soff[u] = pid * page_bytes;
+        kdst[u] = ring_lds + stage * 2 * RTILEB + slot0 * 16;
+      }
+      if (stream_pages) {
+#pragma unroll
+        for (int u = 0; u < PER_T; ++u) {
+          if ((u * kMqWaves + wave) * 64 >= CHUNKS) continue;
+          buffer_load_lds16<true>(koff[u], kpool, soff[u], kdst[u]);
+          buffer_load_lds16<true>(voff[u], vpool, soff[u], kdst[u] + RTILEB);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < PER_T; ++u) {
+          if ((u * kMqWaves + wave) * 64 >= CHUNKS) continue;
+          buffer_load_lds16<false>(koff[u], kpool, soff[u], kdst[u]);
+          buffer_load_lds16<false>(voff[u], vpool, soff[u], kdst[u] + RTILEB);
+        }
+      }
+      return;
+    }
     i32x4_t kr[PER_T], vr[PER_T];
     uint32_t kdst[PER_T];
 #pragma unroll
