@@ -1365,7 +1365,12 @@ hipError_t launch_t(const MultiQueryLaunch& a, MultiQueryParams p) {
       if (e != hipSuccess) return e;
     }
   }
-  if (a.max_parts <= 1) return hipSuccess;
+  // Only sequences of at most one 64-row block are cut into partitions; the
+  // shortest sequence has at least num_query_tokens - (num_seqs - 1) *
+  // max_query_len queries, so a batch of long chunks alone has nothing to
+  // merge and launches no merge kernel.
+  const int64_t min_queries = (int64_t)a.num_query_tokens - (int64_t)(a.num_seqs - 1) * a.max_query_len;
+  if (a.max_parts <= 1 || min_queries * G > kRowsPerBlock) return hipSuccess;
   // Verification batches (every sequence one block) merge on the 16-wave
   // kernel, whose loads go out in one round trip (70B verification shape:
   // 4.7 us against 8.3); other batches, where most workgroups exit at once,

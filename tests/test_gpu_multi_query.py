@@ -41,6 +41,19 @@ def test_workload_small(name, pt):
     check_mq(x, partition_tokens=pt)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("pt", [0, 64])
+@pytest.mark.parametrize("chunks", [[(300, 200), (0, 180), (64, 150)], [(0, 97), (10, 90)]])
+def test_chunks_only(kv, pt, chunks):
+    """Batches of long chunks alone (every sequence more than one 64-row
+    block; the shortest provably so from the batch's query count and longest
+    query, so no merge is launched): 128-row blocks on the two-tile ring, and
+    two 64-row blocks per sequence on the one-tile ring."""
+    name = "chunked13b" if kv == "bf16" else "chunked13b_fp8"
+    x = wl.make_inputs(name, chunks=chunks, num_decodes=0)
+    check_mq(x, partition_tokens=pt, tiles_only=True)
+
+
 def shape_case(h, hkv, d, bs, kv="bf16", seed=0):
     """Query lengths 1, 6, 17, 64/G+1 (two row blocks), 100 and 0, over
     contexts with and without history, ragged last pages."""
