@@ -218,6 +218,21 @@ __device__ __forceinline__ float column_max(float x) {
   return max_of(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// The column maxima of two MFMA results at once: the first half swap leaves
+// a's four-lane groups merged in lanes 0-31 and b's in lanes 32-63, so one
+// row swap finishes both, and a last half swap hands each its maxima in all
+// lanes (three swaps and two maxima for the two, against two swaps and two
+// maxima for each alone).
+__device__ __forceinline__ void column_max2(float& a, float& b) {
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  float x = max_of(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = max_of(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto g = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(g[0]);
+  b = __uint_as_float(g[1]);
+}
+
 // Bytes of the ring kernel's LDS: STAGES (K, V) stages of one step as stored
 // in the cache, plus for E4M3 the widened bf16 tile(s) (V only at D = 128,
 // where the QK product widens K in registers).
@@ -621,31 +636,41 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
     // P^T of tile ct as the B operand, two 16-token tiles per product: k slot
     // j of lane group g4 is token 32 h + 4 g4 + j (j < 4) or 32 h + 16 + 4 g4
     // + j - 4.
+    // Each lane's maxima first, then the column maxima of all tiles (both
+    // tiles' cross-lane steps together).
     uint4 pbits[NCT][NTT / 2];
+    float sv[NCT][NTT][4];
+    float mxs[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      float sv[NTT][4];
-      float mx;
       if constexpr (kFull) {
         float raw = sc[ct][0][0];
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
           for (int j = 0; j < 4; ++j) raw = fmaxf(raw, sc[ct][tt][j]);
-        mx = max_of(m_run[ct], column_max(raw) * p.scale_log2e);
+        mxs[ct] = raw;
       } else {
-        mx = m_run[ct];
+        float mx = m_run[ct];
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int t = t_base + 16 * tt + 4 * g4 + j;
             const bool valid = t < tok1 && t <= last_seen[ct];
-            sv[tt][j] = valid ? sc[ct][tt][j] * p.scale_log2e : -__builtin_inff();
-            mx = fmaxf(mx, sv[tt][j]);
+            sv[ct][tt][j] = valid ? sc[ct][tt][j] * p.scale_log2e : -__builtin_inff();
+            mx = fmaxf(mx, sv[ct][tt][j]);
           }
-        mx = column_max(mx);
+        mxs[ct] = mx;
       }
+    }
+    if constexpr (NCT == 2)
+      column_max2(mxs[0], mxs[1]);
+    else
+      mxs[0] = column_max(mxs[0]);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float mx = kFull ? max_of(m_run[ct], mxs[ct] * p.scale_log2e) : mxs[ct];
       if (__any(mx > m_run[ct] + kRescaleLog2)) {
         const float alpha = fast_exp2(m_run[ct] - mx);
         m_run[ct] = mx;
@@ -661,18 +686,18 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
           // tokens they keep, so which loop runs a step never changes a bit.
           const float e = fast_exp2(fmaf(sc[ct][tt][j], p.scale_log2e, -m_run[ct]));
           if constexpr (kFull)
-            sv[tt][j] = e;
+            sv[ct][tt][j] = e;
           else
-            sv[tt][j] = sv[tt][j] == -__builtin_inff() ? 0.f : e;
+            sv[ct][tt][j] = sv[ct][tt][j] == -__builtin_inff() ? 0.f : e;
         }
       // The running sum adds the weights as rounded to bf16 for the product.
 #pragma unroll
       for (int h = 0; h < NTT / 2; ++h) {
         uint4& pb = pbits[ct][h];
-        pb.x = pack_bf16x2(sv[2 * h][0], sv[2 * h][1]);
-        pb.y = pack_bf16x2(sv[2 * h][2], sv[2 * h][3]);
-        pb.z = pack_bf16x2(sv[2 * h + 1][0], sv[2 * h + 1][1]);
-        pb.w = pack_bf16x2(sv[2 * h + 1][2], sv[2 * h + 1][3]);
+        pb.x = pack_bf16x2(sv[ct][2 * h][0], sv[ct][2 * h][1]);
+        pb.y = pack_bf16x2(sv[ct][2 * h][2], sv[ct][2 * h][3]);
+        pb.z = pack_bf16x2(sv[ct][2 * h + 1][0], sv[ct][2 * h + 1][1]);
+        pb.w = pack_bf16x2(sv[ct][2 * h + 1][2], sv[ct][2 * h + 1][3]);
         l_run[ct] = bf16x2_acc(pb.w, bf16x2_acc(pb.z, bf16x2_acc(pb.y, bf16x2_acc(pb.x, l_run[ct]))));
       }
     }
