@@ -243,6 +243,30 @@ constexpr int ring_lds_bytes() {
   return STAGES * 2 * raw_tile + (sizeof(TC) == 1 ? (D == 128 ? 1 : 2) * bf16_tile : 0);
 }
 
+// bf16 V stages of the ring: each 1 KiB holds R = 1024 / ROWB consecutive
+// tokens chunk-major, 16-byte chunk c of the block's token r at slot c R + r.
+// The 4 consecutive tokens that a 16-lane transposed read takes at one column
+// then sit in 64 contiguous bytes (distinct banks), and the read's column
+// offset is an immediate (16 R bytes per chunk), where the row-major layout
+// needs a swizzle that depends on both the token and the column.
+template <int ROWB>
+__device__ __forceinline__ int vslot_cm(int tok, int ch) {
+  constexpr int R = 1024 / ROWB;
+  return (tok / R) * 1024 + (ch * R + tok % R) * 16;
+}
+
+// Four k slots of the V^T A operand from a chunk-major V stage: lane l16
+// receives column d0 + l16 of tokens tb .. tb + 3 (tb a multiple of 4, d0 of
+// 16), as vt4 does for the row-major layout.
+template <int ROWB>
+__device__ __forceinline__ s16x4_t vt4_cm(const unsigned char* tile, int l16, int tb, int d0) {
+  constexpr int R = 1024 / ROWB;
+  const int t = tb + (l16 >> 2);
+  const int lane_off = (t / R) * 1024 + (((l16 & 3) >> 1) * R + t % R) * 16 + ((l16 & 1) << 3);
+  const unsigned char* a = tile + lane_off + (d0 >> 3) * R * 16;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)a);
+}
+
 // NCT: 16-row tiles per wave (1: 64-row blocks, 2: 128-row blocks, and the
 // 64-row ones too when it is the batch's only ring launch); the kernel serves
 // only the sequences whose blocks it takes.  STEP: tokens staged per step (32
@@ -376,8 +400,9 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
 
   // Stage i: K tile at ring + 2 i RTILEB, V tile right after it.  In the
   // tiles the matrix cores read (the stages for bf16, the widened tile for
-  // E4M3), K rows hold 16-byte chunk ch at position ch ^ kswz<ROWB>(token)
-  // and V rows are in the transposed-read layout (position
+  // E4M3), K rows hold 16-byte chunk ch at position ch ^ kswz<ROWB>(token);
+  // V is chunk-major per 1 KiB (vslot_cm) in the bf16 stages, and in the
+  // widened E4M3 tile rows are in the transposed-read layout (position
   // ch ^ swz<ROWB>(token)).
   __shared__ __attribute__((aligned(16))) unsigned char ring[LDS_BYTES];
   unsigned char* const wide = ring + NSTAGE * 2 * RTILEB;  // E4M3: the widened tile(s)
@@ -437,7 +462,10 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
       koff[u] = voff[u] = (row % BS) * CROWB + pos * 16;
     } else {
       koff[u] = (row % BS) * CROWB + ((pos ^ kswz<ROWB>(row)) << 4);
-      voff[u] = (row % BS) * CROWB + ((pos ^ swz<ROWB>(row)) << 4);
+      // V slot `slot` holds chunk lane / R of token (slot / 64) R + lane % R.
+      constexpr int R = 1024 / ROWB;
+      const int vrow = (slot / 64) * R + lane % R;
+      voff[u] = (vrow % BS) * CROWB + (lane / R) * 16;
     }
   }
   constexpr int kLoadsPerStep = 2 * PER_T;  // per wave that loads (all, but for E4M3 at D = 64)
@@ -706,8 +734,14 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
     for (int h = 0; h < NTT / 2; ++h) {
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        const s16x4_t lo = vt4<ROWB>(vt, l16, 32 * h + 4 * g4, 16 * m);
-        const s16x4_t hi = vt4<ROWB>(vt, l16, 32 * h + 16 + 4 * g4, 16 * m);
+        s16x4_t lo, hi;
+        if constexpr (kFp8) {
+          lo = vt4<ROWB>(vt, l16, 32 * h + 4 * g4, 16 * m);
+          hi = vt4<ROWB>(vt, l16, 32 * h + 16 + 4 * g4, 16 * m);
+        } else {
+          lo = vt4_cm<ROWB>(vt, l16, 32 * h + 4 * g4, 16 * m);
+          hi = vt4_cm<ROWB>(vt, l16, 32 * h + 16 + 4 * g4, 16 * m);
+        }
         const s16x8_t va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
