@@ -243,7 +243,7 @@ constexpr int ring_lds_bytes() {
   return STAGES * 2 * raw_tile + (sizeof(TC) == 1 ? (D == 128 ? 1 : 2) * bf16_tile : 0);
 }
 
-// bf16 V stages of the ring: each 1 KiB holds R = 1024 / ROWB consecutive
+// V tiles of the ring: each 1 KiB holds R = 1024 / ROWB consecutive
 // tokens chunk-major, 16-byte chunk c of the block's token r at slot c R + r.
 // The 4 consecutive tokens that a 16-lane transposed read takes at one column
 // then sit in 64 contiguous bytes (distinct banks), and the read's column
@@ -401,9 +401,8 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
   // Stage i: K tile at ring + 2 i RTILEB, V tile right after it.  In the
   // tiles the matrix cores read (the stages for bf16, the widened tile for
   // E4M3), K rows hold 16-byte chunk ch at position ch ^ kswz<ROWB>(token);
-  // V is chunk-major per 1 KiB (vslot_cm) in the bf16 stages, and in the
-  // widened E4M3 tile rows are in the transposed-read layout (position
-  // ch ^ swz<ROWB>(token)).
+  // V is chunk-major per 1 KiB (vslot_cm): the bf16 stages and the widened
+  // E4M3 tile, and the E4M3 codes as stored.
   __shared__ __attribute__((aligned(16))) unsigned char ring[LDS_BYTES];
   unsigned char* const wide = ring + NSTAGE * 2 * RTILEB;  // E4M3: the widened tile(s)
   unsigned char* const wide_v = wide + (kKRaw ? 0 : TILEB);  // E4M3: the widened V tile
@@ -453,19 +452,19 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
     const int slot = (u * kMqWaves + wave) * 64 + lane;
     const int row = slot / CCH;
     const int pos = slot % CCH;
+    // V, as stored (E4M3 codes) or as read (bf16): chunk-major per 1 KiB,
+    // slot `slot` holding chunk lane / R of token (slot / 64) R + lane % R.
+    constexpr int R = 1024 / CROWB;
+    const int vrow = (slot / 64) * R + lane % R;
+    voff[u] = (vrow % BS) * CROWB + (lane / R) * 16;
     if constexpr (kKRaw) {
       // K codes: 16-byte chunk ch of token `row` at position ch ^ kswz8(row),
       // so the 16 tokens of an 8-byte operand read hit distinct banks.
       koff[u] = (row % BS) * CROWB + ((pos ^ kswz8(row)) << 4);
-      voff[u] = (row % BS) * CROWB + pos * 16;
     } else if constexpr (kFp8) {
-      koff[u] = voff[u] = (row % BS) * CROWB + pos * 16;
+      koff[u] = (row % BS) * CROWB + pos * 16;
     } else {
       koff[u] = (row % BS) * CROWB + ((pos ^ kswz<ROWB>(row)) << 4);
-      // V slot `slot` holds chunk lane / R of token (slot / 64) R + lane % R.
-      constexpr int R = 1024 / ROWB;
-      const int vrow = (slot / 64) * R + lane % R;
-      voff[u] = (vrow % BS) * CROWB + (lane / R) * 16;
     }
   }
   constexpr int kLoadsPerStep = 2 * PER_T;  // per wave that loads (all, but for E4M3 at D = 64)
@@ -593,16 +592,23 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
     for (int u = 0; u < PER_T; ++u) {
       const int c = tid + u * kMqWaves * 64;
       if (c >= CHUNKS) continue;
-      const int tok = c / CCH;
-      const int ch = c % CCH;
       if constexpr (!kKRaw) {
+        const int tok = c / CCH;
+        const int ch = c % CCH;
         const uint4 kw = *reinterpret_cast<const uint4*>(kq + c * 16);
         *reinterpret_cast<uint4*>(kt + tok * ROWB + (((2 * ch) ^ kswz<ROWB>(tok)) << 4)) = fp8x8_to_bf16x8(kw.x, kw.y);
         *reinterpret_cast<uint4*>(kt + tok * ROWB + (((2 * ch + 1) ^ kswz<ROWB>(tok)) << 4)) = fp8x8_to_bf16x8(kw.z, kw.w);
       }
-      const uint4 vw = *reinterpret_cast<const uint4*>(vq + c * 16);
-      *reinterpret_cast<uint4*>(vt + tok * ROWB + (((2 * ch) ^ swz<ROWB>(tok)) << 4)) = fp8x8_to_bf16x8(vw.x, vw.y);
-      *reinterpret_cast<uint4*>(vt + tok * ROWB + (((2 * ch + 1) ^ swz<ROWB>(tok)) << 4)) = fp8x8_to_bf16x8(vw.z, vw.w);
+      // V: consecutive threads take RW consecutive tokens of one code chunk,
+      // then of the next, so that both the code reads and the widened
+      // chunk-major stores of each 8 lanes fill distinct banks.
+      constexpr int RW = 1024 / ROWB;   // widened tokens per KiB
+      constexpr int RC = 1024 / CROWB;  // code tokens per KiB
+      const int tok = c / (RW * CCH) * RW + c % RW;
+      const int ch = c / RW % CCH;
+      const uint4 vw = *reinterpret_cast<const uint4*>(vq + (tok / RC) * 1024 + (ch * RC + tok % RC) * 16);
+      *reinterpret_cast<uint4*>(vt + vslot_cm<ROWB>(tok, 2 * ch)) = fp8x8_to_bf16x8(vw.x, vw.y);
+      *reinterpret_cast<uint4*>(vt + vslot_cm<ROWB>(tok, 2 * ch + 1)) = fp8x8_to_bf16x8(vw.z, vw.w);
     }
   };
 
@@ -734,14 +740,8 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(N
     for (int h = 0; h < NTT / 2; ++h) {
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        s16x4_t lo, hi;
-        if constexpr (kFp8) {
-          lo = vt4<ROWB>(vt, l16, 32 * h + 4 * g4, 16 * m);
-          hi = vt4<ROWB>(vt, l16, 32 * h + 16 + 4 * g4, 16 * m);
-        } else {
-          lo = vt4_cm<ROWB>(vt, l16, 32 * h + 4 * g4, 16 * m);
-          hi = vt4_cm<ROWB>(vt, l16, 32 * h + 16 + 4 * g4, 16 * m);
-        }
+        const s16x4_t lo = vt4_cm<ROWB>(vt, l16, 32 * h + 4 * g4, 16 * m);
+        const s16x4_t hi = vt4_cm<ROWB>(vt, l16, 32 * h + 16 + 4 * g4, 16 * m);
         const s16x8_t va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
