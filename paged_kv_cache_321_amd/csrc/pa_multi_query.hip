@@ -272,10 +272,9 @@ __device__ __forceinline__ s16x4_t vt4_cm(const unsigned char* tile, int l16, in
 // only the sequences whose blocks it takes.  STEP: tokens staged per step (32
 // or 64).
 // Register targets: four waves per SIMD for one tile (the 64-token E4M3
-// kernel needs more than 128 registers and runs at two waves; held to three it
-// measured no faster), three for two tiles.  The two-tile E4M3 kernel, asked for two, took
-// 180 registers; at three it takes 168 with a few values spilled outside the
-// step loops (chunk-only prefill batch over E4M3: 230 -> 199 us).
+// kernel needs more than 128 registers and settles at three), three for two
+// tiles.  The two-tile E4M3 kernel, asked for two, took 180 registers; at
+// three it fits in 168 (chunk-only prefill batch over E4M3: 230 -> 199 us).
 template <typename TC, int D, int BS, int G, int STAGES, int NCT, int STEP = kStepTokens>
 __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(NCT == 1 ? 4 : 3))) void multi_query_kernel(MultiQueryParams p) {
   constexpr bool kFp8 = sizeof(TC) == 1;
