@@ -623,7 +623,7 @@ def baseline_summary(head, others):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: measured on one GPU only (asked for --gpus {args.gpus}); "
               "the decode path needs no collective and is measured at N=1.", file=sys.stderr)
         sys.exit(2)
     import torch
