@@ -349,6 +349,40 @@ def test_work_list_and_in_kernel_lookup_agree(kv):
     assert np.array_equal(bits(part), bits(whole.index_select(0, rows)))
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("n", [40, 80])
+def test_every_work_item_runs(kv, n):
+    """Work items are listed in two classes (full partitions and row blocks
+    first, then each cut sequence's last partition): with the workspace filled
+    with NaN before the call, every partition result the merge reads must have
+    been written by this call.  40 sequences find their items in the kernel,
+    80 take them from the schedule kernel; contexts of 8-1200 tokens in
+    partitions of 128 (1-10 per sequence) and some long chunks."""
+    spec = wl.Spec(f"mqitems{kv}", 32, 8, 128, 16, "bf16", seed=95,
+                   kv_dtype=None if kv == "bf16" else kv, **wl.fp8_scales(kv))
+    g = torch.Generator().manual_seed(12)
+    ctx = torch.randint(8, 1200, (n,), generator=g).tolist()
+    qlen = [min(c, q) for c, q in zip(ctx, torch.randint(1, 7, (n,), generator=g).tolist())]
+    qlen[3] = min(ctx[3], 40)  # 320 rows: three 128-row blocks
+    x = wl.build_inputs(spec, wl.multi_query_plan(ctx, qlen, 16, g))
+    t = on_device(x)
+    t["query_start"] = x.query_start.to("cuda").clone()
+    binding.pa_reshape_and_cache(t["key"], t["value"], t["k_cache"], t["v_cache"], t["slot_mapping"],
+                                 k_scale=x.k_scale, v_scale=x.v_scale)
+    ccode = binding.PA_FP8_E4M3 if kv == "fp8" else binding.PA_BF16
+    nbytes = binding.pa_multi_query_workspace_size(n, int(x.query_start[-1]), spec.num_heads, spec.num_kv_heads,
+                                                   spec.head_dim, 16, x.max_context_len, binding.PA_BF16, 128,
+                                                   ccode)
+    ws = torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device="cuda")  # float NaN everywhere
+    out = torch.empty_like(t["q"])
+    binding.pa_multi_query(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                           t["query_start"], x.scale, x.max_context_len, max(qlen), partition_tokens=128,
+                           workspace=ws, k_scale=x.k_scale, v_scale=x.v_scale)
+    torch.cuda.synchronize()
+    ref, _, _ = oracle_mq_step(x)
+    assert_close(as_f64(out), ref, "bf16", spec.name)
+
+
 @pytest.mark.parametrize("h,hkv,bs,kv", [(40, 40, 16, "bf16"), (64, 8, 32, "bf16"), (64, 8, 32, "fp8")])
 def test_pool_past_2g_elements(h, hkv, bs, kv):
     """Every page of the batch lies past 2^31 elements of a 2.29e9-element
