@@ -145,10 +145,15 @@ __device__ __forceinline__ MqBlock mq_block(const MultiQueryParams& p, int s, in
 }
 
 // Work item `item` of the list multi_query_schedule_kernel writes (the same
-// items in the same order), found by the workgroup itself when the batch has
-// at most 64 sequences: wave 0 counts the items of sequence `lane`, scans the
-// counts, and the lane whose range holds `item` publishes it through LDS.
-// Every thread of the workgroup calls it; false: no such item.
+// items; the second class longest first), found by the workgroup itself when
+// the batch has at most 64 sequences: wave 0 counts the items of sequence
+// `lane`, scans the counts, and the lane whose range holds `item` publishes it
+// through LDS.  Every thread of the workgroup calls it; false: no such item.
+// Measured against both classes in sequence order on the 70B-shaped
+// verification batch: E4M3 32 sequences 78.9 -> 69.9 us, 64 sequences 151.5
+// -> 142.7, 16 sequences 45.6 -> 44.3, 4 queries 73.5 -> 68.4; bf16 32
+// sequences 101.5 -> 99.1, 64 sequences 230.9 -> 197.4.  (Ranking the lengths
+// with a 64-step loop over the lanes instead cost 2-5 us per call.)
 template <int G>
 __device__ __forceinline__ bool find_item(const MultiQueryParams& p, int item, int2* w) {
   __shared__ int2 found;
@@ -156,33 +161,49 @@ __device__ __forceinline__ bool find_item(const MultiQueryParams& p, int item, i
     const int lane = threadIdx.x;
     int n = 0;
     bool single = false;
+    int rest = 0;  // tokens of the last partition of a cut sequence
     if (lane < p.num_seqs) {
       const MqBlock b = mq_block<G>(p, lane, 0);
       if (!b.skip) {
         single = b.nrb == 1;
         n = single ? b.nparts : b.nrb;
+        if (single && n > 1) rest = b.kv_end - (n - 1) * p.partition_tokens;
       }
     }
     // The list's two classes: n0 items of sequence `lane` in the first, and
     // its last partition, when it is cut, in the second.
-    const int last = single && n > 1 ? 1 : 0;
-    const int n0 = n - last;
-    int incl0 = n0, incl1 = last;
+    const bool last = single && n > 1;
+    const int n0 = n - (last ? 1 : 0);
+    int incl0 = n0;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int v0 = __shfl_up(incl0, off);
-      const int v1 = __shfl_up(incl1, off);
-      if (lane >= off) {
-        incl0 += v0;
-        incl1 += v1;
-      }
+      if (lane >= off) incl0 += v0;
     }
     const int start0 = incl0 - n0;
-    const int start1 = __shfl(incl0, 63) + incl1 - last;
+    const int total0 = __shfl(incl0, 63);
     if (lane == 0) found = make_int2(-1, 0);
     if (n0 > 0 && item >= start0 && item < start0 + n0)
       found = make_int2(lane, single ? item - start0 : pack_row_block(item - start0));
-    if (last && item == start1) found = make_int2(lane, n - 1);
+    // Second class, longest first (equal lengths: lower sequence first): the
+    // item's rank r is selected bit by bit from the top with wave-uniform
+    // ballots, keeping the lanes whose length agrees with the selected bits.
+    uint64_t m = __ballot(last);
+    int r = item - total0;
+    if (r >= 0 && r < __popcll(m)) {
+      for (int bit = 31 - __clz(p.partition_tokens); bit >= 0; --bit) {
+        const uint64_t ones = __ballot((rest >> bit) & 1) & m;
+        const int c = __popcll(ones);
+        if (r < c) {
+          m = ones;
+        } else {
+          r -= c;
+          m &= ~ones;
+        }
+      }
+      // m: the lanes of the selected length; the item is the r-th of them.
+      if (((m >> lane) & 1) && __popcll(m & ((1ull << lane) - 1)) == r) found = make_int2(lane, n - 1);
+    }
   }
   __syncthreads();
   *w = found;
@@ -1175,16 +1196,17 @@ __global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(2
 
 // The work list: one item per (sequence, row block) of every sequence with
 // more than one query, or per (sequence, partition) for a sequence whose rows
-// fit one block.  Two classes, in sequence order within each: first every
-// item but the last partition of a cut sequence (a sequence's last row blocks,
-// the ones that see the most tokens, first), then those last partitions, the
-// only ones shorter than the partition length.  Workgroups are placed on the
-// CUs in list order, so the short items spread over the CUs instead of
-// leaving some CUs with only full-length ones (70B-shaped verification over
-// an E4M3 cache, 16 sequences: 50.5 -> 46.1 us; 32: 80.2 -> 79.2; 64: 155.6
-// -> 151.9; the bits do not change).  One workgroup scans the sequences in
-// chunks of its size, once per class; items past the list's capacity (only
-// possible when query ranges overlap) are dropped.
+// fit one block.  Two classes: first every item but the last partition of a
+// cut sequence, in sequence order (a sequence's last row blocks, the ones
+// that see the most tokens, first), then those last partitions, the only
+// ones shorter than the partition length: here in sequence order, in the
+// workgroups' own lookup (batches of at most 64 sequences) longest first.
+// Workgroups are placed on the CUs in list order, so the short items spread
+// over the CUs and the shortest land on the CUs that already hold the most
+// work, instead of some CUs holding only full-length items (an order of
+// items never changes the bits).  One workgroup scans the sequences in chunks
+// of its size, once per class; items past the list's capacity (only possible
+// when query ranges overlap) are dropped.
 template <int G>
 __global__ __launch_bounds__(256) void multi_query_schedule_kernel(MultiQueryParams p) {
   __shared__ int sums[256];
