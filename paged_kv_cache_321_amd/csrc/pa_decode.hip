@@ -188,6 +188,8 @@ hipError_t launch_decode(const DecodeLaunch& a) {
   p.query_start = a.query_start;
   p.num_query_rows = a.num_query_rows;
   p.min_context = a.query_start != nullptr ? 1 : 0;
+  p.order_by_length = a.seq_order == nullptr && !a.shared_pages && a.prefix_leader == nullptr &&
+                      a.num_seqs > 1 && a.num_seqs <= kOrderedSeqs;
   // Shared-prefix decode always runs on the matrix cores (one 16-column tile
   // holds the query heads of up to 16 / G sequences) and always merges.
   const bool shared = a.prefix_leader != nullptr;

@@ -320,6 +320,27 @@ def test_dispatch_order_changes_nothing(name, pt):
     assert torch.equal(a, c)
 
 
+@pytest.mark.parametrize("n", [2, 64, 65, 200, 256, 257])
+@pytest.mark.parametrize("hkv,group", [(4, 1), (2, 4)])
+def test_in_kernel_longest_first(n, hkv, group):
+    """Without seq_order a batch of at most 256 sequences (pages not shared)
+    is dispatched longest context first, each workgroup ranking the lengths
+    itself over up to four 64-lane windows (257 keeps the natural order):
+    rows are the bits of the natural order and match the oracle.  Contexts
+    0-600 with repeats (ties rank by index) and partitions of 64 tokens."""
+    spec = wl.Spec(f"rank{n}x{group}", hkv * group, hkv, 128, 16, "bf16", seed=97)
+    gen = torch.Generator().manual_seed(n)
+    ctx = torch.randint(0, 601, (n,), generator=gen).tolist()
+    ctx[n // 2] = ctx[0]
+    x = wl.build_inputs(spec, wl.uniform_plan(ctx, 16, gen, new_tokens=True))
+    a, _ = gpu_step(x, partition_tokens=64)
+    ident = torch.arange(n, dtype=torch.int32, device="cuda")
+    b, _ = gpu_step(x, partition_tokens=64, seq_order=ident)
+    assert torch.equal(a, b)
+    ref, _, _ = oracle_step(x)
+    assert_close(as_f64(a), ref, "bf16", spec.name)
+
+
 @pytest.mark.parametrize("name,pt", [("llama7b", 64), ("gqa70b", 1024)])
 def test_workspace_reuse(name, pt):
     """One caller-owned workspace serves repeated multi-partition calls."""
