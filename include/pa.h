@@ -263,7 +263,10 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
  * batch or on which physical blocks hold its pages.
  * seq_order: NULL, or a device int32 [num_seqs] permutation of 0..num_seqs-1
  * giving the order in which sequences are dispatched; longest contexts first
- * shortens the tail of a ragged batch.  It never changes a result.
+ * shortens the tail of a ragged batch.  It never changes a result.  With NULL,
+ * a batch of at most 256 sequences without PA_DECODE_SHARED_PAGES is
+ * dispatched longest context first (ties by index), ranked in the kernel from
+ * context_lens; other batches in index order.
  * Precondition: a permutation (entries outside [0, num_seqs) are skipped, and a
  * row whose index is missing is left unwritten).
  * workspace: device buffer of at least pa_decode_workspace_size(...) bytes with
