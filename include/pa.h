@@ -449,7 +449,9 @@ size_t pa_multi_query_workspace_size(int num_seqs, int num_query_tokens, int num
  * fit in 64 has its context cut into partitions of this many tokens, merged
  * by a second kernel; longer chunks are not cut.  The cut changes the
  * rounding of a row's result, so a caller that needs rows bitwise
- * independent of the rest of the batch passes a fixed partition_tokens.
+ * independent of the rest of the batch passes a fixed partition_tokens (and
+ * query ranges that cover every row of q: where rows belong to no sequence,
+ * a short sequence may run uncut, with the same result up to rounding).
  * workspace: at least pa_multi_query_workspace_size(...) bytes, 16-byte
  * aligned.
  * Preconditions (device values): query_start ranges inside [0, num_query_tokens],

@@ -82,6 +82,7 @@ struct MultiQueryParams {
                        // streaming kernel (0: none), the others in the ring kernel
   int one_ring;        // the two-tile ring kernel takes the 64-row blocks too (the
                        // one-tile kernel is not launched)
+  int whole_contexts;  // no sequence is cut into partitions (no merge launch)
   float scale_log2e;   // softmax scale * log2(e), times k_scale for fp8 caches
   float v_scale;       // multiplies the output (1 unless the cache holds fp8 codes)
 };
@@ -139,7 +140,7 @@ __device__ __forceinline__ MqBlock mq_block(const MultiQueryParams& p, int s, in
   if (b.bad) return b;
   const int last_row = min(b.rows, (b.rb + 1) * b.rpb) - 1;
   b.kv_end = b.ctx - b.qlen + last_row / G + 1;
-  if (nrb == 1 && b.kv_end > p.partition_tokens)
+  if (nrb == 1 && b.kv_end > p.partition_tokens && !p.whole_contexts)
     b.nparts = (b.kv_end + p.partition_tokens - 1) / p.partition_tokens;
   return b;
 }
@@ -1379,17 +1380,31 @@ __global__ __launch_bounds__(kMqReduceWaves * 64) void multi_query_reduce_rows_k
 
 template <typename TC, int D, int BS, int G>
 hipError_t launch_t(const MultiQueryLaunch& a, MultiQueryParams p) {
+  // When the query ranges cover every row of q, the shortest sequence has at
+  // least num_query_tokens - (num_seqs - 1) * max_query_len queries.  Shapes
+  // that bound excludes launch nothing for them: a batch whose sequences all
+  // have more than 64 rows cuts no context (only single-block sequences are
+  // cut) and launches no merge kernel, one whose sequences all have more than
+  // the streaming kernel's rows launches no streaming kernel (an empty grid
+  // of 4.7 us after the ring kernel on the 70B verification shape over an
+  // E4M3 cache).  Ranges that leave rows to no sequence can break the bound;
+  // the kernels then serve the short sequences on the ring, uncut, which
+  // computes the same rows (their rounding may differ).
+  const int64_t min_rows =
+      ((int64_t)a.num_query_tokens - (int64_t)(a.num_seqs - 1) * a.max_query_len) * G;
+  p.whole_contexts = a.max_parts <= 1 || min_rows > kRowsPerBlock;
   // E4M3 caches: sequences whose rows fit two 16-row tiles stream on the
   // decode layout (multi_query_stream_kernel), when a partition holds at most
   // 256 pages (one page id per lane and wave).  The choice depends on the
-  // sequence and the partition length alone, so with a fixed partition length
-  // a sequence's rows are the same bits in any batch.  Measured on the 70B
-  // verification shape, 32 sequences, default partitions: E4M3 with 1-4
-  // queries 72-83 us against 87-98 us on the ring; with 6 queries (three
-  // tiles) 119 against 106, and bf16 at every query length 117-144 against
-  // 104-120, so those stay on the ring.
+  // sequence and the partition length alone (with ranges that cover every
+  // row), so with a fixed partition length a sequence's rows are the same
+  // bits in any batch.  Measured on the 70B verification shape, 32
+  // sequences, default partitions: E4M3 with 1-4 queries 72-83 us against
+  // 87-98 us on the ring; with 6 queries (three tiles) 119 against 106, and
+  // bf16 at every query length 117-144 against 104-120, so those stay on the
+  // ring.
   constexpr int kStreamRows = sizeof(TC) == 1 ? 32 : 0;
-  p.stream_rows = a.partition_tokens <= 256 * BS ? kStreamRows : 0;
+  p.stream_rows = a.partition_tokens <= 256 * BS && min_rows <= kStreamRows ? kStreamRows : 0;
   const int rows = a.max_query_len * G;  // rows of the longest sequence
   // Up to 64 sequences each workgroup finds its own work item (one wave's
   // scan, no schedule launch: 70B verification shape, bf16, 107.6 -> 104.5
@@ -1467,12 +1482,7 @@ hipError_t launch_t(const MultiQueryLaunch& a, MultiQueryParams p) {
       if (e != hipSuccess) return e;
     }
   }
-  // Only sequences of at most one 64-row block are cut into partitions; the
-  // shortest sequence has at least num_query_tokens - (num_seqs - 1) *
-  // max_query_len queries, so a batch of long chunks alone has nothing to
-  // merge and launches no merge kernel.
-  const int64_t min_queries = (int64_t)a.num_query_tokens - (int64_t)(a.num_seqs - 1) * a.max_query_len;
-  if (a.max_parts <= 1 || min_queries * G > kRowsPerBlock) return hipSuccess;
+  if (p.whole_contexts) return hipSuccess;  // nothing to merge
   // Verification batches (every sequence one block) merge on the 16-wave
   // kernel, whose loads go out in one round trip (70B verification shape:
   // 4.7 us against 8.3); other batches, where most workgroups exit at once,

@@ -383,6 +383,32 @@ def test_every_work_item_runs(kv, n):
     assert_close(as_f64(out), ref, "bf16", spec.name)
 
 
+@pytest.mark.parametrize("kv,hkv,group", [("bf16", 4, 1), ("fp8", 2, 8)])
+def test_rows_of_no_sequence(kv, hkv, group):
+    """query_start may leave rows of q to no sequence.  The host's bound on
+    the shortest sequence (num_query_tokens - (num_seqs - 1) * max_query_len
+    queries) then does not hold, and a short sequence must still be computed:
+    3 queries over 3000 tokens beside a 100-query chunk, with 97 rows of no
+    sequence after them, at partitions of 256 tokens (bf16: one-tile ring;
+    E4M3 at G = 8: the short rows would otherwise stream)."""
+    spec = wl.Spec(f"mqgap{kv}", hkv * group, hkv, 128, 16, "bf16", seed=99,
+                   kv_dtype=None if kv == "bf16" else kv, **wl.fp8_scales(kv))
+    gen = torch.Generator().manual_seed(14)
+    x = wl.build_inputs(spec, wl.multi_query_plan([2000, 3000], [100, 3], 16, gen))
+    t = on_device(x)
+    binding.pa_reshape_and_cache(t["key"], t["value"], t["k_cache"], t["v_cache"], t["slot_mapping"],
+                                 k_scale=x.k_scale, v_scale=x.v_scale)
+    extra = torch.randn(97, spec.num_heads, spec.head_dim, generator=gen).to(torch.bfloat16).cuda()
+    q = torch.cat([t["q"], extra]).contiguous()
+    out = torch.full_like(q, float("nan"))
+    binding.pa_multi_query(out, q, t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                           x.query_start.to("cuda").clone(), x.scale, x.max_context_len, 100,
+                           partition_tokens=256, k_scale=x.k_scale, v_scale=x.v_scale)
+    torch.cuda.synchronize()
+    ref, _, _ = oracle_mq_step(x)
+    assert_close(as_f64(out[: x.q.shape[0]]), ref, "bf16", spec.name)
+
+
 @pytest.mark.parametrize("h,hkv,bs,kv", [(40, 40, 16, "bf16"), (64, 8, 32, "bf16"), (64, 8, 32, "fp8")])
 def test_pool_past_2g_elements(h, hkv, bs, kv):
     """Every page of the batch lies past 2^31 elements of a 2.29e9-element
