@@ -28,7 +28,7 @@ struct DecodeLaunch {
   const int32_t* block_tables;
   int max_blocks_per_seq;
   const int32_t* context_lens;
-  const int32_t* seq_order;  // null = natural order
+  const int32_t* seq_order;  // null: the kernels choose (longest first for small batches)
   int num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks;
   int max_context_len;
   float scale;
