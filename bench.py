@@ -58,8 +58,8 @@ for _n in ("llama7b", "llama13b", "gqa70b", "beam", "specdec70b", "chunked13b"):
 # Two long sequences of the GQA 70B shape have too few (sequence, kv head,
 # partition) workgroups to fill the chip at the fixed partition length;
 # "+fill" runs the same step at the batch-shaped length (PA_PARTITION_FILL).
-# Verification of 4 drafted tokens over an E4M3 cache (32 rows per sequence)
-# runs on the streaming multi-query kernel.
+# Verification of 4 drafted tokens over an E4M3 cache (32 rows per sequence):
+# the shortest verification rows of the 70B shape.
 # "chunked13b_chunks" keeps only the two prefill chunks of the chunked-prefill
 # batch (no decode rows, so no side-stream launch): the multi-query tile
 # kernel alone, compute-bound.

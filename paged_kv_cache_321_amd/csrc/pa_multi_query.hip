@@ -1393,17 +1393,22 @@ hipError_t launch_t(const MultiQueryLaunch& a, MultiQueryParams p) {
   const int64_t min_rows =
       ((int64_t)a.num_query_tokens - (int64_t)(a.num_seqs - 1) * a.max_query_len) * G;
   p.whole_contexts = a.max_parts <= 1 || min_rows > kRowsPerBlock;
-  // E4M3 caches: sequences whose rows fit two 16-row tiles stream on the
-  // decode layout (multi_query_stream_kernel), when a partition holds at most
-  // 256 pages (one page id per lane and wave).  The choice depends on the
-  // sequence and the partition length alone (with ranges that cover every
-  // row), so with a fixed partition length a sequence's rows are the same
-  // bits in any batch.  Measured on the 70B verification shape, 32
-  // sequences, default partitions: E4M3 with 1-4 queries 72-83 us against
-  // 87-98 us on the ring; with 6 queries (three tiles) 119 against 106, and
-  // bf16 at every query length 117-144 against 104-120, so those stay on the
-  // ring.
-  constexpr int kStreamRows = sizeof(TC) == 1 ? 32 : 0;
+  // E4M3 caches at head_dim 64, or without grouping: sequences whose rows fit
+  // two 16-row tiles stream on the decode layout (multi_query_stream_kernel),
+  // when a partition holds at most 256 pages (one page id per lane and wave).
+  // The choice depends on the shape, the sequence and the partition length
+  // alone (with ranges that cover every row), so with a fixed partition
+  // length a sequence's rows are the same bits in any batch.  Measured over
+  // E4M3, 32 sequences of 1024-8192 tokens, default partitions, streaming
+  // against the ring: head_dim 64 at G = 8, 4 queries 46.7 against 49.6 us
+  // (block size 32: 43.9 / 48.3), G = 4 with 2 queries 37.6 / 43.3; G = 1
+  // (40 heads) with 2-4 queries 283-289 / 292-297 (with 32 rows 373 / 345).
+  // At head_dim 128 with G >= 2 the 64-token E4M3 ring, with its K codes
+  // read in place, wins: G = 8 with 1-4 queries 68.8-71.3 / 63.2-65.1 (block
+  // size 32: 96.4 / 70.8), G = 4 and 2 with 8-32 rows 70.6-80.5 / 64.5-71.2.
+  // bf16 stays on the ring at every query length (117-144 us against 104-120
+  // when last measured).
+  constexpr int kStreamRows = sizeof(TC) == 1 && (D == 64 || G == 1) ? 32 : 0;
   p.stream_rows = a.partition_tokens <= 256 * BS && min_rows <= kStreamRows ? kStreamRows : 0;
   const int rows = a.max_query_len * G;  // rows of the longest sequence
   // Up to 64 sequences each workgroup finds its own work item (one wave's

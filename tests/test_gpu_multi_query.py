@@ -97,11 +97,6 @@ def test_shapes_single_block(h, hkv, d, bs):
     check_mq(x, tiles_only=True)
 
 
-def stream_rows(kv):
-    """Rows of a sequence the streaming kernel takes (E4M3 caches only)."""
-    return 32 if kv == "fp8" else 0
-
-
 def stream_case(h, hkv, d, bs, cap, kv="bf16", seed=0):
     """Sequences of at most `cap` rows (query lengths up to cap / G) over ragged
     contexts, one of them a single query, one empty."""
@@ -120,8 +115,9 @@ def stream_case(h, hkv, d, bs, cap, kv="bf16", seed=0):
 def test_shapes_stream(h, hkv, d, bs, kv):
     """Verification-shaped batches: at most 16, 32 and 48 rows per sequence,
     with and without partitions, single queries in the tiles too.  Over an
-    E4M3 cache the first two run on the streaming kernel at one and two
-    16-row tiles, the third beside the ring kernel; bf16 runs on the ring."""
+    E4M3 cache at head_dim 64 or G = 1 the first two run on the streaming
+    kernel at one and two 16-row tiles, the third beside the ring kernel;
+    E4M3 at head_dim 128 with G >= 2, and bf16, run on the ring."""
     for cap in (16, 32, 48):
         if cap < h // hkv:
             continue
@@ -134,12 +130,12 @@ def test_shapes_stream(h, hkv, d, bs, kv):
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_stream_partition_of_256_pages(kv):
     """A partition of exactly 256 pages (64 per wave, the streaming kernel's
-    bound) and one page more, cut in two; the 48-row sequence beside them runs
-    on the ring."""
+    bound) and one page more, cut in two, at G = 1 (E4M3: streamed); the
+    40-row sequence beside them runs on the ring."""
     bs = 16
-    spec = wl.Spec(f"mqs256{kv}", 64, 8, 128, bs, "bf16", seed=77,
+    spec = wl.Spec(f"mqs256{kv}", 8, 8, 128, bs, "bf16", seed=77,
                    kv_dtype=None if kv == "bf16" else kv, **wl.fp8_scales(kv))
-    plan = wl.multi_query_plan([256 * bs, 256 * bs + 5, 90], [4, 2, 6], bs,
+    plan = wl.multi_query_plan([256 * bs, 256 * bs + 5, 90], [4, 2, 40], bs,
                                torch.Generator().manual_seed(8))
     check_mq(wl.build_inputs(spec, plan), partition_tokens=256 * bs)
 
@@ -292,8 +288,8 @@ def test_fixed_partitions_batch_invariant(kv, pt):
     one tile alone) beside the 120-row one on the ring.  In the batch the
     other sequences run on the three-stage ring, alone on the two-stage one,
     which split a partition of 8 (or 5) steps differently between unmasked and
-    masked steps."""
-    spec = wl.Spec(f"mqinv{kv}", 32, 8, 128, 16, "bf16", seed=91,
+    masked steps.  Head_dim 64, where E4M3 verification rows stream."""
+    spec = wl.Spec(f"mqinv{kv}", 32, 8, 64, 16, "bf16", seed=91,
                    kv_dtype=None if kv == "bf16" else kv, **wl.fp8_scales(kv))
     plan = wl.multi_query_plan([900, 2500, 40, 1300, 700], [6, 5, 1, 30, 3], 16,
                                torch.Generator().manual_seed(4))
@@ -383,22 +379,22 @@ def test_every_work_item_runs(kv, n):
     assert_close(as_f64(out), ref, "bf16", spec.name)
 
 
-@pytest.mark.parametrize("kv,hkv,group", [("bf16", 4, 1), ("fp8", 2, 8)])
-def test_rows_of_no_sequence(kv, hkv, group):
+@pytest.mark.parametrize("kv,hkv,group,d", [("bf16", 4, 1, 128), ("fp8", 2, 8, 64)])
+def test_rows_of_no_sequence(kv, hkv, group, d):
     """query_start may leave rows of q to no sequence.  The host's bound on
     the shortest sequence (num_query_tokens - (num_seqs - 1) * max_query_len
     queries) then does not hold, and a short sequence must still be computed:
     3 queries over 3000 tokens beside a 100-query chunk, with 97 rows of no
     sequence after them, at partitions of 256 tokens (bf16: one-tile ring;
-    E4M3 at G = 8: the short rows would otherwise stream)."""
-    spec = wl.Spec(f"mqgap{kv}", hkv * group, hkv, 128, 16, "bf16", seed=99,
+    E4M3 at G = 8 and head_dim 64: the short rows would otherwise stream)."""
+    spec = wl.Spec(f"mqgap{kv}", hkv * group, hkv, d, 16, "bf16", seed=99,
                    kv_dtype=None if kv == "bf16" else kv, **wl.fp8_scales(kv))
     gen = torch.Generator().manual_seed(14)
     x = wl.build_inputs(spec, wl.multi_query_plan([2000, 3000], [100, 3], 16, gen))
     t = on_device(x)
     binding.pa_reshape_and_cache(t["key"], t["value"], t["k_cache"], t["v_cache"], t["slot_mapping"],
                                  k_scale=x.k_scale, v_scale=x.v_scale)
-    extra = torch.randn(97, spec.num_heads, spec.head_dim, generator=gen).to(torch.bfloat16).cuda()
+    extra = torch.randn(97, spec.num_heads, d, generator=gen).to(torch.bfloat16).cuda()
     q = torch.cat([t["q"], extra]).contiguous()
     out = torch.full_like(q, float("nan"))
     binding.pa_multi_query(out, q, t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
